@@ -1,0 +1,109 @@
+/*
+ * oracle.h -- plain, slow CPU oracle for the decode-time weight-only
+ * quantized linear layer  y = x . dequant(W)^T (. per-row scale).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or constant with the HIP library; neither includes the other.
+ *
+ * Sources (the pages):
+ *  [P1] executorch "backends/cuda/tests/test_int4_quantized_gemm.py"
+ *       (the decode-sized INT4 GEMM test file): `_packed_with_dense`
+ *       (QuantConfig bits=4, group_size=32, symmetric=False, method="min_max"),
+ *       the module docstring and `_dequant_matmul` ("dequant + F.linear"
+ *       reference), `_check_close` (tolerance class), and
+ *       `Int4QuantizedGemmPrecisionTest` (W4A8 against the W4A16 reference).
+ *  [P3] gpt-fast issue #114 "Question about the generated code of
+ *       WeightOnlyInt8Linear": `WeightOnlyInt8Linear.forward`
+ *       (F.linear(x, W.to(x.dtype)) * scales).
+ *
+ * Arithmetic: IEEE-754 binary32/binary64, round-to-nearest-even, no FMA
+ * contraction (built with -ffp-contract=off), no fast-math, denormals kept.
+ * Products of a bf16 activation and a dequantized weight are exact in
+ * binary64, so the GEMM results below are the exact dot products up to one
+ * binary64 rounding per addition (ascending k).
+ *
+ * All arrays are host memory owned by the caller, row-major and contiguous.
+ * bf16 and fp16 values travel as their uint16 bit patterns.
+ */
+#ifndef QGEMM_ORACLE_H
+#define QGEMM_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- number formats, decoded from the IEEE-754 bit layout ---- */
+double orc_bf16_to_double(uint16_t bits);
+double orc_fp16_to_double(uint16_t bits);
+
+/* ---- INT4 group-32 asymmetric min-max quantizer ([P1] _packed_with_dense) ----
+ * w: bf16 [n, k], k % 32 == 0.  Outputs the canonical (unpacked) form:
+ *   codes  uint8  [n, k]      q in 0..15
+ *   scales fp16   [n, k/32]   bit patterns
+ *   zeros  uint8  [n, k/32]   zp in 0..15
+ * Returns the OR of the per-group flags: 1 = a non-finite weight (that group
+ * gets codes 0, scale NaN 0x7E00, zp 0), 2 = range above 15*65504 (scale
+ * saturated to 65504). */
+int orc_quantize_int4_g32(const uint16_t *w, int64_t n, int64_t k,
+                          uint8_t *codes, uint16_t *scales, uint8_t *zeros);
+
+/* One group of 32 values (exposed for the hand-worked pins). */
+int orc_quantize_group32(const uint16_t *w32, uint16_t *scale, uint8_t *zp,
+                         uint8_t *q32);
+
+/* ---- packed tile layout (own format, version 1) ----
+ * Tile = 64 rows x 256 k = 8 groups per row, 9472 bytes:
+ *   [0, 8192)     codes: the 16-byte chunk of (group j, row r) at (j*64 + r)*16
+ *   [8192, 9216)  fp16 scales: row r at 8192 + r*16, group j at +2*j
+ *   [9216, 9472)  zero points: row r's 32-bit LE word at 9216 + r*4,
+ *                 group j in bits [4j, 4j+4)
+ * Inside a chunk, LE dword d holds k_local = 8d+e at nibble position
+ * p = (e & 1)*4 + (e >> 1) (bits [4p, 4p+4)).
+ * Tiles are ordered row-block major: tile = rb*(k/256) + kt.
+ * Rows n >= N of the last row block are zero (codes 0, scale +0, zp 0). */
+int64_t orc_int4_packed_bytes(int64_t n, int64_t k);
+void orc_pack_int4(const uint8_t *codes, const uint16_t *scales,
+                   const uint8_t *zeros, int64_t n, int64_t k, uint8_t *packed);
+void orc_unpack_int4(const uint8_t *packed, int64_t n, int64_t k,
+                     uint8_t *codes, uint16_t *scales, uint8_t *zeros);
+
+/* ---- W4A16: y[m, n] = sum_k x[m,k] * (q[n,k] - zp[n,g]) * s[n,g] ----
+ * ([P1] module docstring and `_dequant_matmul`: dequant then F.linear.)
+ * x bf16 [m, k]; y double [m, n]; rows of W split over `threads` threads. */
+void orc_qgemm_w4a16(const uint16_t *x, int64_t m, int64_t k,
+                     const uint8_t *codes, const uint16_t *scales,
+                     const uint8_t *zeros, int64_t n, double *y, int threads);
+
+/* ---- INT8 per-output-channel symmetric quantizer ----
+ * s[n] = smallest bf16 with 127*s >= max_k |w[n,k]| (1.0 for an all-zero
+ * row); q = clamp(rint(w / s), -127, 127) in binary32.  Returns flag 1 if a
+ * row held a non-finite value (that row: q 0, scale NaN 0x7FC0). */
+int orc_quantize_int8_rowwise(const uint16_t *w, int64_t n, int64_t k,
+                              int8_t *q, uint16_t *scales);
+
+/* ---- W8A16 ([P3] WeightOnlyInt8Linear.forward):
+ * y[m, n] = (sum_k x[m,k] * W[n,k]) * scale[n];  W int8 [n, k], scale bf16 [n]. */
+void orc_qgemm_w8a16(const uint16_t *x, int64_t m, int64_t k, const int8_t *w,
+                     const uint16_t *scales, int64_t n, double *y, int threads);
+
+/* ---- W4A8: per-row symmetric absmax int8 activations ----
+ * a = max_k |x[m,k]|; a == 0 gives xq = 0, sx = 0.  Otherwise
+ * inv = 127/a and sx = a/127 (binary32 divisions), xq = clamp(rint(x*inv),
+ * -127, 127) with a single binary32 multiply. */
+void orc_actquant_int8(const uint16_t *x, int64_t m, int64_t k, int8_t *xq,
+                       float *sx);
+/* y[m,n] = sx[m] * sum_g s[n,g] * I[m,n,g],
+ * I[m,n,g] = sum_{k in g} xq[m,k] * (q[n,k] - zp[n,g])  (exact integer). */
+void orc_qgemm_w4a8(const uint16_t *x, int64_t m, int64_t k,
+                    const uint8_t *codes, const uint16_t *scales,
+                    const uint8_t *zeros, int64_t n, double *y, int threads);
+
+/* Thread count the machine offers (for the CPU baseline). */
+int orc_hardware_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,430 @@
+/*
+ * qgemm_oracle.c -- plain CPU oracle (see oracle.h for the contract).
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and the
+ * benchmark's CPU-baseline leg; never by the product path.  Parity of the
+ * functions below is pinned by tests/test_oracle_*.py against hand-worked
+ * groups, closed forms, invariants and exact brute force.
+ *
+ * Written for obviousness, not speed: one element at a time, ascending k,
+ * binary64 accumulation.  Build: gcc -O2 -std=c11 -ffp-contract=off.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ------------------------------------------------------------------ */
+/* Number formats, from the IEEE-754 bit layouts.                      */
+/* ------------------------------------------------------------------ */
+
+/* bf16: 1 sign, 8 exponent (bias 127), 7 fraction bits = the top half of a
+ * binary32 pattern, so the conversion is exact. */
+double orc_bf16_to_double(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static float bf16_to_float(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* fp16 (binary16): 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double orc_fp16_to_double(uint16_t bits) {
+    int sign = bits >> 15;
+    int e = (bits >> 10) & 0x1f;
+    int frac = bits & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)frac, -24);               /* zero / subnormal */
+    else if (e == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + frac), e - 25);   /* 1.frac * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+#define FP16_MAX_BITS 0x7BFFu   /* 65504 */
+#define FP16_ONE_BITS 0x3C00u
+#define FP16_NAN_BITS 0x7E00u
+#define BF16_MAX_BITS 0x7F7Fu
+#define BF16_ONE_BITS 0x3F80u
+#define BF16_NAN_BITS 0x7FC0u
+
+/* Smallest positive finite fp16 s with mult*s >= r (r > 0, r <= mult*65504).
+ * Positive finite fp16 patterns 0x0001..0x7BFF increase with their value,
+ * so a binary search over the patterns finds it; mult*s is exact in binary64. */
+static uint16_t smallest_fp16_covering(double r, double mult) {
+    uint32_t lo = 1, hi = FP16_MAX_BITS;
+    while (lo < hi) {
+        uint32_t mid = (lo + hi) / 2;
+        if (mult * orc_fp16_to_double((uint16_t)mid) >= r)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    return (uint16_t)lo;
+}
+
+/* Same for bf16 (positive finite patterns 0x0001..0x7F7F). */
+static uint16_t smallest_bf16_covering(double r, double mult) {
+    uint32_t lo = 1, hi = BF16_MAX_BITS;
+    while (lo < hi) {
+        uint32_t mid = (lo + hi) / 2;
+        if (mult * orc_bf16_to_double((uint16_t)mid) >= r)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    return (uint16_t)lo;
+}
+
+static float clampf(float v, float lo, float hi) {
+    return v < lo ? lo : (v > hi ? hi : v);
+}
+
+/* ------------------------------------------------------------------ */
+/* INT4 group-32 asymmetric min-max quantizer.                         */
+/* [P1] `_packed_with_dense`: QuantConfig(bits=4, group_size=32,        */
+/* symmetric=False, method="min_max").  The pages print no formula; the */
+/* reading (range widened to hold 0, 15 steps, fp16 scale rounded up so */
+/* every dequantized value is within half a step, integer zero point,   */
+/* round-half-even, round then add the zero point) is recorded in the   */
+/* design notes.                                                        */
+/* ------------------------------------------------------------------ */
+int orc_quantize_group32(const uint16_t *w32, uint16_t *scale, uint8_t *zp,
+                         uint8_t *q32) {
+    float v[32];
+    float lo = 0.0f, hi = 0.0f;   /* the range always holds 0 */
+    int nonfinite = 0;
+    for (int i = 0; i < 32; i++) {
+        v[i] = bf16_to_float(w32[i]);
+        if (!isfinite(v[i])) nonfinite = 1;
+        if (v[i] < lo) lo = v[i];
+        if (v[i] > hi) hi = v[i];
+    }
+    if (nonfinite) {
+        *scale = FP16_NAN_BITS;
+        *zp = 0;
+        for (int i = 0; i < 32; i++) q32[i] = 0;
+        return 1;
+    }
+    int flags = 0;
+    double r = (double)hi - (double)lo;   /* binary64 range */
+    uint16_t sbits;
+    if (r == 0.0) {
+        sbits = FP16_ONE_BITS;            /* all-zero group */
+    } else if (r > 15.0 * 65504.0) {
+        sbits = FP16_MAX_BITS;            /* saturate, flag it */
+        flags |= 2;
+    } else {
+        sbits = smallest_fp16_covering(r, 15.0);
+    }
+    float s = (float)orc_fp16_to_double(sbits);
+    float z = clampf(rintf(-lo / s), 0.0f, 15.0f);
+    for (int i = 0; i < 32; i++) {
+        float t = rintf(v[i] / s) + z;    /* round first, then add zp */
+        q32[i] = (uint8_t)clampf(t, 0.0f, 15.0f);
+    }
+    *scale = sbits;
+    *zp = (uint8_t)z;
+    return flags;
+}
+
+int orc_quantize_int4_g32(const uint16_t *w, int64_t n, int64_t k,
+                          uint8_t *codes, uint16_t *scales, uint8_t *zeros) {
+    int flags = 0;
+    int64_t groups = k / 32;
+    for (int64_t row = 0; row < n; row++)
+        for (int64_t g = 0; g < groups; g++)
+            flags |= orc_quantize_group32(w + row * k + g * 32,
+                                          scales + row * groups + g,
+                                          zeros + row * groups + g,
+                                          codes + row * k + g * 32);
+    return flags;
+}
+
+/* ------------------------------------------------------------------ */
+/* Packed tile layout, version 1 (our own format; see oracle.h).       */
+/* ------------------------------------------------------------------ */
+enum { T_ROWS = 64, T_GROUPS = 8, T_K = 256, T_CODE_BYTES = 8192,
+       T_SCALE_OFF = 8192, T_ZERO_OFF = 9216, T_BYTES = 9472 };
+
+int64_t orc_int4_packed_bytes(int64_t n, int64_t k) {
+    int64_t row_blocks = (n + T_ROWS - 1) / T_ROWS;
+    return row_blocks * (k / T_K) * (int64_t)T_BYTES;
+}
+
+/* Byte offset and nibble shift of code (row r, k-in-tile kk) inside a tile. */
+static void code_position(int r, int kk, int64_t *byte, int *shift) {
+    int j = kk / 32;          /* group in tile */
+    int kl = kk % 32;         /* k in group */
+    int d = kl / 8;           /* dword in chunk */
+    int e = kl % 8;
+    int p = (e & 1) * 4 + (e >> 1);   /* nibble position in the dword */
+    *byte = (int64_t)(j * T_ROWS + r) * 16 + d * 4 + p / 2;
+    *shift = (p % 2) * 4;
+}
+
+void orc_pack_int4(const uint8_t *codes, const uint16_t *scales,
+                   const uint8_t *zeros, int64_t n, int64_t k, uint8_t *packed) {
+    int64_t kt_count = k / T_K, groups = k / 32;
+    int64_t total = orc_int4_packed_bytes(n, k);
+    memset(packed, 0, (size_t)total);
+    for (int64_t row = 0; row < n; row++) {
+        int64_t rb = row / T_ROWS;
+        int r = (int)(row % T_ROWS);
+        for (int64_t kt = 0; kt < kt_count; kt++) {
+            uint8_t *tile = packed + (rb * kt_count + kt) * T_BYTES;
+            for (int kk = 0; kk < T_K; kk++) {
+                int64_t byte; int shift;
+                code_position(r, kk, &byte, &shift);
+                tile[byte] |= (uint8_t)((codes[row * k + kt * T_K + kk] & 0xF) << shift);
+            }
+            for (int j = 0; j < T_GROUPS; j++) {
+                int64_t g = kt * T_GROUPS + j;
+                uint16_t s = scales[row * groups + g];
+                tile[T_SCALE_OFF + r * 16 + j * 2] = (uint8_t)(s & 0xFF);
+                tile[T_SCALE_OFF + r * 16 + j * 2 + 1] = (uint8_t)(s >> 8);
+                tile[T_ZERO_OFF + r * 4 + j / 2] |=
+                    (uint8_t)((zeros[row * groups + g] & 0xF) << ((j % 2) * 4));
+            }
+        }
+    }
+}
+
+void orc_unpack_int4(const uint8_t *packed, int64_t n, int64_t k,
+                     uint8_t *codes, uint16_t *scales, uint8_t *zeros) {
+    int64_t kt_count = k / T_K, groups = k / 32;
+    for (int64_t row = 0; row < n; row++) {
+        int64_t rb = row / T_ROWS;
+        int r = (int)(row % T_ROWS);
+        for (int64_t kt = 0; kt < kt_count; kt++) {
+            const uint8_t *tile = packed + (rb * kt_count + kt) * T_BYTES;
+            for (int kk = 0; kk < T_K; kk++) {
+                int64_t byte; int shift;
+                code_position(r, kk, &byte, &shift);
+                codes[row * k + kt * T_K + kk] = (tile[byte] >> shift) & 0xF;
+            }
+            for (int j = 0; j < T_GROUPS; j++) {
+                int64_t g = kt * T_GROUPS + j;
+                scales[row * groups + g] =
+                    (uint16_t)(tile[T_SCALE_OFF + r * 16 + j * 2] |
+                               (tile[T_SCALE_OFF + r * 16 + j * 2 + 1] << 8));
+                zeros[row * groups + g] =
+                    (tile[T_ZERO_OFF + r * 4 + j / 2] >> ((j % 2) * 4)) & 0xF;
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* A tiny row-parallel driver: rows of W split into contiguous ranges.  */
+/* ------------------------------------------------------------------ */
+typedef void (*row_fn)(void *ctx, int64_t row_begin, int64_t row_end);
+struct job { row_fn fn; void *ctx; int64_t begin, end; };
+
+static void *run_job(void *arg) {
+    struct job *j = (struct job *)arg;
+    j->fn(j->ctx, j->begin, j->end);
+    return NULL;
+}
+
+static void parallel_rows(row_fn fn, void *ctx, int64_t n, int threads) {
+    if (threads < 1) threads = 1;
+    if (threads > 512) threads = 512;
+    if (threads == 1 || n < 2 * threads) {
+        fn(ctx, 0, n);
+        return;
+    }
+    pthread_t tid[512];
+    struct job jobs[512];
+    int started = 0;
+    for (int t = 0; t < threads; t++) {
+        jobs[t].fn = fn;
+        jobs[t].ctx = ctx;
+        jobs[t].begin = n * t / threads;
+        jobs[t].end = n * (t + 1) / threads;
+        if (pthread_create(&tid[t], NULL, run_job, &jobs[t]) == 0)
+            started = t + 1;
+        else
+            break;
+    }
+    /* Whatever could not be started runs here. */
+    if (started < threads) fn(ctx, jobs[started].begin, n);
+    for (int t = 0; t < started; t++) pthread_join(tid[t], NULL);
+}
+
+int orc_hardware_threads(void) {
+    long c = sysconf(_SC_NPROCESSORS_ONLN);
+    return c > 0 ? (int)c : 1;
+}
+
+/* ------------------------------------------------------------------ */
+/* W4A16: dequant, then the plain dot product ([P1] `_dequant_matmul`). */
+/* ------------------------------------------------------------------ */
+struct w4_ctx {
+    const uint16_t *x; int64_t m, k;
+    const uint8_t *codes; const uint16_t *scales; const uint8_t *zeros;
+    int64_t n; double *y;
+};
+
+static void w4a16_rows(void *p, int64_t b, int64_t e) {
+    struct w4_ctx *c = (struct w4_ctx *)p;
+    int64_t groups = c->k / 32;
+    for (int64_t row = b; row < e; row++)
+        for (int64_t mi = 0; mi < c->m; mi++) {
+            double acc = 0.0;
+            for (int64_t g = 0; g < groups; g++) {
+                double s = orc_fp16_to_double(c->scales[row * groups + g]);
+                int z = c->zeros[row * groups + g];
+                for (int64_t i = 0; i < 32; i++) {
+                    int64_t kk = g * 32 + i;
+                    int q = c->codes[row * c->k + kk];
+                    double wdq = (double)(q - z) * s;        /* dequant */
+                    acc += orc_bf16_to_double(c->x[mi * c->k + kk]) * wdq;
+                }
+            }
+            c->y[mi * c->n + row] = acc;
+        }
+}
+
+void orc_qgemm_w4a16(const uint16_t *x, int64_t m, int64_t k,
+                     const uint8_t *codes, const uint16_t *scales,
+                     const uint8_t *zeros, int64_t n, double *y, int threads) {
+    struct w4_ctx c = {x, m, k, codes, scales, zeros, n, y};
+    parallel_rows(w4a16_rows, &c, n, threads);
+}
+
+/* ------------------------------------------------------------------ */
+/* INT8 per-output-channel symmetric quantizer.                        */
+/* ------------------------------------------------------------------ */
+int orc_quantize_int8_rowwise(const uint16_t *w, int64_t n, int64_t k,
+                              int8_t *q, uint16_t *scales) {
+    int flags = 0;
+    for (int64_t row = 0; row < n; row++) {
+        const uint16_t *wr = w + row * k;
+        double amax = 0.0;
+        int nonfinite = 0;
+        for (int64_t i = 0; i < k; i++) {
+            double v = orc_bf16_to_double(wr[i]);
+            if (!isfinite(v)) nonfinite = 1;
+            if (fabs(v) > amax) amax = fabs(v);
+        }
+        if (nonfinite) {
+            flags |= 1;
+            scales[row] = BF16_NAN_BITS;
+            for (int64_t i = 0; i < k; i++) q[row * k + i] = 0;
+            continue;
+        }
+        uint16_t sbits = amax == 0.0 ? BF16_ONE_BITS
+                                     : smallest_bf16_covering(amax, 127.0);
+        float s = bf16_to_float(sbits);
+        for (int64_t i = 0; i < k; i++) {
+            float t = rintf(bf16_to_float(wr[i]) / s);
+            q[row * k + i] = (int8_t)clampf(t, -127.0f, 127.0f);
+        }
+        scales[row] = sbits;
+    }
+    return flags;
+}
+
+/* ------------------------------------------------------------------ */
+/* W8A16 ([P3] WeightOnlyInt8Linear.forward).                          */
+/* ------------------------------------------------------------------ */
+struct w8_ctx {
+    const uint16_t *x; int64_t m, k; const int8_t *w; const uint16_t *scales;
+    int64_t n; double *y;
+};
+
+static void w8a16_rows(void *p, int64_t b, int64_t e) {
+    struct w8_ctx *c = (struct w8_ctx *)p;
+    for (int64_t row = b; row < e; row++)
+        for (int64_t mi = 0; mi < c->m; mi++) {
+            double acc = 0.0;
+            for (int64_t kk = 0; kk < c->k; kk++)
+                acc += orc_bf16_to_double(c->x[mi * c->k + kk]) *
+                       (double)c->w[row * c->k + kk];
+            c->y[mi * c->n + row] = acc * orc_bf16_to_double(c->scales[row]);
+        }
+}
+
+void orc_qgemm_w8a16(const uint16_t *x, int64_t m, int64_t k, const int8_t *w,
+                     const uint16_t *scales, int64_t n, double *y, int threads) {
+    struct w8_ctx c = {x, m, k, w, scales, n, y};
+    parallel_rows(w8a16_rows, &c, n, threads);
+}
+
+/* ------------------------------------------------------------------ */
+/* W4A8 ([P1] Int4QuantizedGemmPrecisionTest: int8 activations held to */
+/* the W4A16 reference's precision class).                             */
+/* ------------------------------------------------------------------ */
+void orc_actquant_int8(const uint16_t *x, int64_t m, int64_t k, int8_t *xq,
+                       float *sx) {
+    for (int64_t mi = 0; mi < m; mi++) {
+        const uint16_t *xr = x + mi * k;
+        float a = 0.0f;
+        for (int64_t i = 0; i < k; i++) {
+            float v = fabsf(bf16_to_float(xr[i]));
+            if (v > a) a = v;
+        }
+        if (a == 0.0f) {
+            sx[mi] = 0.0f;
+            for (int64_t i = 0; i < k; i++) xq[mi * k + i] = 0;
+            continue;
+        }
+        float inv = 127.0f / a;
+        sx[mi] = a / 127.0f;
+        for (int64_t i = 0; i < k; i++) {
+            float t = rintf(bf16_to_float(xr[i]) * inv);
+            xq[mi * k + i] = (int8_t)clampf(t, -127.0f, 127.0f);
+        }
+    }
+}
+
+struct w4a8_ctx {
+    const int8_t *xq; const float *sx; int64_t m, k;
+    const uint8_t *codes; const uint16_t *scales; const uint8_t *zeros;
+    int64_t n; double *y;
+};
+
+static void w4a8_rows(void *p, int64_t b, int64_t e) {
+    struct w4a8_ctx *c = (struct w4a8_ctx *)p;
+    int64_t groups = c->k / 32;
+    for (int64_t row = b; row < e; row++)
+        for (int64_t mi = 0; mi < c->m; mi++) {
+            double acc = 0.0;
+            for (int64_t g = 0; g < groups; g++) {
+                int64_t isum = 0;     /* exact integer group dot */
+                int z = c->zeros[row * groups + g];
+                for (int64_t i = 0; i < 32; i++) {
+                    int64_t kk = g * 32 + i;
+                    isum += (int64_t)c->xq[mi * c->k + kk] *
+                            (int64_t)(c->codes[row * c->k + kk] - z);
+                }
+                acc += orc_fp16_to_double(c->scales[row * groups + g]) * (double)isum;
+            }
+            c->y[mi * c->n + row] = (double)c->sx[mi] * acc;
+        }
+}
+
+void orc_qgemm_w4a8(const uint16_t *x, int64_t m, int64_t k,
+                    const uint8_t *codes, const uint16_t *scales,
+                    const uint8_t *zeros, int64_t n, double *y, int threads) {
+    int8_t *xq = (int8_t *)malloc((size_t)(m * k));
+    float *sx = (float *)malloc((size_t)m * sizeof(float));
+    if (!xq || !sx) { free(xq); free(sx); abort(); }
+    orc_actquant_int8(x, m, k, xq, sx);
+    struct w4a8_ctx c = {xq, sx, m, k, codes, scales, zeros, n, y};
+    parallel_rows(w4a8_rows, &c, n, threads);
+    free(xq);
+    free(sx);
+}
