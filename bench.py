@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Benchmark: INT4-g32 W4A16 decode GEMV at M = 1 on 39936 x 6656 (one MI355X).
+
+One step = one call of the layer (host checks + the GEMV kernel, plus the
+split-K pass when the shape uses one) on one activation row.  Inputs are
+resident in HBM before the timed region.  Consecutive calls read different
+copies of the packed weight (ceil(1 GiB / bytes) copies), so the 256 MB
+Infinity Cache cannot serve a weight from the previous call; the K timed
+calls are captured once in a HIP graph and replayed, bracketed by device
+synchronizations, and timed with events on the stream the kernels run on.
+
+Effective weight bytes per call = N*K/2 (codes) + N*K/32 * 2.5 (fp16 scale +
+4-bit zero per group of 32), the packed buffer size.  The roofline is HBM
+(8 TB/s peak on MI355X).
+
+The CPU baseline leg times the plain C oracle (tests' reference) on this
+host's cores over a bounded sample of the same workload and checks the GPU
+result against it.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "µs/call and effective weight GB/s (% HBM peak) for INT4-g32 GEMV at M=1"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--n", type=int, default=39936)
+    p.add_argument("--k", type=int, default=6656)
+    p.add_argument("--m", type=int, default=1)
+    p.add_argument("--split", type=int, default=0, help="split-K (0 = library default)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="rough budget of CPU work for the oracle sample")
+    return p.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this layer is benchmarked "
+              "on a single MI355X and the multi-GPU sharding is a design note, not a run.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import gemm_decode_qgemm_amd as qg
+    import synthetic_inputs as si
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    n, k, m = args.n, args.k, args.m
+    if (n, k) in si.MODEL_SHAPES:
+        w_cpu, x_cpu = si.decode_inputs(n, k, m)
+    else:
+        w_cpu, x_cpu = si.int4_weight(n, k, n ^ k), si.activation(m, k, 9100 + m)
+    bytes_eff = qg.int4_packed_bytes(n, k)
+    split = args.split or qg.default_split_k(m, n, k)
+
+    packed0 = qg.quantize_int4_g32(w_cpu.to(dev))
+    copies = max(2, math.ceil((1 << 30) / bytes_eff))
+    packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
+    x = x_cpu.to(dev)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    ws_n = qg.workspace_bytes(m, n, k, split)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def call(i):
+        qg.qgemm_w4a16(x, packs[i % copies], n, split_k=split, out=y, workspace=ws)
+
+    # Eager warm-up (also loads the code object), then capture graphs.
+    for i in range(min(args.warmup, 20)):
+        call(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    g_warm, g_timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g_warm, stream=stream):
+            for i in range(max(args.warmup, 1)):
+                call(i)
+        with torch.cuda.graph(g_timed, stream=stream):
+            for i in range(args.steps):
+                call(i)
+    torch.cuda.synchronize()
+    y_first = None
+
+    with torch.cuda.stream(stream):
+        g_warm.replay()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        g_timed.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    us_call = ms_total * 1e3 / args.steps
+    gbs = bytes_eff / (us_call * 1e-6) / 1e9
+    y_first = y.clone()
+
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": us_call / 1e3,
+        "us_per_call": round(us_call, 3),
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"W4A16 INT4-g32 asymmetric GEMV {n}x{k} M={m}",
+            "n": n, "k": k, "m": m, "split_k": split, "bytes_eff_per_call": bytes_eff,
+            "codes_only_gbs": round((n * k / 2) / (us_call * 1e-6) / 1e9, 2),
+            "rotating_weight_copies": copies, "timing": "HIP graph of K calls, events on its stream",
+            "wall_s": round(wall, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, w_cpu, x_cpu, y_first, bytes_eff)
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(args, w_cpu, x_cpu, y_gpu, bytes_eff):
+    """Time the C oracle on the host's cores on a bounded sample of the same
+    workload (whole weight, M rows), and check the GPU output against it."""
+    import numpy as np
+
+    import oracle
+    import synthetic_inputs as si
+
+    threads = oracle.hardware_threads()
+    codes, scales, zeros, _ = oracle.quantize_int4_g32(si.bf16_bits(w_cpu))
+    xb = si.bf16_bits(x_cpu)
+    times = []
+    ref = None
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        ref = oracle.qgemm_w4a16(xb, codes, scales, zeros, threads=threads)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > args.cpu_seconds or len(times) >= 50:
+            break
+    t = float(np.median(times))
+    y = y_gpu.float().cpu().numpy().astype(np.float64)
+    err = np.abs(y - ref)
+    mean_ref = float(np.abs(ref).mean())
+    return {
+        "value": round(bytes_eff / t / 1e9, 3),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "us_per_call": round(t * 1e6, 1),
+        "sample": f"{len(times)} full calls ({args.n}x{args.k}, M={args.m}), median",
+        "gpu_vs_oracle": {"max_abs_err": float(err.max()),
+                          "mean_rel_err": float(err.mean() / mean_ref),
+                          "bound_max": 1e-2 * mean_ref + 1e-3},
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,23 @@
+"""MI355X (gfx950) decode-time weight-only quantized linear layer.
+
+y = x . dequant(W)^T (. per-row scale) for INT4 group-32 asymmetric weights
+(W4A16, W4A8) and INT8 per-channel weights (W8A16), M = 1..64 activation rows.
+The computation runs in the HIP library libqgemm.so (C ABI: include/qgemm.h);
+this package only binds it.
+"""
+from .binding import (  # noqa: F401
+    FLAG_NONFINITE,
+    FLAG_OVERFLOW,
+    QG_BF16,
+    QG_F32,
+    QGemmError,
+    default_split_k,
+    int4_packed_bytes,
+    qgemm_w4a8,
+    qgemm_w4a16,
+    qgemm_w8a16,
+    quantize_int4_g32,
+    quantize_int8_rowwise,
+    status_string,
+    workspace_bytes,
+)

@@ -1,0 +1,191 @@
+// api.hip -- the C ABI declared in include/qgemm.h: argument checks on the
+// host, then kernel launches on the caller's stream.
+//
+// Rules follow executorch test_int4_quantized_gemm.py,
+// Int4QuantizedGemmLegalityTest (every rule checked before anything is
+// launched; "K must be a multiple of 256"; "static M must be within" the
+// supported buckets, the largest being 64) and
+// Int4QuantizedGemmRulesTest.test_split_k_needs_one_k_tile_per_split
+// (a split is legal iff split <= K / 256).  The library never allocates and
+// never synchronizes.
+#include <stdint.h>
+
+#include "qg_common.h"
+#include "qgemm.h"
+
+namespace qg {
+hipError_t launch_quantize_int4_g32(const void* w, int64_t n, int64_t k, void* packed,
+                                    uint32_t* status, hipStream_t stream);
+hipError_t launch_quantize_int8_rowwise(const void* w, int64_t n, int64_t k, int8_t* q,
+                                        void* scales, uint32_t* status, hipStream_t stream);
+hipError_t launch_w4a16_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
+                             int y_f32, float* partial, int split, int waves, bool nt,
+                             hipStream_t stream);
+size_t w4a16_gemv_smem_bytes(int m, int k, int split, int waves);
+hipError_t launch_splitk_reduce(const float* partial, int split, int64_t mn, void* y, int y_f32,
+                                hipStream_t stream);
+}  // namespace qg
+
+// Launch shape of the M <= 4 GEMV (compile-time defaults; measured on MI355X).
+#ifndef QG_W4_WAVES
+#define QG_W4_WAVES 8
+#endif
+#ifndef QG_W4_NT
+#define QG_W4_NT 0
+#endif
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;   // n, k fit the kernels' int32 indexing
+constexpr size_t kMaxSmem = 64 * 1024;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int32_t check_nk(int64_t n, int64_t k) {
+  if (n < 1 || k < 1 || n > kMaxDim || k > kMaxDim) return QG_E_SHAPE;
+  if (k % QG_TILE_K != 0) return QG_E_K_MULTIPLE;
+  return QG_OK;
+}
+
+int32_t check_mnk(int64_t m, int64_t n, int64_t k) {
+  if (m < 1) return QG_E_SHAPE;
+  int32_t st = check_nk(n, k);
+  if (st != QG_OK) return st;
+  if (m > QG_MAX_M) return QG_E_M_RANGE;
+  return QG_OK;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? QG_OK : QG_E_HIP; }
+
+// Split-K default: the smallest legal split whose grid gives every one of the
+// 256 CUs a workgroup (row blocks x split >= 240), capped by K/256 and 8.
+int32_t default_split(int64_t m, int64_t n, int64_t k) {
+  (void)m;
+  const int64_t rbs = (n + QG_TILE_ROWS - 1) / QG_TILE_ROWS;
+  const int64_t kt = k / QG_TILE_K;
+  int32_t best = 1;
+  for (int32_t s = 1; s <= 8; s *= 2) {
+    if (s > kt) break;
+    best = s;
+    if (rbs * s >= 240) break;
+  }
+  return best;
+}
+
+int32_t resolve_split(int64_t m, int64_t n, int64_t k, int32_t split_k, int32_t* out) {
+  if (split_k == 0) {
+    *out = default_split(m, n, k);
+    return QG_OK;
+  }
+  if (split_k != 1 && split_k != 2 && split_k != 4 && split_k != 8) return QG_E_SPLIT;
+  if (split_k > k / QG_TILE_K) return QG_E_SPLIT;
+  *out = split_k;
+  return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qg_status_string(int32_t s) {
+  switch (s) {
+    case QG_OK: return "ok";
+    case QG_E_NULL: return "a required pointer is NULL";
+    case QG_E_SHAPE: return "m, n and k must be >= 1 (and fit the kernels' limits)";
+    case QG_E_K_MULTIPLE: return "K must be a multiple of 256";
+    case QG_E_M_RANGE: return "M must be within the supported buckets (1..64)";
+    case QG_E_SPLIT: return "split_k must be 0, 1, 2, 4 or 8 and at most K/256 (one K tile per split)";
+    case QG_E_BUFFER: return "a buffer (packed weight or workspace) is too small";
+    case QG_E_ALIGN: return "data pointers must be 16-byte aligned";
+    case QG_E_DTYPE: return "y_dtype must be QG_BF16 or QG_F32";
+    case QG_E_HIP: return "a HIP launch failed";
+    default: return "unknown qgemm status";
+  }
+}
+
+int64_t qg_int4_packed_bytes(int64_t n, int64_t k) {
+  int32_t st = check_nk(n, k);
+  if (st != QG_OK) return st;
+  return ((n + QG_TILE_ROWS - 1) / QG_TILE_ROWS) * (k / QG_TILE_K) * (int64_t)QG_TILE_BYTES;
+}
+
+int32_t qg_default_split_k(int64_t m, int64_t n, int64_t k) {
+  int32_t st = check_mnk(m, n, k);
+  if (st != QG_OK) return st;
+  return default_split(m, n, k);
+}
+
+int64_t qg_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k) {
+  int32_t st = check_mnk(m, n, k);
+  if (st != QG_OK) return st;
+  int32_t split;
+  st = resolve_split(m, n, k, split_k, &split);
+  if (st != QG_OK) return st;
+  return split > 1 ? (int64_t)split * m * n * 4 : 0;
+}
+
+int32_t quantize_int4_g32(const void* w_bf16, int64_t n, int64_t k, void* packed,
+                          int64_t packed_bytes, uint32_t* status_dev, void* stream) {
+  if (!w_bf16 || !packed) return QG_E_NULL;
+  int32_t st = check_nk(n, k);
+  if (st != QG_OK) return st;
+  if (packed_bytes < qg_int4_packed_bytes(n, k)) return QG_E_BUFFER;
+  if (!aligned16(w_bf16) || !aligned16(packed) || ((uintptr_t)status_dev & 3u)) return QG_E_ALIGN;
+  return hip_status(qg::launch_quantize_int4_g32(w_bf16, n, k, packed, status_dev,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+int32_t quantize_int8_rowwise(const void* w_bf16, int64_t n, int64_t k, int8_t* q,
+                              void* scale_bf16, uint32_t* status_dev, void* stream) {
+  if (!w_bf16 || !q || !scale_bf16) return QG_E_NULL;
+  int32_t st = check_nk(n, k);
+  if (st != QG_OK) return st;
+  if (n > 0x7fffffff) return QG_E_SHAPE;
+  if (!aligned16(w_bf16) || !aligned16(q) || !aligned16(scale_bf16) || ((uintptr_t)status_dev & 3u))
+    return QG_E_ALIGN;
+  return hip_status(qg::launch_quantize_int8_rowwise(w_bf16, n, k, q, scale_bf16, status_dev,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
+int32_t qgemm_w4a16(const void* x_bf16, int64_t m, int64_t k, const void* packed,
+                    int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype, int32_t split_k,
+                    void* ws, int64_t ws_bytes, void* stream) {
+  if (!x_bf16 || !packed || !y) return QG_E_NULL;
+  int32_t st = check_mnk(m, n, k);
+  if (st != QG_OK) return st;
+  if (y_dtype != QG_BF16 && y_dtype != QG_F32) return QG_E_DTYPE;
+  int32_t split;
+  st = resolve_split(m, n, k, split_k, &split);
+  if (st != QG_OK) return st;
+  if (packed_bytes < qg_int4_packed_bytes(n, k)) return QG_E_BUFFER;
+  const int64_t need_ws = split > 1 ? (int64_t)split * m * n * 4 : 0;
+  if (need_ws > 0 && (!ws || ws_bytes < need_ws)) return ws ? QG_E_BUFFER : QG_E_NULL;
+  if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || (ws && !aligned16(ws)))
+    return QG_E_ALIGN;
+  if (m > 4) return QG_E_M_RANGE;   // the MFMA path for 5..64 is not built yet
+  if (qg::w4a16_gemv_smem_bytes((int)m, (int)k, split, QG_W4_WAVES) > kMaxSmem) return QG_E_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
+  st = hip_status(qg::launch_w4a16_gemv((int)m, x_bf16, packed, (int)n, (int)k, y,
+                                        y_dtype == QG_F32, partial, split, QG_W4_WAVES,
+                                        QG_W4_NT != 0, s));
+  if (st != QG_OK || split == 1) return st;
+  return hip_status(qg::launch_splitk_reduce(partial, split, m * n, y, y_dtype == QG_F32, s));
+}
+
+int32_t qgemm_w8a16(const void* x_bf16, int64_t m, int64_t k, const int8_t* w,
+                    const void* scale_bf16, int64_t n, void* y, int32_t y_dtype, void* stream) {
+  (void)x_bf16; (void)m; (void)k; (void)w; (void)scale_bf16; (void)n; (void)y; (void)y_dtype;
+  (void)stream;
+  return QG_E_HIP;
+}
+
+int32_t qgemm_w4a8(const void* x_bf16, int64_t m, int64_t k, const void* packed,
+                   int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype, int32_t split_k,
+                   void* ws, int64_t ws_bytes, void* stream) {
+  (void)x_bf16; (void)m; (void)k; (void)packed; (void)packed_bytes; (void)n; (void)y;
+  (void)y_dtype; (void)split_k; (void)ws; (void)ws_bytes; (void)stream;
+  return QG_E_HIP;
+}
+
+}  // extern "C"

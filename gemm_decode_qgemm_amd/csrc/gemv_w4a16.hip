@@ -1,0 +1,293 @@
+// gemv_w4a16.hip -- decode GEMV for the packed INT4 group-32 weight, M = 1..4.
+//
+// Computes y[m, n] = sum_k x[m, k] * (q[n,k] - zp[n,g]) * s[n,g], the
+// "dequant + F.linear" reference of executorch test_int4_quantized_gemm.py
+// (module docstring, `_dequant_matmul`), without ever writing a dequantized
+// weight: gpt-fast issue #114 (feiyuvl's report) shows an unfused int->bf16
+// convert costs the GEMV its bandwidth.
+//
+// Mapping (gfx950, wave64):
+//  * a workgroup owns one 64-row block and one split-K range of 256-k tiles;
+//    lane r of every wave owns row r, waves take tiles round robin, so each
+//    wave streams whole tiles: 10 loads of 16/4 B per lane, every one a run of
+//    whole 128-byte lines;
+//  * x is the same for all 64 lanes, so each lane keeps only 1/16 of a tile's
+//    x in VGPRs (two 16-byte loads per row m per tile, L2-resident) and
+//    v_dot2c_f32_bf16 takes the x pair it needs from the lane that holds it
+//    through a DPP row broadcast: no LDS, no scalar registers, no extra
+//    instruction per product;
+//  * nibbles become exact bf16 pairs (128 + q) with one shift and one and-or
+//    (see nibble_pair_bf16), v_dot2c accumulates x * (128 + q) in fp32, and a
+//    per-group correction subtracts (128 + zp) * X_g, where X_g (the group sum
+//    of x) comes from a 4-lane DPP reduction of the same registers;
+//  * the waves' per-row partials are summed through LDS in wave order, and a
+//    split-K launch writes fp32 partials that a second pass sums in split
+//    order (no atomics: results are bit-reproducible).
+#include "qg_common.h"
+
+namespace qg {
+
+struct TileRegs {
+  u32x4_t c[8];   // code chunks of groups 0..7 for this lane's row
+  u32x4_t sc;     // 8 fp16 scales
+  uint32_t zw;    // 8 zero points
+};
+
+template <bool NT>
+__device__ __forceinline__ void load_tile(TileRegs& t, const uint8_t* tile, int lane) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    t.c[j] = load_stream(reinterpret_cast<const u32x4_t*>(tile + (j * kTileRows + lane) * 16), NT);
+  t.sc = load_stream(reinterpret_cast<const u32x4_t*>(tile + kScaleOff + lane * 16), NT);
+  t.zw = load_stream(reinterpret_cast<const uint32_t*>(tile + kZeroOff + lane * 4), NT);
+}
+
+// Split-K partition of `tiles` 256-k units into `split` contiguous ranges;
+// the first (tiles % split) ranges take one extra unit.
+__device__ __forceinline__ void split_range(int tiles, int split, int s, int& t0, int& t1) {
+  const int base = tiles / split, rem = tiles % split;
+  t0 = s * base + (s < rem ? s : rem);
+  t1 = t0 + base + (s < rem ? 1 : 0);
+}
+
+// x of one tile (256 k = 128 dwords per row m) lives in VGPRs spread over the
+// 16 lanes of each DPP row: lane i holds dwords 4i..4i+3 of each half tile
+// (groups 0-3 in h[0], groups 4-7 in h[1]); the four rows of the wave hold
+// the same copy.  Dword q of group j (within its half) is therefore register
+// q % 4 of lane 4*(j % 4) + q / 4, read with DPP row_newbcast.
+template <int M>
+struct XRegs {
+  u32x4_t h[M][2];
+};
+
+template <int M>
+__device__ __forceinline__ void load_x(XRegs<M>& xr, const uint32_t* x32, int k32, int t, int li) {
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      xr.h[m][h] = *reinterpret_cast<const u32x4_t*>(x32 + (size_t)m * k32 + (size_t)t * 128 +
+                                                    h * 64 + li * 4);
+}
+
+// d0 += x . (128+q) over the even dwords and d1 over the odd dwords of one
+// group: 16 v_dot2c_f32_bf16 whose x operand is broadcast by DPP from the lane
+// that holds it.  The leading `s_nop 1` gives the two wait states a DPP read
+// needs after a VALU write of its source register.  The trailing nop covers a
+// hazard measured on MI355X: a VALU read of a v_dot2c_f32_bf16_dpp result less
+// than two wait states after it sees the old value (the compiler cannot see
+// into the asm to insert them); one-hot tests lose exactly the block's last
+// product without it and are exact with one or more.
+#define QG_DPP_DOT(acc, xr, pr, L) \
+  "v_dot2c_f32_bf16_dpp " acc ", " xr ", " pr " row_newbcast:" #L " row_mask:0xf bank_mask:0xf\n\t"
+#ifndef QG_DOT_TAIL_NOP
+#define QG_DOT_TAIL_NOP 2
+#endif
+#define QG_STR2(x) #x
+#define QG_STR(x) QG_STR2(x)
+#define QG_DOT16(L0, L1, L2, L3)                                                              \
+  "s_nop 1\n\t"                                                                              \
+  QG_DPP_DOT("%0", "%2", "%6", L0) QG_DPP_DOT("%1", "%3", "%7", L0)                          \
+  QG_DPP_DOT("%0", "%4", "%8", L0) QG_DPP_DOT("%1", "%5", "%9", L0)                          \
+  QG_DPP_DOT("%0", "%2", "%10", L1) QG_DPP_DOT("%1", "%3", "%11", L1)                        \
+  QG_DPP_DOT("%0", "%4", "%12", L1) QG_DPP_DOT("%1", "%5", "%13", L1)                        \
+  QG_DPP_DOT("%0", "%2", "%14", L2) QG_DPP_DOT("%1", "%3", "%15", L2)                        \
+  QG_DPP_DOT("%0", "%4", "%16", L2) QG_DPP_DOT("%1", "%5", "%17", L2)                        \
+  QG_DPP_DOT("%0", "%2", "%18", L3) QG_DPP_DOT("%1", "%3", "%19", L3)                        \
+  QG_DPP_DOT("%0", "%4", "%20", L3) QG_DPP_DOT("%1", "%5", "%21", L3)                        \
+  "s_nop " QG_STR(QG_DOT_TAIL_NOP) "\n\t"
+#define QG_DOT16_OPERANDS                                                                    \
+  : "+v"(d0), "+v"(d1)                                                                       \
+  : "v"(xv.x), "v"(xv.y), "v"(xv.z), "v"(xv.w), "v"(pr[0]), "v"(pr[1]), "v"(pr[2]),          \
+    "v"(pr[3]), "v"(pr[4]), "v"(pr[5]), "v"(pr[6]), "v"(pr[7]), "v"(pr[8]), "v"(pr[9]),      \
+    "v"(pr[10]), "v"(pr[11]), "v"(pr[12]), "v"(pr[13]), "v"(pr[14]), "v"(pr[15])
+
+template <int JJ>
+__device__ __forceinline__ void group_dot(float& d0, float& d1, const u32x4_t& xv,
+                                          const uint32_t (&pr)[16]) {
+  if constexpr (JJ == 0) asm(QG_DOT16(0, 1, 2, 3) QG_DOT16_OPERANDS);
+  if constexpr (JJ == 1) asm(QG_DOT16(4, 5, 6, 7) QG_DOT16_OPERANDS);
+  if constexpr (JJ == 2) asm(QG_DOT16(8, 9, 10, 11) QG_DOT16_OPERANDS);
+  if constexpr (JJ == 3) asm(QG_DOT16(12, 13, 14, 15) QG_DOT16_OPERANDS);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, 0xf, 0xf, true));
+}
+
+template <int M, int J>
+__device__ __forceinline__ void do_group(float (&acc)[M], const TileRegs& cur, const XRegs<M>& xc,
+                                         const float (&xq)[M][2], uint32_t mask_s,
+                                         uint32_t magic_v) {
+  const u32x4_t cv = cur.c[J];
+  const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
+  uint32_t pr[16];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[4 * d + i] = nibble_pair_bf16(cw[d], i, mask_s, magic_v);
+  const uint32_t scw[4] = {cur.sc.x, cur.sc.y, cur.sc.z, cur.sc.w};
+  const float s = fp16_to_f32((scw[J >> 1] >> (16 * (J & 1))) & 0xffffu);
+  const float zb = (float)(((cur.zw >> (4 * J)) & 15u) + 128u);
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float d0 = 0.0f, d1 = 0.0f;
+    const u32x4_t xv = xc.h[m][J >> 2];
+    group_dot<J & 3>(d0, d1, xv, pr);
+    const float xg = dpp_mov<0x150 + 4 * (J & 3)>(xq[m][J >> 2]);   // X_J to every lane
+    const float tg = __builtin_fmaf(-zb, xg, d0 + d1);
+    acc[m] = __builtin_fmaf(s, tg, acc[m]);
+  }
+}
+
+template <int M, int WAVES, bool NT>
+__global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
+    void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
+  __shared__ float red[WAVES * M * 64];
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15;
+  const int wave = wave_id_uniform();
+  const int rb = blockIdx.x;
+  const int kt_count = k >> 8;
+  int t0, t1;
+  split_range(kt_count, split, blockIdx.y, t0, t1);
+  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
+  const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
+  const int k32 = k >> 1;
+  const uint32_t mask_s = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+  uint32_t magic_v = 0x43004300u;
+  asm volatile("" : "+v"(magic_v));   // keep the constant in a VGPR
+  // The bf16 pair (1.0, 1.0) for the group sums, also held in a VGPR: as a
+  // literal or inline constant in v_dot2c_f32_bf16 the pair is not read as
+  // two bf16 halves on gfx950 (the inline constant 1.0 arrives as the f32
+  // pattern 0x3F800000, i.e. the pair (0, 1.0)).
+  uint32_t ones_v = 0x3f803f80u;
+  asm volatile("" : "+v"(ones_v));
+
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+
+  TileRegs cur;
+  XRegs<M> xc;
+  int t = t0 + wave;
+  if (t < t1) {
+    load_tile<NT>(cur, tiles + (size_t)t * kTileBytes, lane);
+    load_x<M>(xc, x32, k32, t, li);
+  }
+  for (; t < t1; t += WAVES) {
+    TileRegs nxt;
+    XRegs<M> xn;
+    const bool more = t + WAVES < t1;
+    if (more) {
+      load_tile<NT>(nxt, tiles + (size_t)(t + WAVES) * kTileBytes, lane);
+      load_x<M>(xn, x32, k32, t + WAVES, li);
+    }
+    // X_g: lane i of a row sums its 4 dwords (group 4h + i/4), then the quad
+    // of lanes sharing a group adds up (DPP quad_perm [1,0,3,2], [2,3,0,1]).
+    float xq[M][2];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4_t v = xc.h[m][h];
+        float p = dot2_bf16(v.x, ones_v, 0.0f);
+        p = dot2_bf16(v.y, ones_v, p);
+        p = dot2_bf16(v.z, ones_v, p);
+        p = dot2_bf16(v.w, ones_v, p);
+        p += dpp_mov<0xB1>(p);
+        p += dpp_mov<0x4E>(p);
+        xq[m][h] = p;
+      }
+    do_group<M, 0>(acc, cur, xc, xq, mask_s, magic_v);
+    do_group<M, 1>(acc, cur, xc, xq, mask_s, magic_v);
+    do_group<M, 2>(acc, cur, xc, xq, mask_s, magic_v);
+    do_group<M, 3>(acc, cur, xc, xq, mask_s, magic_v);
+    do_group<M, 4>(acc, cur, xc, xq, mask_s, magic_v);
+    do_group<M, 5>(acc, cur, xc, xq, mask_s, magic_v);
+    do_group<M, 6>(acc, cur, xc, xq, mask_s, magic_v);
+    do_group<M, 7>(acc, cur, xc, xq, mask_s, magic_v);
+    if (more) {
+      cur = nxt;
+      xc = xn;
+    }
+  }
+
+  // Cross-wave sum in wave order (fixed, so repeat calls are bit-identical).
+#pragma unroll
+  for (int m = 0; m < M; ++m) red[(wave * M + m) * 64 + lane] = acc[m];
+  __syncthreads();
+  if (wave < M) {
+    const int m = wave;
+    float v = red[m * 64 + lane];
+    for (int w = 1; w < WAVES; ++w) v += red[(w * M + m) * 64 + lane];
+    const int row = rb * kTileRows + lane;
+    if (row < n) {
+      if (partial != nullptr) {
+        partial[((size_t)blockIdx.y * M + m) * n + row] = v;
+      } else if (y_f32) {
+        static_cast<float*>(y)[(size_t)m * n + row] = v;
+      } else {
+        static_cast<uint16_t*>(y)[(size_t)m * n + row] = (uint16_t)f32_to_bf16_rne(v);
+      }
+    }
+  }
+}
+
+// Second split-K pass: y = sum over s (ascending) of partial[s], no atomics.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial,
+                                                            int split, int64_t mn,
+                                                            void* __restrict__ y, int y_f32) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= mn) return;
+  float v = partial[i];
+  for (int s = 1; s < split; ++s) v += partial[(int64_t)s * mn + i];
+  if (y_f32)
+    static_cast<float*>(y)[i] = v;
+  else
+    static_cast<uint16_t*>(y)[i] = (uint16_t)f32_to_bf16_rne(v);
+}
+
+hipError_t launch_splitk_reduce(const float* partial, int split, int64_t mn, void* y, int y_f32,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0,
+                     stream, partial, split, mn, y, y_f32);
+  return hipGetLastError();
+}
+
+template <int M, int WAVES, bool NT>
+static hipError_t launch_w4a16_t(const void* x, const void* packed, int n, int k, void* y,
+                                 int y_f32, float* partial, int split, hipStream_t stream) {
+  const int rbs = (n + kTileRows - 1) / kTileRows;
+  const int kt = k / kTileK;
+  (void)kt;
+  hipLaunchKernelGGL((w4a16_gemv_kernel<M, WAVES, NT>), dim3(rbs, split), dim3(WAVES * 64), 0,
+                     stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
+                     n, k, y, y_f32, partial, split);
+  return hipGetLastError();
+}
+
+// Shared-memory bytes the GEMV needs (the host checks it against the limit).
+size_t w4a16_gemv_smem_bytes(int m, int k, int split, int waves) {
+  (void)k; (void)split;
+  return (size_t)(waves * m * 64) * sizeof(float);
+}
+
+hipError_t launch_w4a16_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
+                             int y_f32, float* partial, int split, int waves, bool nt,
+                             hipStream_t stream) {
+#define QG_W4_CASE(MM, WW, NTV)                                                          \
+  if (m == MM && waves == WW && nt == NTV)                                               \
+    return launch_w4a16_t<MM, WW, NTV>(x, packed, n, k, y, y_f32, partial, split, stream);
+#define QG_W4_M(MM)       \
+  QG_W4_CASE(MM, 4, false) QG_W4_CASE(MM, 8, false) QG_W4_CASE(MM, 4, true) QG_W4_CASE(MM, 8, true)
+  QG_W4_M(1) QG_W4_M(2) QG_W4_M(3) QG_W4_M(4)
+#undef QG_W4_M
+#undef QG_W4_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qg

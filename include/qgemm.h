@@ -1,0 +1,181 @@
+/*
+ * qgemm.h -- C ABI of the MI355X (gfx950) decode-time weight-only quantized
+ * linear layer:   y[m, n] = sum_k x[m, k] * dequant(W)[n, k]  (* scale[n]).
+ *
+ * Pages this library implements (cited by title and section):
+ *  [P1] executorch "backends/cuda/tests/test_int4_quantized_gemm.py":
+ *       `_packed_with_dense` (INT4, group 32, asymmetric, min-max),
+ *       module docstring and `_dequant_matmul` (dequant + F.linear reference),
+ *       `Int4QuantizedGemmLegalityTest` (validate before launching: dtype,
+ *       shape, "K must be a multiple of 256", static M), `Int4QuantizedGemmRulesTest.
+ *       test_split_k_needs_one_k_tile_per_split` (split <= K / 256),
+ *       `SUPPORTED_BUCKETS` (decode M up to 64), `Int4QuantizedGemmTest.
+ *       test_cuda_graph_replay_matches_eager` (bit-identical replays),
+ *       `Int4QuantizedGemmPrecisionTest` (int8 activations, W4A8).
+ *  [P3] gpt-fast issue #114 "Question about the generated code of
+ *       WeightOnlyInt8Linear": `WeightOnlyInt8Linear.forward`
+ *       (y = F.linear(x, W.to(bf16)) * scales; the int8->bf16 convert must be
+ *       fused into the GEMV, never materialized).
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are DEVICE pointers (HIP global memory) on the current
+ *    device, 16-byte aligned; arrays are row-major and contiguous.
+ *    bf16 / fp16 values are their 16-bit IEEE patterns.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous on that stream; the library never allocates, never
+ *    synchronizes, and keeps no mutable global state (calls are re-entrant).
+ *  - The caller owns every buffer.  Outputs must not alias inputs.
+ *  - On an argument error the call returns a negative qg_status and launches
+ *    nothing (the checks run on the host before any launch).  A HIP launch
+ *    failure returns QG_E_HIP.  Data-dependent conditions (non-finite
+ *    weights, scale overflow) are reported through the optional device word
+ *    `status_dev`: kernels OR flag bits into it; the caller zeroes it first.
+ *  - Results are deterministic: identical inputs, split and device give
+ *    bit-identical outputs, eager or replayed from a HIP graph (no floating
+ *    point atomics anywhere).
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- packed INT4 group-32 weight layout, version 1 ----------------------
+ * The weight is stored as tiles of 64 rows x 256 k (8 groups of 32 per row),
+ * each exactly 9472 bytes = 74 lines of 128 bytes:
+ *   [0, 8192)     codes: 16-byte chunk of (group j, row r) at (j*64 + r)*16;
+ *                 LE dword d of a chunk holds k = 8d+e of the group at nibble
+ *                 position p = (e & 1)*4 + (e >> 1), i.e. bits [4p, 4p+4).
+ *                 (dword >> 4i) & 0x000F000F then yields the codes of
+ *                 k = 8d+2i and 8d+2i+1 in its low and high 16-bit halves.
+ *   [8192, 9216)  fp16 scales: row r's 8 scales at 8192 + 16r, group j at +2j
+ *   [9216, 9472)  zero points: row r's LE 32-bit word at 9216 + 4r,
+ *                 group j in bits [4j, 4j+4)
+ * Tiles are row-block major: tile = (n / 64) * (K / 256) + k / 256.  Rows
+ * n >= N of the last row block are zero.  A wavefront (64 lanes, lane = row)
+ * reads each region as whole 128-byte lines with one 16-byte load per lane. */
+#define QG_INT4_LAYOUT_VERSION 1
+#define QG_TILE_ROWS 64
+#define QG_TILE_K 256
+#define QG_TILE_BYTES 9472
+#define QG_GROUP 32
+#define QG_MAX_M 64
+
+enum qg_dtype { QG_BF16 = 0, QG_F32 = 1 };
+
+enum qg_status {
+    QG_OK = 0,
+    QG_E_NULL = -1,        /* a required pointer is NULL */
+    QG_E_SHAPE = -2,       /* m, n or k < 1 */
+    QG_E_K_MULTIPLE = -3,  /* K % 256 != 0 ([P1] "K must be a multiple of 256") */
+    QG_E_M_RANGE = -4,     /* M > 64 ([P1] "static M must be within" the buckets) */
+    QG_E_SPLIT = -5,       /* split_k not in {0,1,2,4,8} or split_k > K/256 */
+    QG_E_BUFFER = -6,      /* packed_bytes or ws_bytes too small */
+    QG_E_ALIGN = -7,       /* a data pointer is not 16-byte aligned */
+    QG_E_DTYPE = -8,       /* y_dtype is not QG_BF16 / QG_F32 */
+    QG_E_HIP = -9          /* a HIP launch failed */
+};
+
+/* status_dev flag bits */
+#define QG_FLAG_NONFINITE 1u   /* a weight group/row held Inf or NaN */
+#define QG_FLAG_OVERFLOW 2u    /* an INT4 group's range exceeded 15 * 65504 */
+
+/* Human-readable name of a qg_status value (static string). */
+const char *qg_status_string(int32_t status);
+
+/* Bytes of the packed INT4 buffer for an N x K weight:
+ * ceil(N/64) * (K/256) * 9472 (= N*K/2 codes + N*K/32 * 2.5 bytes of fp16
+ * scale and 4-bit zero when N % 64 == 0).  Returns a negative qg_status for
+ * N < 1, K < 1 or K % 256 != 0. */
+int64_t qg_int4_packed_bytes(int64_t n, int64_t k);
+
+/* The split-K factor the library uses when a qgemm call passes split_k = 0
+ * (a static table keyed by the shape), or a negative qg_status. */
+int32_t qg_default_split_k(int64_t m, int64_t n, int64_t k);
+
+/* Workspace bytes a qgemm_w4a16 / qgemm_w4a8 call needs for (m, n, k,
+ * split_k): split * m * n * 4 (fp32 partial sums) when the resolved split is
+ * above 1, else 0.  Negative qg_status on bad arguments. */
+int64_t qg_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k);
+
+/* ---- quantize_int4_g32 ---------------------------------------------------
+ * [P1] `_packed_with_dense`: QuantConfig(bits=4, group_size=32,
+ * symmetric=False, method="min_max").  For each row n and each group g of 32
+ * consecutive k:
+ *   lo = min(0, min v), hi = max(0, max v), r = hi - lo  (binary64)
+ *   s  = the smallest positive fp16 with 15*s >= r  (1.0 when r == 0)
+ *   zp = clamp(rint(-lo / s), 0, 15)                  (binary32, half-even)
+ *   q  = clamp(rint(v / s) + zp, 0, 15)
+ * and writes (q, s, zp) in the layout above.  Every dequantized value
+ * (q - zp) * s lies within s/2 of its input.
+ *   w_bf16        in : bf16 [n, k]
+ *   packed        out: qg_int4_packed_bytes(n, k) bytes (padding rows zeroed)
+ *   packed_bytes  in : size of `packed`
+ *   status_dev    in/out, may be NULL: ORed with QG_FLAG_NONFINITE (that
+ *                 group: codes 0, scale NaN, zp 0) and QG_FLAG_OVERFLOW
+ *                 (that group's scale saturates at 65504).
+ * Errors: QG_E_NULL, QG_E_SHAPE, QG_E_K_MULTIPLE, QG_E_BUFFER, QG_E_ALIGN. */
+int32_t quantize_int4_g32(const void *w_bf16, int64_t n, int64_t k, void *packed,
+                          int64_t packed_bytes, uint32_t *status_dev, void *stream);
+
+/* ---- quantize_int8_rowwise -----------------------------------------------
+ * Per-output-channel symmetric int8, the weight format of [P3]
+ * `WeightOnlyInt8Linear` (int8 [out, in] plus one scale per output row):
+ *   a = max_k |w[n, k]|;  s = the smallest positive bf16 with 127*s >= a
+ *   (1.0 when a == 0);  q = clamp(rint(w / s), -127, 127)  (binary32).
+ *   w_bf16      in : bf16 [n, k]      q  out: int8 [n, k]
+ *   scale_bf16  out: bf16 [n]
+ *   status_dev  in/out, may be NULL: QG_FLAG_NONFINITE (that row: q 0, s NaN).
+ * Errors: QG_E_NULL, QG_E_SHAPE, QG_E_K_MULTIPLE (K % 256), QG_E_ALIGN. */
+int32_t quantize_int8_rowwise(const void *w_bf16, int64_t n, int64_t k, int8_t *q,
+                              void *scale_bf16, uint32_t *status_dev, void *stream);
+
+/* ---- qgemm_w4a16 ---------------------------------------------------------
+ * [P1] module docstring / `_dequant_matmul`: y = x . dequant(W)^T with the
+ * packed INT4 g32 weight above, dequantized in registers (no bf16 copy of W
+ * is ever written).  Accumulation is fp32.
+ *   x_bf16   in : bf16 [m, k], 1 <= m <= 64      packed  in: [n, k] weight
+ *   y        out: [m, n], bf16 (round to nearest even) or fp32 per y_dtype
+ *   split_k  0 (library table) or 1, 2, 4, 8 with split_k <= k/256
+ *   ws       fp32 workspace of qg_workspace_bytes(m, n, k, split_k) bytes
+ *            (NULL allowed when that is 0); contents on return unspecified.
+ * M <= 4 runs the VALU GEMV; 5 <= M <= 64 the MFMA kernel (rows padded to
+ * 16 and masked).  split_k > 1 adds a second, atomic-free pass that sums the
+ * partials in ascending split order.
+ * Errors: QG_E_NULL, QG_E_SHAPE, QG_E_K_MULTIPLE, QG_E_M_RANGE, QG_E_SPLIT,
+ * QG_E_BUFFER, QG_E_ALIGN, QG_E_DTYPE, QG_E_HIP. */
+int32_t qgemm_w4a16(const void *x_bf16, int64_t m, int64_t k, const void *packed,
+                    int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
+                    int32_t split_k, void *ws, int64_t ws_bytes, void *stream);
+
+/* ---- qgemm_w8a16 ---------------------------------------------------------
+ * [P3] `WeightOnlyInt8Linear.forward`: y[m, n] = (sum_k x[m,k] * W[n,k]) *
+ * scale[n], fp32 accumulation, the int8 -> float convert fused into the dot
+ * product.  W int8 [n, k] row-major as given (no repacking), scale bf16 [n].
+ *   x_bf16 in: bf16 [m, k], 1 <= m <= 64;  y out: [m, n] bf16 or fp32.
+ * Errors: QG_E_NULL, QG_E_SHAPE, QG_E_K_MULTIPLE, QG_E_M_RANGE, QG_E_ALIGN,
+ * QG_E_DTYPE, QG_E_HIP. */
+int32_t qgemm_w8a16(const void *x_bf16, int64_t m, int64_t k, const int8_t *w,
+                    const void *scale_bf16, int64_t n, void *y, int32_t y_dtype,
+                    void *stream);
+
+/* ---- qgemm_w4a8 ----------------------------------------------------------
+ * [P1] `Int4QuantizedGemmPrecisionTest`: the decode kernels run the packed
+ * INT4 weight against int8 activations.  Each row of x is quantized inside
+ * the call (per-row symmetric absmax: a = max|x|, inv = 127/a, sx = a/127,
+ * xq = clamp(rint(x * inv), -127, 127) in binary32; a == 0 gives a zero row),
+ * then  y[m,n] = sx[m] * sum_g s[n,g] * sum_{k in g} xq[m,k] * (q[n,k] - zp[n,g])
+ * with exact integer group dots.  Arguments and errors as qgemm_w4a16
+ * (1 <= m <= 4 in this version: QG_E_M_RANGE above). */
+int32_t qgemm_w4a8(const void *x_bf16, int64_t m, int64_t k, const void *packed,
+                   int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
+                   int32_t split_k, void *ws, int64_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QGEMM_H */

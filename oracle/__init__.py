@@ -76,7 +76,14 @@ def _u16(a) -> np.ndarray:
 
 
 def hardware_threads() -> int:
-    return int(_load().orc_hardware_threads())
+    """Threads for the oracle's row-parallel driver: the host's online CPUs,
+    capped by OMP_NUM_THREADS when set (a shared GPU host grants each GPU job
+    a share of its cores)."""
+    n = int(_load().orc_hardware_threads())
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 def bf16_to_float64(bits) -> np.ndarray:
