@@ -33,6 +33,33 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "µs/call and effective weight GB/s (% HBM peak) for INT4-g32 GEMV at M=1"
+COUNTERS = os.path.join(ROOT, "profiles", "w4a16_gemv_39936x6656_m1_counters.json")
+KERNEL_SOURCES = ["gemm_decode_qgemm_amd/csrc/gemv_w4a16.hip", "gemm_decode_qgemm_amd/csrc/qg_common.h",
+                  "gemm_decode_qgemm_amd/csrc/api.hip"]
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the sources that define the timed kernel and its launch."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(n, k, m):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on this exact kernel source and workload; else None."""
+    try:
+        with open(COUNTERS) as fh:
+            c = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256") != kernel_source_hash() or c.get("workload") != [n, k, m]:
+        return None
+    return int(c["hbm_bytes_per_launch"])
 
 
 def parse():
@@ -146,7 +173,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(n, k, m),
         },
     }
 
@@ -181,6 +208,11 @@ def cpu_baseline(args, w_cpu, x_cpu, y_gpu, bytes_eff):
     y = y_gpu.float().cpu().numpy().astype(np.float64)
     err = np.abs(y - ref)
     mean_ref = float(np.abs(ref).mean())
+    # The timed output is bf16: allow half a bf16 ulp of ref on top of the
+    # fp32-output bound (the same reading the parity tests use).
+    _, e = np.frexp(np.maximum(np.abs(ref), np.finfo(np.float32).tiny))
+    within = bool((err <= 1e-2 * mean_ref + 1e-3 + np.ldexp(1.0, e - 9)).all()
+                  and err.mean() / mean_ref <= 2e-3)
     return {
         "value": round(bytes_eff / t / 1e9, 3),
         "unit": "GB/s",
@@ -190,7 +222,7 @@ def cpu_baseline(args, w_cpu, x_cpu, y_gpu, bytes_eff):
         "sample": f"{len(times)} full calls ({args.n}x{args.k}, M={args.m}), median",
         "gpu_vs_oracle": {"max_abs_err": float(err.max()),
                           "mean_rel_err": float(err.mean() / mean_ref),
-                          "bound_max": 1e-2 * mean_ref + 1e-3},
+                          "within_tolerance": within},
     }
 
 

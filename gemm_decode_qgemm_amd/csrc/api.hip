@@ -19,19 +19,24 @@ hipError_t launch_quantize_int4_g32(const void* w, int64_t n, int64_t k, void* p
 hipError_t launch_quantize_int8_rowwise(const void* w, int64_t n, int64_t k, int8_t* q,
                                         void* scales, uint32_t* status, hipStream_t stream);
 hipError_t launch_w4a16_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
-                             int y_f32, float* partial, int split, int waves, bool nt,
+                             int y_f32, float* partial, int split, int waves, int la,
                              hipStream_t stream);
 size_t w4a16_gemv_smem_bytes(int m, int k, int split, int waves);
 hipError_t launch_splitk_reduce(const float* partial, int split, int64_t mn, void* y, int y_f32,
                                 hipStream_t stream);
 }  // namespace qg
 
-// Launch shape of the M <= 4 GEMV (compile-time defaults; measured on MI355X).
-#ifndef QG_W4_WAVES
-#define QG_W4_WAVES 8
+// Launch shape of the M <= 4 GEMV: waves per workgroup and look-ahead (in
+// half tiles), measured on MI355X at the decode layer shapes (weights read
+// with non-temporal loads).  Defaults can be overridden at build time.
+#ifndef QG_W4_WAVES_SMALL_M
+#define QG_W4_WAVES_SMALL_M 16   // M = 1, 2
 #endif
-#ifndef QG_W4_NT
-#define QG_W4_NT 0
+#ifndef QG_W4_WAVES_LARGE_M
+#define QG_W4_WAVES_LARGE_M 8    // M = 3, 4
+#endif
+#ifndef QG_W4_LA
+#define QG_W4_LA 0
 #endif
 
 namespace {
@@ -163,12 +168,12 @@ int32_t qgemm_w4a16(const void* x_bf16, int64_t m, int64_t k, const void* packed
   if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || (ws && !aligned16(ws)))
     return QG_E_ALIGN;
   if (m > 4) return QG_E_M_RANGE;   // the MFMA path for 5..64 is not built yet
-  if (qg::w4a16_gemv_smem_bytes((int)m, (int)k, split, QG_W4_WAVES) > kMaxSmem) return QG_E_SHAPE;
+  const int waves = m <= 2 ? QG_W4_WAVES_SMALL_M : QG_W4_WAVES_LARGE_M;
+  if (qg::w4a16_gemv_smem_bytes((int)m, (int)k, split, waves) > kMaxSmem) return QG_E_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
   st = hip_status(qg::launch_w4a16_gemv((int)m, x_bf16, packed, (int)n, (int)k, y,
-                                        y_dtype == QG_F32, partial, split, QG_W4_WAVES,
-                                        QG_W4_NT != 0, s));
+                                        y_dtype == QG_F32, partial, split, waves, QG_W4_LA, s));
   if (st != QG_OK || split == 1) return st;
   return hip_status(qg::launch_splitk_reduce(partial, split, m * n, y, y_dtype == QG_F32, s));
 }

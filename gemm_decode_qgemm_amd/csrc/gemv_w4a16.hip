@@ -27,19 +27,26 @@
 
 namespace qg {
 
-struct TileRegs {
-  u32x4_t c[8];   // code chunks of groups 0..7 for this lane's row
-  u32x4_t sc;     // 8 fp16 scales
-  uint32_t zw;    // 8 zero points
+// One half tile (4 groups = 128 k) of one lane's row: 4 code chunks, the 4
+// fp16 scales (8 B) and the 4 zero points (16 bits of the row's zero word).
+struct HalfRegs {
+  u32x4_t c[4];
+  u32x2_t sc;
+  uint32_t zw;
 };
 
 template <bool NT>
-__device__ __forceinline__ void load_tile(TileRegs& t, const uint8_t* tile, int lane) {
+__device__ __forceinline__ void load_half(HalfRegs& r, const uint8_t* tile, int half, int lane) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    t.c[j] = load_stream(reinterpret_cast<const u32x4_t*>(tile + (j * kTileRows + lane) * 16), NT);
-  t.sc = load_stream(reinterpret_cast<const u32x4_t*>(tile + kScaleOff + lane * 16), NT);
-  t.zw = load_stream(reinterpret_cast<const uint32_t*>(tile + kZeroOff + lane * 4), NT);
+  for (int j = 0; j < 4; ++j)
+    r.c[j] = load_stream<NT>(
+        reinterpret_cast<const u32x4_t*>(tile + ((4 * half + j) * kTileRows + lane) * 16));
+  // Scales and zero points of the two half tiles share 128-byte lines, and
+  // the other half is read by another wave of the same workgroup moments
+  // later: these loads keep the default (temporal) policy so that wave hits
+  // in L2 instead of fetching the line from HBM again.
+  r.sc = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + kScaleOff + lane * 16 + 8 * half));
+  r.zw = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + kZeroOff + lane * 4 + 2 * half));
 }
 
 // Split-K partition of `tiles` 256-k units into `split` contiguous ranges;
@@ -50,24 +57,20 @@ __device__ __forceinline__ void split_range(int tiles, int split, int s, int& t0
   t1 = t0 + base + (s < rem ? 1 : 0);
 }
 
-// x of one tile (256 k = 128 dwords per row m) lives in VGPRs spread over the
-// 16 lanes of each DPP row: lane i holds dwords 4i..4i+3 of each half tile
-// (groups 0-3 in h[0], groups 4-7 in h[1]); the four rows of the wave hold
-// the same copy.  Dword q of group j (within its half) is therefore register
-// q % 4 of lane 4*(j % 4) + q / 4, read with DPP row_newbcast.
+// x of one half tile (128 k = 64 dwords per row m) lives in VGPRs spread
+// over the 16 lanes of each DPP row: lane i holds dwords 4i..4i+3; the four
+// rows of the wave hold the same copy.  Dword q of the half's group jj is
+// therefore register q % 4 of lane 4*jj + q / 4, read with DPP row_newbcast.
 template <int M>
-struct XRegs {
-  u32x4_t h[M][2];
+struct XHalf {
+  u32x4_t v[M];
 };
 
 template <int M>
-__device__ __forceinline__ void load_x(XRegs<M>& xr, const uint32_t* x32, int k32, int t, int li) {
+__device__ __forceinline__ void load_xhalf(XHalf<M>& xr, const uint32_t* x32, int k32, int hs, int li) {
 #pragma unroll
   for (int m = 0; m < M; ++m)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      xr.h[m][h] = *reinterpret_cast<const u32x4_t*>(x32 + (size_t)m * k32 + (size_t)t * 128 +
-                                                    h * 64 + li * 4);
+    xr.v[m] = *reinterpret_cast<const u32x4_t*>(x32 + (size_t)m * k32 + (size_t)hs * 64 + li * 4);
 }
 
 // d0 += x . (128+q) over the even dwords and d1 over the odd dwords of one
@@ -117,32 +120,59 @@ __device__ __forceinline__ float dpp_mov(float v) {
                                                                CTRL, 0xf, 0xf, true));
 }
 
-template <int M, int J>
-__device__ __forceinline__ void do_group(float (&acc)[M], const TileRegs& cur, const XRegs<M>& xc,
-                                         const float (&xq)[M][2], uint32_t mask_s,
-                                         uint32_t magic_v) {
-  const u32x4_t cv = cur.c[J];
+template <int M, int JJ>
+__device__ __forceinline__ void do_group(float (&acc)[M], const HalfRegs& cur, const XHalf<M>& xc,
+                                         const float (&xq)[M], uint32_t mask_s, uint32_t magic_v) {
+  const u32x4_t cv = cur.c[JJ];
   const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
   uint32_t pr[16];
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[4 * d + i] = nibble_pair_bf16(cw[d], i, mask_s, magic_v);
-  const uint32_t scw[4] = {cur.sc.x, cur.sc.y, cur.sc.z, cur.sc.w};
-  const float s = fp16_to_f32((scw[J >> 1] >> (16 * (J & 1))) & 0xffffu);
-  const float zb = (float)(((cur.zw >> (4 * J)) & 15u) + 128u);
+  const uint32_t sw = (JJ < 2) ? cur.sc.x : cur.sc.y;
+  const float s = fp16_to_f32((sw >> (16 * (JJ & 1))) & 0xffffu);
+  const float zb = (float)(((cur.zw >> (4 * JJ)) & 15u) + 128u);
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     float d0 = 0.0f, d1 = 0.0f;
-    const u32x4_t xv = xc.h[m][J >> 2];
-    group_dot<J & 3>(d0, d1, xv, pr);
-    const float xg = dpp_mov<0x150 + 4 * (J & 3)>(xq[m][J >> 2]);   // X_J to every lane
+    group_dot<JJ>(d0, d1, xc.v[m], pr);
+    const float xg = dpp_mov<0x150 + 4 * JJ>(xq[m]);   // X of group JJ to every lane
     const float tg = __builtin_fmaf(-zb, xg, d0 + d1);
     acc[m] = __builtin_fmaf(s, tg, acc[m]);
   }
 }
 
-template <int M, int WAVES, bool NT>
+// One half tile: group sums of x, then 4 groups of dequant-dot-correct.
+template <int M>
+__device__ __forceinline__ void half_compute(float (&acc)[M], const HalfRegs& cur,
+                                             const XHalf<M>& xc, uint32_t mask_s,
+                                             uint32_t magic_v, uint32_t ones_v) {
+  // X_g: lane i of a row sums its 4 dwords (group i/4 of the half), then the
+  // quad of lanes sharing a group adds up (DPP quad_perm [1,0,3,2], [2,3,0,1]).
+  float xq[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const u32x4_t v = xc.v[m];
+    float p = dot2_bf16(v.x, ones_v, 0.0f);
+    p = dot2_bf16(v.y, ones_v, p);
+    p = dot2_bf16(v.z, ones_v, p);
+    p = dot2_bf16(v.w, ones_v, p);
+    p += dpp_mov<0xB1>(p);
+    p += dpp_mov<0x4E>(p);
+    xq[m] = p;
+  }
+  do_group<M, 0>(acc, cur, xc, xq, mask_s, magic_v);
+  do_group<M, 1>(acc, cur, xc, xq, mask_s, magic_v);
+  do_group<M, 2>(acc, cur, xc, xq, mask_s, magic_v);
+  do_group<M, 3>(acc, cur, xc, xq, mask_s, magic_v);
+}
+
+// Work unit = half tile.  Wave w of a workgroup takes half tiles w, w+WAVES,
+// ... of its row block's split-K range.  LA = look-ahead: the loads of the
+// next LA units are in flight while a unit computes (register sets used in a
+// ring, unrolled, so no copies); LA = 0 loads, waits and computes.
+template <int M, int WAVES, bool NT, int LA>
 __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -171,48 +201,49 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 
-  TileRegs cur;
-  XRegs<M> xc;
-  int t = t0 + wave;
-  if (t < t1) {
-    load_tile<NT>(cur, tiles + (size_t)t * kTileBytes, lane);
-    load_x<M>(xc, x32, k32, t, li);
-  }
-  for (; t < t1; t += WAVES) {
-    TileRegs nxt;
-    XRegs<M> xn;
-    const bool more = t + WAVES < t1;
-    if (more) {
-      load_tile<NT>(nxt, tiles + (size_t)(t + WAVES) * kTileBytes, lane);
-      load_x<M>(xn, x32, k32, t + WAVES, li);
+  const int s1 = 2 * t1;
+  int hs = 2 * t0 + wave;   // half-tile index along k (tile hs/2, half hs%2)
+  auto load = [&](HalfRegs& r, XHalf<M>& xr, int h) {
+    load_half<NT>(r, tiles + (size_t)(h >> 1) * kTileBytes, h & 1, lane);
+    load_xhalf<M>(xr, x32, k32, h, li);
+  };
+  if constexpr (LA == 0) {
+    for (; hs < s1; hs += WAVES) {
+      HalfRegs r;
+      XHalf<M> xr;
+      load(r, xr, hs);
+      half_compute<M>(acc, r, xr, mask_s, magic_v, ones_v);
     }
-    // X_g: lane i of a row sums its 4 dwords (group 4h + i/4), then the quad
-    // of lanes sharing a group adds up (DPP quad_perm [1,0,3,2], [2,3,0,1]).
-    float xq[M][2];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4_t v = xc.h[m][h];
-        float p = dot2_bf16(v.x, ones_v, 0.0f);
-        p = dot2_bf16(v.y, ones_v, p);
-        p = dot2_bf16(v.z, ones_v, p);
-        p = dot2_bf16(v.w, ones_v, p);
-        p += dpp_mov<0xB1>(p);
-        p += dpp_mov<0x4E>(p);
-        xq[m][h] = p;
-      }
-    do_group<M, 0>(acc, cur, xc, xq, mask_s, magic_v);
-    do_group<M, 1>(acc, cur, xc, xq, mask_s, magic_v);
-    do_group<M, 2>(acc, cur, xc, xq, mask_s, magic_v);
-    do_group<M, 3>(acc, cur, xc, xq, mask_s, magic_v);
-    do_group<M, 4>(acc, cur, xc, xq, mask_s, magic_v);
-    do_group<M, 5>(acc, cur, xc, xq, mask_s, magic_v);
-    do_group<M, 6>(acc, cur, xc, xq, mask_s, magic_v);
-    do_group<M, 7>(acc, cur, xc, xq, mask_s, magic_v);
-    if (more) {
-      cur = nxt;
-      xc = xn;
+  } else if constexpr (LA == 1) {
+    HalfRegs ra, rb2;
+    XHalf<M> xa, xb;
+    if (hs < s1) load(ra, xa, hs);
+    while (hs < s1) {
+      if (hs + WAVES < s1) load(rb2, xb, hs + WAVES);
+      half_compute<M>(acc, ra, xa, mask_s, magic_v, ones_v);
+      hs += WAVES;
+      if (hs >= s1) break;
+      if (hs + WAVES < s1) load(ra, xa, hs + WAVES);
+      half_compute<M>(acc, rb2, xb, mask_s, magic_v, ones_v);
+      hs += WAVES;
+    }
+  } else {
+    HalfRegs r0, r1, r2;
+    XHalf<M> x0, x1, x2;
+    if (hs < s1) load(r0, x0, hs);
+    if (hs + WAVES < s1) load(r1, x1, hs + WAVES);
+    while (hs < s1) {
+      if (hs + 2 * WAVES < s1) load(r2, x2, hs + 2 * WAVES);
+      half_compute<M>(acc, r0, x0, mask_s, magic_v, ones_v);
+      hs += WAVES;
+      if (hs >= s1) break;
+      if (hs + 2 * WAVES < s1) load(r0, x0, hs + 2 * WAVES);
+      half_compute<M>(acc, r1, x1, mask_s, magic_v, ones_v);
+      hs += WAVES;
+      if (hs >= s1) break;
+      if (hs + 2 * WAVES < s1) load(r1, x1, hs + 2 * WAVES);
+      half_compute<M>(acc, r2, x2, mask_s, magic_v, ones_v);
+      hs += WAVES;
     }
   }
 
@@ -220,8 +251,7 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
 #pragma unroll
   for (int m = 0; m < M; ++m) red[(wave * M + m) * 64 + lane] = acc[m];
   __syncthreads();
-  if (wave < M) {
-    const int m = wave;
+  for (int m = wave; m < M; m += WAVES) {
     float v = red[m * 64 + lane];
     for (int w = 1; w < WAVES; ++w) v += red[(w * M + m) * 64 + lane];
     const int row = rb * kTileRows + lane;
@@ -258,13 +288,13 @@ hipError_t launch_splitk_reduce(const float* partial, int split, int64_t mn, voi
   return hipGetLastError();
 }
 
-template <int M, int WAVES, bool NT>
+template <int M, int WAVES, bool NT, int LA>
 static hipError_t launch_w4a16_t(const void* x, const void* packed, int n, int k, void* y,
                                  int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
   const int kt = k / kTileK;
   (void)kt;
-  hipLaunchKernelGGL((w4a16_gemv_kernel<M, WAVES, NT>), dim3(rbs, split), dim3(WAVES * 64), 0,
+  hipLaunchKernelGGL((w4a16_gemv_kernel<M, WAVES, NT, LA>), dim3(rbs, split), dim3(WAVES * 64), 0,
                      stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
                      n, k, y, y_f32, partial, split);
   return hipGetLastError();
@@ -277,13 +307,14 @@ size_t w4a16_gemv_smem_bytes(int m, int k, int split, int waves) {
 }
 
 hipError_t launch_w4a16_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
-                             int y_f32, float* partial, int split, int waves, bool nt,
+                             int y_f32, float* partial, int split, int waves, int la,
                              hipStream_t stream) {
-#define QG_W4_CASE(MM, WW, NTV)                                                          \
-  if (m == MM && waves == WW && nt == NTV)                                               \
-    return launch_w4a16_t<MM, WW, NTV>(x, packed, n, k, y, y_f32, partial, split, stream);
-#define QG_W4_M(MM)       \
-  QG_W4_CASE(MM, 4, false) QG_W4_CASE(MM, 8, false) QG_W4_CASE(MM, 4, true) QG_W4_CASE(MM, 8, true)
+#define QG_W4_CASE(MM, WW, LAV)                                                                \
+  if (m == MM && waves == WW && la == LAV)                                                     \
+    return launch_w4a16_t<MM, WW, true, LAV>(x, packed, n, k, y, y_f32, partial, split, stream);
+#define QG_W4_M(MM)                                                                            \
+  QG_W4_CASE(MM, 4, 0) QG_W4_CASE(MM, 8, 0) QG_W4_CASE(MM, 16, 0)                             \
+  QG_W4_CASE(MM, 4, 1) QG_W4_CASE(MM, 8, 1) QG_W4_CASE(MM, 16, 1)
   QG_W4_M(1) QG_W4_M(2) QG_W4_M(3) QG_W4_M(4)
 #undef QG_W4_M
 #undef QG_W4_CASE

@@ -81,9 +81,14 @@ __device__ __forceinline__ u32x16_t sload16(const uint32_t* p) {
 // next scalar load right after it keeps exactly one in flight.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <typename T>
-__device__ __forceinline__ T load_stream(const T* p, bool nontemporal) {
-  return nontemporal ? __builtin_nontemporal_load(p) : *p;
+// Streaming load; NT sets the non-temporal cache policy (the weight is read
+// once per call and should not displace x or the L2-resident partials).
+template <bool NT, typename T>
+__device__ __forceinline__ T load_stream(const T* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
 }
 
 __device__ __forceinline__ int wave_id_uniform() {
