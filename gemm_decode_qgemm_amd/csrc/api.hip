@@ -24,6 +24,9 @@ hipError_t launch_w4a16_gemv(int m, const void* x, const void* packed, int n, in
 size_t w4a16_gemv_smem_bytes(int m, int k, int split, int waves);
 hipError_t launch_splitk_reduce(const float* partial, int split, int64_t mn, void* y, int y_f32,
                                 hipStream_t stream);
+int w8a16_chunks_per_wave(int k);
+hipError_t launch_w8a16_gemv(int m, const void* x, const int8_t* w, const void* scale, int n,
+                             int k, void* y, int y_f32, hipStream_t stream);
 }  // namespace qg
 
 // Launch shape of the M <= 4 GEMV: waves per workgroup and look-ahead (in
@@ -180,9 +183,16 @@ int32_t qgemm_w4a16(const void* x_bf16, int64_t m, int64_t k, const void* packed
 
 int32_t qgemm_w8a16(const void* x_bf16, int64_t m, int64_t k, const int8_t* w,
                     const void* scale_bf16, int64_t n, void* y, int32_t y_dtype, void* stream) {
-  (void)x_bf16; (void)m; (void)k; (void)w; (void)scale_bf16; (void)n; (void)y; (void)y_dtype;
-  (void)stream;
-  return QG_E_HIP;
+  if (!x_bf16 || !w || !scale_bf16 || !y) return QG_E_NULL;
+  int32_t st = check_mnk(m, n, k);
+  if (st != QG_OK) return st;
+  if (y_dtype != QG_BF16 && y_dtype != QG_F32) return QG_E_DTYPE;
+  if (m > 4) return QG_E_M_RANGE;
+  if (qg::w8a16_chunks_per_wave((int)k) < 0) return QG_E_SHAPE;   // K above 65536
+  if (!aligned16(x_bf16) || !aligned16(w) || !aligned16(y) || ((uintptr_t)scale_bf16 & 1u))
+    return QG_E_ALIGN;
+  return hip_status(qg::launch_w8a16_gemv((int)m, x_bf16, w, scale_bf16, (int)n, (int)k, y,
+                                          y_dtype == QG_F32, static_cast<hipStream_t>(stream)));
 }
 
 int32_t qgemm_w4a8(const void* x_bf16, int64_t m, int64_t k, const void* packed,
