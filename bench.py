@@ -34,8 +34,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "µs/call and effective weight GB/s (% HBM peak) for INT4-g32 GEMV at M=1"
 COUNTERS = os.path.join(ROOT, "profiles", "w4a16_gemv_39936x6656_m1_counters.json")
-KERNEL_SOURCES = ["gemm_decode_qgemm_amd/csrc/gemv_w4a16.hip", "gemm_decode_qgemm_amd/csrc/qg_common.h",
-                  "gemm_decode_qgemm_amd/csrc/api.hip"]
+KERNEL_SOURCES = ["gemm_decode_qgemm_amd/csrc/gemv_w4a16.hip", "gemm_decode_qgemm_amd/csrc/w4_common.h",
+                  "gemm_decode_qgemm_amd/csrc/qg_common.h", "gemm_decode_qgemm_amd/csrc/api.hip"]
 
 
 def kernel_source_hash() -> str:

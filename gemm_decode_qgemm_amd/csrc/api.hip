@@ -25,6 +25,8 @@ size_t w4a16_gemv_smem_bytes(int m, int k, int split, int waves);
 hipError_t launch_splitk_reduce(const float* partial, int split, int64_t mn, void* y, int y_f32,
                                 hipStream_t stream);
 int w8a16_chunks_per_wave(int k);
+hipError_t launch_w4a8_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
+                            int y_f32, float* partial, int split, int waves, hipStream_t stream);
 hipError_t launch_w8a16_gemv(int m, const void* x, const int8_t* w, const void* scale, int n,
                              int k, void* y, int y_f32, hipStream_t stream);
 }  // namespace qg
@@ -198,9 +200,26 @@ int32_t qgemm_w8a16(const void* x_bf16, int64_t m, int64_t k, const int8_t* w,
 int32_t qgemm_w4a8(const void* x_bf16, int64_t m, int64_t k, const void* packed,
                    int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype, int32_t split_k,
                    void* ws, int64_t ws_bytes, void* stream) {
-  (void)x_bf16; (void)m; (void)k; (void)packed; (void)packed_bytes; (void)n; (void)y;
-  (void)y_dtype; (void)split_k; (void)ws; (void)ws_bytes; (void)stream;
-  return QG_E_HIP;
+  if (!x_bf16 || !packed || !y) return QG_E_NULL;
+  int32_t st = check_mnk(m, n, k);
+  if (st != QG_OK) return st;
+  if (y_dtype != QG_BF16 && y_dtype != QG_F32) return QG_E_DTYPE;
+  if (m > 4) return QG_E_M_RANGE;
+  int32_t split;
+  st = resolve_split(m, n, k, split_k, &split);
+  if (st != QG_OK) return st;
+  if (packed_bytes < qg_int4_packed_bytes(n, k)) return QG_E_BUFFER;
+  const int64_t need_ws = split > 1 ? (int64_t)split * m * n * 4 : 0;
+  if (need_ws > 0 && (!ws || ws_bytes < need_ws)) return ws ? QG_E_BUFFER : QG_E_NULL;
+  if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || (ws && !aligned16(ws)))
+    return QG_E_ALIGN;
+  const int waves = m <= 2 ? QG_W4_WAVES_SMALL_M : QG_W4_WAVES_LARGE_M;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
+  st = hip_status(qg::launch_w4a8_gemv((int)m, x_bf16, packed, (int)n, (int)k, y,
+                                       y_dtype == QG_F32, partial, split, waves, s));
+  if (st != QG_OK || split == 1) return st;
+  return hip_status(qg::launch_splitk_reduce(partial, split, m * n, y, y_dtype == QG_F32, s));
 }
 
 }  // extern "C"

@@ -24,38 +24,9 @@
 //    split-K launch writes fp32 partials that a second pass sums in split
 //    order (no atomics: results are bit-reproducible).
 #include "qg_common.h"
+#include "w4_common.h"
 
 namespace qg {
-
-// One half tile (4 groups = 128 k) of one lane's row: 4 code chunks, the 4
-// fp16 scales (8 B) and the 4 zero points (16 bits of the row's zero word).
-struct HalfRegs {
-  u32x4_t c[4];
-  u32x2_t sc;
-  uint32_t zw;
-};
-
-template <bool NT>
-__device__ __forceinline__ void load_half(HalfRegs& r, const uint8_t* tile, int half, int lane) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    r.c[j] = load_stream<NT>(
-        reinterpret_cast<const u32x4_t*>(tile + ((4 * half + j) * kTileRows + lane) * 16));
-  // Scales and zero points of the two half tiles share 128-byte lines, and
-  // the other half is read by another wave of the same workgroup moments
-  // later: these loads keep the default (temporal) policy so that wave hits
-  // in L2 instead of fetching the line from HBM again.
-  r.sc = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + kScaleOff + lane * 16 + 8 * half));
-  r.zw = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + kZeroOff + lane * 4 + 2 * half));
-}
-
-// Split-K partition of `tiles` 256-k units into `split` contiguous ranges;
-// the first (tiles % split) ranges take one extra unit.
-__device__ __forceinline__ void split_range(int tiles, int split, int s, int& t0, int& t1) {
-  const int base = tiles / split, rem = tiles % split;
-  t0 = s * base + (s < rem ? s : rem);
-  t1 = t0 + base + (s < rem ? 1 : 0);
-}
 
 // x of one half tile (128 k = 64 dwords per row m) lives in VGPRs spread
 // over the 16 lanes of each DPP row: lane i holds dwords 4i..4i+3; the four
@@ -114,11 +85,6 @@ __device__ __forceinline__ void group_dot(float& d0, float& d1, const u32x4_t& x
   if constexpr (JJ == 3) asm(QG_DOT16(12, 13, 14, 15) QG_DOT16_OPERANDS);
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                               CTRL, 0xf, 0xf, true));
-}
 
 template <int M, int JJ>
 __device__ __forceinline__ void do_group(float (&acc)[M], const HalfRegs& cur, const XHalf<M>& xc,

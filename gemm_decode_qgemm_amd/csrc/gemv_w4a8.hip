@@ -1,0 +1,222 @@
+// gemv_w4a8.hip -- decode GEMV of the packed INT4 group-32 weight against
+// int8 activations, M = 1..4.
+//
+// executorch test_int4_quantized_gemm.py, Int4QuantizedGemmPrecisionTest:
+// the decode buckets run the INT4 weight against int8 activations and are
+// held to the W4A16 reference's precision class.  Each row of x is quantized
+// inside the call, per row and symmetric:
+//   a = max|x[m,:]|, inv = 127/a, sx = a/127 (binary32 divisions),
+//   xq = clamp(rint(x * inv), -127, 127) (one binary32 multiply), a == 0 -> 0;
+// then y[m,n] = sx[m] * sum_g s[n,g] * I[m,n,g] with the exact integer group
+// dot I = sum_{k in g} xq[m,k] * (q[n,k] - zp[n,g]).
+//
+// Mapping (gfx950, wave64), as the W4A16 GEMV: one 64-row block per
+// workgroup, lane = row, waves take half tiles (4 groups = 128 k) round robin.
+//  * Prologue: the workgroup reads its x rows once for the absmax (L2-resident).
+//  * Lane i of each 16-lane DPP row loads x[8i .. 8i+8) of the half tile and
+//    quantizes it into two dwords of int8 in the byte order the nibbles need:
+//    (w & 0x0F0F0F0F) holds the codes of k = 8d + {0,4,1,5}, ((w >> 4) &
+//    0x0F0F0F0F) those of 8d + {2,6,3,7} -- so the dwords are exactly that.
+//  * v_dot4c_i32_i8 multiplies a code dword by the xq dword broadcast from
+//    the lane holding it (DPP row_newbcast), accumulating in int32; the zero
+//    point comes off as zp * (group sum of xq), also broadcast by DPP.
+#include "qg_common.h"
+#include "w4_common.h"
+
+namespace qg {
+
+// The trailing nop: a VALU read of a DPP dot result needs two wait states the
+// compiler cannot see inside the asm (measured on MI355X for v_dot2c; applied
+// to the integer dot as well).
+#define QG_DPP_DOT4(acc, xr, wr, L) \
+  "v_dot4c_i32_i8_dpp " acc ", " xr ", " wr " row_newbcast:" #L " row_mask:0xf bank_mask:0xf\n\t"
+#define QG_DOT8(L0, L1, L2, L3)                                                               \
+  "s_nop 1\n\t"                                                                              \
+  QG_DPP_DOT4("%0", "%2", "%4", L0) QG_DPP_DOT4("%1", "%3", "%5", L0)                       \
+  QG_DPP_DOT4("%0", "%2", "%6", L1) QG_DPP_DOT4("%1", "%3", "%7", L1)                       \
+  QG_DPP_DOT4("%0", "%2", "%8", L2) QG_DPP_DOT4("%1", "%3", "%9", L2)                       \
+  QG_DPP_DOT4("%0", "%2", "%10", L3) QG_DPP_DOT4("%1", "%3", "%11", L3)                     \
+  "s_nop 2\n\t"
+#define QG_DOT8_OPERANDS                                                                    \
+  : "+v"(i0), "+v"(i1)                                                                      \
+  : "v"(xlo), "v"(xhi), "v"(lo[0]), "v"(hi[0]), "v"(lo[1]), "v"(hi[1]), "v"(lo[2]),          \
+    "v"(hi[2]), "v"(lo[3]), "v"(hi[3])
+
+// i0 += sum_d dot4(lo[d], xq_lo @ lane 4*JJ+d); i1 likewise with the high nibbles.
+template <int JJ>
+__device__ __forceinline__ void group_dot4(int& i0, int& i1, uint32_t xlo, uint32_t xhi,
+                                           const uint32_t (&lo)[4], const uint32_t (&hi)[4]) {
+  if constexpr (JJ == 0) asm(QG_DOT8(0, 1, 2, 3) QG_DOT8_OPERANDS);
+  if constexpr (JJ == 1) asm(QG_DOT8(4, 5, 6, 7) QG_DOT8_OPERANDS);
+  if constexpr (JJ == 2) asm(QG_DOT8(8, 9, 10, 11) QG_DOT8_OPERANDS);
+  if constexpr (JJ == 3) asm(QG_DOT8(12, 13, 14, 15) QG_DOT8_OPERANDS);
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, true);
+}
+
+// Quantize 8 bf16 (one 16-byte load) to int8 with the row's inverse scale,
+// packed as (q0,q4,q1,q5) and (q2,q6,q3,q7).
+__device__ __forceinline__ void quant8(const u32x4_t& v, float inv, uint32_t& xlo, uint32_t& xhi) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  int q[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float f = bf16_to_f32(h ? (w[i] >> 16) : (w[i] & 0xffffu));
+      float t = rintf(f * inv);
+      t = __builtin_amdgcn_fmed3f(t, -127.0f, 127.0f);
+      q[2 * i + h] = (int)t;
+    }
+  }
+  auto b = [&](int i) { return (uint32_t)q[i] & 0xffu; };
+  xlo = b(0) | (b(4) << 8) | (b(1) << 16) | (b(5) << 24);
+  xhi = b(2) | (b(6) << 8) | (b(3) << 16) | (b(7) << 24);
+}
+
+template <int M, int JJ>
+__device__ __forceinline__ void do_group_a8(float (&acc)[M], const HalfRegs& cur,
+                                            const uint32_t (&xlo)[M], const uint32_t (&xhi)[M],
+                                            const int (&sxq)[M], uint32_t nib_s) {
+  const u32x4_t cv = cur.c[JJ];
+  const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
+  uint32_t lo[4], hi[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    lo[d] = cw[d] & nib_s;
+    hi[d] = (cw[d] >> 4) & nib_s;
+  }
+  const uint32_t sw = (JJ < 2) ? cur.sc.x : cur.sc.y;
+  const float s = fp16_to_f32((sw >> (16 * (JJ & 1))) & 0xffffu);
+  const int zp = (int)((cur.zw >> (4 * JJ)) & 15u);
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    int i0 = 0, i1 = 0;
+    group_dot4<JJ>(i0, i1, xlo[m], xhi[m], lo, hi);
+    const int sg = dpp_i<0x150 + 4 * JJ>(sxq[m]);   // group sum of xq to every lane
+    const int ig = i0 + i1 - zp * sg;                // exact: |ig| <= 32*127*15
+    acc[m] = __builtin_fmaf(s, (float)ig, acc[m]);
+  }
+}
+
+template <int M, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void w4a8_gemv_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
+    void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
+  __shared__ float red[WAVES * M * 64];
+  __shared__ float amax_w[WAVES][M];
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15;
+  const int wave = wave_id_uniform();
+  const int rb = blockIdx.x;
+  const int kt_count = k >> 8;
+  int t0, t1;
+  split_range(kt_count, split, blockIdx.y, t0, t1);
+  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
+
+  // Per-row absmax of x over the whole K (every split needs the same scale).
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float a = 0.0f;
+    const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)m * k);
+    for (int i = threadIdx.x; i < (k >> 3); i += WAVES * 64) {
+      const u32x4_t v = xr[i];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a = fmaxf(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
+        a = fmaxf(a, fabsf(bf16_to_f32(w[j] >> 16)));
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    if (lane == 0) amax_w[wave][m] = a;
+  }
+  __syncthreads();
+  float inv[M], sx[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float a = amax_w[0][m];
+    for (int ww = 1; ww < WAVES; ++ww) a = fmaxf(a, amax_w[ww][m]);
+    inv[m] = a > 0.0f ? 127.0f / a : 0.0f;
+    sx[m] = a / 127.0f;
+  }
+
+  const uint32_t nib_s = __builtin_amdgcn_readfirstlane(0x0F0F0F0Fu);
+  uint32_t ones_v = 0x01010101u;
+  asm volatile("" : "+v"(ones_v));   // int8 ones in a VGPR, not a literal operand
+
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+
+  for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {
+    HalfRegs r;
+    load_half<true>(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lane);
+    uint32_t xlo[M], xhi[M];
+    int sxq[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + (size_t)m * k + (size_t)hs * 128 + li * 8);
+      quant8(v, inv[m], xlo[m], xhi[m]);
+      // sum of this lane's 8 xq, then over the 4 lanes of its group
+      int p = __builtin_amdgcn_sdot4((int)xlo[m], (int)ones_v, 0, false);
+      p = __builtin_amdgcn_sdot4((int)xhi[m], (int)ones_v, p, false);
+      p += dpp_i<0xB1>(p);
+      p += dpp_i<0x4E>(p);
+      sxq[m] = p;
+    }
+    do_group_a8<M, 0>(acc, r, xlo, xhi, sxq, nib_s);
+    do_group_a8<M, 1>(acc, r, xlo, xhi, sxq, nib_s);
+    do_group_a8<M, 2>(acc, r, xlo, xhi, sxq, nib_s);
+    do_group_a8<M, 3>(acc, r, xlo, xhi, sxq, nib_s);
+  }
+
+#pragma unroll
+  for (int m = 0; m < M; ++m) red[(wave * M + m) * 64 + lane] = acc[m];
+  __syncthreads();
+  for (int m = wave; m < M; m += WAVES) {
+    float v = red[m * 64 + lane];
+    for (int ww = 1; ww < WAVES; ++ww) v += red[(ww * M + m) * 64 + lane];
+    const int row = rb * kTileRows + lane;
+    if (row < n) {
+      if (partial != nullptr) {
+        // split partials stay in the unscaled integer-group domain times s;
+        // the activation scale is the same for every split, applied here
+        partial[((size_t)blockIdx.y * M + m) * n + row] = v * sx[m];
+      } else {
+        v *= sx[m];
+        if (y_f32)
+          static_cast<float*>(y)[(size_t)m * n + row] = v;
+        else
+          static_cast<uint16_t*>(y)[(size_t)m * n + row] = (uint16_t)f32_to_bf16_rne(v);
+      }
+    }
+  }
+}
+
+template <int M, int WAVES>
+static hipError_t launch_w4a8_t(const void* x, const void* packed, int n, int k, void* y,
+                                int y_f32, float* partial, int split, hipStream_t stream) {
+  const int rbs = (n + kTileRows - 1) / kTileRows;
+  hipLaunchKernelGGL((w4a8_gemv_kernel<M, WAVES>), dim3(rbs, split), dim3(WAVES * 64), 0, stream,
+                     static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed), n, k,
+                     y, y_f32, partial, split);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a8_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
+                            int y_f32, float* partial, int split, int waves, hipStream_t stream) {
+#define QG_A8_CASE(MM, WW) \
+  if (m == MM && waves == WW) return launch_w4a8_t<MM, WW>(x, packed, n, k, y, y_f32, partial, split, stream);
+#define QG_A8_M(MM) QG_A8_CASE(MM, 4) QG_A8_CASE(MM, 8) QG_A8_CASE(MM, 16)
+  QG_A8_M(1) QG_A8_M(2) QG_A8_M(3) QG_A8_M(4)
+#undef QG_A8_M
+#undef QG_A8_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qg

@@ -172,7 +172,9 @@ int32_t qgemm_w8a16(const void *x_bf16, int64_t m, int64_t k, const int8_t *w,
  * xq = clamp(rint(x * inv), -127, 127) in binary32; a == 0 gives a zero row),
  * then  y[m,n] = sx[m] * sum_g s[n,g] * sum_{k in g} xq[m,k] * (q[n,k] - zp[n,g])
  * with exact integer group dots.  Arguments and errors as qgemm_w4a16
- * (1 <= m <= 4 in this version: QG_E_M_RANGE above). */
+ * (1 <= m <= 4 in this version: QG_E_M_RANGE above).  The per-row scale is
+ * the pages' precision class on gaussian activations; rows with a few large
+ * outlier channels lose precision (finer activation groups would fix it). */
 int32_t qgemm_w4a8(const void *x_bf16, int64_t m, int64_t k, const void *packed,
                    int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
                    int32_t split_k, void *ws, int64_t ws_bytes, void *stream);
