@@ -24,7 +24,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqgemm.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.hip", "quantize.hip", "gemv_w4a16.hip", "gemv_w8a16.hip", "gemv_w4a8.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemv_w4a16.hip", "gemv_w8a16.hip", "gemv_w4a8.hip",
+           "gemm_w4a16_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -25,6 +25,8 @@ size_t w4a16_gemv_smem_bytes(int m, int k, int split, int waves);
 hipError_t launch_splitk_reduce(const float* partial, int split, int64_t mn, void* y, int y_f32,
                                 hipStream_t stream);
 int w8a16_chunks_per_wave(int k);
+hipError_t launch_w4a16_mfma(int m, const void* x, const void* packed, int n, int k, void* y,
+                             int y_f32, float* partial, int split, hipStream_t stream);
 hipError_t launch_w4a8_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
                             int y_f32, float* partial, int split, int waves, hipStream_t stream);
 hipError_t launch_w8a16_gemv(int m, const void* x, const int8_t* w, const void* scale, int n,
@@ -172,13 +174,18 @@ int32_t qgemm_w4a16(const void* x_bf16, int64_t m, int64_t k, const void* packed
   if (need_ws > 0 && (!ws || ws_bytes < need_ws)) return ws ? QG_E_BUFFER : QG_E_NULL;
   if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || (ws && !aligned16(ws)))
     return QG_E_ALIGN;
-  if (m > 4) return QG_E_M_RANGE;   // the MFMA path for 5..64 is not built yet
-  const int waves = m <= 2 ? QG_W4_WAVES_SMALL_M : QG_W4_WAVES_LARGE_M;
-  if (qg::w4a16_gemv_smem_bytes((int)m, (int)k, split, waves) > kMaxSmem) return QG_E_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
-  st = hip_status(qg::launch_w4a16_gemv((int)m, x_bf16, packed, (int)n, (int)k, y,
-                                        y_dtype == QG_F32, partial, split, waves, QG_W4_LA, s));
+  if (m > 4) {
+    // 5..64 rows: matrix-core kernel (rows padded to 16 and masked).
+    st = hip_status(qg::launch_w4a16_mfma((int)m, x_bf16, packed, (int)n, (int)k, y,
+                                          y_dtype == QG_F32, partial, split, s));
+  } else {
+    const int waves = m <= 2 ? QG_W4_WAVES_SMALL_M : QG_W4_WAVES_LARGE_M;
+    if (qg::w4a16_gemv_smem_bytes((int)m, (int)k, split, waves) > kMaxSmem) return QG_E_SHAPE;
+    st = hip_status(qg::launch_w4a16_gemv((int)m, x_bf16, packed, (int)n, (int)k, y,
+                                          y_dtype == QG_F32, partial, split, waves, QG_W4_LA, s));
+  }
   if (st != QG_OK || split == 1) return st;
   return hip_status(qg::launch_splitk_reduce(partial, split, m * n, y, y_dtype == QG_F32, s));
 }
