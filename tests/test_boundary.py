@@ -1,0 +1,175 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/qgemm.h declares, and rejects every bad argument before launching
+anything (executorch test_int4_quantized_gemm.py, Int4QuantizedGemmLegalityTest:
+every rule is checked and the op "validates before launching";
+Int4QuantizedGemmRulesTest.test_split_k_needs_one_k_tile_per_split).
+
+No call here reaches a kernel: each one carries a definite argument error, so
+these run on a machine without a GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemm.h")
+LIB = os.path.join(ROOT, "gemm_decode_qgemm_amd", "libqgemm.so")
+
+OK, E_NULL, E_SHAPE, E_K, E_M, E_SPLIT, E_BUF, E_ALIGN, E_DTYPE, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+A = 0x10000          # a fake, 16-byte aligned "device" address (never dereferenced)
+U = 0x10008          # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert os.path.exists(LIB), "build the library first (__graft_entry__.build())"
+    l = ctypes.CDLL(LIB)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    sigs = {
+        "qg_status_string": (ctypes.c_char_p, [I32]),
+        "qg_int4_packed_bytes": (I64, [I64, I64]),
+        "qg_default_split_k": (I32, [I64, I64, I64]),
+        "qg_workspace_bytes": (I64, [I64, I64, I64, I32]),
+        "quantize_int4_g32": (I32, [P, I64, I64, P, I64, P, P]),
+        "quantize_int8_rowwise": (I32, [P, I64, I64, P, P, P, P]),
+        "qgemm_w4a16": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
+        "qgemm_w8a16": (I32, [P, I64, I64, P, P, I64, P, I32, P]),
+        "qgemm_w4a8": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(l, name)
+        f.restype, f.argtypes = res, args
+    return l
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 9, names
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in qgemm.h but not exported"
+
+
+def test_status_strings(lib):
+    for code in (OK, E_NULL, E_SHAPE, E_K, E_M, E_SPLIT, E_BUF, E_ALIGN, E_DTYPE, E_HIP):
+        s = lib.qg_status_string(code).decode()
+        assert s and s != "unknown qgemm status"
+    assert "multiple of 256" in lib.qg_status_string(E_K).decode()
+    assert lib.qg_status_string(-99).decode() == "unknown qgemm status"
+
+
+def test_packed_bytes_formula(lib):
+    assert lib.qg_int4_packed_bytes(39936, 6656) == 39936 * 6656 // 2 + 39936 * 6656 // 32 * 5 // 2
+    assert lib.qg_int4_packed_bytes(257, 512) == 5 * 2 * 9472          # padded to 5 row blocks
+    assert lib.qg_int4_packed_bytes(64, 300) == E_K
+    assert lib.qg_int4_packed_bytes(0, 256) == E_SHAPE
+
+
+def test_split_rule_one_k_tile_per_split(lib):
+    for k in (256, 768, 4096):
+        for split in (1, 2, 4, 8):
+            expect = OK if split <= k // 256 else E_SPLIT
+            ws = lib.qg_workspace_bytes(1, 256, k, split)
+            assert (ws >= 0) == (expect == OK), (k, split, ws)
+    assert lib.qg_workspace_bytes(1, 256, 4096, 3) == E_SPLIT
+    assert lib.qg_workspace_bytes(4, 100, 4096, 4) == 4 * 4 * 100 * 4
+    assert lib.qg_workspace_bytes(4, 100, 4096, 1) == 0
+
+
+def test_default_split_table(lib):
+    assert lib.qg_default_split_k(1, 39936, 6656) == 1
+    assert lib.qg_default_split_k(1, 8448, 6656) == 2
+    assert lib.qg_default_split_k(1, 256, 6656) == 8
+    assert lib.qg_default_split_k(1, 256, 256) == 1       # capped by K / 256
+    assert lib.qg_default_split_k(65, 256, 256) == E_M
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, 1, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None), E_NULL),      # x
+    ((A, 1, 256, None, 1 << 20, 64, A, 0, 0, None, 0, None), E_NULL),      # packed
+    ((A, 1, 256, A, 1 << 20, 64, None, 0, 0, None, 0, None), E_NULL),      # y
+    ((A, 0, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None), E_SHAPE),        # m < 1
+    ((A, 1, 256, A, 1 << 20, 0, A, 0, 0, None, 0, None), E_SHAPE),         # n < 1
+    ((A, 1, 288, A, 1 << 20, 64, A, 0, 0, None, 0, None), E_K),            # K % 256
+    ((A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None), E_M),           # M > 64
+    ((A, 1, 256, A, 1 << 20, 64, A, 2, 0, None, 0, None), E_DTYPE),        # y_dtype
+    ((A, 1, 768, A, 1 << 20, 64, A, 0, 4, A, 1 << 20, None), E_SPLIT),     # 4 > 768/256
+    ((A, 1, 4096, A, 1 << 20, 64, A, 0, 3, A, 1 << 20, None), E_SPLIT),    # not a candidate
+    ((A, 1, 256, A, 100, 64, A, 0, 0, None, 0, None), E_BUF),              # packed too small
+    ((A, 2, 4096, A, 1 << 20, 64, A, 0, 4, A, 16, None), E_BUF),           # workspace too small
+    ((A, 2, 4096, A, 1 << 20, 64, A, 0, 4, None, 0, None), E_NULL),        # workspace missing
+    ((U, 1, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None), E_ALIGN),        # x misaligned
+    ((A, 1, 256, U, 1 << 20, 64, A, 0, 0, None, 0, None), E_ALIGN),        # packed misaligned
+])
+def test_qgemm_w4a16_and_w4a8_validate_before_launching(lib, args, expect):
+    assert lib.qgemm_w4a16(*args) == expect
+    # W4A8 shares the rules, except that it stops at M = 4 in this version
+    got = lib.qgemm_w4a8(*args)
+    assert got == expect or (expect == E_M and got == E_M)
+
+
+def test_w4a8_m_range(lib):
+    assert lib.qgemm_w4a8(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, 1, 256, A, A, 64, A, 0, None), E_NULL),
+    ((A, 1, 256, None, A, 64, A, 0, None), E_NULL),
+    ((A, 1, 256, A, None, 64, A, 0, None), E_NULL),
+    ((A, 1, 300, A, A, 64, A, 0, None), E_K),
+    ((A, 5, 256, A, A, 64, A, 0, None), E_M),
+    ((A, 1, 256, A, A, 64, A, 7, None), E_DTYPE),
+    ((A, 1, 256, A, A, 0, A, 0, None), E_SHAPE),
+    ((A, 1, 65536 + 256, A, A, 64, A, 0, None), E_SHAPE),       # K above the VGPR-resident limit
+    ((A, 1, 256, U, A, 64, A, 0, None), E_ALIGN),
+    ((A, 1, 256, A, A + 1, 64, A, 0, None), E_ALIGN),            # scale must be 2-byte aligned
+])
+def test_qgemm_w8a16_validates_before_launching(lib, args, expect):
+    assert lib.qgemm_w8a16(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, 64, 256, A, 1 << 20, None, None), E_NULL),
+    ((A, 64, 256, None, 1 << 20, None, None), E_NULL),
+    ((A, 64, 300, A, 1 << 20, None, None), E_K),
+    ((A, 0, 256, A, 1 << 20, None, None), E_SHAPE),
+    ((A, 64, 256, A, 9471, None, None), E_BUF),
+    ((A, 64, 256, A, 9472, U + 2, None), E_ALIGN),               # status word misaligned
+    ((U, 64, 256, A, 9472, None, None), E_ALIGN),
+])
+def test_quantize_int4_validates_before_launching(lib, args, expect):
+    assert lib.quantize_int4_g32(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, 4, 256, A, A, None, None), E_NULL),
+    ((A, 4, 256, None, A, None, None), E_NULL),
+    ((A, 4, 256, A, None, None, None), E_NULL),
+    ((A, 4, 100, A, A, None, None), E_K),
+    ((A, -1, 256, A, A, None, None), E_SHAPE),
+    ((A, 4, 256, U, A, None, None), E_ALIGN),
+])
+def test_quantize_int8_validates_before_launching(lib, args, expect):
+    assert lib.quantize_int8_rowwise(*args) == expect
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    """The binding raises instead of falling back to anything when the .so is missing."""
+    import importlib.util
+
+    src = os.path.join(ROOT, "gemm_decode_qgemm_amd", "binding.py")
+    copy = tmp_path / "binding.py"
+    copy.write_text(open(src).read())
+    spec = importlib.util.spec_from_file_location("binding_copy", copy)
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError, match="missing"):
+        spec.loader.exec_module(mod)
