@@ -5,9 +5,14 @@ One step = one call of the layer (host checks + the GEMV kernel, plus the
 split-K pass when the shape uses one) on one activation row.  Inputs are
 resident in HBM before the timed region.  Consecutive calls read different
 copies of the packed weight (ceil(1 GiB / bytes) copies), so the 256 MB
-Infinity Cache cannot serve a weight from the previous call; the K timed
-calls are captured once in a HIP graph and replayed, bracketed by device
-synchronizations, and timed with events on the stream the kernels run on.
+Infinity Cache cannot serve a weight from the previous call.  The calls are
+captured in a HIP graph of C = max(200, 2 * copies) calls, and the K timed
+calls are ceil(K / C) back-to-back replays (the last one shorter when C does
+not divide K), bracketed by device synchronizations; an event on the stream
+the kernels run on is recorded between replays, so the whole timed region and
+each replay are timed on the GPU's clock.  value = K calls / the whole timed
+region; the median, min and p90 of the per-replay time per call are reported
+beside it.
 
 Effective weight bytes per call = N*K/2 (codes) + N*K/32 * 2.5 (fp16 scale +
 4-bit zero per group of 32), the packed buffer size.  The roofline is HBM
@@ -66,12 +71,16 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2000)
-    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=1000,
+                   help="untimed calls first; the clocks take a few hundred calls to ramp up from idle")
     p.add_argument("--n", type=int, default=39936)
     p.add_argument("--k", type=int, default=6656)
     p.add_argument("--m", type=int, default=1)
     p.add_argument("--split", type=int, default=0, help="split-K (0 = library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run plain device-to-device copies of the packed-weight size (for scaling "
+                        "the FETCH_SIZE / WRITE_SIZE counters to bytes), then exit")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="rough budget of CPU work for the oracle sample")
     return p.parse_args()
@@ -94,11 +103,13 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     n, k, m = args.n, args.k, args.m
+    bytes_eff = qg.int4_packed_bytes(n, k)
+    if args.calibrate_copy:
+        return calibrate_copy(torch, dev, bytes_eff)
     if (n, k) in si.MODEL_SHAPES:
         w_cpu, x_cpu = si.decode_inputs(n, k, m)
     else:
         w_cpu, x_cpu = si.int4_weight(n, k, n ^ k), si.activation(m, k, 9100 + m)
-    bytes_eff = qg.int4_packed_bytes(n, k)
     split = args.split or qg.default_split_k(m, n, k)
 
     packed0 = qg.quantize_int4_g32(w_cpu.to(dev))
@@ -117,31 +128,39 @@ def main() -> int:
     for i in range(min(args.warmup, 20)):
         call(i)
     torch.cuda.synchronize()
+    chunk = min(args.steps, max(200, 2 * copies))
+    full, rest = divmod(args.steps, chunk)
     stream = torch.cuda.Stream()
-    g_warm, g_timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    g_warm, g_chunk, g_rest = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), None
     with torch.cuda.stream(stream):
         with torch.cuda.graph(g_warm, stream=stream):
             for i in range(max(args.warmup, 1)):
                 call(i)
-        with torch.cuda.graph(g_timed, stream=stream):
-            for i in range(args.steps):
+        with torch.cuda.graph(g_chunk, stream=stream):
+            for i in range(chunk):
                 call(i)
+        if rest:
+            g_rest = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_rest, stream=stream):
+                for i in range(rest):
+                    call(i)
     torch.cuda.synchronize()
-    y_first = None
 
+    replays = [g_chunk] * full + ([g_rest] if rest else [])
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(len(replays) + 1)]
     with torch.cuda.stream(stream):
         g_warm.replay()
         torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
         t0 = time.perf_counter()
-        ev0.record(stream)
-        g_timed.replay()
-        ev1.record(stream)
+        events[0].record(stream)
+        for g, ev in zip(replays, events[1:]):
+            g.replay()
+            ev.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-    ms_total = ev0.elapsed_time(ev1)
+    ms_total = events[0].elapsed_time(events[-1])
     us_call = ms_total * 1e3 / args.steps
+    per_replay = sorted(events[i].elapsed_time(events[i + 1]) * 1e3 / chunk for i in range(full))
     gbs = bytes_eff / (us_call * 1e-6) / 1e9
     y_first = y.clone()
 
@@ -164,7 +183,13 @@ def main() -> int:
             "workload": f"W4A16 INT4-g32 asymmetric GEMV {n}x{k} M={m}",
             "n": n, "k": k, "m": m, "split_k": split, "bytes_eff_per_call": bytes_eff,
             "codes_only_gbs": round((n * k / 2) / (us_call * 1e-6) / 1e9, 2),
-            "rotating_weight_copies": copies, "timing": "HIP graph of K calls, events on its stream",
+            "rotating_weight_copies": copies,
+            "timing": f"{full} replays of a {chunk}-call HIP graph" + (f" + one of {rest}" if rest else "")
+                      + ", events on its stream",
+            "us_per_call_replay": {"median": round(float(np.median(per_replay)), 3) if per_replay else None,
+                                   "min": round(per_replay[0], 3) if per_replay else None,
+                                   "p90": round(float(np.percentile(per_replay, 90)), 3) if per_replay else None},
+            "hip_runtime": torch.version.hip,
             "wall_s": round(wall, 4),
         },
         "roofline": {
@@ -181,6 +206,21 @@ def main() -> int:
         out["cpu_baseline"] = cpu_baseline(args, w_cpu, x_cpu, y_first, bytes_eff)
 
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def calibrate_copy(torch, dev, nbytes):
+    """Plain copies of nbytes each (rotating sources, as the timed GEMV reads
+    its weight): under a counter profiler, FETCH_SIZE and WRITE_SIZE of these
+    copies give the counters' scale to bytes."""
+    copies = max(2, math.ceil((1 << 30) / nbytes))
+    src = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev) for _ in range(copies)]
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    for i in range(3 * copies):
+        dst.copy_(src[i % copies])
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_per_copy": nbytes, "copies": 3 * copies}), flush=True)
     return 0
 
 
@@ -202,7 +242,7 @@ def cpu_baseline(args, w_cpu, x_cpu, y_gpu, bytes_eff):
         t0 = time.perf_counter()
         ref = oracle.qgemm_w4a16(xb, codes, scales, zeros, threads=threads)
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > args.cpu_seconds or len(times) >= 50:
+        if time.perf_counter() - t_start > args.cpu_seconds:
             break
     t = float(np.median(times))
     y = y_gpu.float().cpu().numpy().astype(np.float64)
@@ -219,7 +259,8 @@ def cpu_baseline(args, w_cpu, x_cpu, y_gpu, bytes_eff):
         "cores": threads,
         "kind": "oracle",
         "us_per_call": round(t * 1e6, 1),
-        "sample": f"{len(times)} full calls ({args.n}x{args.k}, M={args.m}), median",
+        "sample": f"{len(times)} full calls ({args.n}x{args.k}, M={args.m}) in "
+                  f"{time.perf_counter() - t_start:.1f} s, median per call",
         "gpu_vs_oracle": {"max_abs_err": float(err.max()),
                           "mean_rel_err": float(err.mean() / mean_ref),
                           "within_tolerance": within},

@@ -19,37 +19,24 @@ hipError_t launch_quantize_int4_g32(const void* w, int64_t n, int64_t k, void* p
 hipError_t launch_quantize_int8_rowwise(const void* w, int64_t n, int64_t k, int8_t* q,
                                         void* scales, uint32_t* status, hipStream_t stream);
 hipError_t launch_w4a16_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
-                             int y_f32, float* partial, int split, int waves, int la,
-                             hipStream_t stream);
-size_t w4a16_gemv_smem_bytes(int m, int k, int split, int waves);
+                             int y_f32, float* partial, int split, int waves, hipStream_t stream);
+hipError_t launch_w4a16_gemv32(int m, const void* x, const void* packed, int n, int k, void* y,
+                               int y_f32, float* partial, int split, int waves, hipStream_t stream);
 hipError_t launch_splitk_reduce(const float* partial, int split, int64_t mn, void* y, int y_f32,
                                 hipStream_t stream);
 int w8a16_chunks_per_wave(int k);
 hipError_t launch_w4a16_mfma(int m, const void* x, const void* packed, int n, int k, void* y,
                              int y_f32, float* partial, int split, hipStream_t stream);
 hipError_t launch_w4a8_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
-                            int y_f32, float* partial, int split, int waves, hipStream_t stream);
+                            int y_f32, float* partial, int split, int rows, int waves,
+                            hipStream_t stream);
 hipError_t launch_w8a16_gemv(int m, const void* x, const int8_t* w, const void* scale, int n,
                              int k, void* y, int y_f32, hipStream_t stream);
 }  // namespace qg
 
-// Launch shape of the M <= 4 GEMV: waves per workgroup and look-ahead (in
-// half tiles), measured on MI355X at the decode layer shapes (weights read
-// with non-temporal loads).  Defaults can be overridden at build time.
-#ifndef QG_W4_WAVES_SMALL_M
-#define QG_W4_WAVES_SMALL_M 16   // M = 1, 2
-#endif
-#ifndef QG_W4_WAVES_LARGE_M
-#define QG_W4_WAVES_LARGE_M 8    // M = 3, 4
-#endif
-#ifndef QG_W4_LA
-#define QG_W4_LA 0
-#endif
-
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;   // n, k fit the kernels' int32 indexing
-constexpr size_t kMaxSmem = 64 * 1024;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -69,19 +56,42 @@ int32_t check_mnk(int64_t m, int64_t n, int64_t k) {
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? QG_OK : QG_E_HIP; }
 
-// Split-K default: the smallest legal split whose grid gives every one of the
-// 256 CUs a workgroup (row blocks x split >= 240), capped by K/256 and 8.
+constexpr int64_t kCUs = 256;   // compute units of an MI355X
+
+// Split-K default, measured on MI355X at the decode layer shapes.
+//  * M <= 4 (GEMV, 32-row workgroups): one split whenever the grid has at
+//    least half a workgroup per CU (N >= 4096): a second split costs a second
+//    launch and the partials' traffic, which the extra parallelism does not
+//    repay at these shapes; below that, the smallest split giving 32
+//    workgroups, at most 4 (N = 256, K = 6656: 5.5 us at 4 against 5.9 at 1).
+//  * M > 4 (matrix-core kernel, 64-row workgroups): the smallest split with
+//    row blocks x split >= 240, at most 8.
+// Both are capped by K / 256 (one tile per split).
 int32_t default_split(int64_t m, int64_t n, int64_t k) {
-  (void)m;
-  const int64_t rbs = (n + QG_TILE_ROWS - 1) / QG_TILE_ROWS;
   const int64_t kt = k / QG_TILE_K;
-  int32_t best = 1;
-  for (int32_t s = 1; s <= 8; s *= 2) {
-    if (s > kt) break;
-    best = s;
-    if (rbs * s >= 240) break;
+  int32_t s = 1;
+  if (m <= 4) {
+    const int64_t n32 = (n + 31) / 32;
+    if (n32 >= kCUs / 2) return 1;
+    while (s < 4 && 2 * s <= kt && n32 * s < 32) s *= 2;
+    return s;
   }
-  return best;
+  const int64_t rbs = (n + QG_TILE_ROWS - 1) / QG_TILE_ROWS;
+  while (s < 8 && 2 * s <= kt && rbs * s < 240) s *= 2;
+  return s;
+}
+
+// Workgroup shape of the M <= 4 INT4 GEMVs: 32 rows and 16 waves, except
+// where the 32-row grid spills a few workgroups into a second round over the
+// CUs while the 64-row grid fits in one (N = 8448: 264 against 132
+// workgroups; 9.1 us against 10.2 at M = 1), for M <= 2 and one split.
+struct GemvShape {
+  int rows, waves;
+};
+GemvShape gemv_shape(int64_t m, int64_t n, int32_t split) {
+  const int64_t n32 = (n + 31) / 32, n64 = (n + 63) / 64;
+  if (m <= 2 && split == 1 && n32 > kCUs && n64 <= kCUs) return {64, 16};
+  return {32, 16};
 }
 
 int32_t resolve_split(int64_t m, int64_t n, int64_t k, int32_t split_k, int32_t* out) {
@@ -181,10 +191,13 @@ int32_t qgemm_w4a16(const void* x_bf16, int64_t m, int64_t k, const void* packed
     st = hip_status(qg::launch_w4a16_mfma((int)m, x_bf16, packed, (int)n, (int)k, y,
                                           y_dtype == QG_F32, partial, split, s));
   } else {
-    const int waves = m <= 2 ? QG_W4_WAVES_SMALL_M : QG_W4_WAVES_LARGE_M;
-    if (qg::w4a16_gemv_smem_bytes((int)m, (int)k, split, waves) > kMaxSmem) return QG_E_SHAPE;
-    st = hip_status(qg::launch_w4a16_gemv((int)m, x_bf16, packed, (int)n, (int)k, y,
-                                          y_dtype == QG_F32, partial, split, waves, QG_W4_LA, s));
+    const GemvShape g = gemv_shape(m, n, split);
+    if (g.rows == 32)
+      st = hip_status(qg::launch_w4a16_gemv32((int)m, x_bf16, packed, (int)n, (int)k, y,
+                                              y_dtype == QG_F32, partial, split, g.waves, s));
+    else
+      st = hip_status(qg::launch_w4a16_gemv((int)m, x_bf16, packed, (int)n, (int)k, y,
+                                            y_dtype == QG_F32, partial, split, g.waves, s));
   }
   if (st != QG_OK || split == 1) return st;
   return hip_status(qg::launch_splitk_reduce(partial, split, m * n, y, y_dtype == QG_F32, s));
@@ -220,11 +233,11 @@ int32_t qgemm_w4a8(const void* x_bf16, int64_t m, int64_t k, const void* packed,
   if (need_ws > 0 && (!ws || ws_bytes < need_ws)) return ws ? QG_E_BUFFER : QG_E_NULL;
   if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || (ws && !aligned16(ws)))
     return QG_E_ALIGN;
-  const int waves = m <= 2 ? QG_W4_WAVES_SMALL_M : QG_W4_WAVES_LARGE_M;
+  const GemvShape g = gemv_shape(m, n, split);
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
   st = hip_status(qg::launch_w4a8_gemv((int)m, x_bf16, packed, (int)n, (int)k, y,
-                                       y_dtype == QG_F32, partial, split, waves, s));
+                                       y_dtype == QG_F32, partial, split, g.rows, g.waves, s));
   if (st != QG_OK || split == 1) return st;
   return hip_status(qg::launch_splitk_reduce(partial, split, m * n, y, y_dtype == QG_F32, s));
 }

@@ -88,7 +88,8 @@ __device__ __forceinline__ void group_dot(float& d0, float& d1, const u32x4_t& x
 
 template <int M, int JJ>
 __device__ __forceinline__ void do_group(float (&acc)[M], const HalfRegs& cur, const XHalf<M>& xc,
-                                         const float (&xq)[M], uint32_t mask_s, uint32_t magic_v) {
+                                         const float (&xq)[M], const float (&zb)[4],
+                                         uint32_t mask_s, uint32_t magic_v) {
   const u32x4_t cv = cur.c[JJ];
   const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
   uint32_t pr[16];
@@ -98,14 +99,13 @@ __device__ __forceinline__ void do_group(float (&acc)[M], const HalfRegs& cur, c
     for (int i = 0; i < 4; ++i) pr[4 * d + i] = nibble_pair_bf16(cw[d], i, mask_s, magic_v);
   const uint32_t sw = (JJ < 2) ? cur.sc.x : cur.sc.y;
   const float s = fp16_to_f32((sw >> (16 * (JJ & 1))) & 0xffffu);
-  const float zb = (float)(((cur.zw >> (4 * JJ)) & 15u) + 128u);
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    float d0 = 0.0f, d1 = 0.0f;
-    group_dot<JJ>(d0, d1, xc.v[m], pr);
+    // The dot starts from -(128 + zp) * X_g, so it ends at sum x * (q - zp).
     const float xg = dpp_mov<0x150 + 4 * JJ>(xq[m]);   // X of group JJ to every lane
-    const float tg = __builtin_fmaf(-zb, xg, d0 + d1);
-    acc[m] = __builtin_fmaf(s, tg, acc[m]);
+    float d0 = -zb[JJ] * xg, d1 = 0.0f;
+    group_dot<JJ>(d0, d1, xc.v[m], pr);
+    acc[m] = __builtin_fmaf(s, d0 + d1, acc[m]);
   }
 }
 
@@ -128,17 +128,23 @@ __device__ __forceinline__ void half_compute(float (&acc)[M], const HalfRegs& cu
     p += dpp_mov<0x4E>(p);
     xq[m] = p;
   }
-  do_group<M, 0>(acc, cur, xc, xq, mask_s, magic_v);
-  do_group<M, 1>(acc, cur, xc, xq, mask_s, magic_v);
-  do_group<M, 2>(acc, cur, xc, xq, mask_s, magic_v);
-  do_group<M, 3>(acc, cur, xc, xq, mask_s, magic_v);
+  // 128 + zp of the 4 groups: the zero nibbles spread to bytes with 0x80 set,
+  // then one byte-to-float conversion each.
+  const uint32_t z02 = (cur.zw & 0x0F0Fu) | 0x8080u;          // groups 0, 2
+  const uint32_t z13 = ((cur.zw >> 4) & 0x0F0Fu) | 0x8080u;   // groups 1, 3
+  const float zb[4] = {(float)(z02 & 0xffu), (float)(z13 & 0xffu), (float)(z02 >> 8),
+                       (float)(z13 >> 8)};
+  do_group<M, 0>(acc, cur, xc, xq, zb, mask_s, magic_v);
+  do_group<M, 1>(acc, cur, xc, xq, zb, mask_s, magic_v);
+  do_group<M, 2>(acc, cur, xc, xq, zb, mask_s, magic_v);
+  do_group<M, 3>(acc, cur, xc, xq, zb, mask_s, magic_v);
 }
 
 // Work unit = half tile.  Wave w of a workgroup takes half tiles w, w+WAVES,
-// ... of its row block's split-K range.  LA = look-ahead: the loads of the
-// next LA units are in flight while a unit computes (register sets used in a
-// ring, unrolled, so no copies); LA = 0 loads, waits and computes.
-template <int M, int WAVES, bool NT, int LA>
+// ... of its row block's split-K range: load, wait, compute (the other
+// resident waves keep the memory system busy; a register look-ahead of one or
+// two units measured no faster on MI355X).
+template <int M, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -167,50 +173,12 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 
-  const int s1 = 2 * t1;
-  int hs = 2 * t0 + wave;   // half-tile index along k (tile hs/2, half hs%2)
-  auto load = [&](HalfRegs& r, XHalf<M>& xr, int h) {
-    load_half<NT>(r, tiles + (size_t)(h >> 1) * kTileBytes, h & 1, lane);
-    load_xhalf<M>(xr, x32, k32, h, li);
-  };
-  if constexpr (LA == 0) {
-    for (; hs < s1; hs += WAVES) {
-      HalfRegs r;
-      XHalf<M> xr;
-      load(r, xr, hs);
-      half_compute<M>(acc, r, xr, mask_s, magic_v, ones_v);
-    }
-  } else if constexpr (LA == 1) {
-    HalfRegs ra, rb2;
-    XHalf<M> xa, xb;
-    if (hs < s1) load(ra, xa, hs);
-    while (hs < s1) {
-      if (hs + WAVES < s1) load(rb2, xb, hs + WAVES);
-      half_compute<M>(acc, ra, xa, mask_s, magic_v, ones_v);
-      hs += WAVES;
-      if (hs >= s1) break;
-      if (hs + WAVES < s1) load(ra, xa, hs + WAVES);
-      half_compute<M>(acc, rb2, xb, mask_s, magic_v, ones_v);
-      hs += WAVES;
-    }
-  } else {
-    HalfRegs r0, r1, r2;
-    XHalf<M> x0, x1, x2;
-    if (hs < s1) load(r0, x0, hs);
-    if (hs + WAVES < s1) load(r1, x1, hs + WAVES);
-    while (hs < s1) {
-      if (hs + 2 * WAVES < s1) load(r2, x2, hs + 2 * WAVES);
-      half_compute<M>(acc, r0, x0, mask_s, magic_v, ones_v);
-      hs += WAVES;
-      if (hs >= s1) break;
-      if (hs + 2 * WAVES < s1) load(r0, x0, hs + 2 * WAVES);
-      half_compute<M>(acc, r1, x1, mask_s, magic_v, ones_v);
-      hs += WAVES;
-      if (hs >= s1) break;
-      if (hs + 2 * WAVES < s1) load(r1, x1, hs + 2 * WAVES);
-      half_compute<M>(acc, r2, x2, mask_s, magic_v, ones_v);
-      hs += WAVES;
-    }
+  for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {   // tile hs/2, half hs%2
+    HalfRegs r;
+    XHalf<M> xr;
+    load_half<true>(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lane);
+    load_xhalf<M>(xr, x32, k32, hs, li);
+    half_compute<M>(acc, r, xr, mask_s, magic_v, ones_v);
   }
 
   // Cross-wave sum in wave order (fixed, so repeat calls are bit-identical).
@@ -229,6 +197,134 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
       } else {
         static_cast<uint16_t*>(y)[(size_t)m * n + row] = (uint16_t)f32_to_bf16_rne(v);
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 32-row variant.  A workgroup owns 32 rows of a 64-row block (the tile's
+// 128-byte lines hold 8 rows each, so halves of a block never share a code
+// line), which doubles the number of workgroups and evens out the work per CU
+// when the row-block count is not a multiple of the CU count.  Lanes 0-31 take
+// groups {0,1} of each half tile for rows 0-31, lanes 32-63 groups {2,3}; each
+// wave-wide code load is two runs of 512 contiguous bytes.  x of a half tile
+// sits 2 dwords per lane: DPP rows 0-1 hold groups {0,1}, rows 2-3 {2,3}
+// (Half32Regs / load_half32 in w4_common.h).
+#define QG_DOT16_2R(L0, L1, L2, L3, L4, L5, L6, L7)                                       \
+  "s_nop 1\n\t"                                                                            \
+  QG_DPP_DOT("%0", "%2", "%4", L0) QG_DPP_DOT("%1", "%3", "%5", L0)                        \
+  QG_DPP_DOT("%0", "%2", "%6", L1) QG_DPP_DOT("%1", "%3", "%7", L1)                        \
+  QG_DPP_DOT("%0", "%2", "%8", L2) QG_DPP_DOT("%1", "%3", "%9", L2)                        \
+  QG_DPP_DOT("%0", "%2", "%10", L3) QG_DPP_DOT("%1", "%3", "%11", L3)                      \
+  QG_DPP_DOT("%0", "%2", "%12", L4) QG_DPP_DOT("%1", "%3", "%13", L4)                      \
+  QG_DPP_DOT("%0", "%2", "%14", L5) QG_DPP_DOT("%1", "%3", "%15", L5)                      \
+  QG_DPP_DOT("%0", "%2", "%16", L6) QG_DPP_DOT("%1", "%3", "%17", L6)                      \
+  QG_DPP_DOT("%0", "%2", "%18", L7) QG_DPP_DOT("%1", "%3", "%19", L7)                      \
+  "s_nop " QG_STR(QG_DOT_TAIL_NOP) "\n\t"
+#define QG_DOT16_2R_OPERANDS                                                               \
+  : "+v"(d0), "+v"(d1)                                                                     \
+  : "v"(xv.x), "v"(xv.y), "v"(pr[0]), "v"(pr[1]), "v"(pr[2]), "v"(pr[3]), "v"(pr[4]),      \
+    "v"(pr[5]), "v"(pr[6]), "v"(pr[7]), "v"(pr[8]), "v"(pr[9]), "v"(pr[10]), "v"(pr[11]),  \
+    "v"(pr[12]), "v"(pr[13]), "v"(pr[14]), "v"(pr[15])
+
+template <int JJ>
+__device__ __forceinline__ void group_dot_2r(float& d0, float& d1, const u32x2_t& xv,
+                                             const uint32_t (&pr)[16]) {
+  if constexpr (JJ == 0) asm(QG_DOT16_2R(0, 1, 2, 3, 4, 5, 6, 7) QG_DOT16_2R_OPERANDS);
+  if constexpr (JJ == 1) asm(QG_DOT16_2R(8, 9, 10, 11, 12, 13, 14, 15) QG_DOT16_2R_OPERANDS);
+}
+
+template <int M, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void w4a16_gemv32_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
+    void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
+  __shared__ float red[WAVES * M * 64];
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15;
+  const int lg = lane >> 5;                       // group pair of this lane
+  const int wave = wave_id_uniform();
+  const int rb = blockIdx.x >> 1;                 // 64-row block
+  const int row = 32 * (blockIdx.x & 1) + (lane & 31);   // row within the block
+  const int kt_count = k >> 8;
+  int t0, t1;
+  split_range(kt_count, split, blockIdx.y, t0, t1);
+  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
+  const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
+  const int k32 = k >> 1;
+  const uint32_t mask_s = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+  uint32_t magic_v = 0x43004300u;
+  asm volatile("" : "+v"(magic_v));
+  uint32_t ones_v = 0x3f803f80u;   // bf16 (1, 1), kept out of literal operands
+  asm volatile("" : "+v"(ones_v));
+
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+
+  for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {
+    Half32Regs r;
+    load_half32<true>(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lg, row);
+    u32x2_t xv[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      xv[m] = *reinterpret_cast<const u32x2_t*>(x32 + (size_t)m * k32 + (size_t)hs * 64 + 32 * lg + 2 * li);
+    // group sums: 8 lanes per group (quad_perm [1,0,3,2], [2,3,0,1], half-row mirror)
+    float xq[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float p = dot2_bf16(xv[m].x, ones_v, 0.0f);
+      p = dot2_bf16(xv[m].y, ones_v, p);
+      p += dpp_mov<0xB1>(p);
+      p += dpp_mov<0x4E>(p);
+      p += dpp_mov<0x141>(p);
+      xq[m] = p;
+    }
+    const float zb0 = (float)((r.zb & 15u) | 0x80u);          // 128 + zp
+    const float zb1 = (float)(((r.zb >> 4) & 15u) | 0x80u);
+    const float s0 = fp16_to_f32(r.sc & 0xffffu);
+    const float s1 = fp16_to_f32(r.sc >> 16);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const u32x4_t cv = r.c[jj];
+      const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
+      uint32_t pr[16];
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[4 * d + i] = nibble_pair_bf16(cw[d], i, mask_s, magic_v);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float xg = jj == 0 ? dpp_mov<0x150>(xq[m]) : dpp_mov<0x158>(xq[m]);
+        float d0 = -(jj == 0 ? zb0 : zb1) * xg, d1 = 0.0f;
+        if (jj == 0)
+          group_dot_2r<0>(d0, d1, xv[m], pr);
+        else
+          group_dot_2r<1>(d0, d1, xv[m], pr);
+        acc[m] = __builtin_fmaf(jj == 0 ? s0 : s1, d0 + d1, acc[m]);
+      }
+    }
+  }
+
+  // Sum over waves and over the two lane halves (same row), in a fixed order.
+#pragma unroll
+  for (int m = 0; m < M; ++m) red[(wave * M + m) * 64 + lane] = acc[m];
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < 32 * M) {
+    const int m = t >> 5, l = t & 31;
+    float v = 0.0f;
+    for (int w = 0; w < WAVES; ++w) {
+      v += red[(w * M + m) * 64 + l];
+      v += red[(w * M + m) * 64 + l + 32];
+    }
+    const int col = rb * kTileRows + 32 * (blockIdx.x & 1) + l;
+    if (col < n) {
+      if (partial != nullptr)
+        partial[((size_t)blockIdx.y * M + m) * n + col] = v;
+      else if (y_f32)
+        static_cast<float*>(y)[(size_t)m * n + col] = v;
+      else
+        static_cast<uint16_t*>(y)[(size_t)m * n + col] = (uint16_t)f32_to_bf16_rne(v);
     }
   }
 }
@@ -254,33 +350,42 @@ hipError_t launch_splitk_reduce(const float* partial, int split, int64_t mn, voi
   return hipGetLastError();
 }
 
-template <int M, int WAVES, bool NT, int LA>
+template <int M, int WAVES>
 static hipError_t launch_w4a16_t(const void* x, const void* packed, int n, int k, void* y,
                                  int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  const int kt = k / kTileK;
-  (void)kt;
-  hipLaunchKernelGGL((w4a16_gemv_kernel<M, WAVES, NT, LA>), dim3(rbs, split), dim3(WAVES * 64), 0,
+  hipLaunchKernelGGL((w4a16_gemv_kernel<M, WAVES>), dim3(rbs, split), dim3(WAVES * 64), 0,
                      stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
                      n, k, y, y_f32, partial, split);
   return hipGetLastError();
 }
 
-// Shared-memory bytes the GEMV needs (the host checks it against the limit).
-size_t w4a16_gemv_smem_bytes(int m, int k, int split, int waves) {
-  (void)k; (void)split;
-  return (size_t)(waves * m * 64) * sizeof(float);
+template <int M, int WAVES>
+static hipError_t launch_w4a16_32_t(const void* x, const void* packed, int n, int k, void* y,
+                                    int y_f32, float* partial, int split, hipStream_t stream) {
+  const int rbs = (n + kTileRows - 1) / kTileRows;
+  hipLaunchKernelGGL((w4a16_gemv32_kernel<M, WAVES>), dim3(2 * rbs, split), dim3(WAVES * 64),
+                     0, stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
+                     n, k, y, y_f32, partial, split);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a16_gemv32(int m, const void* x, const void* packed, int n, int k, void* y,
+                               int y_f32, float* partial, int split, int waves, hipStream_t stream) {
+#define QG_W32_CASE(MM, WW) \
+  if (m == MM && waves == WW) return launch_w4a16_32_t<MM, WW>(x, packed, n, k, y, y_f32, partial, split, stream);
+#define QG_W32_M(MM) QG_W32_CASE(MM, 8) QG_W32_CASE(MM, 16)
+  QG_W32_M(1) QG_W32_M(2) QG_W32_M(3) QG_W32_M(4)
+#undef QG_W32_M
+#undef QG_W32_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_w4a16_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
-                             int y_f32, float* partial, int split, int waves, int la,
-                             hipStream_t stream) {
-#define QG_W4_CASE(MM, WW, LAV)                                                                \
-  if (m == MM && waves == WW && la == LAV)                                                     \
-    return launch_w4a16_t<MM, WW, true, LAV>(x, packed, n, k, y, y_f32, partial, split, stream);
-#define QG_W4_M(MM)                                                                            \
-  QG_W4_CASE(MM, 4, 0) QG_W4_CASE(MM, 8, 0) QG_W4_CASE(MM, 16, 0)                             \
-  QG_W4_CASE(MM, 4, 1) QG_W4_CASE(MM, 8, 1) QG_W4_CASE(MM, 16, 1)
+                             int y_f32, float* partial, int split, int waves, hipStream_t stream) {
+#define QG_W4_CASE(MM, WW) \
+  if (m == MM && waves == WW) return launch_w4a16_t<MM, WW>(x, packed, n, k, y, y_f32, partial, split, stream);
+#define QG_W4_M(MM) QG_W4_CASE(MM, 8) QG_W4_CASE(MM, 16)
   QG_W4_M(1) QG_W4_M(2) QG_W4_M(3) QG_W4_M(4)
 #undef QG_W4_M
 #undef QG_W4_CASE

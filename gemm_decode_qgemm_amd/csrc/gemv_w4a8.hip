@@ -11,7 +11,8 @@
 // dot I = sum_{k in g} xq[m,k] * (q[n,k] - zp[n,g]).
 //
 // Mapping (gfx950, wave64), as the W4A16 GEMV: one 64-row block per
-// workgroup, lane = row, waves take half tiles (4 groups = 128 k) round robin.
+// workgroup, lane = row, waves take half tiles (4 groups = 128 k) round robin
+// (a 32-row variant below halves the block, as the W4A16 one does).
 //  * Prologue: the workgroup reads its x rows once for the absmax (L2-resident).
 //  * Lane i of each 16-lane DPP row loads x[8i .. 8i+8) of the half tile and
 //    quantizes it into two dwords of int8 in the byte order the nibbles need:
@@ -198,6 +199,145 @@ __global__ __launch_bounds__(WAVES * 64) void w4a8_gemv_kernel(
   }
 }
 
+// 32-row variant (the mapping of Half32Regs): lanes 0-31 take groups {0,1}
+// of each half tile, lanes 32-63 groups {2,3}, for the same 32 rows.  Each
+// DPP row holds its lane half's 64 k: lane i quantizes the 8-k segment i % 8,
+// so the code dword d of local group jj meets the xq of lane 4*jj + d, as in
+// group_dot4<0> and group_dot4<1> above (lanes 8-15 repeat lanes 0-7).
+template <int M, int JJ>
+__device__ __forceinline__ void do_group_a8_32(float (&acc)[M], const Half32Regs& cur,
+                                               const uint32_t (&xlo)[M], const uint32_t (&xhi)[M],
+                                               const int (&sxq)[M], uint32_t nib_s) {
+  const u32x4_t cv = cur.c[JJ];
+  const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
+  uint32_t lo[4], hi[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    lo[d] = cw[d] & nib_s;
+    hi[d] = (cw[d] >> 4) & nib_s;
+  }
+  const float s = fp16_to_f32(JJ == 0 ? (cur.sc & 0xffffu) : (cur.sc >> 16));
+  const int zp = (int)((cur.zb >> (4 * JJ)) & 15u);
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    int i0 = 0, i1 = 0;
+    group_dot4<JJ>(i0, i1, xlo[m], xhi[m], lo, hi);
+    const int sg = dpp_i<0x150 + 4 * JJ>(sxq[m]);   // group sum of xq to every lane
+    const int ig = i0 + i1 - zp * sg;                // exact: |ig| <= 32*127*15
+    acc[m] = __builtin_fmaf(s, (float)ig, acc[m]);
+  }
+}
+
+template <int M, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void w4a8_gemv32_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
+    void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
+  __shared__ float red[WAVES * M * 64];
+  __shared__ float amax_w[WAVES][M];
+  const int lane = threadIdx.x & 63;
+  const int seg = lane & 7;                        // 8-k segment of this lane's 64-k window
+  const int lg = lane >> 5;                        // group pair of this lane
+  const int wave = wave_id_uniform();
+  const int rb = blockIdx.x >> 1;                  // 64-row block
+  const int row = 32 * (blockIdx.x & 1) + (lane & 31);
+  const int kt_count = k >> 8;
+  int t0, t1;
+  split_range(kt_count, split, blockIdx.y, t0, t1);
+  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
+
+  // Per-row absmax of x over the whole K (every split needs the same scale).
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float a = 0.0f;
+    const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)m * k);
+    for (int i = threadIdx.x; i < (k >> 3); i += WAVES * 64) {
+      const u32x4_t v = xr[i];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a = fmaxf(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
+        a = fmaxf(a, fabsf(bf16_to_f32(w[j] >> 16)));
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    if (lane == 0) amax_w[wave][m] = a;
+  }
+  __syncthreads();
+  float inv[M], sx[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float a = amax_w[0][m];
+    for (int ww = 1; ww < WAVES; ++ww) a = fmaxf(a, amax_w[ww][m]);
+    inv[m] = a > 0.0f ? 127.0f / a : 0.0f;
+    sx[m] = a / 127.0f;
+  }
+
+  const uint32_t nib_s = __builtin_amdgcn_readfirstlane(0x0F0F0F0Fu);
+  uint32_t ones_v = 0x01010101u;
+  asm volatile("" : "+v"(ones_v));   // int8 ones in a VGPR, not a literal operand
+
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+
+  for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {
+    Half32Regs r;
+    load_half32<true>(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lg, row);
+    uint32_t xlo[M], xhi[M];
+    int sxq[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + (size_t)m * k + (size_t)hs * 128 +
+                                                          64 * lg + 8 * seg);
+      quant8(v, inv[m], xlo[m], xhi[m]);
+      // sum of this lane's 8 xq, then over the 4 lanes of its group
+      int p = __builtin_amdgcn_sdot4((int)xlo[m], (int)ones_v, 0, false);
+      p = __builtin_amdgcn_sdot4((int)xhi[m], (int)ones_v, p, false);
+      p += dpp_i<0xB1>(p);
+      p += dpp_i<0x4E>(p);
+      sxq[m] = p;
+    }
+    do_group_a8_32<M, 0>(acc, r, xlo, xhi, sxq, nib_s);
+    do_group_a8_32<M, 1>(acc, r, xlo, xhi, sxq, nib_s);
+  }
+
+  // Sum over waves and over the two lane halves (same row), in a fixed order.
+#pragma unroll
+  for (int m = 0; m < M; ++m) red[(wave * M + m) * 64 + lane] = acc[m];
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < 32 * M) {
+    const int m = t >> 5, l = t & 31;
+    float v = 0.0f;
+    for (int w = 0; w < WAVES; ++w) {
+      v += red[(w * M + m) * 64 + l];
+      v += red[(w * M + m) * 64 + l + 32];
+    }
+    const int col = rb * kTileRows + 32 * (blockIdx.x & 1) + l;
+    if (col < n) {
+      // split partials carry the activation scale already (the same for every split)
+      v *= sx[m];
+      if (partial != nullptr)
+        partial[((size_t)blockIdx.y * M + m) * n + col] = v;
+      else if (y_f32)
+        static_cast<float*>(y)[(size_t)m * n + col] = v;
+      else
+        static_cast<uint16_t*>(y)[(size_t)m * n + col] = (uint16_t)f32_to_bf16_rne(v);
+    }
+  }
+}
+
+template <int M, int WAVES>
+static hipError_t launch_w4a8_32_t(const void* x, const void* packed, int n, int k, void* y,
+                                   int y_f32, float* partial, int split, hipStream_t stream) {
+  const int rbs = (n + kTileRows - 1) / kTileRows;
+  hipLaunchKernelGGL((w4a8_gemv32_kernel<M, WAVES>), dim3(2 * rbs, split), dim3(WAVES * 64), 0,
+                     stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
+                     n, k, y, y_f32, partial, split);
+  return hipGetLastError();
+}
+
 template <int M, int WAVES>
 static hipError_t launch_w4a8_t(const void* x, const void* packed, int n, int k, void* y,
                                 int y_f32, float* partial, int split, hipStream_t stream) {
@@ -209,10 +349,13 @@ static hipError_t launch_w4a8_t(const void* x, const void* packed, int n, int k,
 }
 
 hipError_t launch_w4a8_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
-                            int y_f32, float* partial, int split, int waves, hipStream_t stream) {
-#define QG_A8_CASE(MM, WW) \
-  if (m == MM && waves == WW) return launch_w4a8_t<MM, WW>(x, packed, n, k, y, y_f32, partial, split, stream);
-#define QG_A8_M(MM) QG_A8_CASE(MM, 4) QG_A8_CASE(MM, 8) QG_A8_CASE(MM, 16)
+                            int y_f32, float* partial, int split, int rows, int waves,
+                            hipStream_t stream) {
+#define QG_A8_CASE(MM, WW)                                                                      \
+  if (m == MM && waves == WW)                                                                   \
+    return rows == 32 ? launch_w4a8_32_t<MM, WW>(x, packed, n, k, y, y_f32, partial, split, stream) \
+                      : launch_w4a8_t<MM, WW>(x, packed, n, k, y, y_f32, partial, split, stream);
+#define QG_A8_M(MM) QG_A8_CASE(MM, 8) QG_A8_CASE(MM, 16)
   QG_A8_M(1) QG_A8_M(2) QG_A8_M(3) QG_A8_M(4)
 #undef QG_A8_M
 #undef QG_A8_CASE

@@ -86,10 +86,20 @@ def test_split_rule_one_k_tile_per_split(lib):
 
 
 def test_default_split_table(lib):
-    assert lib.qg_default_split_k(1, 39936, 6656) == 1
-    assert lib.qg_default_split_k(1, 8448, 6656) == 2
-    assert lib.qg_default_split_k(1, 256, 6656) == 8
+    # M <= 4: one split from N = 4096 up; below, 32 workgroups of 32 rows, at most 4
+    for n, k in ((39936, 6656), (8448, 6656), (6656, 4096), (6656, 19968), (4096, 256)):
+        for m in (1, 4):
+            assert lib.qg_default_split_k(m, n, k) == 1, (m, n, k)
+    assert lib.qg_default_split_k(1, 256, 6656) == 4
+    assert lib.qg_default_split_k(3, 512, 6656) == 2
+    assert lib.qg_default_split_k(1, 1024, 6656) == 1
     assert lib.qg_default_split_k(1, 256, 256) == 1       # capped by K / 256
+    assert lib.qg_default_split_k(1, 256, 512) == 2
+    # M > 4: row blocks of 64 x split >= 240, at most 8
+    assert lib.qg_default_split_k(16, 39936, 6656) == 1
+    assert lib.qg_default_split_k(16, 8448, 6656) == 2
+    assert lib.qg_default_split_k(64, 6656, 19968) == 4
+    assert lib.qg_default_split_k(64, 256, 6656) == 8
     assert lib.qg_default_split_k(65, 256, 256) == E_M
 
 

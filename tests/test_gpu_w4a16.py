@@ -167,6 +167,22 @@ def test_w4a16_every_split(dev, m):
         assert_w16(y, ref, f"split={split} M={m}")
 
 
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_w4a16_both_workgroup_shapes_ragged_n(dev, m):
+    """N = 8200 (8200 % 64 = 8): 257 workgroups of 32 rows or 129 of 64.  With
+    one split and M <= 2 the library takes the 64-row GEMV, otherwise the
+    32-row one; both must mask the 8-row tail and match the oracle."""
+    n, k = 8200, 512
+    w, codes, scales, zeros = _weight(n, k, 44)
+    packed = _gpu_packed(w, dev)
+    x = si.activation(m, k, 60 + m)
+    ref = _ref(x, codes, scales, zeros)
+    for split in (1, 2):
+        for dt in (torch.float32, torch.bfloat16):
+            y = qg.qgemm_w4a16(x.to(dev), packed, n, split_k=split, out_dtype=dt)
+            assert_w16(y, ref, f"N=8200 M={m} split={split} {dt}")
+
+
 def test_w4a16_uneven_split_partition(dev):
     """K = 6656 has 26 tiles: splits 4 and 8 give uneven ranges (7,7,6,6 / 4,4,3,...)."""
     n, k = 320, 6656

@@ -69,7 +69,9 @@ def test_mfma_runtime_m_and_tails(dev, n, k, m):
 
 
 def test_mfma_matches_decode_path_row_by_row(dev):
-    """Row m of an M = 16 call equals (to fp32 rounding) the M = 1 GEMV of row m."""
+    """Row m of an M = 16 call equals the M = 1 GEMV of row m up to fp32 rounding:
+    both add the same exact products in different orders (about sqrt(K) * 2^-24
+    * |y|, ~1e-4 here); a layout or masking slip would be O(1)."""
     n, k = 1024, 2048
     w, *_ = _weight(n, k, 17)
     packed = qg.quantize_int4_g32(w.to(dev))
@@ -77,7 +79,7 @@ def test_mfma_matches_decode_path_row_by_row(dev):
     y16 = qg.qgemm_w4a16(x, packed, n, out_dtype=torch.float32)
     for r in (0, 7, 15):
         y1 = qg.qgemm_w4a16(x[r:r + 1].contiguous(), packed, n, out_dtype=torch.float32)
-        torch.testing.assert_close(y16[r:r + 1], y1, rtol=1e-5, atol=1e-4)
+        torch.testing.assert_close(y16[r:r + 1], y1, rtol=1e-4, atol=1e-3)
 
 
 def test_mfma_repeat_and_graph_replay_are_bit_identical(dev):

@@ -82,6 +82,21 @@ def test_w4a8_small_shapes(dev, n, k, m):
     assert_w4a8_class(y, r16, f"{n}x{k} M={m}")
 
 
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_w4a8_both_workgroup_shapes_ragged_n(dev, m):
+    """N = 8200: the 64-row kernel (one split, M <= 2) and the 32-row kernel
+    (otherwise), each with an 8-row tail, against the W4A8 oracle."""
+    n, k = 8200, 512
+    w, codes, scales, zeros = _weight(n, k, 45)
+    packed = qg.quantize_int4_g32(w.to(dev))
+    x = si.activation(m, k, 70 + m)
+    r8, r16 = _refs(x, codes, scales, zeros)
+    for split in (1, 2):
+        y = qg.qgemm_w4a8(x.to(dev), packed, n, split_k=split, out_dtype=torch.float32)
+        assert_w16(y, r8, f"N=8200 M={m} split={split}")
+        assert_w4a8_class(y, r16, f"N=8200 M={m} split={split}")
+
+
 def test_w4a8_every_split(dev):
     n, k = 320, 6656
     w, codes, scales, zeros = _weight(n, k, 12)
