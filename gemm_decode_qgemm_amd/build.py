@@ -38,9 +38,15 @@ FLAGS = [
 ]
 
 
+# Per-source flags.  The matrix-core kernel asks the backend to write MFMA
+# results to ordinary VGPRs (the AGPR form costs a v_accvgpr_read per result
+# element before the fp32 epilogue of every group).
+SOURCE_FLAGS = {"gemm_w4a16_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, extra: list[str], objdir: str) -> str:
     obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

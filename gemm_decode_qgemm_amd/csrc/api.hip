@@ -64,8 +64,9 @@ constexpr int64_t kCUs = 256;   // compute units of an MI355X
 //    launch and the partials' traffic, which the extra parallelism does not
 //    repay at these shapes; below that, the smallest split giving 32
 //    workgroups, at most 4 (N = 256, K = 6656: 5.5 us at 4 against 5.9 at 1).
-//  * M > 4 (matrix-core kernel, 64-row workgroups): the smallest split with
-//    row blocks x split >= 240, at most 8.
+//  * M > 4 (matrix-core kernel): the smallest split with 64-row blocks x
+//    split >= 120, at most 8 (6656 x 19968, M = 16: 24.4 us at 2 against 39.6
+//    at 1; 8448 x 6656: 15.6 us at 1 against 18.3 at 2).
 // Both are capped by K / 256 (one tile per split).
 int32_t default_split(int64_t m, int64_t n, int64_t k) {
   const int64_t kt = k / QG_TILE_K;
@@ -77,7 +78,7 @@ int32_t default_split(int64_t m, int64_t n, int64_t k) {
     return s;
   }
   const int64_t rbs = (n + QG_TILE_ROWS - 1) / QG_TILE_ROWS;
-  while (s < 8 && 2 * s <= kt && rbs * s < 240) s *= 2;
+  while (s < 8 && 2 * s <= kt && rbs * s < 120) s *= 2;
   return s;
 }
 

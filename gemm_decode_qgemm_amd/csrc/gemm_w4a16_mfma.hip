@@ -7,180 +7,270 @@
 // 16..64 activation rows each weight feeds enough products for the matrix
 // cores to pay off.
 //
-// Mapping (gfx950): a workgroup = one 64-row block of the weight, 4 waves, one
-// 16-row n-tile each; M is padded to MT 16-row m-tiles.  Per half tile (4
-// groups, 128 k) the workgroup stages x[0:16*MT, 128 k] into LDS (double
-// buffered) together with each row's 4 group sums X[m][g]; each wave then
-// runs, per group, one v_mfma_f32_16x16x32_bf16 per m-tile:
-//   A = x (16 m x 32 k, exact bf16), B = 128 + q (32 k x 16 n, exact bf16,
-//   built from the nibbles with one shift and one and-or per pair),
-// into a fresh accumulator P, and folds P into fp32 results as
-//   y[m][n] += s[n,g] * (P[m][n] - (128 + zp[n,g]) * X[m][g]).
-// The products are exact and the fp32 accumulation matches the decode path,
-// so no bf16 rounding of dequantized weights enters the result.
+// Arithmetic, per group g and 16 x 16 output tile, with v_mfma_f32_16x16x32_bf16:
+//   P = x (16 m x 32 k, exact bf16) . (128 + q) (32 k x 16 n, exact bf16),
+//   X = x . ones (the group sums, landing in the accumulator layout),
+//   y[m][n] += s[n,g] * (P[m][n] - (128 + zp[n,g]) * X[m]),
+// so every product is exact and the sums are fp32, as in the decode GEMV.
+//
+// Mapping (gfx950):
+//  * a wave owns a whole 64-row block (4 n-tiles of 16 rows) and MT m-tiles
+//    for a range of half tiles (4 groups = 128 k); a workgroup is KW x MG
+//    waves: KW waves split the block's K range round robin, MG wave groups
+//    take different m-tiles (each loads the block's weights: the second read
+//    is an L2 hit), and the KW partial sums are added through LDS in wave
+//    order at the end (no atomics, bit-reproducible);
+//  * weights: lane (i, a) = (lane % 16, lane / 16) loads the whole 16-byte
+//    chunk of group a, row 16t + i -- one wave-wide load is 4 runs of 256
+//    contiguous bytes, and the 4 loads of a half tile cover its code lines
+//    exactly -- then a 4 x 4 transpose across the wave's 16-lane rows
+//    (v_permlane32_swap, v_permlane16_swap) leaves in register j the dword a
+//    of group j, which is what the B operand of the MFMA wants from that lane;
+//  * activations: the A operand comes straight from global memory (x is a
+//    few hundred KB and stays in L2), 16 bytes per lane per group and m-tile,
+//    and is reused by the 4 n-tiles;
+//  * the next half tile's weights (and, for MT = 1, activations) are loaded
+//    while the current one computes.
 #include "qg_common.h"
 #include "w4_common.h"
 
 namespace qg {
 
-constexpr int kXRow = 128 + 8;   // LDS row of 128 bf16 plus 16 bytes of padding
 
-template <int MT>
-__global__ __launch_bounds__(256) void w4a16_mfma_kernel(
+#ifndef QG_MFMA_SCHED_BARRIER
+#define QG_MFMA_SCHED_BARRIER 1
+#endif
+
+// (row r, register j) -> (row j, register r) over the wave's four 16-lane rows:
+// v_permlane32_swap exchanges the upper 32 lanes of its first operand with the
+// lower 32 of its second, v_permlane16_swap the odd 16-lane rows of the first
+// with the even rows of the second (both checked on MI355X).
+__device__ __forceinline__ void transpose_rows4(u32x4_t& v) {
+  const auto s02 = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+  const auto t01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+  const auto t23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+  v = u32x4_t{t01[0], t01[1], t23[0], t23[1]};
+}
+
+// bf16 pairs (128 + q) of nibbles 2e, 2e+1 of a code dword, in plain C: the
+// result feeds an MFMA source operand, and the compiler must see the VALU op
+// that writes it to insert the wait states the MFMA read needs (an inline-asm
+// v_and_or_b32 here, invisible to it, gave corrupted products on MI355X).
+// `mask_s` holds 0x000F000F in an SGPR and `magic_v` 0x43004300 in a VGPR, so
+// the and + or select to one v_and_or_b32 (VOP3 takes no 32-bit literal).
+__device__ __forceinline__ uint32_t nibble_pair_mfma(uint32_t w, int e, uint32_t mask_s,
+                                                     uint32_t magic_v) {
+  return ((w >> (4 * e)) & mask_s) | magic_v;
+}
+
+template <int NT, int MT>
+struct MfmaUnit {
+  u32x4_t w[NT];       // code chunks (group a, row i of n-tile t), transposed after the load
+  u32x2_t sc[NT];      // fp16 scales of that row, the half tile's 4 groups
+  uint32_t zw[NT];     // zero points of that row, the half tile's 4 groups (16 bits)
+  u32x4_t xa[MT][4];   // A operands: x[16 mt + i][32 g + 8 a .. + 8] per group g
+};
+
+// NT n-tiles of 16 rows per wave (NT in {1, 2, 4, 8}); a workgroup owns the
+// n-tiles NT * blockIdx.x .. + NT - 1 of the weight, i.e. 16 * NT rows, which
+// span part of a 64-row block or (NT = 8) two of them.  PIPE: software
+// pipeline over two register sets (PFX: the next unit's activations too), or
+// load-wait-compute per unit with the other resident waves covering latency.
+template <int NT, int MT, int KW, int MG, bool PIPE, bool PFX>
+__global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT * 16][kXRow];
-  __shared__ __attribute__((aligned(16))) float xsum[2][4][MT * 16];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = wave_id_uniform();        // n-tile of this wave
-  const int b = lane & 15, a = lane >> 4;
-  const int rb = blockIdx.x;
+  constexpr int WAVES = KW * MG;
+  constexpr int kNT = NT;
+  __shared__ f32x4_t red[WAVES][kNT][64];
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, a = lane >> 4;
+  const int wave = wave_id_uniform();
+  const int kw = wave % KW, mg = wave / KW;
+  const int tile0 = NT * blockIdx.x;                // first n-tile of this workgroup
+  const int rbs = (n + kTileRows - 1) / kTileRows;
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
-  const int s0 = 2 * t0, s1 = 2 * t1;        // half-tile range
-  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
-  const int nrow = 16 * wave + b;            // this lane's weight row within the block
+  // n-tile t lies in row block (tile0 + t) / 4; a block past the last one (NT = 8
+  // with an odd block count) reads the last block instead: its rows are >= n
+  // and never stored.
+  auto tiles_of = [&](int t) {
+    const int b = min((tile0 + t) >> 2, rbs - 1);
+    return packed + (size_t)b * kt_count * kTileBytes;
+  };
   const uint32_t mask_s = __builtin_amdgcn_readfirstlane(0x000F000Fu);
   uint32_t magic_v = 0x43004300u;
-  asm volatile("" : "+v"(magic_v));
+  asm volatile("" : "+v"(magic_v));     // an empty asm: keeps the constant in a VGPR
+  uint32_t one2 = 0x3f803f80u;          // bf16 pair (1, 1), kept in a VGPR
+  asm volatile("" : "+v"(one2));
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{one2, one2, one2, one2});
 
-  // ---- x staging: chunk c = (row, 16-byte piece) of the half tile; 4
-  // consecutive threads hold one group of one row.
-  constexpr int kPasses = MT;                // 16*MT rows x 16 pieces / 256 threads
-  u32x4_t xr[kPasses];
-  auto stage_load = [&](int hs) {
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const int c = p * 256 + tid;
-      const int row = c >> 4, piece = c & 15;
-      xr[p] = u32x4_t{0, 0, 0, 0};
-      if (row < m)
-        xr[p] = *reinterpret_cast<const u32x4_t*>(x + (size_t)row * k + (size_t)hs * 128 + piece * 8);
-    }
-  };
-  auto stage_store = [&](int bf) {
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const int c = p * 256 + tid;
-      const int row = c >> 4, piece = c & 15;
-      *reinterpret_cast<u32x4_t*>(&xs[bf][row][piece * 8]) = xr[p];
-      const u32x4_t v = xr[p];
-      float sum = 0.0f;
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sum += bf16_to_f32(w[i] & 0xffffu) + bf16_to_f32(w[i] >> 16);
-      sum += dpp_mov<0xB1>(sum);             // the 4 pieces of a group: quad reduction
-      sum += dpp_mov<0x4E>(sum);
-      if ((piece & 3) == 0) xsum[bf][piece >> 2][row] = sum;
-    }
-  };
-
-  // ---- weights of one half tile for this lane: the code dword of its
-  // k-slice a for each of the 4 groups, and its row's scales / zero points.
-  struct WRegs {
-    uint32_t c[4];
-    u32x2_t sc;
-    uint32_t zw;
-  };
-  auto load_w = [&](WRegs& r, int hs) {
-    const uint8_t* tile = tiles + (size_t)(hs >> 1) * kTileBytes;
+  auto load_w = [&](MfmaUnit<NT, MT>& u, int hs) {
     const int half = hs & 1;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      r.c[jj] = load_stream<true>(reinterpret_cast<const uint32_t*>(
-          tile + ((4 * half + jj) * kTileRows + nrow) * 16 + 4 * a));
-    r.sc = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + kScaleOff + nrow * 16 + 8 * half));
-    r.zw = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + kZeroOff + nrow * 4 + 2 * half));
+    for (int t = 0; t < kNT; ++t) {
+      const uint8_t* tile = tiles_of(t) + (size_t)(hs >> 1) * kTileBytes;
+      const int row = 16 * ((tile0 + t) & 3) + i;
+      u.w[t] = load_stream<true>(
+          reinterpret_cast<const u32x4_t*>(tile + ((4 * half + a) * kTileRows + row) * 16));
+      u.sc[t] = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + kScaleOff + row * 16 + 8 * half));
+      u.zw[t] = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + kZeroOff + row * 4 + 2 * half));
+    }
   };
-
-  f32x4_t acc[MT];
+  // Rows of x at or past m read row m - 1 instead (a valid address, no
+  // branch and no select): output row r of an MFMA depends on row r of its A
+  // operand only, and those rows are never stored.
+  auto load_x = [&](MfmaUnit<NT, MT>& u, int hs) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  auto compute = [&](int bf, const WRegs& r) {
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = min(16 * (mg * MT + mt) + i, m - 1);
+      const uint16_t* xr = x + (size_t)row * k + (size_t)hs * 128 + 8 * a;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      uint32_t bp[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bp[i] = nibble_pair_bf16(r.c[jj], i, mask_s, magic_v);
-      const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, u32x4_t{bp[0], bp[1], bp[2], bp[3]});
-      const uint32_t sw = (jj < 2) ? r.sc.x : r.sc.y;
-      const float s = fp16_to_f32((sw >> (16 * (jj & 1))) & 0xffffu);
-      const float zb = (float)(((r.zw >> (4 * jj)) & 15u) + 128u);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&xs[bf][16 * mt + b][32 * jj + 8 * a]);
-        const f32x4_t xg = *reinterpret_cast<const f32x4_t*>(&xsum[bf][jj][16 * mt + 4 * a]);
-        const f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, av), bv, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[mt][e] = __builtin_fmaf(s, __builtin_fmaf(-zb, xg[e], p[e]), acc[mt][e]);
-      }
+      for (int g = 0; g < 4; ++g) u.xa[mt][g] = *reinterpret_cast<const u32x4_t*>(xr + 32 * g);
     }
   };
 
-  WRegs wc, wn;
-  stage_load(s0);
-  stage_store(0);
-  load_w(wc, s0);
-  __syncthreads();
-  for (int hs = s0; hs < s1; ++hs) {
-    const int bf = (hs - s0) & 1;
-    const bool next = hs + 1 < s1;
-    if (next) {
-      stage_load(hs + 1);
-      load_w(wn, hs + 1);
-    }
-    compute(bf, wc);
-    if (next) stage_store(bf ^ 1);
-    __syncthreads();
-    if (next) wc = wn;
-  }
+  f32x4_t acc[kNT][MT];
+#pragma unroll
+  for (int t = 0; t < kNT; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // ---- results: lane (b, a) holds rows 16*mt + 4a + e of column nrow.
-  const int col = rb * kTileRows + nrow;
-  if (col < n) {
+  auto compute = [&](MfmaUnit<NT, MT>& u) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int t = 0; t < kNT; ++t) transpose_rows4(u.w[t]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * mt + 4 * a + e;
-        if (row < m) {
-          const float v = acc[mt][e];
-          if (partial != nullptr)
-            partial[((size_t)blockIdx.y * m + row) * n + col] = v;
-          else if (y_f32)
-            static_cast<float*>(y)[(size_t)row * n + col] = v;
-          else
-            static_cast<uint16_t*>(y)[(size_t)row * n + col] = (uint16_t)f32_to_bf16_rne(v);
+    for (int g = 0; g < 4; ++g) {
+      f32x4_t xg[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        xg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u.xa[mt][g]), ones,
+                                                        f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) {
+        const uint32_t dw = u.w[t][g];
+        uint32_t bp[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bp[e] = nibble_pair_mfma(dw, e, mask_s, magic_v);
+        const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, u32x4_t{bp[0], bp[1], bp[2], bp[3]});
+        const uint32_t sw = g < 2 ? u.sc[t].x : u.sc[t].y;
+        const float s = fp16_to_f32((sw >> (16 * (g & 1))) & 0xffffu);
+        const float zb = (float)(((u.zw[t] >> (4 * g)) & 15u) | 0x80u);   // 128 + zp
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, u.xa[mt][g]), bv, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[t][mt][e] = __builtin_fmaf(s, __builtin_fmaf(-zb, xg[mt][e], p[e]), acc[t][mt][e]);
         }
       }
+      // keep each group's MFMA results from being hoisted into the next group
+      // (their registers would all be live at once)
+      if constexpr (QG_MFMA_SCHED_BARRIER) __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Software pipeline over two register sets used in turn (no copies): the
+  // next unit's loads are issued before the current unit computes.  The loop
+  // conditions are wave-uniform.
+  const int h_end = 2 * t1;
+  int hs = 2 * t0 + kw;
+  if constexpr (!PIPE) {
+    for (; hs < h_end; hs += KW) {
+      MfmaUnit<NT, MT> u;
+      load_w(u, hs);
+      load_x(u, hs);
+      compute(u);
+    }
+  } else if (hs < h_end) {
+    MfmaUnit<NT, MT> ua, ub;
+    load_w(ua, hs);
+    load_x(ua, hs);
+    while (true) {
+      if (hs + KW >= h_end) { compute(ua); break; }
+      load_w(ub, hs + KW);
+      if constexpr (PFX) load_x(ub, hs + KW);
+      compute(ua);
+      if constexpr (!PFX) load_x(ub, hs + KW);
+      hs += KW;
+      if (hs + KW >= h_end) { compute(ub); break; }
+      load_w(ua, hs + KW);
+      if constexpr (PFX) load_x(ua, hs + KW);
+      compute(ub);
+      if constexpr (!PFX) load_x(ua, hs + KW);
+      hs += KW;
+    }
+  }
+
+  // ---- the KW partial sums of each m-tile, in wave order; lane (i, a) of
+  // n-tile t holds rows 4a + e of column 16t + i.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) red[wave][t][lane] = acc[t][mt];
+    __syncthreads();
+    for (int q = threadIdx.x; q < MG * kNT * 64; q += WAVES * 64) {
+      const int l = q & 63, t = (q >> 6) % kNT, g = q / (kNT * 64);
+      f32x4_t v = red[g * KW][t][l];
+      for (int w = 1; w < KW; ++w) {
+        const f32x4_t r = red[g * KW + w][t][l];
+        v = f32x4_t{v[0] + r[0], v[1] + r[1], v[2] + r[2], v[3] + r[3]};
+      }
+      const int col = 16 * (tile0 + t) + (l & 15);
+      if (col < n) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * (g * MT + mt) + 4 * (l >> 4) + e;
+          if (row < m) {
+            if (partial != nullptr)
+              partial[((size_t)blockIdx.y * m + row) * n + col] = v[e];
+            else if (y_f32)
+              static_cast<float*>(y)[(size_t)row * n + col] = v[e];
+            else
+              static_cast<uint16_t*>(y)[(size_t)row * n + col] = (uint16_t)f32_to_bf16_rne(v[e]);
+          }
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
-template <int MT>
+template <int NT, int MT, int KW, int MG, bool PIPE, bool PFX>
 static hipError_t launch_mfma_t(const void* x, int m, const void* packed, int n, int k, void* y,
                                 int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_mfma_kernel<MT>), dim3(rbs, split), dim3(256), 0, stream,
+  hipLaunchKernelGGL((w4a16_mfma_kernel<NT, MT, KW, MG, PIPE, PFX>),
+                     dim3((4 * rbs + NT - 1) / NT, split), dim3(KW * MG * 64), 0, stream,
                      static_cast<const uint16_t*>(x), m, static_cast<const uint8_t*>(packed), n, k,
                      y, y_f32, partial, split);
   return hipGetLastError();
 }
 
+// Workgroup layout per m-tile count, measured on MI355X at 39936 x 6656,
+// 8448 x 6656 and 6656 x 19968 (NT n-tiles per wave, MT m-tiles per wave, KW
+// waves along K, MG wave groups along M; at most 8 waves, so no wave is held
+// to fewer than 256 VGPRs):
+//   16 rows: (4, 1, 4, 1), pipelined with activation prefetch;
+//   32 rows: (4, 2, 4, 1), load-wait-compute (the pipelined form needs 2
+//            register sets of 2 m-tiles and runs at one wave per SIMD);
+//   48 rows: (4, 1, 2, 3), pipelined;
+//   64 rows: (4, 2, 4, 2), load-wait-compute (pipelined, it spills).
 hipError_t launch_w4a16_mfma(int m, const void* x, const void* packed, int n, int k, void* y,
                              int y_f32, float* partial, int split, hipStream_t stream) {
-  const int mt = (m + 15) / 16;
-  switch (mt) {
-    case 1: return launch_mfma_t<1>(x, m, packed, n, k, y, y_f32, partial, split, stream);
-    case 2: return launch_mfma_t<2>(x, m, packed, n, k, y, y_f32, partial, split, stream);
-    case 3: return launch_mfma_t<3>(x, m, packed, n, k, y, y_f32, partial, split, stream);
-    case 4: return launch_mfma_t<4>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+#define QG_MF(NT, MT, KW, MG, PIPE, PFX) \
+  return launch_mfma_t<NT, MT, KW, MG, PIPE, PFX>(x, m, packed, n, k, y, y_f32, partial, split, stream)
+  switch ((m + 15) / 16) {
+    case 1: QG_MF(4, 1, 4, 1, true, true);
+    case 2: QG_MF(4, 2, 4, 1, false, false);
+    case 3: QG_MF(4, 1, 2, 3, true, true);
+    case 4: QG_MF(4, 2, 4, 2, false, false);
     default: return hipErrorInvalidValue;
   }
+#undef QG_MF
 }
 
 }  // namespace qg

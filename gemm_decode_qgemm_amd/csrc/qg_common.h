@@ -22,7 +22,6 @@ constexpr int kTileBytes = 9472;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -61,25 +60,14 @@ __device__ __forceinline__ uint32_t and_or_sv(uint32_t a, uint32_t mask_s, uint3
 // in bf16 and its 7-bit fraction has unit spacing, so OR-ing a nibble into the
 // low bits adds it exactly.  `w >> 4i` masked with 0x000F000F selects the
 // codes of k = 8d+2i (low half) and 8d+2i+1 (high half) of a packed dword.
-// `mask_s` must hold 0x000F000F and `magic_v` 0x43004300.
+// `mask_s` must hold 0x000F000F and `magic_v` 0x43004300.  The result comes
+// from inline asm, whose VALU write the compiler cannot see: it may feed VALU
+// and DPP instructions (which the asm blocks pad with wait states themselves)
+// but not an MFMA source operand directly.
 __device__ __forceinline__ uint32_t nibble_pair_bf16(uint32_t w, int i, uint32_t mask_s,
                                                      uint32_t magic_v) {
   return and_or_sv(i == 0 ? w : (w >> (4 * i)), mask_s, magic_v);
 }
-
-typedef uint32_t u32x16_t __attribute__((ext_vector_type(16)));
-typedef const __attribute__((address_space(4))) u32x16_t* const_u32x16_ptr;
-
-// 16 dwords from a wave-uniform address into scalar registers (s_load_dwordx16).
-__device__ __forceinline__ u32x16_t sload16(const uint32_t* p) {
-  return *(const_u32x16_ptr)(p);
-}
-
-// Wait until every outstanding scalar-memory / LDS access has returned
-// (s_waitcnt lgkmcnt(0); vmcnt and expcnt left at their maxima).  Scalar loads
-// may return out of order, so this is the only safe wait for them; issuing the
-// next scalar load right after it keeps exactly one in flight.
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Streaming load; NT sets the non-temporal cache policy (the weight is read
 // once per call and should not displace x or the L2-resident partials).
