@@ -22,6 +22,10 @@ The CPU baseline leg times the plain C oracle (tests' reference) on this
 host's cores over a bounded sample of the same workload and checks the GPU
 result against it.
 
+Other layers of the same path use the same protocol: --op w4a16 with
+--m 2..64 (M > 4 runs the matrix-core kernel), --op w4a8 (M <= 4) and
+--op w8a16 (int8 per-channel, bytes = N*K + 2*N); --n/--k pick the shape.
+
 Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -37,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix-core peak of an MI355X
 METRIC = "µs/call and effective weight GB/s (% HBM peak) for INT4-g32 GEMV at M=1"
 COUNTERS = os.path.join(ROOT, "profiles", "w4a16_gemv_39936x6656_m1_counters.json")
 KERNEL_SOURCES = ["gemm_decode_qgemm_amd/csrc/gemv_w4a16.hip", "gemm_decode_qgemm_amd/csrc/w4_common.h",
@@ -73,6 +78,7 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=1000,
                    help="untimed calls first; the clocks take a few hundred calls to ramp up from idle")
+    p.add_argument("--op", choices=("w4a16", "w4a8", "w8a16"), default="w4a16")
     p.add_argument("--n", type=int, default=39936)
     p.add_argument("--k", type=int, default=6656)
     p.add_argument("--m", type=int, default=1)
@@ -103,26 +109,40 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     n, k, m = args.n, args.k, args.m
-    bytes_eff = qg.int4_packed_bytes(n, k)
+    op = args.op
+    bytes_eff = n * k + 2 * n if op == "w8a16" else qg.int4_packed_bytes(n, k)
     if args.calibrate_copy:
         return calibrate_copy(torch, dev, bytes_eff)
-    if (n, k) in si.MODEL_SHAPES:
-        w_cpu, x_cpu = si.decode_inputs(n, k, m)
-    else:
-        w_cpu, x_cpu = si.int4_weight(n, k, n ^ k), si.activation(m, k, 9100 + m)
-    split = args.split or qg.default_split_k(m, n, k)
-
-    packed0 = qg.quantize_int4_g32(w_cpu.to(dev))
     copies = max(2, math.ceil((1 << 30) / bytes_eff))
-    packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
-    x = x_cpu.to(dev)
     y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-    ws_n = qg.workspace_bytes(m, n, k, split)
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
+    split = None
+    if op == "w8a16":
+        w_cpu, s_cpu, x_cpu = si.int8_layer(n, k, m)
+        wq0, sc = w_cpu.to(dev), s_cpu.to(dev)
+        wqs = [wq0] + [wq0.clone() for _ in range(copies - 1)]
+        x = x_cpu.to(dev)
 
-    def call(i):
-        qg.qgemm_w4a16(x, packs[i % copies], n, split_k=split, out=y, workspace=ws)
+        def call(i):
+            qg.qgemm_w8a16(x, wqs[i % copies], sc, out=y)
+
+        oracle_inputs = (w_cpu, s_cpu, x_cpu)
+    else:
+        if (n, k) in si.MODEL_SHAPES:
+            w_cpu, x_cpu = si.decode_inputs(n, k, m)
+        else:
+            w_cpu, x_cpu = si.int4_weight(n, k, n ^ k), si.activation(m, k, 9100 + m)
+        split = args.split or qg.default_split_k(m, n, k)
+        packed0 = qg.quantize_int4_g32(w_cpu.to(dev))
+        packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
+        x = x_cpu.to(dev)
+        ws = torch.empty(max(qg.workspace_bytes(m, n, k, split), 1), dtype=torch.uint8, device=dev)
+        fn = qg.qgemm_w4a16 if op == "w4a16" else qg.qgemm_w4a8
+
+        def call(i):
+            fn(x, packs[i % copies], n, split_k=split, out=y, workspace=ws)
+
+        oracle_inputs = (w_cpu, None, x_cpu)
+    torch.cuda.synchronize()
 
     # Eager warm-up (also loads the code object), then capture graphs.
     for i in range(min(args.warmup, 20)):
@@ -164,8 +184,13 @@ def main() -> int:
     gbs = bytes_eff / (us_call * 1e-6) / 1e9
     y_first = y.clone()
 
+    headline = op == "w4a16" and (n, k, m) == (39936, 6656, 1)
+    kernel = {"w4a16": "GEMV" if m <= 4 else "matrix-core GEMM", "w4a8": "GEMV", "w8a16": "GEMV"}[op]
+    label = {"w4a16": "W4A16 INT4-g32 asymmetric", "w4a8": "W4A8 INT4-g32 x per-row int8",
+             "w8a16": "W8A16 INT8 per-channel"}[op]
     out = {
-        "metric": METRIC,
+        "metric": METRIC if headline else
+        f"µs/call and effective weight GB/s (% HBM peak) for {label} {kernel} at M={m}",
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -180,9 +205,9 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"W4A16 INT4-g32 asymmetric GEMV {n}x{k} M={m}",
-            "n": n, "k": k, "m": m, "split_k": split, "bytes_eff_per_call": bytes_eff,
-            "codes_only_gbs": round((n * k / 2) / (us_call * 1e-6) / 1e9, 2),
+            "workload": f"{label} {kernel} {n}x{k} M={m}",
+            "op": op, "n": n, "k": k, "m": m, "split_k": split, "bytes_eff_per_call": bytes_eff,
+            "codes_only_gbs": round((n * k / (1 if op == "w8a16" else 2)) / (us_call * 1e-6) / 1e9, 2),
             "rotating_weight_copies": copies,
             "timing": f"{full} replays of a {chunk}-call HIP graph" + (f" + one of {rest}" if rest else "")
                       + ", events on its stream",
@@ -198,12 +223,16 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(n, k, m),
+            "traffic": measured_traffic(n, k, m) if headline else None,
         },
     }
+    if m > 4:
+        tflops = 2.0 * m * n * k / (us_call * 1e-6) / 1e12
+        out["roofline"]["matrix_core"] = {"achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                                          "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args, w_cpu, x_cpu, y_first, bytes_eff)
+        out["cpu_baseline"] = cpu_baseline(args, oracle_inputs, y_first, bytes_eff)
 
     print(json.dumps(out), flush=True)
     return 0
@@ -224,23 +253,36 @@ def calibrate_copy(torch, dev, nbytes):
     return 0
 
 
-def cpu_baseline(args, w_cpu, x_cpu, y_gpu, bytes_eff):
-    """Time the C oracle on the host's cores on a bounded sample of the same
-    workload (whole weight, M rows), and check the GPU output against it."""
+def cpu_baseline(args, oracle_inputs, y_gpu, bytes_eff):
+    """Time the C oracle of the same op on the host's cores on a bounded sample
+    of the same workload (whole weight, M rows), and check the GPU output
+    against it."""
     import numpy as np
 
     import oracle
     import synthetic_inputs as si
 
     threads = oracle.hardware_threads()
-    codes, scales, zeros, _ = oracle.quantize_int4_g32(si.bf16_bits(w_cpu))
+    w_cpu, s_cpu, x_cpu = oracle_inputs
     xb = si.bf16_bits(x_cpu)
+    if args.op == "w8a16":
+        wi8 = w_cpu.numpy()
+        sb = si.bf16_bits(s_cpu)
+
+        def run():
+            return oracle.qgemm_w8a16(xb, wi8, sb, threads=threads)
+    else:
+        codes, scales, zeros, _ = oracle.quantize_int4_g32(si.bf16_bits(w_cpu))
+        fn = oracle.qgemm_w4a16 if args.op == "w4a16" else oracle.qgemm_w4a8
+
+        def run():
+            return fn(xb, codes, scales, zeros, threads=threads)
     times = []
     ref = None
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        ref = oracle.qgemm_w4a16(xb, codes, scales, zeros, threads=threads)
+        ref = run()
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start > args.cpu_seconds:
             break
