@@ -64,42 +64,35 @@ __device__ __forceinline__ uint32_t nibble_pair_mfma(uint32_t w, int e, uint32_t
   return ((w >> (4 * e)) & mask_s) | magic_v;
 }
 
-template <int NT, int MT>
+constexpr int kNT = 4;   // n-tiles of 16 rows per wave: a whole 64-row block
+
+template <int MT>
 struct MfmaUnit {
-  u32x4_t w[NT];       // code chunks (group a, row i of n-tile t), transposed after the load
-  u32x2_t sc[NT];      // fp16 scales of that row, the half tile's 4 groups
-  uint32_t zw[NT];     // zero points of that row, the half tile's 4 groups (16 bits)
+  u32x4_t w[kNT];      // code chunks (group a, row 16t + i), transposed after the load
+  u32x2_t scl;         // fp16 scales of row `lane` (the half tile's 4 groups)
+  uint32_t zwl;        // zero points of row `lane` (16 bits)
   u32x4_t xa[MT][4];   // A operands: x[16 mt + i][32 g + 8 a .. + 8] per group g
 };
 
-// NT n-tiles of 16 rows per wave (NT in {1, 2, 4, 8}); a workgroup owns the
-// n-tiles NT * blockIdx.x .. + NT - 1 of the weight, i.e. 16 * NT rows, which
-// span part of a 64-row block or (NT = 8) two of them.  PIPE: software
-// pipeline over two register sets (PFX: the next unit's activations too), or
-// load-wait-compute per unit with the other resident waves covering latency.
-template <int NT, int MT, int KW, int MG, bool PIPE, bool PFX>
+// A wave owns one 64-row block (the 4 n-tiles) for a range of half tiles.
+// PIPE: software pipeline over two register sets (PFX: the next unit's
+// activations too), or load-wait-compute per unit with the other resident
+// waves covering the latency.
+template <int MT, int KW, int MG, bool PIPE, bool PFX>
 __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
   constexpr int WAVES = KW * MG;
-  constexpr int kNT = NT;
   __shared__ f32x4_t red[WAVES][kNT][64];
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, a = lane >> 4;
   const int wave = wave_id_uniform();
   const int kw = wave % KW, mg = wave / KW;
-  const int tile0 = NT * blockIdx.x;                // first n-tile of this workgroup
-  const int rbs = (n + kTileRows - 1) / kTileRows;
+  const int rb = blockIdx.x;
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
-  // n-tile t lies in row block (tile0 + t) / 4; a block past the last one (NT = 8
-  // with an odd block count) reads the last block instead: its rows are >= n
-  // and never stored.
-  auto tiles_of = [&](int t) {
-    const int b = min((tile0 + t) >> 2, rbs - 1);
-    return packed + (size_t)b * kt_count * kTileBytes;
-  };
+  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
   const uint32_t mask_s = __builtin_amdgcn_readfirstlane(0x000F000Fu);
   uint32_t magic_v = 0x43004300u;
   asm volatile("" : "+v"(magic_v));     // an empty asm: keeps the constant in a VGPR
@@ -107,22 +100,24 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
   asm volatile("" : "+v"(one2));
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{one2, one2, one2, one2});
 
-  auto load_w = [&](MfmaUnit<NT, MT>& u, int hs) {
+  // Codes: lane (i, a) loads the chunk of group a, row 16t + i.  Scales and
+  // zero points: lane l loads those of row l only (one 8-byte and one 2-byte
+  // load per half tile; per n-tile loads with 4 lanes per row cost a quarter
+  // of the kernel's time); compute() hands row 16t + i to lane (i, a).
+  auto load_w = [&](MfmaUnit<MT>& u, int hs) {
+    const uint8_t* tile = tiles + (size_t)(hs >> 1) * kTileBytes;
     const int half = hs & 1;
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) {
-      const uint8_t* tile = tiles_of(t) + (size_t)(hs >> 1) * kTileBytes;
-      const int row = 16 * ((tile0 + t) & 3) + i;
+    for (int t = 0; t < kNT; ++t)
       u.w[t] = load_stream<true>(
-          reinterpret_cast<const u32x4_t*>(tile + ((4 * half + a) * kTileRows + row) * 16));
-      u.sc[t] = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + kScaleOff + row * 16 + 8 * half));
-      u.zw[t] = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + kZeroOff + row * 4 + 2 * half));
-    }
+          reinterpret_cast<const u32x4_t*>(tile + ((4 * half + a) * kTileRows + 16 * t + i) * 16));
+    u.scl = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + kScaleOff + lane * 16 + 8 * half));
+    u.zwl = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + kZeroOff + lane * 4 + 2 * half));
   };
   // Rows of x at or past m read row m - 1 instead (a valid address, no
   // branch and no select): output row r of an MFMA depends on row r of its A
   // operand only, and those rows are never stored.
-  auto load_x = [&](MfmaUnit<NT, MT>& u, int hs) {
+  auto load_x = [&](MfmaUnit<MT>& u, int hs) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int row = min(16 * (mg * MT + mt) + i, m - 1);
@@ -138,9 +133,17 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](MfmaUnit<NT, MT>& u) {
+  auto compute = [&](MfmaUnit<MT>& u) {
 #pragma unroll
     for (int t = 0; t < kNT; ++t) transpose_rows4(u.w[t]);
+    // Row 16t + i's metadata to lane (i, a): the same transpose applied to
+    // four copies of a register leaves row t of it, in register t, in every
+    // 16-lane row.
+    u32x4_t s0{u.scl.x, u.scl.x, u.scl.x, u.scl.x}, s1{u.scl.y, u.scl.y, u.scl.y, u.scl.y};
+    u32x4_t zz{u.zwl, u.zwl, u.zwl, u.zwl};
+    transpose_rows4(s0);
+    transpose_rows4(s1);
+    transpose_rows4(zz);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       f32x4_t xg[MT];
@@ -155,9 +158,9 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) bp[e] = nibble_pair_mfma(dw, e, mask_s, magic_v);
         const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, u32x4_t{bp[0], bp[1], bp[2], bp[3]});
-        const uint32_t sw = g < 2 ? u.sc[t].x : u.sc[t].y;
+        const uint32_t sw = g < 2 ? s0[t] : s1[t];
         const float s = fp16_to_f32((sw >> (16 * (g & 1))) & 0xffffu);
-        const float zb = (float)(((u.zw[t] >> (4 * g)) & 15u) | 0x80u);   // 128 + zp
+        const float zb = (float)(((zz[t] >> (4 * g)) & 15u) | 0x80u);   // 128 + zp
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -180,13 +183,13 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
   int hs = 2 * t0 + kw;
   if constexpr (!PIPE) {
     for (; hs < h_end; hs += KW) {
-      MfmaUnit<NT, MT> u;
+      MfmaUnit<MT> u;
       load_w(u, hs);
       load_x(u, hs);
       compute(u);
     }
   } else if (hs < h_end) {
-    MfmaUnit<NT, MT> ua, ub;
+    MfmaUnit<MT> ua, ub;
     load_w(ua, hs);
     load_x(ua, hs);
     while (true) {
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
         const f32x4_t r = red[g * KW + w][t][l];
         v = f32x4_t{v[0] + r[0], v[1] + r[1], v[2] + r[2], v[3] + r[3]};
       }
-      const int col = 16 * (tile0 + t) + (l & 15);
+      const int col = rb * kTileRows + 16 * t + (l & 15);
       if (col < n) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -239,35 +242,41 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
   }
 }
 
-template <int NT, int MT, int KW, int MG, bool PIPE, bool PFX>
+template <int MT, int KW, int MG, bool PIPE, bool PFX>
 static hipError_t launch_mfma_t(const void* x, int m, const void* packed, int n, int k, void* y,
                                 int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_mfma_kernel<NT, MT, KW, MG, PIPE, PFX>),
-                     dim3((4 * rbs + NT - 1) / NT, split), dim3(KW * MG * 64), 0, stream,
-                     static_cast<const uint16_t*>(x), m, static_cast<const uint8_t*>(packed), n, k,
-                     y, y_f32, partial, split);
+  hipLaunchKernelGGL((w4a16_mfma_kernel<MT, KW, MG, PIPE, PFX>), dim3(rbs, split),
+                     dim3(KW * MG * 64), 0, stream, static_cast<const uint16_t*>(x), m,
+                     static_cast<const uint8_t*>(packed), n, k, y, y_f32, partial, split);
   return hipGetLastError();
 }
 
+#ifndef QG_MFMA_KW1
+#define QG_MFMA_KW1 4
+#endif
+#ifndef QG_MFMA_PIPE1
+#define QG_MFMA_PIPE1 1
+#endif
+
 // Workgroup layout per m-tile count, measured on MI355X at 39936 x 6656,
-// 8448 x 6656 and 6656 x 19968 (NT n-tiles per wave, MT m-tiles per wave, KW
-// waves along K, MG wave groups along M; at most 8 waves, so no wave is held
-// to fewer than 256 VGPRs):
-//   16 rows: (4, 1, 4, 1), pipelined with activation prefetch;
-//   32 rows: (4, 2, 4, 1), load-wait-compute (the pipelined form needs 2
+// 8448 x 6656 and 6656 x 19968 (MT m-tiles per wave, KW waves along K, MG
+// wave groups along M; at most 8 waves, so no wave is held to fewer than 256
+// VGPRs):
+//   16 rows: (1, 4, 1), pipelined with activation prefetch;
+//   32 rows: (2, 4, 1), load-wait-compute (the pipelined form needs 2
 //            register sets of 2 m-tiles and runs at one wave per SIMD);
-//   48 rows: (4, 1, 2, 3), pipelined;
-//   64 rows: (4, 2, 4, 2), load-wait-compute (pipelined, it spills).
+//   48 rows: (1, 2, 3), pipelined;
+//   64 rows: (2, 4, 2), load-wait-compute (pipelined, it spills).
 hipError_t launch_w4a16_mfma(int m, const void* x, const void* packed, int n, int k, void* y,
                              int y_f32, float* partial, int split, hipStream_t stream) {
-#define QG_MF(NT, MT, KW, MG, PIPE, PFX) \
-  return launch_mfma_t<NT, MT, KW, MG, PIPE, PFX>(x, m, packed, n, k, y, y_f32, partial, split, stream)
+#define QG_MF(MT, KW, MG, PIPE, PFX) \
+  return launch_mfma_t<MT, KW, MG, PIPE, PFX>(x, m, packed, n, k, y, y_f32, partial, split, stream)
   switch ((m + 15) / 16) {
-    case 1: QG_MF(4, 1, 4, 1, true, true);
-    case 2: QG_MF(4, 2, 4, 1, false, false);
-    case 3: QG_MF(4, 1, 2, 3, true, true);
-    case 4: QG_MF(4, 2, 4, 2, false, false);
+    case 1: QG_MF(1, QG_MFMA_KW1, 1, QG_MFMA_PIPE1 != 0, true);
+    case 2: QG_MF(2, 4, 1, false, false);
+    case 3: QG_MF(1, 2, 3, true, true);
+    case 4: QG_MF(2, 4, 2, false, false);
     default: return hipErrorInvalidValue;
   }
 #undef QG_MF
