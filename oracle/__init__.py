@@ -54,6 +54,8 @@ def _load():
         "orc_qgemm_w8a16": (None, [P, I64, I64, P, P, I64, P, I]),
         "orc_actquant_int8": (None, [P, I64, I64, P, P]),
         "orc_qgemm_w4a8": (None, [P, I64, I64, P, P, P, I64, P, I]),
+        "orc_actquant_int8_g32": (None, [P, I64, I64, P, P]),
+        "orc_qgemm_w4a8_g32": (None, [P, I64, I64, P, P, P, I64, P, I]),
         "orc_hardware_threads": (I, []),
     }
     for name, (res, args) in sig.items():
@@ -194,6 +196,28 @@ def actquant_int8(x_bits):
     sx = np.empty(m, np.float32)
     _load().orc_actquant_int8(_ptr(x), m, k, _ptr(xq), _ptr(sx))
     return xq, sx
+
+
+def actquant_int8_g32(x_bits):
+    """Per-group-32 activation quantization: (xq [m, k] int8, sx [m, k/32] float32)."""
+    x = _u16(x_bits)
+    m, k = x.shape
+    xq = np.empty((m, k), np.int8)
+    sx = np.empty((m, k // 32), np.float32)
+    _load().orc_actquant_int8_g32(_ptr(x), m, k, _ptr(xq), _ptr(sx))
+    return xq, sx
+
+
+def qgemm_w4a8_g32(x_bits, codes, scales, zeros, threads: int = 1) -> np.ndarray:
+    x = _u16(x_bits)
+    m, k = x.shape
+    n = codes.shape[0]
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = _u16(scales)
+    zeros = np.ascontiguousarray(zeros, np.uint8)
+    y = np.empty((m, n), np.float64)
+    _load().orc_qgemm_w4a8_g32(_ptr(x), m, k, _ptr(codes), _ptr(scales), _ptr(zeros), n, _ptr(y), threads)
+    return y
 
 
 def qgemm_w4a8(x_bits, codes, scales, zeros, threads: int = 1) -> np.ndarray:

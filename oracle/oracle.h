@@ -100,6 +100,15 @@ void orc_qgemm_w4a8(const uint16_t *x, int64_t m, int64_t k,
                     const uint8_t *codes, const uint16_t *scales,
                     const uint8_t *zeros, int64_t n, double *y, int threads);
 
+/* ---- W4A8 with per-group-32 activation scales ----
+ * The per-row rule above applied to each group of 32 consecutive k of a row
+ * (sx is [m, k/32]); y[m,n] = sum_g sx[m,g] * s[n,g] * I[m,n,g]. */
+void orc_actquant_int8_g32(const uint16_t *x, int64_t m, int64_t k, int8_t *xq,
+                           float *sx);
+void orc_qgemm_w4a8_g32(const uint16_t *x, int64_t m, int64_t k,
+                        const uint8_t *codes, const uint16_t *scales,
+                        const uint8_t *zeros, int64_t n, double *y, int threads);
+
 /* Thread count the machine offers (for the CPU baseline). */
 int orc_hardware_threads(void);
 

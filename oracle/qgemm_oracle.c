@@ -367,27 +367,40 @@ void orc_qgemm_w8a16(const uint16_t *x, int64_t m, int64_t k, const int8_t *w,
 /* W4A8 ([P1] Int4QuantizedGemmPrecisionTest: int8 activations held to */
 /* the W4A16 reference's precision class).                             */
 /* ------------------------------------------------------------------ */
+/* Symmetric absmax int8 quantization of one span of activations:
+ * a = max |x|; a == 0 gives xq = 0, sx = 0; otherwise inv = 127/a and
+ * sx = a/127 (binary32 divisions), xq = clamp(rint(x * inv), -127, 127). */
+static void quant_span(const uint16_t *xr, int64_t len, int8_t *xq, float *sx) {
+    float a = 0.0f;
+    for (int64_t i = 0; i < len; i++) {
+        float v = fabsf(bf16_to_float(xr[i]));
+        if (v > a) a = v;
+    }
+    if (a == 0.0f) {
+        *sx = 0.0f;
+        for (int64_t i = 0; i < len; i++) xq[i] = 0;
+        return;
+    }
+    float inv = 127.0f / a;
+    *sx = a / 127.0f;
+    for (int64_t i = 0; i < len; i++) {
+        float t = rintf(bf16_to_float(xr[i]) * inv);
+        xq[i] = (int8_t)clampf(t, -127.0f, 127.0f);
+    }
+}
+
 void orc_actquant_int8(const uint16_t *x, int64_t m, int64_t k, int8_t *xq,
                        float *sx) {
-    for (int64_t mi = 0; mi < m; mi++) {
-        const uint16_t *xr = x + mi * k;
-        float a = 0.0f;
-        for (int64_t i = 0; i < k; i++) {
-            float v = fabsf(bf16_to_float(xr[i]));
-            if (v > a) a = v;
-        }
-        if (a == 0.0f) {
-            sx[mi] = 0.0f;
-            for (int64_t i = 0; i < k; i++) xq[mi * k + i] = 0;
-            continue;
-        }
-        float inv = 127.0f / a;
-        sx[mi] = a / 127.0f;
-        for (int64_t i = 0; i < k; i++) {
-            float t = rintf(bf16_to_float(xr[i]) * inv);
-            xq[mi * k + i] = (int8_t)clampf(t, -127.0f, 127.0f);
-        }
-    }
+    for (int64_t mi = 0; mi < m; mi++) quant_span(x + mi * k, k, xq + mi * k, sx + mi);
+}
+
+/* The same rule per group of 32 consecutive k of a row: sx is [m, k/32]. */
+void orc_actquant_int8_g32(const uint16_t *x, int64_t m, int64_t k, int8_t *xq,
+                           float *sx) {
+    int64_t groups = k / 32;
+    for (int64_t mi = 0; mi < m; mi++)
+        for (int64_t g = 0; g < groups; g++)
+            quant_span(x + mi * k + g * 32, 32, xq + mi * k + g * 32, sx + mi * groups + g);
 }
 
 struct w4a8_ctx {
@@ -425,6 +438,44 @@ void orc_qgemm_w4a8(const uint16_t *x, int64_t m, int64_t k,
     orc_actquant_int8(x, m, k, xq, sx);
     struct w4a8_ctx c = {xq, sx, m, k, codes, scales, zeros, n, y};
     parallel_rows(w4a8_rows, &c, n, threads);
+    free(xq);
+    free(sx);
+}
+
+/* W4A8 with one activation scale per group of 32:
+ * y[m,n] = sum_g sx[m,g] * s[n,g] * I[m,n,g]; every product is exact in
+ * binary64 (24 + 11 + 16 significant bits), the sum over g is in binary64. */
+static void w4a8_g32_rows(void *p, int64_t b, int64_t e) {
+    struct w4a8_ctx *c = (struct w4a8_ctx *)p;
+    int64_t groups = c->k / 32;
+    for (int64_t row = b; row < e; row++)
+        for (int64_t mi = 0; mi < c->m; mi++) {
+            double acc = 0.0;
+            for (int64_t g = 0; g < groups; g++) {
+                int64_t isum = 0;
+                int zg = c->zeros[row * groups + g];
+                for (int64_t i = 0; i < 32; i++) {
+                    int64_t kk = g * 32 + i;
+                    isum += (int64_t)c->xq[mi * c->k + kk] *
+                            (int64_t)(c->codes[row * c->k + kk] - zg);
+                }
+                acc += (double)c->sx[mi * groups + g] *
+                       orc_fp16_to_double(c->scales[row * groups + g]) * (double)isum;
+            }
+            c->y[mi * c->n + row] = acc;
+        }
+}
+
+void orc_qgemm_w4a8_g32(const uint16_t *x, int64_t m, int64_t k,
+                        const uint8_t *codes, const uint16_t *scales,
+                        const uint8_t *zeros, int64_t n, double *y, int threads) {
+    int64_t groups = k / 32;
+    int8_t *xq = (int8_t *)malloc((size_t)(m * k));
+    float *sx = (float *)malloc((size_t)(m * groups) * sizeof(float));
+    if (!xq || !sx) { free(xq); free(sx); abort(); }
+    orc_actquant_int8_g32(x, m, k, xq, sx);
+    struct w4a8_ctx c = {xq, sx, m, k, codes, scales, zeros, n, y};
+    parallel_rows(w4a8_g32_rows, &c, n, threads);
     free(xq);
     free(sx);
 }

@@ -10,7 +10,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "qgemm_oracle.c")
-PINS = [os.path.join(ROOT, "tests", f) for f in ("test_oracle_int4.py", "test_oracle_int8.py")]
+PINS = [os.path.join(ROOT, "tests", f) for f in ("test_oracle_int4.py", "test_oracle_int8.py",
+                                                 "test_oracle_w4a8_g32.py")]
 
 # (id, original text, planted text): each is a single, plausible slip.
 MUTANTS = [
@@ -37,6 +38,13 @@ MUTANTS = [
     ("actquant_128_levels", "float inv = 127.0f / a;", "float inv = 128.0f / a;"),
     ("w4a8_zero_point_dropped", "(int64_t)(c->codes[row * c->k + kk] - z)", "(int64_t)(c->codes[row * c->k + kk])"),
     ("w4a8_act_scale_dropped", "c->y[mi * c->n + row] = (double)c->sx[mi] * acc;", "c->y[mi * c->n + row] = acc;"),
+    ("g32_first_group_scale_for_all", "(double)c->sx[mi * groups + g] *", "(double)c->sx[mi * groups] *"),
+    ("g32_groups_of_the_row_scale", "quant_span(x + mi * k + g * 32, 32, xq + mi * k + g * 32, sx + mi * groups + g);",
+     "{ quant_span(x + mi * k + g * 32, 32, xq + mi * k + g * 32, sx + mi * groups + g); "
+     "if (g) sx[mi * groups + g] = sx[mi * groups]; }"),
+    ("g32_zero_point_of_next_group", "int zg = c->zeros[row * groups + g];",
+     "int zg = c->zeros[row * groups + (g + 1) % groups];"),
+    ("g32_span_shifted", "quant_span(x + mi * k + g * 32, 32,", "quant_span(x + mi * k + g * 32 + (g > 0), 32,"),
 ]
 
 

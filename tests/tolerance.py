@@ -8,7 +8,11 @@ then adds half a bf16 ulp of ref, and the mean-relative bound is unchanged.
 
 W4A8 against the W4A16 reference: the precision class of executorch
 test_int4_quantized_gemm.py `_check_close` (rtol 0.03, atol 8.0, mean
-relative error below 0.02).
+relative error below 0.02), and the three checks of its
+Int4QuantizedGemmPrecisionTest against the unquantized (dense) product:
+the W4A8 error against dense may be at most 1.10x the W4A16 error in the
+mean, the W4A8 - W4A16 difference at most 2% of mean|W4A16|, and the largest
+W4A8 error at most the largest W4A16 error + max(2, 2% of max|dense|).
 """
 from __future__ import annotations
 
@@ -63,3 +67,24 @@ def assert_w4a8_class(y, ref_w4a16, label: str = "") -> None:
     assert not over.any(), f"{label}: {int(over.sum())} elements outside rtol 0.03 / atol 8"
     mean_rel = err.mean() / np.abs(ref).mean()
     assert mean_rel < 0.02, f"{label}: mean relative error {mean_rel:.3g} >= 0.02"
+
+
+def precision_class_failures(a8, a16, dense) -> list[str]:
+    """The dense-reference checks of the pages' W4A8 precision test; returns
+    the failed ones (empty when the case passes)."""
+    a8, a16, dense = _as_f64(a8), _as_f64(a16), _as_f64(dense)
+    bad = []
+    if not np.isfinite(a8).all():
+        return ["non-finite"]
+    e8 = np.abs(a8 - dense)
+    e16 = np.abs(a16 - dense)
+    ratio = e8.mean() / max(e16.mean(), 1e-6)
+    mean_rel = np.abs(a8 - a16).mean() / max(np.abs(a16).mean(), 1e-6)
+    allowance = max(2.0, 0.02 * np.abs(dense).max())
+    if ratio > 1.10:
+        bad.append(f"dense error ratio {ratio:.3f} > 1.10")
+    if mean_rel > 0.02:
+        bad.append(f"mean relative difference {mean_rel:.4f} > 0.02")
+    if e8.max() > e16.max() + allowance:
+        bad.append(f"max error {e8.max():.3g} > {e16.max():.3g} + {allowance:.3g}")
+    return bad
