@@ -23,7 +23,7 @@ host's cores over a bounded sample of the same workload and checks the GPU
 result against it.
 
 Other layers of the same path use the same protocol: --op w4a16 with
---m 2..64 (M > 4 runs the matrix-core kernel), --op w4a8 (M <= 4) and
+--m 2..64 (M > 4 runs the matrix-core kernel), --op w4a8 / w4a8_g32 (M <= 4) and
 --op w8a16 (int8 per-channel, bytes = N*K + 2*N); --n/--k pick the shape.
 
 Prints ONE JSON line.
@@ -78,7 +78,7 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=1000,
                    help="untimed calls first; the clocks take a few hundred calls to ramp up from idle")
-    p.add_argument("--op", choices=("w4a16", "w4a8", "w8a16"), default="w4a16")
+    p.add_argument("--op", choices=("w4a16", "w4a8", "w4a8_g32", "w8a16"), default="w4a16")
     p.add_argument("--n", type=int, default=39936)
     p.add_argument("--k", type=int, default=6656)
     p.add_argument("--m", type=int, default=1)
@@ -136,7 +136,7 @@ def main() -> int:
         packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
         x = x_cpu.to(dev)
         ws = torch.empty(max(qg.workspace_bytes(m, n, k, split), 1), dtype=torch.uint8, device=dev)
-        fn = qg.qgemm_w4a16 if op == "w4a16" else qg.qgemm_w4a8
+        fn = {"w4a16": qg.qgemm_w4a16, "w4a8": qg.qgemm_w4a8, "w4a8_g32": qg.qgemm_w4a8_g32}[op]
 
         def call(i):
             fn(x, packs[i % copies], n, split_k=split, out=y, workspace=ws)
@@ -185,9 +185,9 @@ def main() -> int:
     y_first = y.clone()
 
     headline = op == "w4a16" and (n, k, m) == (39936, 6656, 1)
-    kernel = {"w4a16": "GEMV" if m <= 4 else "matrix-core GEMM", "w4a8": "GEMV", "w8a16": "GEMV"}[op]
+    kernel = "matrix-core GEMM" if (op == "w4a16" and m > 4) else "GEMV"
     label = {"w4a16": "W4A16 INT4-g32 asymmetric", "w4a8": "W4A8 INT4-g32 x per-row int8",
-             "w8a16": "W8A16 INT8 per-channel"}[op]
+             "w4a8_g32": "W4A8 INT4-g32 x per-group-32 int8", "w8a16": "W8A16 INT8 per-channel"}[op]
     out = {
         "metric": METRIC if headline else
         f"µs/call and effective weight GB/s (% HBM peak) for {label} {kernel} at M={m}",
@@ -273,7 +273,8 @@ def cpu_baseline(args, oracle_inputs, y_gpu, bytes_eff):
             return oracle.qgemm_w8a16(xb, wi8, sb, threads=threads)
     else:
         codes, scales, zeros, _ = oracle.quantize_int4_g32(si.bf16_bits(w_cpu))
-        fn = oracle.qgemm_w4a16 if args.op == "w4a16" else oracle.qgemm_w4a8
+        fn = {"w4a16": oracle.qgemm_w4a16, "w4a8": oracle.qgemm_w4a8,
+              "w4a8_g32": oracle.qgemm_w4a8_g32}[args.op]
 
         def run():
             return fn(xb, codes, scales, zeros, threads=threads)

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     default_split_k,
     int4_packed_bytes,
     qgemm_w4a8,
+    qgemm_w4a8_g32,
     qgemm_w4a16,
     qgemm_w8a16,
     quantize_int4_g32,

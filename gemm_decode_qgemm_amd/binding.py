@@ -48,6 +48,7 @@ def _load() -> ctypes.CDLL:
         "qgemm_w4a16": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "qgemm_w8a16": (I32, [P, I64, I64, P, P, I64, P, I32, P]),
         "qgemm_w4a8": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
+        "qgemm_w4a8_g32": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -193,4 +194,18 @@ def qgemm_w4a8(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_k: int = 
     st = lib.qgemm_w4a8(x.data_ptr(), m, k, packed.data_ptr(), packed.numel(), n, y.data_ptr(),
                         yd, split_k, _ptr(ws), ws_bytes, _stream(x.device))
     _check(st, "qgemm_w4a8")
+    return y
+
+
+def qgemm_w4a8_g32(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_k: int = 0,
+                   out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A8 with one int8 activation scale per group of 32 (quantized inside the call)."""
+    _dev(x, "x", torch.bfloat16, 2)
+    m, k = x.shape
+    y, yd = _out(m, n, out_dtype, x.device, out)
+    ws, ws_bytes = _workspace(m, n, k, split_k, x.device, workspace)
+    st = lib.qgemm_w4a8_g32(x.data_ptr(), m, k, packed.data_ptr(), packed.numel(), n, y.data_ptr(),
+                            yd, split_k, _ptr(ws), ws_bytes, _stream(x.device))
+    _check(st, "qgemm_w4a8_g32")
     return y

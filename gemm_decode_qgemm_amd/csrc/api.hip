@@ -30,6 +30,9 @@ hipError_t launch_w4a16_mfma(int m, const void* x, const void* packed, int n, in
 hipError_t launch_w4a8_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
                             int y_f32, float* partial, int split, int rows, int waves,
                             hipStream_t stream);
+hipError_t launch_w4a8_gemv_lds(int m, bool group_scales, const void* x, const void* packed, int n,
+                                int k, void* y, int y_f32, float* partial, int split,
+                                hipStream_t stream);
 hipError_t launch_w8a16_gemv(int m, const void* x, const int8_t* w, const void* scale, int n,
                              int k, void* y, int y_f32, hipStream_t stream);
 }  // namespace qg
@@ -218,9 +221,9 @@ int32_t qgemm_w8a16(const void* x_bf16, int64_t m, int64_t k, const int8_t* w,
                                           y_dtype == QG_F32, static_cast<hipStream_t>(stream)));
 }
 
-int32_t qgemm_w4a8(const void* x_bf16, int64_t m, int64_t k, const void* packed,
-                   int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype, int32_t split_k,
-                   void* ws, int64_t ws_bytes, void* stream) {
+static int32_t w4a8_common(const void* x_bf16, int64_t m, int64_t k, const void* packed,
+                           int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype, int32_t split_k,
+                           void* ws, int64_t ws_bytes, void* stream, bool group_scales) {
   if (!x_bf16 || !packed || !y) return QG_E_NULL;
   int32_t st = check_mnk(m, n, k);
   if (st != QG_OK) return st;
@@ -234,13 +237,33 @@ int32_t qgemm_w4a8(const void* x_bf16, int64_t m, int64_t k, const void* packed,
   if (need_ws > 0 && (!ws || ws_bytes < need_ws)) return ws ? QG_E_BUFFER : QG_E_NULL;
   if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || (ws && !aligned16(ws)))
     return QG_E_ALIGN;
-  const GemvShape g = gemv_shape(m, n, split);
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
-  st = hip_status(qg::launch_w4a8_gemv((int)m, x_bf16, packed, (int)n, (int)k, y,
-                                       y_dtype == QG_F32, partial, split, g.rows, g.waves, s));
+  if (group_scales || m > 1) {
+    // activations quantized once per workgroup through LDS
+    st = hip_status(qg::launch_w4a8_gemv_lds((int)m, group_scales, x_bf16, packed, (int)n, (int)k,
+                                             y, y_dtype == QG_F32, partial, split, s));
+  } else {
+    const GemvShape g = gemv_shape(m, n, split);
+    st = hip_status(qg::launch_w4a8_gemv((int)m, x_bf16, packed, (int)n, (int)k, y,
+                                         y_dtype == QG_F32, partial, split, g.rows, g.waves, s));
+  }
   if (st != QG_OK || split == 1) return st;
   return hip_status(qg::launch_splitk_reduce(partial, split, m * n, y, y_dtype == QG_F32, s));
+}
+
+int32_t qgemm_w4a8(const void* x_bf16, int64_t m, int64_t k, const void* packed,
+                   int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype, int32_t split_k,
+                   void* ws, int64_t ws_bytes, void* stream) {
+  return w4a8_common(x_bf16, m, k, packed, packed_bytes, n, y, y_dtype, split_k, ws, ws_bytes,
+                     stream, false);
+}
+
+int32_t qgemm_w4a8_g32(const void* x_bf16, int64_t m, int64_t k, const void* packed,
+                       int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype, int32_t split_k,
+                       void* ws, int64_t ws_bytes, void* stream) {
+  return w4a8_common(x_bf16, m, k, packed, packed_bytes, n, y, y_dtype, split_k, ws, ws_bytes,
+                     stream, true);
 }
 
 }  // extern "C"

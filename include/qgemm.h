@@ -174,10 +174,23 @@ int32_t qgemm_w8a16(const void *x_bf16, int64_t m, int64_t k, const int8_t *w,
  * with exact integer group dots.  Arguments and errors as qgemm_w4a16
  * (1 <= m <= 4 in this version: QG_E_M_RANGE above).  The per-row scale is
  * the pages' precision class on gaussian activations; rows with a few large
- * outlier channels lose precision (finer activation groups would fix it). */
+ * outlier channels lose precision (qgemm_w4a8_g32 below keeps it). */
 int32_t qgemm_w4a8(const void *x_bf16, int64_t m, int64_t k, const void *packed,
                    int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
                    int32_t split_k, void *ws, int64_t ws_bytes, void *stream);
+
+/* ---- qgemm_w4a8_g32 ------------------------------------------------------
+ * [P1] `Int4QuantizedGemmPrecisionTest` with its outlier activations
+ * (channels 0, K/3, 2K/3, K-1 scaled by 50, 35, 25, 20): W4A8 with one
+ * activation scale per group of 32 consecutive k of a row, so an outlier
+ * only coarsens its own group.  Per row m and group g:
+ *   a = max |x[m, 32g .. 32g+31]|, inv = 127/a, sx[m,g] = a/127 (binary32),
+ *   xq = clamp(rint(x * inv), -127, 127); a == 0 gives a zero group;
+ *   y[m,n] = sum_g sx[m,g] * s[n,g] * sum_{k in g} xq[m,k] * (q[n,k] - zp[n,g]).
+ * Arguments, buffers, workspace and errors exactly as qgemm_w4a8. */
+int32_t qgemm_w4a8_g32(const void *x_bf16, int64_t m, int64_t k, const void *packed,
+                       int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
+                       int32_t split_k, void *ws, int64_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -39,6 +39,7 @@ def lib():
         "qgemm_w4a16": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "qgemm_w8a16": (I32, [P, I64, I64, P, P, I64, P, I32, P]),
         "qgemm_w4a8": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
+        "qgemm_w4a8_g32": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(l, name)
@@ -122,13 +123,14 @@ def test_default_split_table(lib):
 ])
 def test_qgemm_w4a16_and_w4a8_validate_before_launching(lib, args, expect):
     assert lib.qgemm_w4a16(*args) == expect
-    # W4A8 shares the rules, except that it stops at M = 4 in this version
-    got = lib.qgemm_w4a8(*args)
-    assert got == expect or (expect == E_M and got == E_M)
+    # W4A8 (both activation granularities) shares the rules
+    assert lib.qgemm_w4a8(*args) == expect
+    assert lib.qgemm_w4a8_g32(*args) == expect
 
 
 def test_w4a8_m_range(lib):
     assert lib.qgemm_w4a8(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
+    assert lib.qgemm_w4a8_g32(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
 
 
 @pytest.mark.parametrize("args,expect", [
