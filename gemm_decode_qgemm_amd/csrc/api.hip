@@ -65,8 +65,10 @@ constexpr int64_t kCUs = 256;   // compute units of an MI355X
 //  * M <= 4 (GEMV, 32-row workgroups): one split whenever the grid has at
 //    least half a workgroup per CU (N >= 4096): a second split costs a second
 //    launch and the partials' traffic, which the extra parallelism does not
-//    repay at these shapes; below that, the smallest split giving 32
-//    workgroups, at most 4 (N = 256, K = 6656: 5.5 us at 4 against 5.9 at 1).
+//    repay at these shapes (6656 x 4096: 5.1 us at 1 against 7.1 at 2);
+//    below that, the smallest split giving a workgroup per CU, at most 4
+//    (2048 x 8192, M = 4: 7.4 us at 4 against 11.7 at 1; 256 x 6656: 5.3 us
+//    at 4, 5.9 at 8).
 //  * M > 4 (matrix-core kernel): the smallest split with 64-row blocks x
 //    split >= 120, at most 8 (6656 x 19968, M = 16: 24.4 us at 2 against 39.6
 //    at 1; 8448 x 6656: 15.6 us at 1 against 18.3 at 2).
@@ -76,8 +78,14 @@ int32_t default_split(int64_t m, int64_t n, int64_t k) {
   int32_t s = 1;
   if (m <= 4) {
     const int64_t n32 = (n + 31) / 32;
-    if (n32 >= kCUs / 2) return 1;
-    while (s < 4 && 2 * s <= kt && n32 * s < 32) s *= 2;
+    if (n32 >= kCUs / 2) {
+      // M >= 3 with a 32-row grid just past one round (M <= 2 takes the
+      // 64-row kernel there instead): 8448 x 6656, M = 4: 14.1 us at 2
+      // against 15.7 at 1.
+      if (m >= 3 && n32 > kCUs && 2 * n32 <= 3 * kCUs && kt >= 2) return 2;
+      return 1;
+    }
+    while (s < 4 && 2 * s <= kt && n32 * s < kCUs) s *= 2;
     return s;
   }
   const int64_t rbs = (n + QG_TILE_ROWS - 1) / QG_TILE_ROWS;

@@ -87,13 +87,17 @@ def test_split_rule_one_k_tile_per_split(lib):
 
 
 def test_default_split_table(lib):
-    # M <= 4: one split from N = 4096 up; below, 32 workgroups of 32 rows, at most 4
-    for n, k in ((39936, 6656), (8448, 6656), (6656, 4096), (6656, 19968), (4096, 256)):
+    # M <= 4: one split from N = 4096 up; below, a workgroup of 32 rows per CU, at most 4
+    for n, k in ((39936, 6656), (6656, 4096), (6656, 19968), (4096, 256),
+                 (8192, 2048), (6144, 2048), (32000, 2048)):
         for m in (1, 4):
             assert lib.qg_default_split_k(m, n, k) == 1, (m, n, k)
+    # a 32-row grid just past one round: M <= 2 runs 64-row workgroups, M >= 3 splits in 2
+    assert [lib.qg_default_split_k(m, 8448, 6656) for m in (1, 2, 3, 4)] == [1, 1, 2, 2]
+    assert lib.qg_default_split_k(1, 2048, 8192) == 4
     assert lib.qg_default_split_k(1, 256, 6656) == 4
-    assert lib.qg_default_split_k(3, 512, 6656) == 2
-    assert lib.qg_default_split_k(1, 1024, 6656) == 1
+    assert lib.qg_default_split_k(3, 512, 6656) == 4
+    assert lib.qg_default_split_k(1, 3072, 6656) == 4
     assert lib.qg_default_split_k(1, 256, 256) == 1       # capped by K / 256
     assert lib.qg_default_split_k(1, 256, 512) == 2
     # M > 4: row blocks of 64 x split >= 120, at most 8
