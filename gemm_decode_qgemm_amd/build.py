@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libqgemm.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["api.hip", "quantize.hip", "gemv_w4a16.hip", "gemv_w8a16.hip", "gemv_w4a8.hip",
-           "gemm_w4a16_mfma.hip"]
+           "gemm_w4a16_mfma.hip", "gemv_w4a16_mx4.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -41,7 +41,8 @@ FLAGS = [
 # Per-source flags.  The matrix-core kernel asks the backend to write MFMA
 # results to ordinary VGPRs (the AGPR form costs a v_accvgpr_read per result
 # element before the fp32 epilogue of every group).
-SOURCE_FLAGS = {"gemm_w4a16_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"gemm_w4a16_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "gemv_w4a16_mx4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, extra: list[str], objdir: str) -> str:

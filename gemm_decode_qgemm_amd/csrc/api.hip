@@ -22,6 +22,9 @@ hipError_t launch_w4a16_gemv(int m, const void* x, const void* packed, int n, in
                              int y_f32, float* partial, int split, int waves, hipStream_t stream);
 hipError_t launch_w4a16_gemv32(int m, const void* x, const void* packed, int n, int k, void* y,
                                int y_f32, float* partial, int split, int waves, hipStream_t stream);
+hipError_t launch_w4a16_gemv_mx4(int m, const void* x, const void* packed, int n, int k, void* y,
+                                 int y_f32, float* partial, int split, int waves,
+                                 hipStream_t stream);
 hipError_t launch_splitk_reduce(const float* partial, int split, int64_t mn, void* y, int y_f32,
                                 hipStream_t stream);
 int w8a16_chunks_per_wave(int k);
@@ -65,10 +68,11 @@ constexpr int64_t kCUs = 256;   // compute units of an MI355X
 //  * M <= 4 (GEMV, 32-row workgroups): one split whenever the grid has at
 //    least half a workgroup per CU (N >= 4096): a second split costs a second
 //    launch and the partials' traffic, which the extra parallelism does not
-//    repay at these shapes (6656 x 4096: 5.1 us at 1 against 7.1 at 2);
-//    below that, the smallest split giving a workgroup per CU, at most 4
-//    (2048 x 8192, M = 4: 7.4 us at 4 against 11.7 at 1; 256 x 6656: 5.3 us
-//    at 4, 5.9 at 8).
+//    repay at these shapes (6656 x 4096: 5.1 us at 1 against 7.1 at 2 for
+//    M = 1, 5.4 against 7.4 for M = 4; 8448 x 6656, M = 4: 10.7 against
+//    11.1); below that, the smallest split giving a workgroup per CU, at
+//    most 4 (2048 x 8192, M = 4: 6.7 us at 4 against 7.4 at 1; 256 x 6656:
+//    5.3 us at 4, 5.9 at 8).
 //  * M > 4 (matrix-core kernel): the smallest split with 64-row blocks x
 //    split >= 120, at most 8 (6656 x 19968, M = 16: 24.4 us at 2 against 39.6
 //    at 1; 8448 x 6656: 15.6 us at 1 against 18.3 at 2).
@@ -78,13 +82,7 @@ int32_t default_split(int64_t m, int64_t n, int64_t k) {
   int32_t s = 1;
   if (m <= 4) {
     const int64_t n32 = (n + 31) / 32;
-    if (n32 >= kCUs / 2) {
-      // M >= 3 with a 32-row grid just past one round (M <= 2 takes the
-      // 64-row kernel there instead): 8448 x 6656, M = 4: 14.1 us at 2
-      // against 15.7 at 1.
-      if (m >= 3 && n32 > kCUs && 2 * n32 <= 3 * kCUs && kt >= 2) return 2;
-      return 1;
-    }
+    if (n32 >= kCUs / 2) return 1;
     while (s < 4 && 2 * s <= kt && n32 * s < kCUs) s *= 2;
     return s;
   }
@@ -96,13 +94,14 @@ int32_t default_split(int64_t m, int64_t n, int64_t k) {
 // Workgroup shape of the M <= 4 INT4 GEMVs: 32 rows and 16 waves, except
 // where the 32-row grid spills a few workgroups into a second round over the
 // CUs while the 64-row grid fits in one (N = 8448: 264 against 132
-// workgroups; 9.1 us against 10.2 at M = 1), for M <= 2 and one split.
+// workgroups; 9.1 us against 10.2 at M = 1), for M = 1 and one split (at
+// M = 2 the matrix-instruction GEMV on 32 rows is as fast: 10.7 us).
 struct GemvShape {
   int rows, waves;
 };
 GemvShape gemv_shape(int64_t m, int64_t n, int32_t split) {
   const int64_t n32 = (n + 31) / 32, n64 = (n + 63) / 64;
-  if (m <= 2 && split == 1 && n32 > kCUs && n64 <= kCUs) return {64, 16};
+  if (m == 1 && split == 1 && n32 > kCUs && n64 <= kCUs) return {64, 16};
   return {32, 16};
 }
 
@@ -203,8 +202,13 @@ int32_t qgemm_w4a16(const void* x_bf16, int64_t m, int64_t k, const void* packed
     st = hip_status(qg::launch_w4a16_mfma((int)m, x_bf16, packed, (int)n, (int)k, y,
                                           y_dtype == QG_F32, partial, split, s));
   } else {
+    // M = 1: v_dot2c GEMV; M = 2..4: the same 32-row mapping on the 4x4x4
+    // matrix instruction, whose cost does not grow with M.
     const GemvShape g = gemv_shape(m, n, split);
-    if (g.rows == 32)
+    if (m >= 2)
+      st = hip_status(qg::launch_w4a16_gemv_mx4((int)m, x_bf16, packed, (int)n, (int)k, y,
+                                                y_dtype == QG_F32, partial, split, g.waves, s));
+    else if (g.rows == 32)
       st = hip_status(qg::launch_w4a16_gemv32((int)m, x_bf16, packed, (int)n, (int)k, y,
                                               y_dtype == QG_F32, partial, split, g.waves, s));
     else

@@ -1,4 +1,6 @@
-// gemv_w4a16.hip -- decode GEMV for the packed INT4 group-32 weight, M = 1..4.
+// gemv_w4a16.hip -- decode GEMV for the packed INT4 group-32 weight, M = 1
+// (the kernels are written for any M <= 4, but M = 2..4 run faster on the
+// matrix instruction, gemv_w4a16_mx4.hip, and only M = 1 is instantiated).
 //
 // Computes y[m, n] = sum_k x[m, k] * (q[n,k] - zp[n,g]) * s[n,g], the
 // "dequant + F.linear" reference of executorch test_int4_quantized_gemm.py
@@ -374,8 +376,9 @@ hipError_t launch_w4a16_gemv32(int m, const void* x, const void* packed, int n, 
                                int y_f32, float* partial, int split, int waves, hipStream_t stream) {
 #define QG_W32_CASE(MM, WW) \
   if (m == MM && waves == WW) return launch_w4a16_32_t<MM, WW>(x, packed, n, k, y, y_f32, partial, split, stream);
-#define QG_W32_M(MM) QG_W32_CASE(MM, 8) QG_W32_CASE(MM, 16)
-  QG_W32_M(1) QG_W32_M(2) QG_W32_M(3) QG_W32_M(4)
+  // M = 2..4 run on the matrix-instruction GEMV (gemv_w4a16_mx4.hip).
+#define QG_W32_M(MM) QG_W32_CASE(MM, 16)
+  QG_W32_M(1)
 #undef QG_W32_M
 #undef QG_W32_CASE
   return hipErrorInvalidValue;
@@ -385,8 +388,8 @@ hipError_t launch_w4a16_gemv(int m, const void* x, const void* packed, int n, in
                              int y_f32, float* partial, int split, int waves, hipStream_t stream) {
 #define QG_W4_CASE(MM, WW) \
   if (m == MM && waves == WW) return launch_w4a16_t<MM, WW>(x, packed, n, k, y, y_f32, partial, split, stream);
-#define QG_W4_M(MM) QG_W4_CASE(MM, 8) QG_W4_CASE(MM, 16)
-  QG_W4_M(1) QG_W4_M(2) QG_W4_M(3) QG_W4_M(4)
+#define QG_W4_M(MM) QG_W4_CASE(MM, 16)
+  QG_W4_M(1)
 #undef QG_W4_M
 #undef QG_W4_CASE
   return hipErrorInvalidValue;
