@@ -42,7 +42,8 @@ FLAGS = [
 # results to ordinary VGPRs (the AGPR form costs a v_accvgpr_read per result
 # element before the fp32 epilogue of every group).
 SOURCE_FLAGS = {"gemm_w4a16_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-                "gemv_w4a16_mx4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+                "gemv_w4a16_mx4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "gemv_w4a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, extra: list[str], objdir: str) -> str:

@@ -36,6 +36,9 @@ hipError_t launch_w4a8_gemv(int m, const void* x, const void* packed, int n, int
 hipError_t launch_w4a8_gemv_lds(int m, bool group_scales, const void* x, const void* packed, int n,
                                 int k, void* y, int y_f32, float* partial, int split,
                                 hipStream_t stream);
+hipError_t launch_w4a8_gemv_mx4(int m, bool group_scales, const void* x, const void* packed, int n,
+                                int k, void* y, int y_f32, float* partial, int split,
+                                hipStream_t stream);
 hipError_t launch_w8a16_gemv(int m, const void* x, const int8_t* w, const void* scale, int n,
                              int k, void* y, int y_f32, hipStream_t stream);
 }  // namespace qg
@@ -251,8 +254,12 @@ static int32_t w4a8_common(const void* x_bf16, int64_t m, int64_t k, const void*
     return QG_E_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
-  if (group_scales || m > 1) {
-    // activations quantized once per workgroup through LDS
+  if (m > 1) {
+    // M = 2..4: group dots on the 4x4x4 int8 matrix instruction
+    st = hip_status(qg::launch_w4a8_gemv_mx4((int)m, group_scales, x_bf16, packed, (int)n, (int)k,
+                                             y, y_dtype == QG_F32, partial, split, s));
+  } else if (group_scales) {
+    // M = 1, one scale per group: activations quantized once per workgroup through LDS
     st = hip_status(qg::launch_w4a8_gemv_lds((int)m, group_scales, x_bf16, packed, (int)n, (int)k,
                                              y, y_dtype == QG_F32, partial, split, s));
   } else {

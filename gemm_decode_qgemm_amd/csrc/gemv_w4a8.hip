@@ -10,9 +10,14 @@
 // then y[m,n] = sx[m] * sum_g s[n,g] * I[m,n,g] with the exact integer group
 // dot I = sum_{k in g} xq[m,k] * (q[n,k] - zp[n,g]).
 //
-// Mapping (gfx950, wave64), as the W4A16 GEMV: one 64-row block per
-// workgroup, lane = row, waves take half tiles (4 groups = 128 k) round robin
-// (a 32-row variant below halves the block, as the W4A16 one does).
+// Kernels: M = 1 with per-row scales on the v_dot4c GEMVs below; M = 1 with
+// one scale per group of 32 on w4a8_gemv_lds_kernel; M = 2..4 (both scale
+// kinds) on w4a8_gemv_mx4_kernel, the 4x4x4 int8 matrix instruction.
+//
+// Mapping of the M = 1 v_dot4c GEMV (gfx950, wave64), as the W4A16 GEMV: one
+// 64-row block per workgroup, lane = row, waves take half tiles (4 groups =
+// 128 k) round robin (a 32-row variant below halves the block, as the W4A16
+// one does).
 //  * Prologue: the workgroup reads its x rows once for the absmax (L2-resident).
 //  * Lane i of each 16-lane DPP row loads x[8i .. 8i+8) of the half tile and
 //    quantizes it into two dwords of int8 in the byte order the nibbles need:
@@ -513,6 +518,245 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_lds_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Group dots on v_mfma_i32_4x4x4_16b_i8 (as gemv_w4a16_mx4.hip does for bf16),
+// with the 32-row mapping of w4a8_gemv32_kernel and no barrier in the loop.
+// Per half tile, a wave quantizes the M x 128 activations itself, one 8-k
+// segment per lane (lane l < 16 M: row l / 16, segment l % 16, so each group
+// of 32 is a lane quad), and leaves in a wave-private LDS slot the int8 codes
+// (in quant8's byte order), each group's sum of xq and, per group of 32, its
+// sx.  Then per group: A = xq (row i = activation row m, in lane 4b+i), B =
+// the lane's own codes (lane 4b+j = weight row): a code dword gives two 4-k
+// steps, (w & 0x0F0F0F0F) and ((w >> 4) & 0x0F0F0F0F), whose byte order
+// quant8 matches, so a group is 8 instructions with exact int32
+// accumulation, D[m] in element m of the lane; the zero point is one integer
+// multiply-add per activation row.  The cost per weight does not grow with M.
+__device__ __forceinline__ i32x4_t mfma_i8_4x4x4(uint32_t a, uint32_t b, i32x4_t c) {
+  return __builtin_amdgcn_mfma_i32_4x4x4i8((int)a, (int)b, c, 0, 0, 0);
+}
+
+// xq rows in a wave's slot are 144 bytes apart (16 segments of 8 bytes plus
+// 16): an A-operand read touches (row i, group pair) chunks at 144 i + 64 pair
+// bytes, distinct 16-byte positions modulo 128 and 256 bytes (disjoint banks).
+constexpr int kA8XRowBytes = 144;
+
+// max(a, |x|) over the 8 bf16 of a 16-byte load.
+__device__ __forceinline__ float absmax8(const u32x4_t& v, float a) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a = fmaxf(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
+    a = fmaxf(a, fabsf(bf16_to_f32(w[j] >> 16)));
+  }
+  return a;
+}
+
+template <int M, bool GS>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void w4a8_gemv_mx4_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
+    void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
+  constexpr int WAVES = 16;
+  __shared__ __attribute__((aligned(16))) uint8_t xq_s[WAVES][M * kA8XRowBytes];
+  __shared__ __attribute__((aligned(16))) int gsum_s[WAVES][4][4];          // [group][m]
+  __shared__ __attribute__((aligned(16))) float gsx_s[WAVES][GS ? 4 : 1][4];
+  __shared__ float red[WAVES * M * 64];
+  __shared__ float amax_w[WAVES][M];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int lg = lane >> 5;
+  const int xrow = (lane & 3) < M ? (lane & 3) : M - 1;   // A row of this lane
+  const int wave = wave_id_uniform();
+  const int rb = blockIdx.x >> 1;
+  const int row = 32 * (blockIdx.x & 1) + (lane & 31);
+  const int kt_count = k >> 8;
+  int t0, t1;
+  split_range(kt_count, split, blockIdx.y, t0, t1);
+  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
+  // Quantizing lanes: l < 16 M takes k = 8 (l % 16) .. + 8 of x row l / 16.
+  const bool qlane = lane < 16 * M;
+  const int qm = qlane ? lane >> 4 : 0, qs = lane & 15;
+  const uint16_t* xsrc = x + (size_t)qm * k + 8 * qs;
+  uint8_t* const slot = xq_s[wave];
+
+  int hs = 2 * t0 + wave;
+  const int h_end = 2 * t1;
+  Half32Regs r;
+  float inv_q = 0.0f, sx_row[M];
+  if constexpr (!GS) {
+    // Per-row absmax over the whole row (the workgroup reads x once from L2).
+    // The first pass of x loads goes out first, then the first half tile's
+    // weight loads, so the wait for x does not wait for HBM and the weight
+    // loads stay in flight through the reduction and its barrier.
+    const int k8 = k >> 3;
+    u32x4_t v0[M];
+    // Threads past the row's end re-read its first 8 values (k8 >= 32), which
+    // leaves the maximum unchanged and needs no branch.
+    const int i0 = tid < k8 ? tid : 0;
+#pragma unroll
+    for (int m = 0; m < M; ++m) v0[m] = reinterpret_cast<const u32x4_t*>(x + (size_t)m * k)[i0];
+    // Unconditional (a branch here makes the compiler wait for these loads
+    // with the x loads): a wave without a half tile loads the range's last
+    // one, which another wave reads as well (an L2 hit), and discards it.
+    const int hf = hs < h_end ? hs : h_end - 1;
+    load_half32<true>(r, tiles + (size_t)(hf >> 1) * kTileBytes, hf & 1, lg, row);
+    float am[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) am[m] = absmax8(v0[m], 0.0f);
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      for (int i = tid + WAVES * 64; i < k8; i += WAVES * 64)
+        am[m] = absmax8(reinterpret_cast<const u32x4_t*>(x + (size_t)m * k)[i], am[m]);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      // wave max: the 16-lane rows by DPP, then the four row maxima
+      float a = am[m];
+      a = fmaxf(a, dpp_fa<0xB1>(a));    // quad_perm [1,0,3,2]
+      a = fmaxf(a, dpp_fa<0x4E>(a));    // quad_perm [2,3,0,1]
+      a = fmaxf(a, dpp_fa<0x124>(a));   // row_ror:4
+      a = fmaxf(a, dpp_fa<0x128>(a));   // row_ror:8
+      const int ai = __float_as_int(a);
+      a = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(ai, 0)),
+                      __int_as_float(__builtin_amdgcn_readlane(ai, 16))),
+                fmaxf(__int_as_float(__builtin_amdgcn_readlane(ai, 32)),
+                      __int_as_float(__builtin_amdgcn_readlane(ai, 48))));
+      if (lane == 0) amax_w[wave][m] = a;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float a = amax_w[0][m];
+      for (int ww = 1; ww < WAVES; ++ww) a = fmaxf(a, amax_w[ww][m]);
+      if (m == qm) inv_q = a > 0.0f ? 127.0f / a : 0.0f;
+      sx_row[m] = a / 127.0f;
+    }
+  } else {
+    if (hs < h_end) load_half32<true>(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lg, row);
+  }
+
+  const uint32_t nib_s = __builtin_amdgcn_readfirstlane(0x0F0F0F0Fu);
+  uint32_t ones_v = 0x01010101u;
+  asm volatile("" : "+v"(ones_v));
+
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+
+  for (bool first = true; hs < h_end; hs += WAVES, first = false) {   // tile hs/2, half hs%2
+    if (!first) load_half32<true>(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lg, row);
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (qlane) v = *reinterpret_cast<const u32x4_t*>(xsrc + (size_t)hs * 128);
+    // ---- quantize this lane's segment; the quad holds one group of 32.
+    float inv = inv_q, sxv = 0.0f;
+    if constexpr (GS) {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      float a = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a = fmaxf(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
+        a = fmaxf(a, fabsf(bf16_to_f32(w[j] >> 16)));
+      }
+      a = fmaxf(a, dpp_fa<0xB1>(a));
+      a = fmaxf(a, dpp_fa<0x4E>(a));
+      inv = a > 0.0f ? 127.0f / a : 0.0f;
+      sxv = a / 127.0f;
+    }
+    uint32_t lo, hi;
+    quant8(v, inv, lo, hi);
+    int p = __builtin_amdgcn_sdot4((int)lo, (int)ones_v, 0, false);
+    p = __builtin_amdgcn_sdot4((int)hi, (int)ones_v, p, false);
+    p += dpp_i<0xB1>(p);                           // group sum of xq over the quad
+    p += dpp_i<0x4E>(p);
+    // The slot is private to the wave and a wave's LDS operations complete in
+    // order (see gemv_w4a16_mx4.hip); the fences keep the compiler from moving
+    // LDS accesses across.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (qlane) {
+      *reinterpret_cast<u32x2_t*>(slot + qm * kA8XRowBytes + 8 * qs) = u32x2_t{lo, hi};
+      if ((qs & 3) == 0) {
+        gsum_s[wave][qs >> 2][qm] = p;
+        if constexpr (GS) gsx_s[wave][qs >> 2][qm] = sxv;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int g = 2 * lg + jj;                   // group within the half tile
+      const uint8_t* xp = slot + xrow * kA8XRowBytes + 32 * g;
+      const u32x4_t xa0 = *reinterpret_cast<const u32x4_t*>(xp);
+      const u32x4_t xa1 = *reinterpret_cast<const u32x4_t*>(xp + 16);
+      const uint32_t xa[8] = {xa0.x, xa0.y, xa0.z, xa0.w, xa1.x, xa1.y, xa1.z, xa1.w};
+      const u32x4_t cv = r.c[jj];
+      const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
+      i32x4_t d = {0, 0, 0, 0};
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd) {
+        d = mfma_i8_4x4x4(xa[2 * dd], cw[dd] & nib_s, d);
+        d = mfma_i8_4x4x4(xa[2 * dd + 1], (cw[dd] >> 4) & nib_s, d);
+      }
+      const i32x4_t sg = *reinterpret_cast<const i32x4_t*>(&gsum_s[wave][g][0]);
+      const float s = fp16_to_f32(jj == 0 ? (r.sc & 0xffffu) : (r.sc >> 16));
+      const int zp = (int)((r.zb >> (4 * jj)) & 15u);
+      f32x4_t sxg = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (GS) sxg = *reinterpret_cast<const f32x4_t*>(&gsx_s[wave][g][0]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int ig = d[m] - zp * sg[m];          // exact: |ig| <= 32*127*15
+        const float scale = GS ? s * sxg[m] : s;
+        acc[m] = __builtin_fmaf(scale, (float)ig, acc[m]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int m = 0; m < M; ++m) red[(wave * M + m) * 64 + lane] = acc[m];
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < 32 * M) {
+    const int m = t >> 5, l = t & 31;
+    float v = 0.0f;
+    for (int w = 0; w < WAVES; ++w) {
+      v += red[(w * M + m) * 64 + l];
+      v += red[(w * M + m) * 64 + l + 32];
+    }
+    const int col = rb * kTileRows + 32 * (blockIdx.x & 1) + l;
+    if (col < n) {
+      if constexpr (!GS) v *= sx_row[m];
+      if (partial != nullptr)
+        partial[((size_t)blockIdx.y * M + m) * n + col] = v;
+      else if (y_f32)
+        static_cast<float*>(y)[(size_t)m * n + col] = v;
+      else
+        static_cast<uint16_t*>(y)[(size_t)m * n + col] = (uint16_t)f32_to_bf16_rne(v);
+    }
+  }
+}
+
+template <int M, bool GS>
+static hipError_t launch_w4a8_mx4_t(const void* x, const void* packed, int n, int k, void* y,
+                                    int y_f32, float* partial, int split, hipStream_t stream) {
+  const int rbs = (n + kTileRows - 1) / kTileRows;
+  hipLaunchKernelGGL((w4a8_gemv_mx4_kernel<M, GS>), dim3(2 * rbs, split), dim3(1024), 0, stream,
+                     static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed), n, k,
+                     y, y_f32, partial, split);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a8_gemv_mx4(int m, bool group_scales, const void* x, const void* packed, int n,
+                                int k, void* y, int y_f32, float* partial, int split,
+                                hipStream_t stream) {
+#define QG_A8X(MM)                                                                              \
+  if (m == MM)                                                                                  \
+    return group_scales ? launch_w4a8_mx4_t<MM, true>(x, packed, n, k, y, y_f32, partial, split, stream) \
+                        : launch_w4a8_mx4_t<MM, false>(x, packed, n, k, y, y_f32, partial, split, stream);
+  QG_A8X(2) QG_A8X(3) QG_A8X(4)
+#undef QG_A8X
+  return hipErrorInvalidValue;
+}
+
 template <int M, bool GS>
 static hipError_t launch_w4a8_lds_t(const void* x, const void* packed, int n, int k, void* y,
                                     int y_f32, float* partial, int split, hipStream_t stream) {
@@ -526,12 +770,9 @@ static hipError_t launch_w4a8_lds_t(const void* x, const void* packed, int n, in
 hipError_t launch_w4a8_gemv_lds(int m, bool group_scales, const void* x, const void* packed, int n,
                                 int k, void* y, int y_f32, float* partial, int split,
                                 hipStream_t stream) {
-#define QG_A8L(MM)                                                                              \
-  if (m == MM)                                                                                  \
-    return group_scales ? launch_w4a8_lds_t<MM, true>(x, packed, n, k, y, y_f32, partial, split, stream) \
-                        : launch_w4a8_lds_t<MM, false>(x, packed, n, k, y, y_f32, partial, split, stream);
-  QG_A8L(1) QG_A8L(2) QG_A8L(3) QG_A8L(4)
-#undef QG_A8L
+  // Only M = 1 with one scale per group runs here: M = 2..4 run on
+  // w4a8_gemv_mx4_kernel, M = 1 per-row scales on w4a8_gemv32_kernel.
+  if (m == 1 && group_scales) return launch_w4a8_lds_t<1, true>(x, packed, n, k, y, y_f32, partial, split, stream);
   return hipErrorInvalidValue;
 }
 
@@ -562,8 +803,9 @@ hipError_t launch_w4a8_gemv(int m, const void* x, const void* packed, int n, int
   if (m == MM && waves == WW)                                                                   \
     return rows == 32 ? launch_w4a8_32_t<MM, WW>(x, packed, n, k, y, y_f32, partial, split, stream) \
                       : launch_w4a8_t<MM, WW>(x, packed, n, k, y, y_f32, partial, split, stream);
-#define QG_A8_M(MM) QG_A8_CASE(MM, 8) QG_A8_CASE(MM, 16)
-  QG_A8_M(1) QG_A8_M(2) QG_A8_M(3) QG_A8_M(4)
+  // M = 1 only: M = 2..4 run on w4a8_gemv_mx4_kernel.
+#define QG_A8_M(MM) QG_A8_CASE(MM, 16)
+  QG_A8_M(1)
 #undef QG_A8_M
 #undef QG_A8_CASE
   return hipErrorInvalidValue;
