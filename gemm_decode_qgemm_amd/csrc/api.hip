@@ -76,9 +76,11 @@ constexpr int64_t kCUs = 256;   // compute units of an MI355X
 //    11.1); below that, the smallest split giving a workgroup per CU, at
 //    most 4 (2048 x 8192, M = 4: 6.7 us at 4 against 7.4 at 1; 256 x 6656:
 //    5.3 us at 4, 5.9 at 8).
-//  * M > 4 (matrix-core kernel): the smallest split with 64-row blocks x
-//    split >= 120, at most 8 (6656 x 19968, M = 16: 24.4 us at 2 against 39.6
-//    at 1; 8448 x 6656: 15.6 us at 1 against 18.3 at 2).
+//  * M > 4 (matrix-core kernels): the smallest split with 64-row blocks x
+//    split >= 120 for the register form, at most 8 (6656 x 19968, M = 16:
+//    24.7 us at 2 against 40.3 at 1; 8448 x 6656: 15.7 us at 1 against 17.7
+//    at 2), >= 300 for the LDS-staged form, whose 4-wave workgroups need more
+//    of them in flight (8448 x 6656, M = 32: 19.6 us at 4 against 26.5 at 1).
 // Both are capped by K / 256 (one tile per split).
 int32_t default_split(int64_t m, int64_t n, int64_t k) {
   const int64_t kt = k / QG_TILE_K;
@@ -90,7 +92,8 @@ int32_t default_split(int64_t m, int64_t n, int64_t k) {
     return s;
   }
   const int64_t rbs = (n + QG_TILE_ROWS - 1) / QG_TILE_ROWS;
-  while (s < 8 && 2 * s <= kt && rbs * s < 120) s *= 2;
+  const int64_t want = qg::mfma_lds_form(m, k) ? 300 : 120;
+  while (s < 8 && 2 * s <= kt && rbs * s < want) s *= 2;
   return s;
 }
 

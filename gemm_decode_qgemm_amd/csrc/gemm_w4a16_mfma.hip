@@ -13,7 +13,9 @@
 //   y[m][n] += s[n,g] * (P[m][n] - (128 + zp[n,g]) * X[m]),
 // so every product is exact and the sums are fp32, as in the decode GEMV.
 //
-// Mapping (gfx950):
+// Two forms; mfma_lds_form() (qg_common.h) picks one per call.
+//
+// Register form (16 and 64 rows, 48 rows with K < 6144), mapping (gfx950):
 //  * a wave owns a whole 64-row block (4 n-tiles of 16 rows) and MT m-tiles
 //    for a range of half tiles (4 groups = 128 k); a workgroup is KW x MG
 //    waves: KW waves split the block's K range round robin, MG wave groups
@@ -242,6 +244,185 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// LDS-staged form (32 rows, 48 rows with K >= 6144): a workgroup is one 64-row block (4 waves, wave t = n-tile t)
+// and streams x through LDS one 256-k tile at a time, shared by its 4 waves;
+// each wave keeps all MT m-tiles of its n-tile in registers, so a weight
+// operand is expanded once for up to 4 products.  The zero point rides in a
+// second MFMA per product whose B operand is -(128 + zp) in every slot (an
+// exact bf16), so each group ends with one FMA per output: y += s * D.
+//
+// Pipeline: while tile kt is computed, tile kt+1's activations are copied
+// into the other LDS buffer by global_load_lds_dwordx4 (no VGPRs) and its
+// codes and metadata are loaded into the other register set; one barrier per
+// tile.  LDS layout: 16-byte piece c of x row r (k = 8c .. 8c+8 of the tile)
+// sits at piece index 32 r + (c ^ (r & 7)), so the A-operand read of lanes
+// (i, a) = (lane % 16, lane / 16) -- row 16 mt + i, piece 4 g + a -- hits 8
+// distinct bank quads in any 8 consecutive lanes; the swizzle is applied on
+// the global side of the copy, whose LDS side is 64 consecutive pieces.
+struct Mfma2W {
+  u32x4_t c0, c1;   // code chunks of groups a and 4 + a, row 16t + i
+  u32x4_t sc;       // the row's 8 fp16 scales
+  uint32_t zw;      // the row's 8 zero points
+};
+
+template <int MT>
+__global__ __launch_bounds__(256) void w4a16_mfma2_kernel(
+    const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ packed, int n, int k,
+    void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
+  constexpr int MR = 16 * MT;                      // staged x rows
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][MR * 512];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int i = lane & 15, a = lane >> 4;
+  const int t = wave_id_uniform();                 // n-tile: rows 16t .. 16t+15 of the block
+  const int rb = blockIdx.x;
+  const int kt_count = k >> 8;
+  int t0, t1;
+  split_range(kt_count, split, blockIdx.y, t0, t1);
+  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
+  const uint32_t mask_s = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+  uint32_t magic_v = 0x43004300u;
+  asm volatile("" : "+v"(magic_v));
+
+  // Copy x[:, 256 kt .. +256] into xs[buf]: wave t issues pieces 64u .. 64u+63
+  // for u = t, t + 4, ...; rows at or past m repeat row m - 1 (their outputs
+  // are never stored).
+  auto stage = [&](int kt, int buf) {
+#pragma unroll
+    for (int u = t; u < MR / 2; u += 4) {
+      const int r = 2 * u + (lane >> 5);
+      const int c = (lane & 31) ^ (r & 7);
+      const int src = r < m ? r : m - 1;
+      __builtin_amdgcn_global_load_lds(x + (size_t)src * k + (size_t)kt * 256 + 8 * c,
+                                       (__attribute__((address_space(3))) void*)(xs[buf] + 1024 * u),
+                                       16, 0, 0);
+    }
+  };
+  auto load_w = [&](Mfma2W& w, int kt) {
+    const uint8_t* tile = tiles + (size_t)kt * kTileBytes;
+    w.c0 = load_stream<true>(reinterpret_cast<const u32x4_t*>(tile + (a * kTileRows + 16 * t + i) * 16));
+    w.c1 = load_stream<true>(reinterpret_cast<const u32x4_t*>(tile + ((4 + a) * kTileRows + 16 * t + i) * 16));
+    w.sc = load_stream<false>(reinterpret_cast<const u32x4_t*>(tile + kScaleOff + (16 * t + i) * 16));
+    w.zw = load_stream<false>(reinterpret_cast<const uint32_t*>(tile + kZeroOff + (16 * t + i) * 4));
+  };
+  // Every wave's copies into LDS must have landed before the barrier that
+  // hands the buffer to the other waves.
+  auto sync = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Per group: 2 MT products (all code products first, then all zero-point
+  // products, so dependent pairs are MT instructions apart), and the previous
+  // group's scale FMAs while these are in flight.
+  auto compute = [&](Mfma2W& w, int buf) {
+    transpose_rows4(w.c0);
+    transpose_rows4(w.c1);
+    const uint8_t* xb = xs[buf];
+    f32x4_t dp[MT];
+    float sp = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const uint32_t dw = g < 4 ? w.c0[g] : w.c1[g - 4];
+      uint32_t bp[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bp[e] = nibble_pair_mfma(dw, e, mask_s, magic_v);
+      const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, u32x4_t{bp[0], bp[1], bp[2], bp[3]});
+      const uint32_t z = (w.zw >> (4 * g)) & 15u;
+      const uint32_t zn = (z | (z << 16)) | 0xC300C300u;     // bf16 pair -(128 + zp)
+      const bf16x8_t bz = __builtin_bit_cast(bf16x8_t, u32x4_t{zn, zn, zn, zn});
+      const float s = fp16_to_f32((w.sc[g >> 1] >> (16 * (g & 1))) & 0xffffu);
+      bf16x8_t av[MT];
+      f32x4_t d[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = 16 * mt + i;
+        av[mt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                  xb + 16 * (32 * r + ((4 * g + a) ^ (r & 7)))));
+        d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bz, d[mt], 0, 0, 0);
+      if (g > 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[mt][e] = __builtin_fmaf(sp, dp[mt][e], acc[mt][e]);
+            // pin the update here: left alone, the compiler sinks every
+            // group's FMAs past the tile's barrier and keeps all 8 groups'
+            // products live
+            asm volatile("" : "+v"(acc[mt][e]));
+          }
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) dp[mt] = d[mt];
+      sp = s;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[mt][e] = __builtin_fmaf(sp, dp[mt][e], acc[mt][e]);
+        asm volatile("" : "+v"(acc[mt][e]));
+      }
+  };
+
+  if (t0 < t1) {
+    Mfma2W cur;
+    stage(t0, 0);
+    load_w(cur, t0);
+    sync();
+    for (int kt = t0; kt < t1; ++kt) {
+      Mfma2W nxt = cur;
+      const bool more = kt + 1 < t1;            // uniform
+      if (more) {
+        stage(kt + 1, (kt + 1 - t0) & 1);
+        load_w(nxt, kt + 1);
+      }
+      compute(cur, (kt - t0) & 1);
+      cur = nxt;
+      if (more) sync();
+    }
+  }
+
+  // lane (i, a) holds rows 16 mt + 4a + e of column 16t + i of the block
+  const int col = rb * kTileRows + 16 * t + i;
+  if (col < n) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * mt + 4 * a + e;
+        if (row < m) {
+          if (partial != nullptr)
+            partial[((size_t)blockIdx.y * m + row) * n + col] = acc[mt][e];
+          else if (y_f32)
+            static_cast<float*>(y)[(size_t)row * n + col] = acc[mt][e];
+          else
+            static_cast<uint16_t*>(y)[(size_t)row * n + col] = (uint16_t)f32_to_bf16_rne(acc[mt][e]);
+        }
+      }
+  }
+}
+
+template <int MT>
+static hipError_t launch_mfma2_t(const void* x, int m, const void* packed, int n, int k, void* y,
+                                 int y_f32, float* partial, int split, hipStream_t stream) {
+  const int rbs = (n + kTileRows - 1) / kTileRows;
+  hipLaunchKernelGGL((w4a16_mfma2_kernel<MT>), dim3(rbs, split), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(x), m, static_cast<const uint8_t*>(packed), n, k,
+                     y, y_f32, partial, split);
+  return hipGetLastError();
+}
+
 template <int MT, int KW, int MG, bool PIPE, bool PFX>
 static hipError_t launch_mfma_t(const void* x, int m, const void* packed, int n, int k, void* y,
                                 int y_f32, float* partial, int split, hipStream_t stream) {
@@ -259,7 +440,7 @@ static hipError_t launch_mfma_t(const void* x, int m, const void* packed, int n,
 #define QG_MFMA_PIPE1 1
 #endif
 
-// Workgroup layout per m-tile count, measured on MI355X at 39936 x 6656,
+// Register form: workgroup layout per m-tile count, measured on MI355X at 39936 x 6656,
 // 8448 x 6656 and 6656 x 19968 (MT m-tiles per wave, KW waves along K, MG
 // wave groups along M; at most 8 waves, so no wave is held to fewer than 256
 // VGPRs):
@@ -272,6 +453,10 @@ hipError_t launch_w4a16_mfma(int m, const void* x, const void* packed, int n, in
                              int y_f32, float* partial, int split, hipStream_t stream) {
 #define QG_MF(MT, KW, MG, PIPE, PFX) \
   return launch_mfma_t<MT, KW, MG, PIPE, PFX>(x, m, packed, n, k, y, y_f32, partial, split, stream)
+  if (mfma_lds_form(m, k)) {
+    if ((m + 15) / 16 == 2) return launch_mfma2_t<2>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+    return launch_mfma2_t<3>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+  }
   switch ((m + 15) / 16) {
     case 1: QG_MF(1, QG_MFMA_KW1, 1, QG_MFMA_PIPE1 != 0, true);
     case 2: QG_MF(2, 4, 1, false, false);

@@ -103,6 +103,6 @@ def test_default_split_regret_on_the_layer_shapes():
 
 
 def test_default_split_regret_matrix_core_buckets():
-    rows = _regrets(((39936, 6656), (8448, 6656), (6656, 19968)), (16, 64), lambda n, k: n ^ k)
+    rows = _regrets(((39936, 6656), (8448, 6656), (6656, 19968)), (16, 32, 48, 64), lambda n, k: n ^ k)
     worst = max(rows, key=lambda r: r["regret"])
     assert worst["regret"] <= MAX_REGRET, worst
