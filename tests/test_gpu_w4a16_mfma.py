@@ -41,7 +41,7 @@ def _ref(x, codes, scales, zeros):
 
 
 @pytest.mark.parametrize("n,k", LARGE_SHAPES)
-@pytest.mark.parametrize("m", si.LARGE_M)
+@pytest.mark.parametrize("m", sorted(set(si.LARGE_M) | {32, 48}))
 def test_mfma_large_buckets_every_split(dev, n, k, m):
     w, codes, scales, zeros = _weight(n, k, si.model_weight_seed(n, k))
     packed = qg.quantize_int4_g32(w.to(dev))
@@ -110,3 +110,21 @@ def test_m_above_64_is_rejected(dev):
     with pytest.raises(qg.QGemmError) as e:
         qg.qgemm_w4a16(si.activation(65, 256, 1).to(dev), packed, 256)
     assert e.value.status == -4
+
+
+@pytest.mark.parametrize("m", [17, 24, 32, 33, 47, 48])
+@pytest.mark.parametrize("n,k", [(320, 6656), (257, 6144), (1100, 6400)])
+def test_mfma_lds_form_ragged(dev, n, k, m):
+    """The LDS-staged form (17..32 rows, and 33..48 rows with K >= 6144): runtime
+    M inside a bucket, N tails (257, 1100), an odd tile count (K = 6400: 25
+    tiles, uneven split ranges) and every legal split."""
+    w, codes, scales, zeros = _weight(n, k, 7 * n + k)
+    packed = qg.quantize_int4_g32(w.to(dev))
+    x = si.activation(m, k, 900 + m)
+    ref = _ref(x, codes, scales, zeros)
+    xd = x.to(dev)
+    for split in [s for s in si.SPLITS if s <= k // 256]:
+        y = qg.qgemm_w4a16(xd, packed, n, split_k=split, out_dtype=torch.float32)
+        assert_w16(y, ref, f"{n}x{k} M={m} split={split}")
+    yb = qg.qgemm_w4a16(xd, packed, n, out_dtype=torch.bfloat16)
+    assert_w16(yb, ref, f"{n}x{k} M={m} bf16")
