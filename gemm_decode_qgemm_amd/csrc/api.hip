@@ -79,8 +79,9 @@ constexpr int64_t kCUs = 256;   // compute units of an MI355X
 //  * M > 4 (matrix-core kernels): the smallest split with 64-row blocks x
 //    split >= 120 for the register form, at most 8 (6656 x 19968, M = 16:
 //    24.7 us at 2 against 40.3 at 1; 8448 x 6656: 15.7 us at 1 against 17.7
-//    at 2), >= 300 for the LDS-staged form, whose 4-wave workgroups need more
-//    of them in flight (8448 x 6656, M = 32: 19.6 us at 4 against 26.5 at 1).
+//    at 2), >= 300 for the LDS-staged form (17..64 rows), whose workgroups
+//    hold more LDS and need more of them in flight (8448 x 6656, M = 32: 19.6
+//    us at 4 against 26.5 at 1; M = 64: 32.4 at 4 against 37.6 at 1).
 // Both are capped by K / 256 (one tile per split).
 int32_t default_split(int64_t m, int64_t n, int64_t k) {
   const int64_t kt = k / QG_TILE_K;
@@ -92,7 +93,7 @@ int32_t default_split(int64_t m, int64_t n, int64_t k) {
     return s;
   }
   const int64_t rbs = (n + QG_TILE_ROWS - 1) / QG_TILE_ROWS;
-  const int64_t want = qg::mfma_lds_form(m, k) ? 300 : 120;
+  const int64_t want = qg::mfma_lds_form(m) ? 300 : 120;
   while (s < 8 && 2 * s <= kt && rbs * s < want) s *= 2;
   return s;
 }

@@ -15,7 +15,7 @@
 //
 // Two forms; mfma_lds_form() (qg_common.h) picks one per call.
 //
-// Register form (16 and 64 rows, 48 rows with K < 6144), mapping (gfx950):
+// Register form (up to 16 rows), mapping (gfx950):
 //  * a wave owns a whole 64-row block (4 n-tiles of 16 rows) and MT m-tiles
 //    for a range of half tiles (4 groups = 128 k); a workgroup is KW x MG
 //    waves: KW waves split the block's K range round robin, MG wave groups
@@ -245,10 +245,11 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// LDS-staged form (32 rows, 48 rows with K >= 6144): a workgroup is one 64-row block (4 waves, wave t = n-tile t)
-// and streams x through LDS one 256-k tile at a time, shared by its 4 waves;
-// each wave keeps all MT m-tiles of its n-tile in registers, so a weight
-// operand is expanded once for up to 4 products.  The zero point rides in a
+// LDS-staged form (17..64 rows): a workgroup is one 64-row block of 4 MG
+// waves (wave w: n-tile w % 4, m-tiles MT (w / 4) .. + MT) and streams x
+// through LDS one 256-k tile at a time, shared by all its waves; a wave keeps
+// its MT m-tiles of its n-tile in registers, so a weight operand is expanded
+// once for MT products (and by MG waves).  The zero point rides in a
 // second MFMA per product whose B operand is -(128 + zp) in every slot (an
 // exact bf16), so each group ends with one FMA per output: y += s * D.
 //
@@ -266,16 +267,18 @@ struct Mfma2W {
   uint32_t zw;      // the row's 8 zero points
 };
 
-template <int MT>
-__global__ __launch_bounds__(256) void w4a16_mfma2_kernel(
+template <int MT, int MG>
+__global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
-  constexpr int MR = 16 * MT;                      // staged x rows
+  constexpr int MR = 16 * MT * MG;                 // staged x rows
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][MR * 512];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int i = lane & 15, a = lane >> 4;
-  const int t = wave_id_uniform();                 // n-tile: rows 16t .. 16t+15 of the block
+  const int wv = wave_id_uniform();
+  const int t = wv & 3;                            // n-tile: rows 16t .. 16t+15 of the block
+  const int mg = wv >> 2;                          // m-tiles mg MT .. mg MT + MT - 1
   const int rb = blockIdx.x;
   const int kt_count = k >> 8;
   int t0, t1;
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(256) void w4a16_mfma2_kernel(
   // are never stored).
   auto stage = [&](int kt, int buf) {
 #pragma unroll
-    for (int u = t; u < MR / 2; u += 4) {
+    for (int u = wv; u < MR / 2; u += 4 * MG) {
       const int r = 2 * u + (lane >> 5);
       const int c = (lane & 31) ^ (r & 7);
       const int src = r < m ? r : m - 1;
@@ -341,7 +344,7 @@ __global__ __launch_bounds__(256) void w4a16_mfma2_kernel(
       f32x4_t d[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int r = 16 * mt + i;
+        const int r = 16 * (mg * MT + mt) + i;
         av[mt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
                                                   xb + 16 * (32 * r + ((4 * g + a) ^ (r & 7)))));
         d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
@@ -400,7 +403,7 @@ __global__ __launch_bounds__(256) void w4a16_mfma2_kernel(
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = 16 * mt + 4 * a + e;
+        const int row = 16 * (mg * MT + mt) + 4 * a + e;
         if (row < m) {
           if (partial != nullptr)
             partial[((size_t)blockIdx.y * m + row) * n + col] = acc[mt][e];
@@ -413,11 +416,11 @@ __global__ __launch_bounds__(256) void w4a16_mfma2_kernel(
   }
 }
 
-template <int MT>
+template <int MT, int MG = 1>
 static hipError_t launch_mfma2_t(const void* x, int m, const void* packed, int n, int k, void* y,
                                  int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_mfma2_kernel<MT>), dim3(rbs, split), dim3(256), 0, stream,
+  hipLaunchKernelGGL((w4a16_mfma2_kernel<MT, MG>), dim3(rbs, split), dim3(256 * MG), 0, stream,
                      static_cast<const uint16_t*>(x), m, static_cast<const uint8_t*>(packed), n, k,
                      y, y_f32, partial, split);
   return hipGetLastError();
@@ -440,30 +443,32 @@ static hipError_t launch_mfma_t(const void* x, int m, const void* packed, int n,
 #define QG_MFMA_PIPE1 1
 #endif
 
-// Register form: workgroup layout per m-tile count, measured on MI355X at 39936 x 6656,
-// 8448 x 6656 and 6656 x 19968 (MT m-tiles per wave, KW waves along K, MG
-// wave groups along M; at most 8 waves, so no wave is held to fewer than 256
-// VGPRs):
-//   16 rows: (1, 4, 1), pipelined with activation prefetch;
-//   32 rows: (2, 4, 1), load-wait-compute (the pipelined form needs 2
-//            register sets of 2 m-tiles and runs at one wave per SIMD);
-//   48 rows: (1, 2, 3), pipelined;
-//   64 rows: (2, 4, 2), load-wait-compute (pipelined, it spills).
+// Register form, up to 16 rows: one m-tile per wave, 4 waves along K,
+// pipelined with activation prefetch (measured on MI355X at 39936 x 6656,
+// 8448 x 6656 and 6656 x 19968).  The same template with 2 m-tiles per wave
+// or wave groups along M ran 32..64 rows before the LDS-staged form, which
+// is faster there (39936 x 6656: 32 rows 57.4 us against 52.7, 64 rows 115.5
+// against 91.9).
 hipError_t launch_w4a16_mfma(int m, const void* x, const void* packed, int n, int k, void* y,
                              int y_f32, float* partial, int split, hipStream_t stream) {
 #define QG_MF(MT, KW, MG, PIPE, PFX) \
   return launch_mfma_t<MT, KW, MG, PIPE, PFX>(x, m, packed, n, k, y, y_f32, partial, split, stream)
-  if (mfma_lds_form(m, k)) {
-    if ((m + 15) / 16 == 2) return launch_mfma2_t<2>(x, m, packed, n, k, y, y_f32, partial, split, stream);
-    return launch_mfma2_t<3>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+  if (mfma_lds_form(m)) {
+    // (m-tiles per wave, waves per n-tile): 64 rows as 2 x 2 (94 VGPRs, 4 waves
+    // per SIMD) beat 4 x 1 (150 VGPRs, 2 per SIMD) everywhere measured
+    // (39936 x 6656: 91.9 us against 99.1; 8448 x 6656: 32.4 against 41.3);
+    // 48 rows as 1 x 3, except on the largest layers, where 3 x 1 wins
+    // (39936 x 6656: 83.3 us against 94.6; 8448 x 6656: 36.4 against 31.8).
+    switch ((m + 15) / 16) {
+      case 2: return launch_mfma2_t<2, 1>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+      case 3:
+        if (n >= 32768 && k >= 6144) return launch_mfma2_t<3, 1>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+        return launch_mfma2_t<1, 3>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+      case 4: return launch_mfma2_t<2, 2>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+      default: return hipErrorInvalidValue;
+    }
   }
-  switch ((m + 15) / 16) {
-    case 1: QG_MF(1, QG_MFMA_KW1, 1, QG_MFMA_PIPE1 != 0, true);
-    case 2: QG_MF(2, 4, 1, false, false);
-    case 3: QG_MF(1, 2, 3, true, true);
-    case 4: QG_MF(2, 4, 2, false, false);
-    default: return hipErrorInvalidValue;
-  }
+  QG_MF(1, QG_MFMA_KW1, 1, QG_MFMA_PIPE1 != 0, true);
 #undef QG_MF
 }
 

@@ -80,16 +80,11 @@ __device__ __forceinline__ T load_stream(const T* p) {
     return *p;
 }
 
-// Which matrix-core kernel runs M = 5..64 (host side): the LDS-staged form
-// for 32 rows, and for 48 rows with K >= 6144; the register form otherwise.
-// Measured on MI355X over nine layer shapes and every split: 39936 x 6656,
-// M = 32: 51.4 us against 57.4, M = 48: 83.5 against 120.6; at 48 rows with
-// K = 2048 / 4096 and at 64 rows the register form is as fast or faster
-// (6656 x 4096, M = 64: 19.0 us against 29.2).
-inline bool mfma_lds_form(int64_t m, int64_t k) {
-  const int64_t mt = (m + 15) / 16;
-  return mt == 2 || (mt == 3 && k >= 6144);
-}
+// Which matrix-core kernel runs M = 5..64 (host side): the register form up
+// to 16 rows, the LDS-staged form above (measured on MI355X over five layer
+// shapes and every split: 39936 x 6656, 32 rows 52.7 us against 57.4, 64 rows
+// 91.9 against 115.5; 8448 x 6656, 64 rows 32.4 against 39.9).
+inline bool mfma_lds_form(int64_t m) { return m > 16; }
 
 __device__ __forceinline__ int wave_id_uniform() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));

@@ -101,17 +101,18 @@ def test_default_split_table(lib):
     assert lib.qg_default_split_k(1, 3072, 6656) == 4
     assert lib.qg_default_split_k(1, 256, 256) == 1       # capped by K / 256
     assert lib.qg_default_split_k(1, 256, 512) == 2
-    # M > 4: row blocks of 64 x split >= 120 for the register-form kernel (16 and
-    # 64 rows, 48 rows with K < 6144), >= 300 for the LDS-staged one (32 rows,
-    # 48 rows with K >= 6144), at most 8
+    # M > 4: row blocks of 64 x split >= 120 for the register-form kernel (up to
+    # 16 rows), >= 300 for the LDS-staged one (17..64 rows), at most 8
     assert lib.qg_default_split_k(16, 39936, 6656) == 1
     assert lib.qg_default_split_k(16, 8448, 6656) == 1
-    assert lib.qg_default_split_k(64, 6656, 19968) == 2
+    assert lib.qg_default_split_k(16, 6656, 19968) == 2
+    assert lib.qg_default_split_k(64, 6656, 19968) == 4
     assert lib.qg_default_split_k(64, 256, 6656) == 8
+    assert lib.qg_default_split_k(64, 39936, 6656) == 1
     assert lib.qg_default_split_k(32, 8448, 6656) == 4
     assert lib.qg_default_split_k(32, 39936, 6656) == 1
     assert lib.qg_default_split_k(48, 6656, 19968) == 4
-    assert lib.qg_default_split_k(48, 6656, 4096) == 2
+    assert lib.qg_default_split_k(48, 6656, 4096) == 4
     assert lib.qg_default_split_k(17, 5376, 4096) == 4
     assert lib.qg_default_split_k(65, 256, 256) == E_M
 
