@@ -24,7 +24,12 @@ result against it.
 
 Other layers of the same path use the same protocol: --op w4a16 with
 --m 2..64 (M > 4 runs the matrix-core kernel), --op w4a8 / w4a8_g32 (M <= 4) and
---op w8a16 (int8 per-channel, bytes = N*K + 2*N); --n/--k pick the shape.
+--op w8a16 (int8 per-channel, bytes = N*K + 2*N); --n/--k pick the shape.  The
+offline weight quantizers run the same way: --op quantize_int4 (bytes = the
+bf16 weight read + the packed weight written) and --op quantize_int8 (bf16
+read + int8 codes and bf16 scales written), the bf16 inputs and the outputs
+both rotating over >= 1 GiB; their CPU leg runs the oracle quantizer and
+compares the bytes.
 
 Prints ONE JSON line.
 """
@@ -78,7 +83,8 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=1000,
                    help="untimed calls first; the clocks take a few hundred calls to ramp up from idle")
-    p.add_argument("--op", choices=("w4a16", "w4a8", "w4a8_g32", "w8a16"), default="w4a16")
+    p.add_argument("--op", choices=("w4a16", "w4a8", "w4a8_g32", "w8a16", "quantize_int4", "quantize_int8"),
+                   default="w4a16")
     p.add_argument("--n", type=int, default=39936)
     p.add_argument("--k", type=int, default=6656)
     p.add_argument("--m", type=int, default=1)
@@ -110,6 +116,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     n, k, m = args.n, args.k, args.m
     op = args.op
+    if op.startswith("quantize"):
+        return bench_quantizer(args, torch, qg, si, dev)
     bytes_eff = n * k + 2 * n if op == "w8a16" else qg.int4_packed_bytes(n, k)
     if args.calibrate_copy:
         return calibrate_copy(torch, dev, bytes_eff)
@@ -234,6 +242,126 @@ def main() -> int:
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, oracle_inputs, y_first, bytes_eff)
 
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def graph_time(torch, call, steps, warmup):
+    """The timing protocol of main(): warm-up graph, then `steps` calls in
+    replays of one captured chunk, events on the capture stream.  Returns
+    (us per call, per-replay us per call sorted, chunk, full, rest, wall s)."""
+    import numpy as np  # noqa: F401
+
+    for i in range(min(warmup, 20)):
+        call(i)
+    torch.cuda.synchronize()
+    chunk = min(steps, 200)
+    full, rest = divmod(steps, chunk)
+    stream = torch.cuda.Stream()
+    g_warm, g_chunk, g_rest = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), None
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g_warm, stream=stream):
+            for i in range(max(warmup, 1)):
+                call(i)
+        with torch.cuda.graph(g_chunk, stream=stream):
+            for i in range(chunk):
+                call(i)
+        if rest:
+            g_rest = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_rest, stream=stream):
+                for i in range(rest):
+                    call(i)
+    torch.cuda.synchronize()
+    replays = [g_chunk] * full + ([g_rest] if rest else [])
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(len(replays) + 1)]
+    with torch.cuda.stream(stream):
+        g_warm.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        events[0].record(stream)
+        for g, ev in zip(replays, events[1:]):
+            g.replay()
+            ev.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    us_call = events[0].elapsed_time(events[-1]) * 1e3 / steps
+    per_replay = sorted(events[i].elapsed_time(events[i + 1]) * 1e3 / chunk for i in range(full))
+    return us_call, per_replay, chunk, full, rest, wall
+
+
+def bench_quantizer(args, torch, qg, si, dev):
+    """The offline weight quantizers (INT4 g32 pack, INT8 row-wise) on one
+    GPU: HBM-bound streams, bytes = bf16 read + quantized weight written."""
+    import numpy as np
+
+    n, k = args.n, args.k
+    int4 = args.op == "quantize_int4"
+    w_cpu = si.int4_weight(n, k, n ^ k)           # a bf16 weight of the layers' distribution
+    out_bytes = qg.int4_packed_bytes(n, k) if int4 else n * k + 2 * n
+    bytes_eff = 2 * n * k + out_bytes
+    copies = max(2, math.ceil((1 << 30) / bytes_eff))
+    w0 = w_cpu.to(dev)
+    ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+    if int4:
+        outs = [torch.empty(out_bytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+
+        def call(i):
+            qg.quantize_int4_g32(ws[i % copies], out=outs[i % copies])
+    else:
+        outs = [(torch.empty((n, k), dtype=torch.int8, device=dev), torch.empty(n, dtype=torch.bfloat16, device=dev))
+                for _ in range(copies)]
+
+        def call(i):
+            qg.quantize_int8_rowwise(ws[i % copies], out=outs[i % copies])
+    torch.cuda.synchronize()
+    us_call, per_replay, chunk, full, rest, wall = graph_time(torch, call, args.steps, args.warmup)
+    gbs = bytes_eff / (us_call * 1e-6) / 1e9
+    name = "INT4-g32 quantize + pack" if int4 else "INT8 row-wise quantize"
+    out = {
+        "metric": f"µs/call and streamed GB/s (% HBM peak) for the {name} of a bf16 weight",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": us_call / 1e3, "us_per_call": round(us_call, 3),
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{name} {n}x{k}", "op": args.op, "n": n, "k": k,
+                   "bytes_eff_per_call": bytes_eff, "rotating_copies": copies,
+                   "timing": f"{full} replays of a {chunk}-call HIP graph" + (f" + one of {rest}" if rest else "")
+                             + ", events on its stream",
+                   "us_per_call_replay": {"median": round(float(np.median(per_replay)), 3) if per_replay else None,
+                                          "min": round(per_replay[0], 3) if per_replay else None},
+                   "hip_runtime": torch.version.hip, "wall_s": round(wall, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        bits = si.bf16_bits(w_cpu)
+        times = []
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            if int4:
+                c, s, z, _ = oracle.quantize_int4_g32(bits)
+                ref = oracle.pack_int4(c, s, z)
+            else:
+                ref = oracle.quantize_int8_rowwise(bits)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start > args.cpu_seconds:
+                break
+        t = float(np.median(times))
+        if int4:
+            same = bool(np.array_equal(outs[0].cpu().numpy(), ref))
+        else:
+            q_ref, s_ref = ref[0], ref[1]
+            same = bool(np.array_equal(outs[0][0].cpu().numpy(), q_ref)
+                        and np.array_equal(si.bf16_bits(outs[0][1].cpu()), s_ref))
+        out["cpu_baseline"] = {
+            "value": round(bytes_eff / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "us_per_call": round(t * 1e6, 1),
+            "sample": f"{len(times)} full calls ({n}x{k}) in {time.perf_counter() - t_start:.1f} s, median per call",
+            "gpu_vs_oracle": {"bit_exact": same},
+        }
     print(json.dumps(out), flush=True)
     return 0
 

@@ -120,12 +120,19 @@ def quantize_int4_g32(w: torch.Tensor, status: torch.Tensor | None = None,
     return out
 
 
-def quantize_int8_rowwise(w: torch.Tensor, status: torch.Tensor | None = None):
-    """bf16 [n, k] -> (int8 [n, k], bf16 scale [n])."""
+def quantize_int8_rowwise(w: torch.Tensor, status: torch.Tensor | None = None,
+                          out: tuple | None = None):
+    """bf16 [n, k] -> (int8 [n, k], bf16 scale [n]); `out` = (q, scale) to write into."""
     _dev(w, "w", torch.bfloat16, 2)
     n, k = w.shape
-    q = torch.empty((n, k), dtype=torch.int8, device=w.device)
-    s = torch.empty(n, dtype=torch.bfloat16, device=w.device)
+    if out is None:
+        q = torch.empty((n, k), dtype=torch.int8, device=w.device)
+        s = torch.empty(n, dtype=torch.bfloat16, device=w.device)
+    else:
+        q, s = out
+        _dev(q, "q", torch.int8, 2)
+        if tuple(q.shape) != (n, k) or s.dtype != torch.bfloat16 or s.numel() != n or not s.is_contiguous():
+            raise ValueError("out must be (int8 [n, k], contiguous bf16 [n])")
     st = lib.quantize_int8_rowwise(w.data_ptr(), n, k, q.data_ptr(), s.data_ptr(), _ptr(status),
                                    _stream(w.device))
     _check(st, "quantize_int8_rowwise")

@@ -149,30 +149,72 @@ __device__ uint32_t bf16_scale_covering(double a) {
 }
 
 // One 256-thread block per row: absmax reduction, then scale and codes.
+// Threads take 16-byte pieces (8 values) of the row, piece p = tid + 256 j;
+// the first kQ8Held pieces of each thread stay in registers between the two
+// passes (all of them for K <= 8192), later ones are read again; codes are
+// written 8 bytes per piece.
+constexpr int kQ8Held = 4;
+
+__device__ __forceinline__ void absmax8_flag(const uint4& u, float& amax, int& bad) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float v = bf16_to_f32(h ? (w[j] >> 16) : (w[j] & 0xffffu));
+      bad |= !__builtin_isfinite(v);
+      const float a = fabsf(v);
+      amax = a > amax ? a : amax;
+    }
+}
+
+// 8 codes rint(v / s) clamped to [-127, 127], packed little-endian.
+__device__ __forceinline__ uint2 codes8(const uint4& u, float s) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float t = rintf(bf16_to_f32(h ? (w[j] >> 16) : (w[j] & 0xffffu)) / s);
+      t = t < -127.0f ? -127.0f : (t > 127.0f ? 127.0f : t);
+      const int e = 2 * j + h;
+      out[e >> 2] |= ((uint32_t)(int)t & 0xffu) << (8 * (e & 3));
+    }
+  return make_uint2(out[0], out[1]);
+}
+
 __global__ __launch_bounds__(256) void quantize_int8_rowwise_kernel(
     const uint16_t* __restrict__ w, int64_t k, int8_t* __restrict__ q,
     uint16_t* __restrict__ scales, uint32_t* __restrict__ status) {
   __shared__ float red_max[4];
   __shared__ int red_bad[4];
   const int64_t row = blockIdx.x;
-  const uint16_t* wr = w + row * k;
+  const uint4* wr = reinterpret_cast<const uint4*>(w + row * k);
+  uint2* qr = reinterpret_cast<uint2*>(q + row * k);
+  const int pieces = (int)(k >> 3);
+  const int tid = threadIdx.x;
+  uint4 held[kQ8Held];
   float amax = 0.0f;
   int bad = 0;
-  for (int64_t i = threadIdx.x; i < k; i += 256) {
-    float v = bf16_to_f32(wr[i]);
-    bad |= !__builtin_isfinite(v);
-    float a = fabsf(v);
-    amax = a > amax ? a : amax;
+#pragma unroll
+  for (int j = 0; j < kQ8Held; ++j) {
+    const int p = tid + 256 * j;
+    held[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (p < pieces) held[j] = wr[p];
   }
+#pragma unroll
+  for (int j = 0; j < kQ8Held; ++j) absmax8_flag(held[j], amax, bad);   // zeros change nothing
+  for (int p = tid + 256 * kQ8Held; p < pieces; p += 256) absmax8_flag(wr[p], amax, bad);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     float o = __shfl_xor(amax, off, 64);
     amax = o > amax ? o : amax;
     bad |= __shfl_xor(bad, off, 64);
   }
-  if ((threadIdx.x & 63) == 0) {
-    red_max[threadIdx.x >> 6] = amax;
-    red_bad[threadIdx.x >> 6] = bad;
+  if ((tid & 63) == 0) {
+    red_max[tid >> 6] = amax;
+    red_bad[tid >> 6] = bad;
   }
   __syncthreads();
   amax = red_max[0];
@@ -182,8 +224,8 @@ __global__ __launch_bounds__(256) void quantize_int8_rowwise_kernel(
     bad |= red_bad[i];
   }
   if (bad) {
-    for (int64_t i = threadIdx.x; i < k; i += 256) q[row * k + i] = 0;
-    if (threadIdx.x == 0) {
+    for (int p = tid; p < pieces; p += 256) qr[p] = make_uint2(0u, 0u);
+    if (tid == 0) {
       scales[row] = 0x7fc0u;
       if (status != nullptr) atomicOr(status, QG_FLAG_NONFINITE);
     }
@@ -191,12 +233,13 @@ __global__ __launch_bounds__(256) void quantize_int8_rowwise_kernel(
   }
   const uint32_t sbits = amax == 0.0f ? 0x3f80u : bf16_scale_covering((double)amax);
   const float s = bf16_to_f32(sbits);
-  for (int64_t i = threadIdx.x; i < k; i += 256) {
-    float t = rintf(bf16_to_f32(wr[i]) / s);
-    t = t < -127.0f ? -127.0f : (t > 127.0f ? 127.0f : t);
-    q[row * k + i] = (int8_t)(int)t;
+#pragma unroll
+  for (int j = 0; j < kQ8Held; ++j) {
+    const int p = tid + 256 * j;
+    if (p < pieces) qr[p] = codes8(held[j], s);
   }
-  if (threadIdx.x == 0) scales[row] = (uint16_t)sbits;
+  for (int p = tid + 256 * kQ8Held; p < pieces; p += 256) qr[p] = codes8(wr[p], s);
+  if (tid == 0) scales[row] = (uint16_t)sbits;
 }
 
 // ---- host launchers (called by the C ABI after validation) ----
