@@ -334,18 +334,17 @@ __global__ __launch_bounds__(WAVES * 64) void w4a8_gemv32_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Activations quantized once per workgroup, through LDS (32 rows, 16 waves).
-// The workgroup walks its K range in chunks of 16 half tiles (2048 k), one
-// half tile per wave.  For each chunk every thread quantizes one 8-k segment
-// of x into LDS (int8 in the byte order of the nibbles, as quant8), then
-// after one barrier each wave runs the integer group dots of its half tile
-// reading xq from LDS.  The chunk buffers alternate, so one barrier per chunk
-// orders both the writes before the reads and the reads before the rewrite.
-//  GS = false: one activation scale per row (the absmax prologue above);
-//  GS = true:  one scale per group of 32: the 4 segments of a group are held
-//              by a lane quad, whose DPP max gives the group's absmax; then
-//              inv = 127 / a and sx = a / 127 (binary32 divisions), and the
-//              group's partial sum is scaled by sx * s.
+// One activation scale per group of 32, M = 1: activations quantized once per
+// workgroup, through LDS (32 rows, 16 waves).  The workgroup walks its K range
+// in chunks of 16 half tiles (2048 k), one half tile per wave.  For each chunk
+// every thread quantizes one 8-k segment of x into LDS (int8 in the byte
+// order of the nibbles, as quant8): the 4 segments of a group are held by a
+// lane quad, whose DPP max gives the group's absmax; then inv = 127 / a and
+// sx = a / 127 (binary32 divisions).  After one barrier each wave runs the
+// integer group dots of its half tile reading xq from LDS and scales each
+// group's sum by sx * s.  The chunk buffers alternate, so one barrier per
+// chunk orders both the writes before the reads and the reads before the
+// rewrite.
 constexpr int kA8Chunk = 16;                 // half tiles per chunk
 constexpr int kA8Segs = kA8Chunk * 16;       // 8-k segments per chunk
 
@@ -355,7 +354,7 @@ __device__ __forceinline__ float dpp_fa(float v) {
                                                                CTRL, 0xf, 0xf, true));
 }
 
-template <int M, bool GS>
+template <int M>
 __global__ __launch_bounds__(1024) void w4a8_gemv_lds_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -363,7 +362,6 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_lds_kernel(
   __shared__ u32x2_t xq_s[2][M][kA8Segs];
   __shared__ float sx_s[2][M][kA8Segs / 4];
   __shared__ float red[WAVES * M * 64];
-  __shared__ float amax_w[WAVES][M];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int seg = lane & 7;
@@ -375,35 +373,6 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_lds_kernel(
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
   const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
-
-  float inv_row[M], sx_row[M];
-  if constexpr (!GS) {
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float a = 0.0f;
-      const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)m * k);
-      for (int i = tid; i < (k >> 3); i += WAVES * 64) {
-        const u32x4_t v = xr[i];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          a = fmaxf(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
-          a = fmaxf(a, fabsf(bf16_to_f32(w[j] >> 16)));
-        }
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
-      if (lane == 0) amax_w[wave][m] = a;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float a = amax_w[0][m];
-      for (int ww = 1; ww < WAVES; ++ww) a = fmaxf(a, amax_w[ww][m]);
-      inv_row[m] = a > 0.0f ? 127.0f / a : 0.0f;
-      sx_row[m] = a / 127.0f;
-    }
-  }
 
   const uint32_t nib_s = __builtin_amdgcn_readfirstlane(0x0F0F0F0Fu);
   uint32_t ones_v = 0x01010101u;
@@ -426,26 +395,21 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_lds_kernel(
       const int m = tid >> 8, sg = tid & (kA8Segs - 1);
       if (m < M && sg < nh * 16) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + (size_t)m * k + (size_t)cb * 128 + sg * 8);
-        float inv, sxv = 0.0f;
-        if constexpr (GS) {
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-          float a = 0.0f;
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float a = 0.0f;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            a = fmaxf(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
-            a = fmaxf(a, fabsf(bf16_to_f32(w[j] >> 16)));
-          }
-          a = fmaxf(a, dpp_fa<0xB1>(a));          // the lane quad holds one group of 32
-          a = fmaxf(a, dpp_fa<0x4E>(a));
-          inv = a > 0.0f ? 127.0f / a : 0.0f;
-          sxv = a / 127.0f;
-        } else {
-          inv = inv_row[m];
+        for (int j = 0; j < 4; ++j) {
+          a = fmaxf(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
+          a = fmaxf(a, fabsf(bf16_to_f32(w[j] >> 16)));
         }
+        a = fmaxf(a, dpp_fa<0xB1>(a));          // the lane quad holds one group of 32
+        a = fmaxf(a, dpp_fa<0x4E>(a));
+        const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+        const float sxv = a / 127.0f;
         uint32_t lo, hi;
         quant8(v, inv, lo, hi);
         xq_s[buf][m][sg] = u32x2_t{lo, hi};
-        if (GS && (sg & 3) == 0) sx_s[buf][m][sg >> 2] = sxv;
+        if ((sg & 3) == 0) sx_s[buf][m][sg >> 2] = sxv;
       }
     }
     __syncthreads();
@@ -486,8 +450,7 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_lds_kernel(
             group_dot4<1>(i0, i1, xlo[m], xhi[m], lo, hi);
           const int sg = jj == 0 ? dpp_i<0x150>(sxq[m]) : dpp_i<0x154>(sxq[m]);
           const int ig = i0 + i1 - zp * sg;
-          float scale = s;
-          if constexpr (GS) scale = s * sx_s[buf][m][wave * 4 + lg * 2 + jj];
+          const float scale = s * sx_s[buf][m][wave * 4 + lg * 2 + jj];
           acc[m] = __builtin_fmaf(scale, (float)ig, acc[m]);
         }
       }
@@ -507,7 +470,6 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_lds_kernel(
     }
     const int col = rb * kTileRows + 32 * (blockIdx.x & 1) + l;
     if (col < n) {
-      if constexpr (!GS) v *= sx_row[m];
       if (partial != nullptr)
         partial[((size_t)blockIdx.y * M + m) * n + col] = v;
       else if (y_f32)
@@ -757,11 +719,11 @@ hipError_t launch_w4a8_gemv_mx4(int m, bool group_scales, const void* x, const v
   return hipErrorInvalidValue;
 }
 
-template <int M, bool GS>
+template <int M>
 static hipError_t launch_w4a8_lds_t(const void* x, const void* packed, int n, int k, void* y,
                                     int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a8_gemv_lds_kernel<M, GS>), dim3(2 * rbs, split), dim3(1024), 0, stream,
+  hipLaunchKernelGGL((w4a8_gemv_lds_kernel<M>), dim3(2 * rbs, split), dim3(1024), 0, stream,
                      static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed), n, k,
                      y, y_f32, partial, split);
   return hipGetLastError();
@@ -772,7 +734,7 @@ hipError_t launch_w4a8_gemv_lds(int m, bool group_scales, const void* x, const v
                                 hipStream_t stream) {
   // Only M = 1 with one scale per group runs here: M = 2..4 run on
   // w4a8_gemv_mx4_kernel, M = 1 per-row scales on w4a8_gemv32_kernel.
-  if (m == 1 && group_scales) return launch_w4a8_lds_t<1, true>(x, packed, n, k, y, y_f32, partial, split, stream);
+  if (m == 1 && group_scales) return launch_w4a8_lds_t<1>(x, packed, n, k, y, y_f32, partial, split, stream);
   return hipErrorInvalidValue;
 }
 
