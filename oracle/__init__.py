@@ -56,6 +56,11 @@ def _load():
         "orc_qgemm_w4a8": (None, [P, I64, I64, P, P, P, I64, P, I]),
         "orc_actquant_int8_g32": (None, [P, I64, I64, P, P]),
         "orc_qgemm_w4a8_g32": (None, [P, I64, I64, P, P, P, I64, P, I]),
+        "orc_quantize_int4_g32_dq": (I, [P, I64, I64, P, P, P, P]),
+        "orc_int4_dq_packed_bytes": (I64, [I64, I64]),
+        "orc_pack_int4_dq": (None, [P, P, P, P, I64, I64, P]),
+        "orc_unpack_int4_dq": (None, [P, I64, I64, P, P, P, P]),
+        "orc_qgemm_w4a16_dq": (None, [P, I64, I64, P, P, P, P, I64, P, I]),
         "orc_hardware_threads": (I, []),
     }
     for name, (res, args) in sig.items():
@@ -164,6 +169,62 @@ def qgemm_w4a16(x_bits, codes, scales, zeros, threads: int = 1) -> np.ndarray:
     zeros = np.ascontiguousarray(zeros, np.uint8)
     y = np.empty((m, n), np.float64)
     _load().orc_qgemm_w4a16(_ptr(x), m, k, _ptr(codes), _ptr(scales), _ptr(zeros), n, _ptr(y), threads)
+    return y
+
+
+# ------------------------------------------- INT4 g32 with scale codes
+def quantize_int4_g32_dq(w_bits):
+    """W bf16 bits [n, k] -> (codes u8 [n,k], scale codes u8 [n,k/32],
+    row steps fp16 bits u16 [n], zeros u8 [n,k/32], flags)."""
+    w = _u16(w_bits)
+    n, k = w.shape
+    assert k % 32 == 0
+    codes = np.empty((n, k), np.uint8)
+    scode = np.empty((n, k // 32), np.uint8)
+    sstep = np.empty(n, np.uint16)
+    zeros = np.empty((n, k // 32), np.uint8)
+    f = _load().orc_quantize_int4_g32_dq(_ptr(w), n, k, _ptr(codes), _ptr(scode), _ptr(sstep), _ptr(zeros))
+    return codes, scode, sstep, zeros, int(f)
+
+
+def int4_dq_packed_bytes(n: int, k: int) -> int:
+    return int(_load().orc_int4_dq_packed_bytes(n, k))
+
+
+def pack_int4_dq(codes, scode, sstep, zeros) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scode = np.ascontiguousarray(scode, np.uint8)
+    sstep = _u16(sstep)
+    zeros = np.ascontiguousarray(zeros, np.uint8)
+    n, k = codes.shape
+    assert k % 256 == 0, "the packed layout needs K % 256 == 0"
+    out = np.empty(int4_dq_packed_bytes(n, k), np.uint8)
+    _load().orc_pack_int4_dq(_ptr(codes), _ptr(scode), _ptr(sstep), _ptr(zeros), n, k, _ptr(out))
+    return out
+
+
+def unpack_int4_dq(packed, n: int, k: int):
+    packed = np.ascontiguousarray(packed, np.uint8)
+    assert packed.size >= int4_dq_packed_bytes(n, k)
+    codes = np.empty((n, k), np.uint8)
+    scode = np.empty((n, k // 32), np.uint8)
+    sstep = np.empty(n, np.uint16)
+    zeros = np.empty((n, k // 32), np.uint8)
+    _load().orc_unpack_int4_dq(_ptr(packed), n, k, _ptr(codes), _ptr(scode), _ptr(sstep), _ptr(zeros))
+    return codes, scode, sstep, zeros
+
+
+def qgemm_w4a16_dq(x_bits, codes, scode, sstep, zeros, threads: int = 1) -> np.ndarray:
+    x = _u16(x_bits)
+    m, k = x.shape
+    n = codes.shape[0]
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scode = np.ascontiguousarray(scode, np.uint8)
+    sstep = _u16(sstep)
+    zeros = np.ascontiguousarray(zeros, np.uint8)
+    y = np.empty((m, n), np.float64)
+    _load().orc_qgemm_w4a16_dq(_ptr(x), m, k, _ptr(codes), _ptr(scode), _ptr(sstep), _ptr(zeros), n,
+                               _ptr(y), threads)
     return y
 
 

@@ -109,6 +109,38 @@ void orc_qgemm_w4a8_g32(const uint16_t *x, int64_t m, int64_t k,
                         const uint8_t *codes, const uint16_t *scales,
                         const uint8_t *zeros, int64_t n, double *y, int threads);
 
+/* ---- INT4 group-32 with scale codes ([P1] `_packed_with_dense` storage:
+ * `scale` uint8 codes [N, K/32] times `scale_step` fp16 [N, 1]) ----
+ * Per row: step = smallest fp16 with 3825*step >= the largest group range
+ * (ranges widened to hold 0, as above; 1.0 for an all-zero row; 65504 and
+ * flag 2 above 3825*65504).  Per group: c = smallest integer in 1..255 with
+ * 15*c*step >= the group's range, s = c*step (exact in binary32), then zp and
+ * the codes exactly as orc_quantize_group32 with that s.  Zero points are the
+ * integers 0..15 (a zero_point_step of 1).  A row holding a non-finite value
+ * gets step NaN 0x7E00 and all codes 0 (flag 1).
+ *   codes u8 [n,k], scode u8 [n,k/32], sstep fp16 [n], zeros u8 [n,k/32]. */
+int orc_quantize_int4_g32_dq(const uint16_t *w, int64_t n, int64_t k, uint8_t *codes,
+                             uint8_t *scode, uint16_t *sstep, uint8_t *zeros);
+
+/* ---- packed layout, version 2 (scale codes) ----
+ * Row block of 64 rows = a 128-byte head (row r's fp16 step at 2r) followed
+ * by K/256 tiles of 8960 bytes:
+ *   [0, 8192)     codes, exactly as version 1
+ *   [8192, 8704)  scale codes: row r's 8 bytes at 8192 + 8r, group j at +j
+ *   [8704, 8960)  zero points: row r's 32-bit LE word at 8704 + 4r, group j
+ *                 in bits [4j, 4j+4)
+ * Row blocks follow each other; rows n >= N are zero. */
+int64_t orc_int4_dq_packed_bytes(int64_t n, int64_t k);
+void orc_pack_int4_dq(const uint8_t *codes, const uint8_t *scode, const uint16_t *sstep,
+                      const uint8_t *zeros, int64_t n, int64_t k, uint8_t *packed);
+void orc_unpack_int4_dq(const uint8_t *packed, int64_t n, int64_t k, uint8_t *codes,
+                        uint8_t *scode, uint16_t *sstep, uint8_t *zeros);
+
+/* y[m, n] = sum_k x[m,k] * (q[n,k] - zp[n,g]) * scode[n,g] * sstep[n]. */
+void orc_qgemm_w4a16_dq(const uint16_t *x, int64_t m, int64_t k, const uint8_t *codes,
+                        const uint8_t *scode, const uint16_t *sstep, const uint8_t *zeros,
+                        int64_t n, double *y, int threads);
+
 /* Thread count the machine offers (for the CPU baseline). */
 int orc_hardware_threads(void);
 

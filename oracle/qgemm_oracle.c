@@ -479,3 +479,178 @@ void orc_qgemm_w4a8_g32(const uint16_t *x, int64_t m, int64_t k,
     free(xq);
     free(sx);
 }
+
+/* ------------------------------------------------------------------ */
+/* INT4 group-32 with scale codes: the stored form of [P1]              */
+/* `_packed_with_dense` (`scale` uint8 codes, `scale_step` fp16 per     */
+/* row; legality rules "scale codes must be uint8", "scale_step must be */
+/* float16", step shape [N, 1]).  A group's scale is code x row step.   */
+/* Reading recorded in the design notes: the row step is the smallest   */
+/* fp16 with 255 x 15 x step >= the row's largest group range, a        */
+/* group's code the smallest c in 1..255 with 15 x c x step >= its      */
+/* range, so every group still spans its range in 15 steps; zero points */
+/* stay integers 0..15 (zero_point_step 1); then the codes exactly as   */
+/* in orc_quantize_group32, with the scale c x step.                    */
+/* ------------------------------------------------------------------ */
+static void group_range(const uint16_t *w32, float *lo, float *hi, int *nonfinite) {
+    *lo = 0.0f;
+    *hi = 0.0f;
+    for (int i = 0; i < 32; i++) {
+        float v = bf16_to_float(w32[i]);
+        if (!isfinite(v)) *nonfinite = 1;
+        if (v < *lo) *lo = v;
+        if (v > *hi) *hi = v;
+    }
+}
+
+int orc_quantize_int4_g32_dq(const uint16_t *w, int64_t n, int64_t k, uint8_t *codes,
+                             uint8_t *scode, uint16_t *sstep, uint8_t *zeros) {
+    int flags = 0;
+    int64_t groups = k / 32;
+    for (int64_t row = 0; row < n; row++) {
+        const uint16_t *wr = w + row * k;
+        /* pass 1: the largest group range of the row */
+        int nonfinite = 0;
+        double rmax = 0.0;
+        for (int64_t g = 0; g < groups; g++) {
+            float lo, hi;
+            group_range(wr + g * 32, &lo, &hi, &nonfinite);
+            double r = (double)hi - (double)lo;
+            if (r > rmax) rmax = r;
+        }
+        if (nonfinite) {   /* the whole row: NaN step, codes 0 */
+            flags |= 1;
+            sstep[row] = FP16_NAN_BITS;
+            for (int64_t g = 0; g < groups; g++) {
+                scode[row * groups + g] = 0;
+                zeros[row * groups + g] = 0;
+            }
+            for (int64_t i = 0; i < k; i++) codes[row * k + i] = 0;
+            continue;
+        }
+        uint16_t step;
+        if (rmax == 0.0) {
+            step = FP16_ONE_BITS;
+        } else if (rmax > 3825.0 * 65504.0) {
+            step = FP16_MAX_BITS;
+            flags |= 2;
+        } else {
+            step = smallest_fp16_covering(rmax, 3825.0);   /* 3825 = 255 x 15 */
+        }
+        sstep[row] = step;
+        double ds = orc_fp16_to_double(step);
+        /* pass 2: per group, its scale code, zero point and codes */
+        for (int64_t g = 0; g < groups; g++) {
+            const uint16_t *w32 = wr + g * 32;
+            float lo, hi;
+            int dummy = 0;
+            group_range(w32, &lo, &hi, &dummy);
+            double r = (double)hi - (double)lo;
+            int c = 1;
+            while (c < 255 && 15.0 * c * ds < r) c++;     /* 15 c ds is exact in binary64 */
+            float s = (float)(c * ds);                      /* exact: 8 x 11 significant bits */
+            float z = clampf(rintf(-lo / s), 0.0f, 15.0f);
+            for (int i = 0; i < 32; i++) {
+                float t = rintf(bf16_to_float(w32[i]) / s) + z;
+                codes[row * k + g * 32 + i] = (uint8_t)clampf(t, 0.0f, 15.0f);
+            }
+            scode[row * groups + g] = (uint8_t)c;
+            zeros[row * groups + g] = (uint8_t)z;
+        }
+    }
+    return flags;
+}
+
+/* Packed layout, version 2 (scale codes; see oracle.h). */
+enum { D_ROWS = 64, D_HEAD = 128, D_TILE = 8960, D_SCODE_OFF = 8192, D_ZERO_OFF = 8704 };
+
+int64_t orc_int4_dq_packed_bytes(int64_t n, int64_t k) {
+    int64_t row_blocks = (n + D_ROWS - 1) / D_ROWS;
+    return row_blocks * (D_HEAD + (k / T_K) * (int64_t)D_TILE);
+}
+
+void orc_pack_int4_dq(const uint8_t *codes, const uint8_t *scode, const uint16_t *sstep,
+                      const uint8_t *zeros, int64_t n, int64_t k, uint8_t *packed) {
+    int64_t kt_count = k / T_K, groups = k / 32;
+    int64_t block_bytes = D_HEAD + kt_count * D_TILE;
+    memset(packed, 0, (size_t)orc_int4_dq_packed_bytes(n, k));
+    for (int64_t row = 0; row < n; row++) {
+        uint8_t *block = packed + (row / D_ROWS) * block_bytes;
+        int r = (int)(row % D_ROWS);
+        block[2 * r] = (uint8_t)(sstep[row] & 0xFF);
+        block[2 * r + 1] = (uint8_t)(sstep[row] >> 8);
+        for (int64_t kt = 0; kt < kt_count; kt++) {
+            uint8_t *tile = block + D_HEAD + kt * D_TILE;
+            for (int kk = 0; kk < T_K; kk++) {
+                int64_t byte; int shift;
+                code_position(r, kk, &byte, &shift);
+                tile[byte] |= (uint8_t)((codes[row * k + kt * T_K + kk] & 0xF) << shift);
+            }
+            for (int j = 0; j < T_GROUPS; j++) {
+                int64_t g = kt * T_GROUPS + j;
+                tile[D_SCODE_OFF + r * 8 + j] = scode[row * groups + g];
+                tile[D_ZERO_OFF + r * 4 + j / 2] |=
+                    (uint8_t)((zeros[row * groups + g] & 0xF) << ((j % 2) * 4));
+            }
+        }
+    }
+}
+
+void orc_unpack_int4_dq(const uint8_t *packed, int64_t n, int64_t k, uint8_t *codes,
+                        uint8_t *scode, uint16_t *sstep, uint8_t *zeros) {
+    int64_t kt_count = k / T_K, groups = k / 32;
+    int64_t block_bytes = D_HEAD + kt_count * D_TILE;
+    for (int64_t row = 0; row < n; row++) {
+        const uint8_t *block = packed + (row / D_ROWS) * block_bytes;
+        int r = (int)(row % D_ROWS);
+        sstep[row] = (uint16_t)(block[2 * r] | (block[2 * r + 1] << 8));
+        for (int64_t kt = 0; kt < kt_count; kt++) {
+            const uint8_t *tile = block + D_HEAD + kt * D_TILE;
+            for (int kk = 0; kk < T_K; kk++) {
+                int64_t byte; int shift;
+                code_position(r, kk, &byte, &shift);
+                codes[row * k + kt * T_K + kk] = (tile[byte] >> shift) & 0xF;
+            }
+            for (int j = 0; j < T_GROUPS; j++) {
+                int64_t g = kt * T_GROUPS + j;
+                scode[row * groups + g] = tile[D_SCODE_OFF + r * 8 + j];
+                zeros[row * groups + g] = (tile[D_ZERO_OFF + r * 4 + j / 2] >> ((j % 2) * 4)) & 0xF;
+            }
+        }
+    }
+}
+
+/* W4A16 on the scale-code form: dequant (q - zp) * (c * step), then the dot. */
+struct w4dq_ctx {
+    const uint16_t *x; int64_t m, k;
+    const uint8_t *codes, *scode; const uint16_t *sstep; const uint8_t *zeros;
+    int64_t n; double *y;
+};
+
+static void w4a16_dq_rows(void *p, int64_t b, int64_t e) {
+    struct w4dq_ctx *c = (struct w4dq_ctx *)p;
+    int64_t groups = c->k / 32;
+    for (int64_t row = b; row < e; row++) {
+        double step = orc_fp16_to_double(c->sstep[row]);
+        for (int64_t mi = 0; mi < c->m; mi++) {
+            double acc = 0.0;
+            for (int64_t g = 0; g < groups; g++) {
+                double s = (double)c->scode[row * groups + g] * step;
+                int z = c->zeros[row * groups + g];
+                for (int64_t i = 0; i < 32; i++) {
+                    int64_t kk = g * 32 + i;
+                    double wdq = (double)(c->codes[row * c->k + kk] - z) * s;
+                    acc += orc_bf16_to_double(c->x[mi * c->k + kk]) * wdq;
+                }
+            }
+            c->y[mi * c->n + row] = acc;
+        }
+    }
+}
+
+void orc_qgemm_w4a16_dq(const uint16_t *x, int64_t m, int64_t k, const uint8_t *codes,
+                        const uint8_t *scode, const uint16_t *sstep, const uint8_t *zeros,
+                        int64_t n, double *y, int threads) {
+    struct w4dq_ctx c = {x, m, k, codes, scode, sstep, zeros, n, y};
+    parallel_rows(w4a16_dq_rows, &c, n, threads);
+}

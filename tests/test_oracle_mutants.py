@@ -11,7 +11,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "qgemm_oracle.c")
 PINS = [os.path.join(ROOT, "tests", f) for f in ("test_oracle_int4.py", "test_oracle_int8.py",
-                                                 "test_oracle_w4a8_g32.py")]
+                                                 "test_oracle_w4a8_g32.py", "test_oracle_int4_dq.py")]
 
 # (id, original text, planted text): each is a single, plausible slip.
 MUTANTS = [
@@ -45,6 +45,17 @@ MUTANTS = [
     ("g32_zero_point_of_next_group", "int zg = c->zeros[row * groups + g];",
      "int zg = c->zeros[row * groups + (g + 1) % groups];"),
     ("g32_span_shifted", "quant_span(x + mi * k + g * 32, 32,", "quant_span(x + mi * k + g * 32 + (g > 0), 32,"),
+    ("dq_code_rounded_to_nearest", "while (c < 255 && 15.0 * c * ds < r) c++;",
+     "while (c < 255 && 15.0 * c * ds < r) c++; "
+     "if (c > 1 && r - 15.0 * (c - 1) * ds < 15.0 * c * ds - r) c--;"),
+    ("dq_step_without_the_15", "smallest_fp16_covering(rmax, 3825.0)", "smallest_fp16_covering(rmax, 255.0)"),
+    ("dq_code_may_be_zero", "int c = 1;", "int c = 0;"),
+    ("dq_head_bytes_swapped", "block[2 * r] = (uint8_t)(sstep[row] & 0xFF);",
+     "block[2 * r] = (uint8_t)(sstep[row] >> 8);"),
+    ("dq_scale_code_transposed", "tile[D_SCODE_OFF + r * 8 + j] = scode[row * groups + g];",
+     "tile[D_SCODE_OFF + j * 64 + r] = scode[row * groups + g];"),
+    ("dq_gemm_step_of_row_0", "double step = orc_fp16_to_double(c->sstep[row]);",
+     "double step = orc_fp16_to_double(c->sstep[0]);"),
 ]
 
 
