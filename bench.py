@@ -23,7 +23,8 @@ host's cores over a bounded sample of the same workload and checks the GPU
 result against it.
 
 Other layers of the same path use the same protocol: --op w4a16 with
---m 2..64 (M > 4 runs the matrix-core kernel), --op w4a8 / w4a8_g32 (M <= 4) and
+--m 2..64 (M > 4 runs the matrix-core kernel), --op w4a16_dq (the scale-code
+weight, M <= 4, bytes = its packed size), --op w4a8 / w4a8_g32 (M <= 4) and
 --op w8a16 (int8 per-channel, bytes = N*K + 2*N); --n/--k pick the shape.  The
 offline weight quantizers run the same way: --op quantize_int4 (bytes = the
 bf16 weight read + the packed weight written) and --op quantize_int8 (bf16
@@ -83,7 +84,8 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=1000,
                    help="untimed calls first; the clocks take a few hundred calls to ramp up from idle")
-    p.add_argument("--op", choices=("w4a16", "w4a8", "w4a8_g32", "w8a16", "quantize_int4", "quantize_int8"),
+    p.add_argument("--op", choices=("w4a16", "w4a16_dq", "w4a8", "w4a8_g32", "w8a16", "quantize_int4",
+                                    "quantize_int8"),
                    default="w4a16")
     p.add_argument("--n", type=int, default=39936)
     p.add_argument("--k", type=int, default=6656)
@@ -118,7 +120,12 @@ def main() -> int:
     op = args.op
     if op.startswith("quantize"):
         return bench_quantizer(args, torch, qg, si, dev)
-    bytes_eff = n * k + 2 * n if op == "w8a16" else qg.int4_packed_bytes(n, k)
+    if op == "w8a16":
+        bytes_eff = n * k + 2 * n
+    elif op == "w4a16_dq":
+        bytes_eff = qg.int4_dq_packed_bytes(n, k)
+    else:
+        bytes_eff = qg.int4_packed_bytes(n, k)
     if args.calibrate_copy:
         return calibrate_copy(torch, dev, bytes_eff)
     copies = max(2, math.ceil((1 << 30) / bytes_eff))
@@ -140,11 +147,13 @@ def main() -> int:
         else:
             w_cpu, x_cpu = si.int4_weight(n, k, n ^ k), si.activation(m, k, 9100 + m)
         split = args.split or qg.default_split_k(m, n, k)
-        packed0 = qg.quantize_int4_g32(w_cpu.to(dev))
+        quant = qg.quantize_int4_g32_dq if op == "w4a16_dq" else qg.quantize_int4_g32
+        packed0 = quant(w_cpu.to(dev))
         packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
         x = x_cpu.to(dev)
         ws = torch.empty(max(qg.workspace_bytes(m, n, k, split), 1), dtype=torch.uint8, device=dev)
-        fn = {"w4a16": qg.qgemm_w4a16, "w4a8": qg.qgemm_w4a8, "w4a8_g32": qg.qgemm_w4a8_g32}[op]
+        fn = {"w4a16": qg.qgemm_w4a16, "w4a16_dq": qg.qgemm_w4a16_dq, "w4a8": qg.qgemm_w4a8,
+              "w4a8_g32": qg.qgemm_w4a8_g32}[op]
 
         def call(i):
             fn(x, packs[i % copies], n, split_k=split, out=y, workspace=ws)
@@ -194,7 +203,9 @@ def main() -> int:
 
     headline = op == "w4a16" and (n, k, m) == (39936, 6656, 1)
     kernel = "matrix-core GEMM" if (op == "w4a16" and m > 4) else "GEMV"
-    label = {"w4a16": "W4A16 INT4-g32 asymmetric", "w4a8": "W4A8 INT4-g32 x per-row int8",
+    label = {"w4a16": "W4A16 INT4-g32 asymmetric",
+             "w4a16_dq": "W4A16 INT4-g32 asymmetric, uint8 scale codes x per-row fp16 step",
+             "w4a8": "W4A8 INT4-g32 x per-row int8",
              "w4a8_g32": "W4A8 INT4-g32 x per-group-32 int8", "w8a16": "W8A16 INT8 per-channel"}[op]
     out = {
         "metric": METRIC if headline else
@@ -399,6 +410,11 @@ def cpu_baseline(args, oracle_inputs, y_gpu, bytes_eff):
 
         def run():
             return oracle.qgemm_w8a16(xb, wi8, sb, threads=threads)
+    elif args.op == "w4a16_dq":
+        codes, scode, sstep, zeros, _ = oracle.quantize_int4_g32_dq(si.bf16_bits(w_cpu))
+
+        def run():
+            return oracle.qgemm_w4a16_dq(xb, codes, scode, sstep, zeros, threads=threads)
     else:
         codes, scales, zeros, _ = oracle.quantize_int4_g32(si.bf16_bits(w_cpu))
         fn = {"w4a16": oracle.qgemm_w4a16, "w4a8": oracle.qgemm_w4a8,

@@ -43,7 +43,10 @@ def _load() -> ctypes.CDLL:
         "qg_int4_packed_bytes": (I64, [I64, I64]),
         "qg_default_split_k": (I32, [I64, I64, I64]),
         "qg_workspace_bytes": (I64, [I64, I64, I64, I32]),
+        "qg_int4_dq_packed_bytes": (I64, [I64, I64]),
         "quantize_int4_g32": (I32, [P, I64, I64, P, I64, P, P]),
+        "quantize_int4_g32_dq": (I32, [P, I64, I64, P, I64, P, P]),
+        "qgemm_w4a16_dq": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "quantize_int8_rowwise": (I32, [P, I64, I64, P, P, P, P]),
         "qgemm_w4a16": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "qgemm_w8a16": (I32, [P, I64, I64, P, P, I64, P, I32, P]),
@@ -94,6 +97,12 @@ def int4_packed_bytes(n: int, k: int) -> int:
     return v
 
 
+def int4_dq_packed_bytes(n: int, k: int) -> int:
+    v = int(lib.qg_int4_dq_packed_bytes(n, k))
+    _check(min(v, 0), "qg_int4_dq_packed_bytes")
+    return v
+
+
 def default_split_k(m: int, n: int, k: int) -> int:
     v = int(lib.qg_default_split_k(m, n, k))
     _check(min(v, 0), "qg_default_split_k")
@@ -117,6 +126,20 @@ def quantize_int4_g32(w: torch.Tensor, status: torch.Tensor | None = None,
     st = lib.quantize_int4_g32(w.data_ptr(), n, k, out.data_ptr(), out.numel(), _ptr(status),
                                _stream(w.device))
     _check(st, "quantize_int4_g32")
+    return out
+
+
+def quantize_int4_g32_dq(w: torch.Tensor, status: torch.Tensor | None = None,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 [n, k] -> packed INT4 g32 weight with scale codes (uint8, layout v2)."""
+    _dev(w, "w", torch.bfloat16, 2)
+    n, k = w.shape
+    nbytes = int4_dq_packed_bytes(n, k)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    st = lib.quantize_int4_g32_dq(w.data_ptr(), n, k, out.data_ptr(), out.numel(), _ptr(status),
+                                  _stream(w.device))
+    _check(st, "quantize_int4_g32_dq")
     return out
 
 
@@ -169,6 +192,20 @@ def qgemm_w4a16(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_k: int =
     st = lib.qgemm_w4a16(x.data_ptr(), m, k, packed.data_ptr(), packed.numel(), n, y.data_ptr(),
                          yd, split_k, _ptr(ws), ws_bytes, _stream(x.device))
     _check(st, "qgemm_w4a16")
+    return y
+
+
+def qgemm_w4a16_dq(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_k: int = 0,
+                   out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y[m, n] = x . dequant(W)^T for a packed INT4 g32 weight with scale codes (m <= 4)."""
+    _dev(x, "x", torch.bfloat16, 2)
+    m, k = x.shape
+    y, yd = _out(m, n, out_dtype, x.device, out)
+    ws, ws_bytes = _workspace(m, n, k, split_k, x.device, workspace)
+    st = lib.qgemm_w4a16_dq(x.data_ptr(), m, k, packed.data_ptr(), packed.numel(), n, y.data_ptr(),
+                            yd, split_k, _ptr(ws), ws_bytes, _stream(x.device))
+    _check(st, "qgemm_w4a16_dq")
     return y
 
 

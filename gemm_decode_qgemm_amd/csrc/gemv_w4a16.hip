@@ -236,7 +236,7 @@ __device__ __forceinline__ void group_dot_2r(float& d0, float& d1, const u32x2_t
   if constexpr (JJ == 1) asm(QG_DOT16_2R(8, 9, 10, 11, 12, 13, 14, 15) QG_DOT16_2R_OPERANDS);
 }
 
-template <int M, int WAVES>
+template <int M, int WAVES, bool DQ = false>
 __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv32_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -250,7 +250,9 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv32_kernel(
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
-  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
+  using L = W4Layout<DQ>;
+  float step;
+  const uint8_t* tiles = L::tiles(packed, rb, kt_count, row, step);
   const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
   const int k32 = k >> 1;
   const uint32_t mask_s = __builtin_amdgcn_readfirstlane(0x000F000Fu);
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv32_kernel(
 
   for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {
     Half32Regs r;
-    load_half32<true>(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lg, row);
+    L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
     u32x2_t xv[M];
 #pragma unroll
     for (int m = 0; m < M; ++m)
@@ -283,8 +285,8 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv32_kernel(
     }
     const float zb0 = (float)((r.zb & 15u) | 0x80u);          // 128 + zp
     const float zb1 = (float)(((r.zb >> 4) & 15u) | 0x80u);
-    const float s0 = fp16_to_f32(r.sc & 0xffffu);
-    const float s1 = fp16_to_f32(r.sc >> 16);
+    const float s0 = L::scale(r.sc, 0, step);
+    const float s1 = L::scale(r.sc, 1, step);
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const u32x4_t cv = r.c[jj];
@@ -369,6 +371,17 @@ static hipError_t launch_w4a16_32_t(const void* x, const void* packed, int n, in
   hipLaunchKernelGGL((w4a16_gemv32_kernel<M, WAVES>), dim3(2 * rbs, split), dim3(WAVES * 64),
                      0, stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
                      n, k, y, y_f32, partial, split);
+  return hipGetLastError();
+}
+
+// M = 1 on the scale-code layout (version 2).
+hipError_t launch_w4a16_gemv32_dq(int m, const void* x, const void* packed, int n, int k, void* y,
+                                  int y_f32, float* partial, int split, hipStream_t stream) {
+  if (m != 1) return hipErrorInvalidValue;
+  const int rbs = (n + kTileRows - 1) / kTileRows;
+  hipLaunchKernelGGL((w4a16_gemv32_kernel<1, 16, true>), dim3(2 * rbs, split), dim3(16 * 64), 0, stream,
+                     static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed), n, k, y, y_f32,
+                     partial, split);
   return hipGetLastError();
 }
 

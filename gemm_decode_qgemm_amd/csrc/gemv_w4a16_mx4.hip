@@ -61,7 +61,7 @@ constexpr int kMx4PairBytes = 144;
 
 // 8 waves per SIMD (two 16-wave workgroups per CU) keep enough weight loads
 // in flight; the kernel fits the 64 VGPRs that allows without spilling.
-template <int M, int WAVES>
+template <int M, int WAVES, bool DQ = false>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8))) void w4a16_gemv_mx4_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -77,7 +77,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8)))
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
-  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
+  using L = W4Layout<DQ>;
+  float step;
+  const uint8_t* tiles = L::tiles(packed, rb, kt_count, row, step);
   // Staging: lane l < 16 M copies k = 8 (l % 16) .. + 8 of x row l / 16.
   const bool stager = lane < 16 * M;
   const int sm = stager ? lane >> 4 : 0, sc = lane & 15;
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8)))
 
   for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {   // tile hs/2, half hs%2
     Half32Regs r;
-    load_half32<true>(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lg, row);
+    L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
     u32x4_t xv = {0u, 0u, 0u, 0u};
     if (stager) xv = *reinterpret_cast<const u32x4_t*>(xsrc + (size_t)hs * 128);
     // Group sums of x: 8 k per stager lane, then the 4 lanes of a group.
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8)))
         const u32x2_t a = (t & 1) ? u32x2_t{xq.z, xq.w} : u32x2_t{xq.x, xq.y};
         d = mfma_4x4x4(a, b, d);
       }
-      const float s = fp16_to_f32((r.sc >> (16 * jj)) & 0xffffu);
+      const float s = L::scale(r.sc, jj, step);
       const f32x4_t xg = *reinterpret_cast<const f32x4_t*>(&xsum[wave][2 * lg + jj][0]);
       const float zb = (float)(((r.zb >> (4 * jj)) & 15u) | 0x80u);   // 128 + zp
 #pragma unroll
@@ -174,11 +176,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8)))
   }
 }
 
-template <int M, int WAVES>
+template <int M, int WAVES, bool DQ>
 static hipError_t launch_mx4_t(const void* x, const void* packed, int n, int k, void* y, int y_f32,
                                float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_gemv_mx4_kernel<M, WAVES>), dim3(2 * rbs, split), dim3(WAVES * 64), 0,
+  hipLaunchKernelGGL((w4a16_gemv_mx4_kernel<M, WAVES, DQ>), dim3(2 * rbs, split), dim3(WAVES * 64), 0,
                      stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
                      n, k, y, y_f32, partial, split);
   return hipGetLastError();
@@ -188,12 +190,23 @@ hipError_t launch_w4a16_gemv_mx4(int m, const void* x, const void* packed, int n
                                  int y_f32, float* partial, int split, int waves,
                                  hipStream_t stream) {
 #define QG_MX4_CASE(MM, WW) \
-  if (m == MM && waves == WW) return launch_mx4_t<MM, WW>(x, packed, n, k, y, y_f32, partial, split, stream);
+  if (m == MM && waves == WW) return launch_mx4_t<MM, WW, false>(x, packed, n, k, y, y_f32, partial, split, stream);
 #define QG_MX4_M(MM) QG_MX4_CASE(MM, 16)
   QG_MX4_M(2) QG_MX4_M(3) QG_MX4_M(4)
 #undef QG_MX4_M
 #undef QG_MX4_CASE
   return hipErrorInvalidValue;
+}
+
+// M = 2..4 on the scale-code layout (version 2).
+hipError_t launch_w4a16_gemv_mx4_dq(int m, const void* x, const void* packed, int n, int k, void* y,
+                                    int y_f32, float* partial, int split, hipStream_t stream) {
+  switch (m) {
+    case 2: return launch_mx4_t<2, 16, true>(x, packed, n, k, y, y_f32, partial, split, stream);
+    case 3: return launch_mx4_t<3, 16, true>(x, packed, n, k, y, y_f32, partial, split, stream);
+    case 4: return launch_mx4_t<4, 16, true>(x, packed, n, k, y, y_f32, partial, split, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace qg

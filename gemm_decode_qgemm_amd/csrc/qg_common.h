@@ -18,6 +18,12 @@ constexpr int kGroupsPerTile = 8;
 constexpr int kScaleOff = 8192;
 constexpr int kZeroOff = 9216;
 constexpr int kTileBytes = 9472;
+// Version 2 (scale codes): a row block is a 128-byte head of the 64 rows'
+// fp16 scale steps, then tiles of codes | uint8 scale codes | zero points.
+constexpr int kDqHeadBytes = 128;
+constexpr int kDqScodeOff = 8192;
+constexpr int kDqZeroOff = 8704;
+constexpr int kDqTileBytes = 8960;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));

@@ -18,11 +18,12 @@ __device__ __forceinline__ double fp16_value(uint32_t bits) {
   return (double)fp16_to_f32(bits);
 }
 
-// Smallest positive finite fp16 s with 15*s >= r, for 0 < r <= 15*65504.
-// Start from r/15 truncated to fp16, then step to the answer; 15*s is exact
-// in binary64, so each comparison is exact.
-__device__ uint32_t fp16_scale_covering(double r) {
-  double t = r / 15.0;
+// Smallest positive finite fp16 s with mult*s >= r, for 0 < r <= mult*65504
+// (mult = 15 for a group scale, 3825 = 255 x 15 for a row step).  Start from
+// r/mult truncated to fp16, then step to the answer; mult*s is exact in
+// binary64, so each comparison is exact.
+__device__ uint32_t fp16_covering(double r, double mult) {
+  double t = r / mult;
   uint32_t b;
   if (t >= 65504.0) {
     b = 0x7bffu;
@@ -34,9 +35,71 @@ __device__ uint32_t fp16_scale_covering(double r) {
     uint32_t f = (uint32_t)((2.0 * m - 1.0) * 1024.0);
     b = ((uint32_t)(e + 14) << 10) | f;        // exponent field (e-1)+15
   }
-  while (15.0 * fp16_value(b) < r) ++b;
-  while (b > 1u && 15.0 * fp16_value(b - 1u) >= r) --b;
+  if (b == 0u) b = 1u;
+  while (mult * fp16_value(b) < r) ++b;
+  while (b > 1u && mult * fp16_value(b - 1u) >= r) --b;
   return b;
+}
+
+__device__ uint32_t fp16_scale_covering(double r) { return fp16_covering(r, 15.0); }
+
+// Zero point and codes of a group for scale s: zp = clamp(rint(-lo/s), 0, 15),
+// q = clamp(rint(v/s) + zp, 0, 15) (IEEE division, round half to even).
+__device__ __forceinline__ uint32_t group_codes(const float (&v)[32], float lo, float s, uint32_t (&q)[32]) {
+  float z = rintf(-lo / s);
+  z = z < 0.0f ? 0.0f : (z > 15.0f ? 15.0f : z);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    float t = rintf(v[i] / s) + z;
+    t = t < 0.0f ? 0.0f : (t > 15.0f ? 15.0f : t);
+    q[i] = (uint32_t)t;
+  }
+  return (uint32_t)z;
+}
+
+__device__ __forceinline__ void unpack_bf16x32(const uint32_t (&wb)[16], float (&v)[32]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[2 * i] = bf16_to_f32(wb[i] & 0xffffu);
+    v[2 * i + 1] = bf16_to_f32(wb[i] >> 16);
+  }
+}
+
+// The group's range widened to hold 0; false if a value is not finite.
+__device__ __forceinline__ bool group_range(const float (&v)[32], float& lo, float& hi) {
+  lo = 0.0f;
+  hi = 0.0f;
+  bool finite = true;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    finite &= __builtin_isfinite(v[i]);
+    lo = v[i] < lo ? v[i] : lo;
+    hi = v[i] > hi ? v[i] : hi;
+  }
+  return finite;
+}
+
+__device__ __forceinline__ void load_group(const uint16_t* src16, uint32_t (&wb)[16]) {
+  const uint4* src = reinterpret_cast<const uint4*>(src16);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint4 u = src[c];
+    wb[4 * c] = u.x; wb[4 * c + 1] = u.y; wb[4 * c + 2] = u.z; wb[4 * c + 3] = u.w;
+  }
+}
+
+// The 4 code dwords of a group in the packed nibble order (k = 8d+e at
+// nibble position (e & 1)*4 + (e >> 1) of dword d).
+__device__ __forceinline__ uint4 pack_chunk(const uint32_t (&q)[32]) {
+  uint32_t dw[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc |= q[8 * d + e] << (4 * ((e & 1) * 4 + (e >> 1)));
+    dw[d] = acc;
+  }
+  return make_uint4(dw[0], dw[1], dw[2], dw[3]);
 }
 
 // One group of 32 bf16 weights -> scale bits, zero point, codes; returns flags.
@@ -73,16 +136,7 @@ __device__ uint32_t quantize_group(const uint32_t (&wb)[16], uint32_t& sbits,
   } else {
     sbits = fp16_scale_covering(r);
   }
-  float s = fp16_to_f32(sbits);
-  float z = rintf(-lo / s);
-  z = z < 0.0f ? 0.0f : (z > 15.0f ? 15.0f : z);
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float t = rintf(v[i] / s) + z;
-    t = t < 0.0f ? 0.0f : (t > 15.0f ? 15.0f : t);
-    q[i] = (uint32_t)t;
-  }
-  zp = (uint32_t)z;
+  zp = group_codes(v, lo, fp16_to_f32(sbits), q);
   return flags;
 }
 
@@ -137,6 +191,132 @@ __global__ __launch_bounds__(256) void quantize_int4_g32_kernel(
       make_uint4(sword[0], sword[1], sword[2], sword[3]);
   *reinterpret_cast<uint32_t*>(tile + kZeroOff + r * 4) = zword;
   if (flags != 0 && status != nullptr) atomicOr(status, flags);
+}
+
+// ---- scale-code layout (version 2) -----------------------------------
+// Same reading as above, with a group's scale stored as a uint8 code times a
+// per-row fp16 step: step = smallest fp16 with 3825*step >= the row's
+// largest group range; code = smallest c in 1..255 with 15*c*step >= the
+// group's range; then zero point and codes as above with s = c*step.  A row
+// holding a non-finite value gets step NaN and all codes 0 (flag 1).
+
+// Pass 1: one wave per row (rows of the padded last block too): the largest
+// group range, then the row's step into the block's head.
+__global__ __launch_bounds__(256) void quantize_int4_dq_step_kernel(
+    const uint16_t* __restrict__ w, int64_t n, int64_t k, uint8_t* __restrict__ packed,
+    int64_t block_bytes, int64_t rows_padded, uint32_t* __restrict__ status) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows_padded) return;                 // whole waves leave together
+  const int lane = threadIdx.x & 63;
+  double rmax = 0.0;
+  bool finite = true;
+  if (row < n) {
+    for (int64_t g = lane; g < k / 32; g += 64) {
+      uint32_t wb[16];
+      load_group(w + row * k + g * 32, wb);
+      float v[32], lo, hi;
+      unpack_bf16x32(wb, v);
+      finite &= group_range(v, lo, hi);
+      const double r = (double)hi - (double)lo;
+      rmax = r > rmax ? r : rmax;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const double o = __shfl_xor(rmax, off);
+    rmax = o > rmax ? o : rmax;
+  }
+  const bool all_finite = __all(finite);
+  if (lane == 0) {
+    uint32_t bits = 0, flags = 0;
+    if (row < n) {
+      if (!all_finite) {
+        bits = 0x7e00u;
+        flags = QG_FLAG_NONFINITE;
+      } else if (rmax == 0.0) {
+        bits = 0x3c00u;
+      } else if (rmax > 3825.0 * 65504.0) {
+        bits = 0x7bffu;
+        flags = QG_FLAG_OVERFLOW;
+      } else {
+        bits = fp16_covering(rmax, 3825.0);
+      }
+    }
+    *reinterpret_cast<uint16_t*>(packed + (row / kTileRows) * block_bytes + 2 * (row % kTileRows)) =
+        (uint16_t)bits;
+    if (flags != 0 && status != nullptr) atomicOr(status, flags);
+  }
+}
+
+// Smallest c in 1..255 with 15*c*step >= r (255 if none): start from the
+// quotient, then step to the answer with exact binary64 comparisons.
+__device__ uint32_t dq_scale_code(double r, double step) {
+  const double t = r / (15.0 * step);
+  uint32_t c = t >= 255.0 ? 255u : (t <= 1.0 ? 1u : (uint32_t)ceil(t));
+  while (c < 255u && 15.0 * (double)c * step < r) ++c;
+  while (c > 1u && 15.0 * (double)(c - 1u) * step >= r) --c;
+  return c;
+}
+
+// Pass 2: one thread per (row, 256-k tile), as quantize_int4_g32_kernel:
+// 8 code chunks, 8 scale codes (8 B) and the zero word (4 B) of its row.
+__global__ __launch_bounds__(256) void quantize_int4_dq_kernel(
+    const uint16_t* __restrict__ w, int64_t n, int64_t k, uint8_t* __restrict__ packed,
+    int64_t block_bytes, int64_t tiles) {
+  const int64_t wave_global = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wave_global >= tiles) return;
+  const int64_t kt_count = k / kTileK;
+  const int64_t rb = wave_global / kt_count;
+  const int64_t kt = wave_global % kt_count;
+  const int r = threadIdx.x & 63;
+  const int64_t row = rb * kTileRows + r;
+  uint8_t* block = packed + rb * block_bytes;
+  uint8_t* tile = block + kDqHeadBytes + kt * kDqTileBytes;
+  const uint32_t sbits = *reinterpret_cast<const uint16_t*>(block + 2 * r);   // written by pass 1
+  // padding rows and rows with a non-finite value keep all-zero codes
+  const bool live = row < n && (sbits & 0x7c00u) != 0x7c00u;
+  const double step = fp16_value(sbits);
+
+  uint32_t zword = 0;
+  uint32_t cword[2] = {0, 0};
+  for (int j = 0; j < kGroupsPerTile; ++j) {
+    uint4 chunk = make_uint4(0, 0, 0, 0);
+    if (live) {
+      uint32_t wb[16];
+      load_group(w + row * k + kt * kTileK + j * 32, wb);
+      float v[32], lo, hi;
+      unpack_bf16x32(wb, v);
+      group_range(v, lo, hi);
+      const uint32_t c = dq_scale_code((double)hi - (double)lo, step);
+      const float s = (float)((double)c * step);     // exact: 8 x 11 significant bits
+      uint32_t q[32];
+      const uint32_t zp = group_codes(v, lo, s, q);
+      chunk = pack_chunk(q);
+      cword[j >> 2] |= c << (8 * (j & 3));
+      zword |= zp << (4 * j);
+    }
+    *reinterpret_cast<uint4*>(tile + (j * kTileRows + r) * 16) = chunk;
+  }
+  *reinterpret_cast<uint2*>(tile + kDqScodeOff + r * 8) = make_uint2(cword[0], cword[1]);
+  *reinterpret_cast<uint32_t*>(tile + kDqZeroOff + r * 4) = zword;
+}
+
+hipError_t launch_quantize_int4_g32_dq(const void* w, int64_t n, int64_t k, void* packed,
+                                       uint32_t* status, hipStream_t stream) {
+  const int64_t rbs = (n + kTileRows - 1) / kTileRows;
+  const int64_t kt_count = k / kTileK;
+  const int64_t block_bytes = kDqHeadBytes + kt_count * kDqTileBytes;
+  const int64_t rows_padded = rbs * kTileRows;
+  hipLaunchKernelGGL(quantize_int4_dq_step_kernel, dim3((unsigned)((rows_padded + 3) / 4)), dim3(256),
+                     0, stream, static_cast<const uint16_t*>(w), n, k, static_cast<uint8_t*>(packed),
+                     block_bytes, rows_padded, status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t tiles = rbs * kt_count;
+  hipLaunchKernelGGL(quantize_int4_dq_kernel, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(w), n, k, static_cast<uint8_t*>(packed), block_bytes,
+                     tiles);
+  return hipGetLastError();
 }
 
 // Smallest positive finite bf16 s with 127*s >= a, for a > 0 finite.

@@ -53,6 +53,52 @@ __device__ __forceinline__ void load_half32(Half32Regs& r, const uint8_t* tile, 
   r.zb = load_stream<false>(tile + kZeroOff + row * 4 + 2 * half + lg);
 }
 
+// The two packed layouts seen by the 32-row kernels.  Version 1: tiles of
+// 9472 bytes with fp16 scales.  Version 2 (scale codes): each 64-row block
+// starts with a 128-byte head of fp16 row steps, its tiles are 8960 bytes,
+// and a group's scale is its uint8 code times the row's step (exact in
+// binary32: 8 x 11 significant bits).  Codes sit at the same place in both.
+template <bool DQ>
+struct W4Layout;
+
+template <>
+struct W4Layout<false> {
+  static constexpr int kTile = kTileBytes;
+  __device__ static const uint8_t* tiles(const uint8_t* packed, int rb, int kt_count, int, float& step) {
+    step = 1.0f;
+    return packed + (size_t)rb * kt_count * kTileBytes;
+  }
+  __device__ static void load(Half32Regs& r, const uint8_t* tile, int half, int lg, int row) {
+    load_half32<true>(r, tile, half, lg, row);
+  }
+  // scale of group 2 lg + jj of the half tile
+  __device__ static float scale(uint32_t sc, int jj, float) {
+    return fp16_to_f32((sc >> (16 * jj)) & 0xffffu);
+  }
+};
+
+template <>
+struct W4Layout<true> {
+  static constexpr int kTile = kDqTileBytes;
+  __device__ static const uint8_t* tiles(const uint8_t* packed, int rb, int kt_count, int row, float& step) {
+    const uint8_t* block = packed + (size_t)rb * (kDqHeadBytes + (size_t)kt_count * kDqTileBytes);
+    step = fp16_to_f32(*reinterpret_cast<const uint16_t*>(block + 2 * row));
+    return block + kDqHeadBytes;
+  }
+  __device__ static void load(Half32Regs& r, const uint8_t* tile, int half, int lg, int row) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      r.c[j] = load_stream<true>(
+          reinterpret_cast<const u32x4_t*>(tile + ((4 * half + 2 * lg + j) * kTileRows + row) * 16));
+    // temporal, as in load_half32: the other half tile's metadata shares these lines
+    r.sc = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + kDqScodeOff + row * 8 + 4 * half + 2 * lg));
+    r.zb = load_stream<false>(tile + kDqZeroOff + row * 4 + 2 * half + lg);
+  }
+  __device__ static float scale(uint32_t sc, int jj, float step) {
+    return (float)((sc >> (8 * jj)) & 0xffu) * step;
+  }
+};
+
 // Split-K partition of `tiles` 256-k units into `split` contiguous ranges;
 // the first (tiles % split) ranges take one extra unit.
 __device__ __forceinline__ void split_range(int tiles, int split, int s, int& t0, int& t1) {

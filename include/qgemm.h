@@ -62,6 +62,21 @@ extern "C" {
 #define QG_TILE_ROWS 64
 #define QG_TILE_K 256
 #define QG_TILE_BYTES 9472
+
+/* ---- packed INT4 layout, version 2: scale codes --------------------------
+ * The stored form of [P1] `_packed_with_dense`: a group's scale is a uint8
+ * code times a per-row fp16 step ([P1] legality rules "scale codes must be
+ * uint8", "scale_step must be float16", step shape [N, 1]).  Each 64-row
+ * block is a 128-byte head (row r's fp16 step at 2r) followed by K/256 tiles
+ * of 8960 bytes = 70 lines:
+ *   [0, 8192)     codes, exactly as version 1
+ *   [8192, 8704)  scale codes: row r's 8 bytes at 8192 + 8r, group j at +j
+ *   [8704, 8960)  zero points: row r's LE 32-bit word at 8704 + 4r, group j
+ *                 in bits [4j, 4j+4)
+ * Row blocks follow each other; rows n >= N of the last block are zero.
+ * 0.546875 bytes per weight + 2 per row (version 1: 0.578125). */
+#define QG_DQ_HEAD_BYTES 128
+#define QG_DQ_TILE_BYTES 8960
 #define QG_GROUP 32
 #define QG_MAX_M 64
 
@@ -151,6 +166,42 @@ int32_t quantize_int8_rowwise(const void *w_bf16, int64_t n, int64_t k, int8_t *
 int32_t qgemm_w4a16(const void *x_bf16, int64_t m, int64_t k, const void *packed,
                     int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
                     int32_t split_k, void *ws, int64_t ws_bytes, void *stream);
+
+/* Bytes of the version 2 (scale-code) buffer for an N x K weight:
+ * ceil(N/64) * (128 + (K/256) * 8960), or a negative qg_status as above. */
+int64_t qg_int4_dq_packed_bytes(int64_t n, int64_t k);
+
+/* ---- quantize_int4_g32_dq ------------------------------------------------
+ * [P1] `_packed_with_dense` in its stored form (uint8 scale codes with a
+ * per-row fp16 `scale_step`).  Per row n, with lo, hi and r of each group as
+ * in quantize_int4_g32:
+ *   step = the smallest positive fp16 with 3825*step >= max_g r  (3825 =
+ *          255*15; 1.0 when every r is 0)
+ *   c    = the smallest integer in 1..255 with 15*c*step >= r, per group
+ *   s    = c * step  (exact in binary32), then zp and q exactly as in
+ *          quantize_int4_g32 with that s.
+ * Zero points stay integers 0..15 (a zero_point_step of 1).  Every
+ * dequantized value (q - zp) * s lies within s/2 of its input.
+ *   w_bf16        in : bf16 [n, k]
+ *   packed        out: qg_int4_dq_packed_bytes(n, k) bytes, layout version 2
+ *   packed_bytes  in : size of `packed`
+ *   status_dev    in/out, may be NULL: QG_FLAG_NONFINITE (that row: step
+ *                 NaN, every code 0), QG_FLAG_OVERFLOW (max_g r above
+ *                 3825 * 65504: step 65504, codes at most 255).
+ * Two launches on `stream` (row steps, then tiles).
+ * Errors: QG_E_NULL, QG_E_SHAPE, QG_E_K_MULTIPLE, QG_E_BUFFER, QG_E_ALIGN. */
+int32_t quantize_int4_g32_dq(const void *w_bf16, int64_t n, int64_t k, void *packed,
+                             int64_t packed_bytes, uint32_t *status_dev, void *stream);
+
+/* ---- qgemm_w4a16_dq ------------------------------------------------------
+ * qgemm_w4a16 on a version 2 (scale-code) weight:
+ *   y[m, n] = sum_g c[n,g] * step[n] * sum_{k in g} x[m,k] * (q[n,k] - zp[n,g]),
+ * dequantized in registers, fp32 accumulation.  Arguments, workspace
+ * (qg_workspace_bytes) and errors as qgemm_w4a16, with packed_bytes checked
+ * against qg_int4_dq_packed_bytes and 1 <= m <= 4 (QG_E_M_RANGE above). */
+int32_t qgemm_w4a16_dq(const void *x_bf16, int64_t m, int64_t k, const void *packed,
+                       int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
+                       int32_t split_k, void *ws, int64_t ws_bytes, void *stream);
 
 /* ---- qgemm_w8a16 ---------------------------------------------------------
  * [P3] `WeightOnlyInt8Linear.forward`: y[m, n] = (sum_k x[m,k] * W[n,k]) *

@@ -34,7 +34,10 @@ def lib():
         "qg_int4_packed_bytes": (I64, [I64, I64]),
         "qg_default_split_k": (I32, [I64, I64, I64]),
         "qg_workspace_bytes": (I64, [I64, I64, I64, I32]),
+        "qg_int4_dq_packed_bytes": (I64, [I64, I64]),
         "quantize_int4_g32": (I32, [P, I64, I64, P, I64, P, P]),
+        "quantize_int4_g32_dq": (I32, [P, I64, I64, P, I64, P, P]),
+        "qgemm_w4a16_dq": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "quantize_int8_rowwise": (I32, [P, I64, I64, P, P, P, P]),
         "qgemm_w4a16": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "qgemm_w8a16": (I32, [P, I64, I64, P, P, I64, P, I32, P]),
@@ -73,6 +76,12 @@ def test_packed_bytes_formula(lib):
     assert lib.qg_int4_packed_bytes(257, 512) == 5 * 2 * 9472          # padded to 5 row blocks
     assert lib.qg_int4_packed_bytes(64, 300) == E_K
     assert lib.qg_int4_packed_bytes(0, 256) == E_SHAPE
+    # version 2 (scale codes): a 128-byte head of row steps per 64-row block,
+    # then tiles of 8960 bytes: N*K/2 codes + N*K/32 * 1.5 + 2N when N % 64 == 0
+    assert lib.qg_int4_dq_packed_bytes(39936, 6656) == 39936 * 6656 // 2 + 39936 * 6656 // 32 * 3 // 2 + 2 * 39936
+    assert lib.qg_int4_dq_packed_bytes(257, 512) == 5 * (128 + 2 * 8960)
+    assert lib.qg_int4_dq_packed_bytes(64, 300) == E_K
+    assert lib.qg_int4_dq_packed_bytes(64, 0) == E_SHAPE
 
 
 def test_split_rule_one_k_tile_per_split(lib):
@@ -136,6 +145,8 @@ def test_default_split_table(lib):
 ])
 def test_qgemm_w4a16_and_w4a8_validate_before_launching(lib, args, expect):
     assert lib.qgemm_w4a16(*args) == expect
+    # the scale-code layout shares the rules (its buffer size is checked against its own formula)
+    assert lib.qgemm_w4a16_dq(*args) == expect
     # W4A8 (both activation granularities) shares the rules
     assert lib.qgemm_w4a8(*args) == expect
     assert lib.qgemm_w4a8_g32(*args) == expect
@@ -144,6 +155,9 @@ def test_qgemm_w4a16_and_w4a8_validate_before_launching(lib, args, expect):
 def test_w4a8_m_range(lib):
     assert lib.qgemm_w4a8(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
     assert lib.qgemm_w4a8_g32(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
+    assert lib.qgemm_w4a16_dq(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
+    # 9088 bytes hold a 64 x 256 scale-code weight, 9087 do not
+    assert lib.qgemm_w4a16_dq(A, 1, 256, A, 9087, 64, A, 0, 0, None, 0, None) == E_BUF
 
 
 @pytest.mark.parametrize("args,expect", [
@@ -173,6 +187,16 @@ def test_qgemm_w8a16_validates_before_launching(lib, args, expect):
 ])
 def test_quantize_int4_validates_before_launching(lib, args, expect):
     assert lib.quantize_int4_g32(*args) == expect
+
+
+def test_quantize_int4_dq_validates_before_launching(lib):
+    assert lib.quantize_int4_g32_dq(None, 64, 256, A, 1 << 20, None, None) == E_NULL
+    assert lib.quantize_int4_g32_dq(A, 64, 256, None, 1 << 20, None, None) == E_NULL
+    assert lib.quantize_int4_g32_dq(A, 64, 300, A, 1 << 20, None, None) == E_K
+    assert lib.quantize_int4_g32_dq(A, 0, 256, A, 1 << 20, None, None) == E_SHAPE
+    assert lib.quantize_int4_g32_dq(A, 64, 256, A, 9087, None, None) == E_BUF
+    assert lib.quantize_int4_g32_dq(A, 64, 256, A, 9088, U + 2, None) == E_ALIGN
+    assert lib.quantize_int4_g32_dq(U, 64, 256, A, 9088, None, None) == E_ALIGN
 
 
 @pytest.mark.parametrize("args,expect", [
