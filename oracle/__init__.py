@@ -61,6 +61,11 @@ def _load():
         "orc_pack_int4_dq": (None, [P, P, P, P, I64, I64, P]),
         "orc_unpack_int4_dq": (None, [P, I64, I64, P, P, P, P]),
         "orc_qgemm_w4a16_dq": (None, [P, I64, I64, P, P, P, P, I64, P, I]),
+        "orc_quantize_intn_g32": (I, [P, I64, I64, I, P, P, P]),
+        "orc_quantize_group32_bits": (I, [P, I, P, P, P]),
+        "orc_intn_packed_bytes": (I64, [I64, I64, I]),
+        "orc_pack_intn": (None, [P, P, P, I64, I64, I, P]),
+        "orc_unpack_intn": (None, [P, I64, I64, I, P, P, P]),
         "orc_hardware_threads": (I, []),
     }
     for name, (res, args) in sig.items():
@@ -170,6 +175,54 @@ def qgemm_w4a16(x_bits, codes, scales, zeros, threads: int = 1) -> np.ndarray:
     y = np.empty((m, n), np.float64)
     _load().orc_qgemm_w4a16(_ptr(x), m, k, _ptr(codes), _ptr(scales), _ptr(zeros), n, _ptr(y), threads)
     return y
+
+
+# ------------------------------------------------------- INT5 / INT6 g32
+def quantize_group32_bits(w32_bits, bits: int):
+    """One group at 5 or 6 bits: returns (scale_bits, zp, codes[32], flags)."""
+    w = _u16(w32_bits).reshape(32)
+    s = np.zeros(1, np.uint16)
+    z = np.zeros(1, np.uint8)
+    q = np.zeros(32, np.uint8)
+    f = _load().orc_quantize_group32_bits(_ptr(w), bits, _ptr(s), _ptr(z), _ptr(q))
+    return int(s[0]), int(z[0]), q, int(f)
+
+
+def quantize_intn_g32(w_bits, bits: int):
+    """W bf16 bits [n, k] -> (codes u8 [n,k] in 0..2^bits-1, scales u16 [n,k/32], zeros u8, flags)."""
+    w = _u16(w_bits)
+    n, k = w.shape
+    assert k % 32 == 0 and bits in (5, 6)
+    codes = np.empty((n, k), np.uint8)
+    scales = np.empty((n, k // 32), np.uint16)
+    zeros = np.empty((n, k // 32), np.uint8)
+    f = _load().orc_quantize_intn_g32(_ptr(w), n, k, bits, _ptr(codes), _ptr(scales), _ptr(zeros))
+    return codes, scales, zeros, int(f)
+
+
+def intn_packed_bytes(n: int, k: int, bits: int) -> int:
+    return int(_load().orc_intn_packed_bytes(n, k, bits))
+
+
+def pack_intn(codes, scales, zeros, bits: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = _u16(scales)
+    zeros = np.ascontiguousarray(zeros, np.uint8)
+    n, k = codes.shape
+    assert k % 256 == 0 and bits in (5, 6)
+    out = np.empty(intn_packed_bytes(n, k, bits), np.uint8)
+    _load().orc_pack_intn(_ptr(codes), _ptr(scales), _ptr(zeros), n, k, bits, _ptr(out))
+    return out
+
+
+def unpack_intn(packed, n: int, k: int, bits: int):
+    packed = np.ascontiguousarray(packed, np.uint8)
+    assert packed.size >= intn_packed_bytes(n, k, bits)
+    codes = np.empty((n, k), np.uint8)
+    scales = np.empty((n, k // 32), np.uint16)
+    zeros = np.empty((n, k // 32), np.uint8)
+    _load().orc_unpack_intn(_ptr(packed), n, k, bits, _ptr(codes), _ptr(scales), _ptr(zeros))
+    return codes, scales, zeros
 
 
 # ------------------------------------------- INT4 g32 with scale codes

@@ -141,6 +141,33 @@ void orc_qgemm_w4a16_dq(const uint16_t *x, int64_t m, int64_t k, const uint8_t *
                         const uint8_t *scode, const uint16_t *sstep, const uint8_t *zeros,
                         int64_t n, double *y, int threads);
 
+/* ---- INT5 / INT6 group-32 (the pages' INT5/INT6 quantized-GEMM family) ----
+ * The INT4 reading with L = 2^bits - 1 steps: s = smallest positive fp16
+ * with L*s >= r (1.0 for r == 0; 65504 and flag 2 above L*65504),
+ * zp = clamp(rint(-lo/s), 0, L), q = clamp(rint(v/s) + zp, 0, L).
+ * bits is 5 or 6; outputs as orc_quantize_int4_g32 (codes up to L).  The
+ * dequant-then-dot reference orc_qgemm_w4a16 takes these codes unchanged. */
+int orc_quantize_intn_g32(const uint16_t *w, int64_t n, int64_t k, int bits,
+                          uint8_t *codes, uint16_t *scales, uint8_t *zeros);
+int orc_quantize_group32_bits(const uint16_t *w32, int bits, uint16_t *scale, uint8_t *zp,
+                              uint8_t *q32);
+
+/* ---- packed layout for 5 / 6 bits (hb = bits - 4 high bits per code) ----
+ * Tiles of 64 rows x 256 k, row-block major, 8192 + 2048*hb + 1536 bytes
+ * (11776 for INT5, 13824 for INT6):
+ *   [0, 8192)                 the low 4 bits of every code, exactly as v1
+ *   [8192, 8192 + 2048 hb)    high planes: the (4 hb)-byte chunk of (group j,
+ *                             row r) at 8192 + (j*64 + r)*4*hb; bit order
+ *                             in the chunk: see high_bit_position
+ *   [.., + 1024)              fp16 scales: row r at +16r, group j at +2j
+ *   [.., + 512)               zero points, one byte each: row r at +8r, group j at +j
+ * Rows n >= N of the last row block are zero. */
+int64_t orc_intn_packed_bytes(int64_t n, int64_t k, int bits);
+void orc_pack_intn(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                   int64_t n, int64_t k, int bits, uint8_t *packed);
+void orc_unpack_intn(const uint8_t *packed, int64_t n, int64_t k, int bits,
+                     uint8_t *codes, uint16_t *scales, uint8_t *zeros);
+
 /* Thread count the machine offers (for the CPU baseline). */
 int orc_hardware_threads(void);
 

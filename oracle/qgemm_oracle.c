@@ -100,8 +100,10 @@ static float clampf(float v, float lo, float hi) {
 /* round-half-even, round then add the zero point) is recorded in the   */
 /* design notes.                                                        */
 /* ------------------------------------------------------------------ */
-int orc_quantize_group32(const uint16_t *w32, uint16_t *scale, uint8_t *zp,
-                         uint8_t *q32) {
+/* One group of 32 with `levels` steps (15 for INT4, 31 for INT5, 63 for
+ * INT6): the same reading with 2^bits - 1 in place of 15. */
+static int quantize_group_levels(const uint16_t *w32, int levels, uint16_t *scale,
+                                 uint8_t *zp, uint8_t *q32) {
     float v[32];
     float lo = 0.0f, hi = 0.0f;   /* the range always holds 0 */
     int nonfinite = 0;
@@ -122,21 +124,32 @@ int orc_quantize_group32(const uint16_t *w32, uint16_t *scale, uint8_t *zp,
     uint16_t sbits;
     if (r == 0.0) {
         sbits = FP16_ONE_BITS;            /* all-zero group */
-    } else if (r > 15.0 * 65504.0) {
+    } else if (r > levels * 65504.0) {
         sbits = FP16_MAX_BITS;            /* saturate, flag it */
         flags |= 2;
     } else {
-        sbits = smallest_fp16_covering(r, 15.0);
+        sbits = smallest_fp16_covering(r, (double)levels);
     }
     float s = (float)orc_fp16_to_double(sbits);
-    float z = clampf(rintf(-lo / s), 0.0f, 15.0f);
+    float top = (float)levels;
+    float z = clampf(rintf(-lo / s), 0.0f, top);
     for (int i = 0; i < 32; i++) {
         float t = rintf(v[i] / s) + z;    /* round first, then add zp */
-        q32[i] = (uint8_t)clampf(t, 0.0f, 15.0f);
+        q32[i] = (uint8_t)clampf(t, 0.0f, top);
     }
     *scale = sbits;
     *zp = (uint8_t)z;
     return flags;
+}
+
+int orc_quantize_group32(const uint16_t *w32, uint16_t *scale, uint8_t *zp,
+                         uint8_t *q32) {
+    return quantize_group_levels(w32, 15, scale, zp, q32);
+}
+
+int orc_quantize_group32_bits(const uint16_t *w32, int bits, uint16_t *scale, uint8_t *zp,
+                              uint8_t *q32) {
+    return quantize_group_levels(w32, (1 << bits) - 1, scale, zp, q32);
 }
 
 int orc_quantize_int4_g32(const uint16_t *w, int64_t n, int64_t k,
@@ -653,4 +666,111 @@ void orc_qgemm_w4a16_dq(const uint16_t *x, int64_t m, int64_t k, const uint8_t *
                         int64_t n, double *y, int threads) {
     struct w4dq_ctx c = {x, m, k, codes, scode, sstep, zeros, n, y};
     parallel_rows(w4a16_dq_rows, &c, n, threads);
+}
+
+/* ------------------------------------------------------------------ */
+/* INT5 / INT6 group-32 (the pages' INT5/INT6 family): the INT4 reading */
+/* with 31 / 63 steps, fp16 scale, integer zero point 0..2^bits-1.      */
+/* ------------------------------------------------------------------ */
+int orc_quantize_intn_g32(const uint16_t *w, int64_t n, int64_t k, int bits,
+                          uint8_t *codes, uint16_t *scales, uint8_t *zeros) {
+    int flags = 0;
+    int64_t groups = k / 32;
+    for (int64_t row = 0; row < n; row++)
+        for (int64_t g = 0; g < groups; g++)
+            flags |= orc_quantize_group32_bits(w + row * k + g * 32, bits,
+                                               scales + row * groups + g,
+                                               zeros + row * groups + g,
+                                               codes + row * k + g * 32);
+    return flags;
+}
+
+/* Packed layout for 5 and 6 bits (see oracle.h): the low 4 bits of every
+ * code exactly as version 1, the high bits in a plane of hb = bits - 4 bits
+ * per code. */
+static int64_t intn_tile_bytes(int bits) { return 8192 + 2048 * (bits - 4) + 1024 + 512; }
+
+int64_t orc_intn_packed_bytes(int64_t n, int64_t k, int bits) {
+    int64_t row_blocks = (n + T_ROWS - 1) / T_ROWS;
+    return row_blocks * (k / T_K) * intn_tile_bytes(bits);
+}
+
+/* Bit of the high plane (counted from the row's (4*hb)-byte group chunk,
+ * little-endian) that holds high bit b of k-in-group kl.  Code dword d of
+ * the low chunk holds k = 8d+e, pair p = e/2 being k = 8d+2p (even) and
+ * 8d+2p+1 (odd).  INT5 (hb = 1): one plane dword; the even k's bit at
+ * 4d + p, the odd k's at 16 + 4d + p.  INT6 (hb = 2): plane dword d/2; in
+ * it the even k's two bits at 8(d%2) + 2p + b, the odd k's 16 higher.  So
+ * (plane >> shift) & mask puts a pair's high bits where
+ * (dword >> 4p) & 0x000F000F puts its low bits, 4 places lower. */
+static int high_bit_position(int kl, int b, int hb) {
+    int d = kl / 8, p = (kl % 8) / 2, odd = kl % 2;
+    if (hb == 1) return 16 * odd + 4 * d + p;
+    return 32 * (d / 2) + 16 * odd + 8 * (d % 2) + 2 * p + b;
+}
+
+void orc_pack_intn(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                   int64_t n, int64_t k, int bits, uint8_t *packed) {
+    int hb = bits - 4;
+    int64_t tb = intn_tile_bytes(bits), kt_count = k / T_K, groups = k / 32;
+    int64_t hi_off = 8192, s_off = 8192 + 2048 * hb, z_off = s_off + 1024;
+    memset(packed, 0, (size_t)orc_intn_packed_bytes(n, k, bits));
+    for (int64_t row = 0; row < n; row++) {
+        int64_t rb = row / T_ROWS;
+        int r = (int)(row % T_ROWS);
+        for (int64_t kt = 0; kt < kt_count; kt++) {
+            uint8_t *tile = packed + (rb * kt_count + kt) * tb;
+            for (int kk = 0; kk < T_K; kk++) {
+                int q = codes[row * k + kt * T_K + kk];
+                int64_t byte; int shift;
+                code_position(r, kk, &byte, &shift);
+                tile[byte] |= (uint8_t)((q & 0xF) << shift);
+                int j = kk / 32, kl = kk % 32;
+                uint8_t *chunk = tile + hi_off + (int64_t)(j * T_ROWS + r) * 4 * hb;
+                for (int b = 0; b < hb; b++) {
+                    int pos = high_bit_position(kl, b, hb);
+                    chunk[pos / 8] |= (uint8_t)(((q >> (4 + b)) & 1) << (pos % 8));
+                }
+            }
+            for (int j = 0; j < T_GROUPS; j++) {
+                int64_t g = kt * T_GROUPS + j;
+                uint16_t sc = scales[row * groups + g];
+                tile[s_off + r * 16 + j * 2] = (uint8_t)(sc & 0xFF);
+                tile[s_off + r * 16 + j * 2 + 1] = (uint8_t)(sc >> 8);
+                tile[z_off + r * 8 + j] = zeros[row * groups + g];
+            }
+        }
+    }
+}
+
+void orc_unpack_intn(const uint8_t *packed, int64_t n, int64_t k, int bits,
+                     uint8_t *codes, uint16_t *scales, uint8_t *zeros) {
+    int hb = bits - 4;
+    int64_t tb = intn_tile_bytes(bits), kt_count = k / T_K, groups = k / 32;
+    int64_t hi_off = 8192, s_off = 8192 + 2048 * hb, z_off = s_off + 1024;
+    for (int64_t row = 0; row < n; row++) {
+        int64_t rb = row / T_ROWS;
+        int r = (int)(row % T_ROWS);
+        for (int64_t kt = 0; kt < kt_count; kt++) {
+            const uint8_t *tile = packed + (rb * kt_count + kt) * tb;
+            for (int kk = 0; kk < T_K; kk++) {
+                int64_t byte; int shift;
+                code_position(r, kk, &byte, &shift);
+                int q = (tile[byte] >> shift) & 0xF;
+                int j = kk / 32, kl = kk % 32;
+                const uint8_t *chunk = tile + hi_off + (int64_t)(j * T_ROWS + r) * 4 * hb;
+                for (int b = 0; b < hb; b++) {
+                    int pos = high_bit_position(kl, b, hb);
+                    q |= ((chunk[pos / 8] >> (pos % 8)) & 1) << (4 + b);
+                }
+                codes[row * k + kt * T_K + kk] = (uint8_t)q;
+            }
+            for (int j = 0; j < T_GROUPS; j++) {
+                int64_t g = kt * T_GROUPS + j;
+                scales[row * groups + g] =
+                    (uint16_t)(tile[s_off + r * 16 + j * 2] | (tile[s_off + r * 16 + j * 2 + 1] << 8));
+                zeros[row * groups + g] = tile[z_off + r * 8 + j];
+            }
+        }
+    }
 }

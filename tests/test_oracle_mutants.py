@@ -11,14 +11,15 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "qgemm_oracle.c")
 PINS = [os.path.join(ROOT, "tests", f) for f in ("test_oracle_int4.py", "test_oracle_int8.py",
-                                                 "test_oracle_w4a8_g32.py", "test_oracle_int4_dq.py")]
+                                                 "test_oracle_w4a8_g32.py", "test_oracle_int4_dq.py",
+                                                 "test_oracle_intn.py")]
 
 # (id, original text, planted text): each is a single, plausible slip.
 MUTANTS = [
     ("add_then_round", "rintf(v[i] / s) + z", "rintf(v[i] / s + z)"),
     ("range_not_widened_to_zero", "float lo = 0.0f, hi = 0.0f;", "float lo = INFINITY, hi = -INFINITY;"),
-    ("scale_one_ulp_small", "sbits = smallest_fp16_covering(r, 15.0);",
-     "sbits = smallest_fp16_covering(r, 15.0) - 1;"),
+    ("scale_one_ulp_small", "sbits = smallest_fp16_covering(r, (double)levels);",
+     "sbits = smallest_fp16_covering(r, (double)levels) - 1;"),
     ("zero_point_sign", "rintf(-lo / s)", "rintf(lo / s)"),
     ("half_away_rounding", "float t = rintf(v[i] / s) + z;", "float t = roundf(v[i] / s) + z;"),
     ("nibble_order_linear", "(e & 1) * 4 + (e >> 1)", "e"),
@@ -54,6 +55,15 @@ MUTANTS = [
      "block[2 * r] = (uint8_t)(sstep[row] >> 8);"),
     ("dq_scale_code_transposed", "tile[D_SCODE_OFF + r * 8 + j] = scode[row * groups + g];",
      "tile[D_SCODE_OFF + j * 64 + r] = scode[row * groups + g];"),
+    ("intn_levels_off_by_one", "return quantize_group_levels(w32, (1 << bits) - 1, scale, zp, q32);",
+     "return quantize_group_levels(w32, (1 << bits), scale, zp, q32);"),
+    ("int5_plane_pair_and_dword_swapped", "if (hb == 1) return 16 * odd + 4 * d + p;",
+     "if (hb == 1) return 16 * odd + 4 * p + d;"),
+    ("int6_plane_bit_and_pair_swapped", "8 * (d % 2) + 2 * p + b;", "8 * (d % 2) + 4 * b + p;"),
+    ("intn_zero_bytes_swapped", "tile[z_off + r * 8 + j] = zeros[row * groups + g];",
+     "tile[z_off + r * 8 + (j ^ 1)] = zeros[row * groups + g];"),
+    ("intn_scales_at_the_v1_offset", "int64_t hi_off = 8192, s_off = 8192 + 2048 * hb, z_off = s_off + 1024;",
+     "int64_t hi_off = 8192, s_off = 8192 + 1024 * hb, z_off = s_off + 1024;"),
     ("dq_gemm_step_of_row_0", "double step = orc_fp16_to_double(c->sstep[row]);",
      "double step = orc_fp16_to_double(c->sstep[0]);"),
 ]
