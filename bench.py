@@ -24,7 +24,8 @@ result against it.
 
 Other layers of the same path use the same protocol: --op w4a16 with
 --m 2..64 (M > 4 runs the matrix-core kernel), --op w4a16_dq (the scale-code
-weight, M <= 4, bytes = its packed size), --op w4a8 / w4a8_g32 (M <= 4) and
+weight, M <= 4, bytes = its packed size), --op wn_a16 --bits 5|6 (INT5 / INT6,
+M = 1, bytes = the packed size), --op w4a8 / w4a8_g32 (M <= 4) and
 --op w8a16 (int8 per-channel, bytes = N*K + 2*N); --n/--k pick the shape.  The
 offline weight quantizers run the same way: --op quantize_int4 (bytes = the
 bf16 weight read + the packed weight written) and --op quantize_int8 (bf16
@@ -84,9 +85,10 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=1000,
                    help="untimed calls first; the clocks take a few hundred calls to ramp up from idle")
-    p.add_argument("--op", choices=("w4a16", "w4a16_dq", "w4a8", "w4a8_g32", "w8a16", "quantize_int4",
-                                    "quantize_int8"),
+    p.add_argument("--op", choices=("w4a16", "w4a16_dq", "wn_a16", "w4a8", "w4a8_g32", "w8a16",
+                                    "quantize_int4", "quantize_int8"),
                    default="w4a16")
+    p.add_argument("--bits", type=int, default=6, help="code width of --op wn_a16 (5 or 6)")
     p.add_argument("--n", type=int, default=39936)
     p.add_argument("--k", type=int, default=6656)
     p.add_argument("--m", type=int, default=1)
@@ -124,6 +126,8 @@ def main() -> int:
         bytes_eff = n * k + 2 * n
     elif op == "w4a16_dq":
         bytes_eff = qg.int4_dq_packed_bytes(n, k)
+    elif op == "wn_a16":
+        bytes_eff = qg.intn_packed_bytes(n, k, args.bits)
     else:
         bytes_eff = qg.int4_packed_bytes(n, k)
     if args.calibrate_copy:
@@ -147,13 +151,18 @@ def main() -> int:
         else:
             w_cpu, x_cpu = si.int4_weight(n, k, n ^ k), si.activation(m, k, 9100 + m)
         split = args.split or qg.default_split_k(m, n, k)
-        quant = qg.quantize_int4_g32_dq if op == "w4a16_dq" else qg.quantize_int4_g32
-        packed0 = quant(w_cpu.to(dev))
+        if op == "w4a16_dq":
+            packed0 = qg.quantize_int4_g32_dq(w_cpu.to(dev))
+        elif op == "wn_a16":
+            packed0 = qg.quantize_intn_g32(w_cpu.to(dev), args.bits)
+        else:
+            packed0 = qg.quantize_int4_g32(w_cpu.to(dev))
         packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
         x = x_cpu.to(dev)
         ws = torch.empty(max(qg.workspace_bytes(m, n, k, split), 1), dtype=torch.uint8, device=dev)
         fn = {"w4a16": qg.qgemm_w4a16, "w4a16_dq": qg.qgemm_w4a16_dq, "w4a8": qg.qgemm_w4a8,
-              "w4a8_g32": qg.qgemm_w4a8_g32}[op]
+              "w4a8_g32": qg.qgemm_w4a8_g32,
+              "wn_a16": lambda *a, **kw: qg.qgemm_wn_a16(*a[:3], args.bits, **kw)}[op]
 
         def call(i):
             fn(x, packs[i % copies], n, split_k=split, out=y, workspace=ws)
@@ -205,6 +214,7 @@ def main() -> int:
     kernel = "matrix-core GEMM" if (op == "w4a16" and m > 4) else "GEMV"
     label = {"w4a16": "W4A16 INT4-g32 asymmetric",
              "w4a16_dq": "W4A16 INT4-g32 asymmetric, uint8 scale codes x per-row fp16 step",
+             "wn_a16": f"W{args.bits}A16 INT{args.bits}-g32 asymmetric",
              "w4a8": "W4A8 INT4-g32 x per-row int8",
              "w4a8_g32": "W4A8 INT4-g32 x per-group-32 int8", "w8a16": "W8A16 INT8 per-channel"}[op]
     out = {
@@ -226,7 +236,9 @@ def main() -> int:
         "config": {
             "workload": f"{label} {kernel} {n}x{k} M={m}",
             "op": op, "n": n, "k": k, "m": m, "split_k": split, "bytes_eff_per_call": bytes_eff,
-            "codes_only_gbs": round((n * k / (1 if op == "w8a16" else 2)) / (us_call * 1e-6) / 1e9, 2),
+            **({"bits": args.bits} if op == "wn_a16" else {}),
+            "codes_only_gbs": round((n * k * {"w8a16": 8, "wn_a16": args.bits}.get(op, 4) / 8)
+                                    / (us_call * 1e-6) / 1e9, 2),
             "rotating_weight_copies": copies,
             "timing": f"{full} replays of a {chunk}-call HIP graph" + (f" + one of {rest}" if rest else "")
                       + ", events on its stream",
@@ -410,6 +422,11 @@ def cpu_baseline(args, oracle_inputs, y_gpu, bytes_eff):
 
         def run():
             return oracle.qgemm_w8a16(xb, wi8, sb, threads=threads)
+    elif args.op == "wn_a16":
+        codes, scales, zeros, _ = oracle.quantize_intn_g32(si.bf16_bits(w_cpu), args.bits)
+
+        def run():
+            return oracle.qgemm_w4a16(xb, codes, scales, zeros, threads=threads)
     elif args.op == "w4a16_dq":
         codes, scode, sstep, zeros, _ = oracle.quantize_int4_g32_dq(si.bf16_bits(w_cpu))
 

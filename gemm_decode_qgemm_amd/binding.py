@@ -44,6 +44,9 @@ def _load() -> ctypes.CDLL:
         "qg_default_split_k": (I32, [I64, I64, I64]),
         "qg_workspace_bytes": (I64, [I64, I64, I64, I32]),
         "qg_int4_dq_packed_bytes": (I64, [I64, I64]),
+        "qg_intn_packed_bytes": (I64, [I64, I64, I32]),
+        "quantize_intn_g32": (I32, [P, I64, I64, I32, P, I64, P, P]),
+        "qgemm_wn_a16": (I32, [P, I64, I64, I32, P, I64, I64, P, I32, I32, P, I64, P]),
         "quantize_int4_g32": (I32, [P, I64, I64, P, I64, P, P]),
         "quantize_int4_g32_dq": (I32, [P, I64, I64, P, I64, P, P]),
         "qgemm_w4a16_dq": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
@@ -103,6 +106,12 @@ def int4_dq_packed_bytes(n: int, k: int) -> int:
     return v
 
 
+def intn_packed_bytes(n: int, k: int, bits: int) -> int:
+    v = int(lib.qg_intn_packed_bytes(n, k, bits))
+    _check(min(v, 0), "qg_intn_packed_bytes")
+    return v
+
+
 def default_split_k(m: int, n: int, k: int) -> int:
     v = int(lib.qg_default_split_k(m, n, k))
     _check(min(v, 0), "qg_default_split_k")
@@ -140,6 +149,20 @@ def quantize_int4_g32_dq(w: torch.Tensor, status: torch.Tensor | None = None,
     st = lib.quantize_int4_g32_dq(w.data_ptr(), n, k, out.data_ptr(), out.numel(), _ptr(status),
                                   _stream(w.device))
     _check(st, "quantize_int4_g32_dq")
+    return out
+
+
+def quantize_intn_g32(w: torch.Tensor, bits: int, status: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 [n, k] -> packed INT5 / INT6 g32 weight (uint8; bits = 5 or 6)."""
+    _dev(w, "w", torch.bfloat16, 2)
+    n, k = w.shape
+    nbytes = intn_packed_bytes(n, k, bits)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    st = lib.quantize_intn_g32(w.data_ptr(), n, k, bits, out.data_ptr(), out.numel(), _ptr(status),
+                               _stream(w.device))
+    _check(st, "quantize_intn_g32")
     return out
 
 
@@ -206,6 +229,20 @@ def qgemm_w4a16_dq(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_k: in
     st = lib.qgemm_w4a16_dq(x.data_ptr(), m, k, packed.data_ptr(), packed.numel(), n, y.data_ptr(),
                             yd, split_k, _ptr(ws), ws_bytes, _stream(x.device))
     _check(st, "qgemm_w4a16_dq")
+    return y
+
+
+def qgemm_wn_a16(x: torch.Tensor, packed: torch.Tensor, n: int, bits: int, *, split_k: int = 0,
+                 out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y[1, n] = x . dequant(W)^T for a packed INT5 / INT6 g32 weight (M = 1)."""
+    _dev(x, "x", torch.bfloat16, 2)
+    m, k = x.shape
+    y, yd = _out(m, n, out_dtype, x.device, out)
+    ws, ws_bytes = _workspace(m, n, k, split_k, x.device, workspace)
+    st = lib.qgemm_wn_a16(x.data_ptr(), m, k, bits, packed.data_ptr(), packed.numel(), n, y.data_ptr(),
+                          yd, split_k, _ptr(ws), ws_bytes, _stream(x.device))
+    _check(st, "qgemm_wn_a16")
     return y
 
 

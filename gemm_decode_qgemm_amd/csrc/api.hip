@@ -22,6 +22,10 @@ hipError_t launch_w4a16_gemv32_dq(int m, const void* x, const void* packed, int 
                                   int y_f32, float* partial, int split, hipStream_t stream);
 hipError_t launch_w4a16_gemv_mx4_dq(int m, const void* x, const void* packed, int n, int k, void* y,
                                     int y_f32, float* partial, int split, hipStream_t stream);
+hipError_t launch_quantize_intn_g32(const void* w, int64_t n, int64_t k, int bits, void* packed,
+                                    uint32_t* status, hipStream_t stream);
+hipError_t launch_wn_a16_gemv32(int bits, const void* x, const void* packed, int n, int k, void* y,
+                                int y_f32, float* partial, int split, hipStream_t stream);
 hipError_t launch_quantize_int8_rowwise(const void* w, int64_t n, int64_t k, int8_t* q,
                                         void* scales, uint32_t* status, hipStream_t stream);
 hipError_t launch_w4a16_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
@@ -145,6 +149,7 @@ const char* qg_status_string(int32_t s) {
     case QG_E_ALIGN: return "data pointers must be 16-byte aligned";
     case QG_E_DTYPE: return "y_dtype must be QG_BF16 or QG_F32";
     case QG_E_HIP: return "a HIP launch failed";
+    case QG_E_BITS: return "bits must be 5 or 6";
     default: return "unknown qgemm status";
   }
 }
@@ -160,6 +165,14 @@ int64_t qg_int4_dq_packed_bytes(int64_t n, int64_t k) {
   if (st != QG_OK) return st;
   return ((n + QG_TILE_ROWS - 1) / QG_TILE_ROWS) *
          (QG_DQ_HEAD_BYTES + (k / QG_TILE_K) * (int64_t)QG_DQ_TILE_BYTES);
+}
+
+int64_t qg_intn_packed_bytes(int64_t n, int64_t k, int32_t bits) {
+  int32_t st = check_nk(n, k);
+  if (st != QG_OK) return st;
+  if (bits != 5 && bits != 6) return QG_E_BITS;
+  return ((n + QG_TILE_ROWS - 1) / QG_TILE_ROWS) * (k / QG_TILE_K) *
+         (int64_t)(8192 + 2048 * (bits - 4) + 1536);
 }
 
 int32_t qg_default_split_k(int64_t m, int64_t n, int64_t k) {
@@ -197,6 +210,18 @@ int32_t quantize_int4_g32_dq(const void* w_bf16, int64_t n, int64_t k, void* pac
   if (!aligned16(w_bf16) || !aligned16(packed) || ((uintptr_t)status_dev & 3u)) return QG_E_ALIGN;
   return hip_status(qg::launch_quantize_int4_g32_dq(w_bf16, n, k, packed, status_dev,
                                                     static_cast<hipStream_t>(stream)));
+}
+
+int32_t quantize_intn_g32(const void* w_bf16, int64_t n, int64_t k, int32_t bits, void* packed,
+                          int64_t packed_bytes, uint32_t* status_dev, void* stream) {
+  if (!w_bf16 || !packed) return QG_E_NULL;
+  int32_t st = check_nk(n, k);
+  if (st != QG_OK) return st;
+  if (bits != 5 && bits != 6) return QG_E_BITS;
+  if (packed_bytes < qg_intn_packed_bytes(n, k, bits)) return QG_E_BUFFER;
+  if (!aligned16(w_bf16) || !aligned16(packed) || ((uintptr_t)status_dev & 3u)) return QG_E_ALIGN;
+  return hip_status(qg::launch_quantize_intn_g32(w_bf16, n, k, bits, packed, status_dev,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 int32_t quantize_int8_rowwise(const void* w_bf16, int64_t n, int64_t k, int8_t* q,
@@ -276,6 +301,31 @@ int32_t qgemm_w4a16_dq(const void* x_bf16, int64_t m, int64_t k, const void* pac
   else
     st = hip_status(qg::launch_w4a16_gemv32_dq((int)m, x_bf16, packed, (int)n, (int)k, y,
                                                y_dtype == QG_F32, partial, split, s));
+  if (st != QG_OK || split == 1) return st;
+  return hip_status(qg::launch_splitk_reduce(partial, split, m * n, y, y_dtype == QG_F32, s));
+}
+
+int32_t qgemm_wn_a16(const void* x_bf16, int64_t m, int64_t k, int32_t bits, const void* packed,
+                     int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype, int32_t split_k,
+                     void* ws, int64_t ws_bytes, void* stream) {
+  if (!x_bf16 || !packed || !y) return QG_E_NULL;
+  int32_t st = check_mnk(m, n, k);
+  if (st != QG_OK) return st;
+  if (bits != 5 && bits != 6) return QG_E_BITS;
+  if (y_dtype != QG_BF16 && y_dtype != QG_F32) return QG_E_DTYPE;
+  if (m > 1) return QG_E_M_RANGE;
+  int32_t split;
+  st = resolve_split(m, n, k, split_k, &split);
+  if (st != QG_OK) return st;
+  if (packed_bytes < qg_intn_packed_bytes(n, k, bits)) return QG_E_BUFFER;
+  const int64_t need_ws = split > 1 ? (int64_t)split * m * n * 4 : 0;
+  if (need_ws > 0 && (!ws || ws_bytes < need_ws)) return ws ? QG_E_BUFFER : QG_E_NULL;
+  if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || (ws && !aligned16(ws)))
+    return QG_E_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
+  st = hip_status(qg::launch_wn_a16_gemv32(bits, x_bf16, packed, (int)n, (int)k, y, y_dtype == QG_F32,
+                                           partial, split, s));
   if (st != QG_OK || split == 1) return st;
   return hip_status(qg::launch_splitk_reduce(partial, split, m * n, y, y_dtype == QG_F32, s));
 }

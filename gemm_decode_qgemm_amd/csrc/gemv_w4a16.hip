@@ -333,6 +333,151 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv32_kernel(
   }
 }
 
+// ---- INT5 / INT6 (the pages' INT5/INT6 family), M = 1 ----------------------
+// Tiles of 64 rows x 256 k: the low 4 bits of every code exactly as the INT4
+// layout, then HB = bits - 4 high-bit planes (a (4 HB)-byte chunk per group
+// and row at 8192 + (j*64 + r)*4*HB), fp16 scales (row r at +16r) and one
+// zero-point byte per group (row r at +8r).  The plane's bit order puts a
+// pair's high bits where (dword >> 4i) & 0x000F000F puts its low bits, four
+// places lower: INT5: (plane >> (4d + i)) & 0x00010001; INT6: (plane dword
+// d/2 >> (8(d%2) + 2i)) & 0x00030003.  Codes up to 63 keep 128 + q exact in
+// bf16, so the arithmetic is the INT4 GEMV's.
+template <int HB>
+struct WnRegs {
+  u32x4_t c[2];        // low-nibble chunks of groups 2lg, 2lg + 1
+  uint32_t hp[2][HB];  // their high planes
+  uint32_t sc;         // two fp16 scales
+  uint32_t zb;         // two zero-point bytes
+};
+
+template <int HB>
+__device__ __forceinline__ int wn_tile_bytes() { return 8192 + 2048 * HB + 1536; }
+
+template <int HB>
+__device__ __forceinline__ void load_wn_half(WnRegs<HB>& r, const uint8_t* tile, int half, int lg, int row) {
+  constexpr int kS = 8192 + 2048 * HB, kZ = kS + 1024;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int g = 4 * half + 2 * lg + j;
+    r.c[j] = load_stream<true>(reinterpret_cast<const u32x4_t*>(tile + (g * kTileRows + row) * 16));
+    if constexpr (HB == 1) {
+      r.hp[j][0] = load_stream<true>(reinterpret_cast<const uint32_t*>(tile + 8192 + (g * kTileRows + row) * 4));
+    } else {
+      const u32x2_t h = load_stream<true>(reinterpret_cast<const u32x2_t*>(tile + 8192 + (g * kTileRows + row) * 8));
+      r.hp[j][0] = h.x;
+      r.hp[j][1] = h.y;
+    }
+  }
+  // temporal: the other half tile's metadata shares these lines
+  r.sc = load_stream<false>(reinterpret_cast<const uint32_t*>(tile + kS + row * 16 + 8 * half + 4 * lg));
+  r.zb = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + kZ + row * 8 + 4 * half + 2 * lg));
+}
+
+template <int HB>
+__device__ __forceinline__ uint32_t wide_pair(uint32_t lo_dword, const uint32_t (&hp)[HB], int d, int i,
+                                              uint32_t mask_s, uint32_t magic_v) {
+  const uint32_t lo = nibble_pair_bf16(lo_dword, i, mask_s, magic_v);   // (128 + low) pair
+  uint32_t hi;
+  if constexpr (HB == 1)
+    hi = (hp[0] >> (4 * d + i)) & 0x00010001u;
+  else
+    hi = (hp[d >> 1] >> (8 * (d & 1) + 2 * i)) & 0x00030003u;
+  return lo | (hi << 4);
+}
+
+template <int HB, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void wn_a16_gemv32_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
+    void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
+  __shared__ float red[WAVES * 64];
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15;
+  const int lg = lane >> 5;
+  const int wave = wave_id_uniform();
+  const int rb = blockIdx.x >> 1;
+  const int row = 32 * (blockIdx.x & 1) + (lane & 31);
+  const int kt_count = k >> 8;
+  int t0, t1;
+  split_range(kt_count, split, blockIdx.y, t0, t1);
+  const int tb = wn_tile_bytes<HB>();
+  const uint8_t* tiles = packed + (size_t)rb * kt_count * tb;
+  const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
+  const uint32_t mask_s = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+  uint32_t magic_v = 0x43004300u;
+  asm volatile("" : "+v"(magic_v));
+  uint32_t ones_v = 0x3f803f80u;
+  asm volatile("" : "+v"(ones_v));
+
+  float acc = 0.0f;
+  for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {
+    WnRegs<HB> r;
+    load_wn_half<HB>(r, tiles + (size_t)(hs >> 1) * tb, hs & 1, lg, row);
+    const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(x32 + (size_t)hs * 64 + 32 * lg + 2 * li);
+    float p = dot2_bf16(xv.x, ones_v, 0.0f);
+    p = dot2_bf16(xv.y, ones_v, p);
+    p += dpp_mov<0xB1>(p);
+    p += dpp_mov<0x4E>(p);
+    p += dpp_mov<0x141>(p);
+    const float xq = p;
+    const float zb0 = (float)((r.zb & 0xffu) | 0x80u);          // 128 + zp (zp <= 63)
+    const float zb1 = (float)(((r.zb >> 8) & 0xffu) | 0x80u);
+    const float s0 = fp16_to_f32(r.sc & 0xffffu);
+    const float s1 = fp16_to_f32(r.sc >> 16);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const u32x4_t cv = r.c[jj];
+      const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
+      uint32_t pr[16];
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[4 * d + i] = wide_pair<HB>(cw[d], r.hp[jj], d, i, mask_s, magic_v);
+      const float xg = jj == 0 ? dpp_mov<0x150>(xq) : dpp_mov<0x158>(xq);
+      float d0 = -(jj == 0 ? zb0 : zb1) * xg, d1 = 0.0f;
+      if (jj == 0)
+        group_dot_2r<0>(d0, d1, xv, pr);
+      else
+        group_dot_2r<1>(d0, d1, xv, pr);
+      acc = __builtin_fmaf(jj == 0 ? s0 : s1, d0 + d1, acc);
+    }
+  }
+
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < 32) {
+    float v = 0.0f;
+    for (int w = 0; w < WAVES; ++w) {
+      v += red[w * 64 + t];
+      v += red[w * 64 + t + 32];
+    }
+    const int col = rb * kTileRows + 32 * (blockIdx.x & 1) + t;
+    if (col < n) {
+      if (partial != nullptr)
+        partial[(size_t)blockIdx.y * n + col] = v;
+      else if (y_f32)
+        static_cast<float*>(y)[col] = v;
+      else
+        static_cast<uint16_t*>(y)[col] = (uint16_t)f32_to_bf16_rne(v);
+    }
+  }
+}
+
+hipError_t launch_wn_a16_gemv32(int bits, const void* x, const void* packed, int n, int k, void* y,
+                                int y_f32, float* partial, int split, hipStream_t stream) {
+  const int rbs = (n + kTileRows - 1) / kTileRows;
+  const dim3 grid(2 * rbs, split), block(16 * 64);
+  if (bits == 5)
+    hipLaunchKernelGGL((wn_a16_gemv32_kernel<1, 16>), grid, block, 0, stream, static_cast<const uint16_t*>(x),
+                       static_cast<const uint8_t*>(packed), n, k, y, y_f32, partial, split);
+  else if (bits == 6)
+    hipLaunchKernelGGL((wn_a16_gemv32_kernel<2, 16>), grid, block, 0, stream, static_cast<const uint16_t*>(x),
+                       static_cast<const uint8_t*>(packed), n, k, y, y_f32, partial, split);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 // Second split-K pass: y = sum over s (ascending) of partial[s], no atomics.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial,
                                                             int split, int64_t mn,

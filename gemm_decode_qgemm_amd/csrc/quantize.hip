@@ -45,13 +45,14 @@ __device__ uint32_t fp16_scale_covering(double r) { return fp16_covering(r, 15.0
 
 // Zero point and codes of a group for scale s: zp = clamp(rint(-lo/s), 0, 15),
 // q = clamp(rint(v/s) + zp, 0, 15) (IEEE division, round half to even).
-__device__ __forceinline__ uint32_t group_codes(const float (&v)[32], float lo, float s, uint32_t (&q)[32]) {
+__device__ __forceinline__ uint32_t group_codes(const float (&v)[32], float lo, float s, uint32_t (&q)[32],
+                                                float top = 15.0f) {
   float z = rintf(-lo / s);
-  z = z < 0.0f ? 0.0f : (z > 15.0f ? 15.0f : z);
+  z = z < 0.0f ? 0.0f : (z > top ? top : z);
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     float t = rintf(v[i] / s) + z;
-    t = t < 0.0f ? 0.0f : (t > 15.0f ? 15.0f : t);
+    t = t < 0.0f ? 0.0f : (t > top ? top : t);
     q[i] = (uint32_t)t;
   }
   return (uint32_t)z;
@@ -316,6 +317,107 @@ hipError_t launch_quantize_int4_g32_dq(const void* w, int64_t n, int64_t k, void
   hipLaunchKernelGGL(quantize_int4_dq_kernel, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(w), n, k, static_cast<uint8_t*>(packed), block_bytes,
                      tiles);
+  return hipGetLastError();
+}
+
+// ---- INT5 / INT6 (the pages' INT5/INT6 family) ----------------------------
+// The INT4 reading with L = 2^bits - 1 steps: s = smallest fp16 with L*s >= r,
+// zp = clamp(rint(-lo/s), 0, L), q = clamp(rint(v/s) + zp, 0, L).  Layout:
+// the low 4 bits of each code as the INT4 tile, then HB = bits - 4 high-bit
+// planes, fp16 scales and one zero-point byte per group (tile of 8192 +
+// 2048 HB + 1536 bytes).  A plane chunk (4 HB bytes per group and row) holds,
+// for code dword d and pair p (k = 8d+2p even, 8d+2p+1 odd): INT5 the even
+// k's bit at 4d + p and the odd k's at 16 + 4d + p; INT6 in dword d/2 the
+// even k's two bits at 8(d%2) + 2p + b, the odd k's 16 higher.
+template <int HB>
+__global__ __launch_bounds__(256) void quantize_intn_g32_kernel(
+    const uint16_t* __restrict__ w, int64_t n, int64_t k, uint8_t* __restrict__ packed,
+    int64_t tiles, uint32_t* __restrict__ status) {
+  constexpr int L = (1 << (HB + 4)) - 1;
+  constexpr int64_t kTile = 8192 + 2048 * HB + 1536;
+  constexpr int kS = 8192 + 2048 * HB, kZ = kS + 1024;
+  const int64_t wave_global = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wave_global >= tiles) return;
+  const int64_t kt_count = k / kTileK;
+  const int64_t rb = wave_global / kt_count;
+  const int64_t kt = wave_global % kt_count;
+  const int r = threadIdx.x & 63;
+  const int64_t row = rb * kTileRows + r;
+  uint8_t* tile = packed + wave_global * kTile;
+
+  uint32_t flags = 0;
+  uint32_t sword[4] = {0, 0, 0, 0};
+  uint32_t zword[2] = {0, 0};
+  for (int j = 0; j < kGroupsPerTile; ++j) {
+    uint4 chunk = make_uint4(0, 0, 0, 0);
+    uint32_t plane[HB];
+#pragma unroll
+    for (int h = 0; h < HB; ++h) plane[h] = 0;
+    if (row < n) {
+      uint32_t wb[16];
+      load_group(w + row * k + kt * kTileK + j * 32, wb);
+      float v[32], lo, hi;
+      unpack_bf16x32(wb, v);
+      uint32_t q[32], sbits, zp;
+      if (!group_range(v, lo, hi)) {
+        sbits = 0x7e00u;
+        zp = 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) q[i] = 0;
+        flags |= QG_FLAG_NONFINITE;
+      } else {
+        const double rng = (double)hi - (double)lo;
+        if (rng == 0.0) {
+          sbits = 0x3c00u;
+        } else if (rng > (double)L * 65504.0) {
+          sbits = 0x7bffu;
+          flags |= QG_FLAG_OVERFLOW;
+        } else {
+          sbits = fp16_covering(rng, (double)L);
+        }
+        zp = group_codes(v, lo, fp16_to_f32(sbits), q, (float)L);
+      }
+      uint32_t lowq[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) lowq[i] = q[i] & 15u;
+      chunk = pack_chunk(lowq);
+#pragma unroll
+      for (int kl = 0; kl < 32; ++kl) {
+        const int d = kl >> 3, pp = (kl & 7) >> 1, odd = kl & 1;
+        if constexpr (HB == 1) {
+          plane[0] |= ((q[kl] >> 4) & 1u) << (16 * odd + 4 * d + pp);
+        } else {
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            plane[d >> 1] |= ((q[kl] >> (4 + b)) & 1u) << (16 * odd + 8 * (d & 1) + 2 * pp + b);
+        }
+      }
+      sword[j >> 1] |= sbits << (16 * (j & 1));
+      zword[j >> 2] |= zp << (8 * (j & 3));
+    }
+    *reinterpret_cast<uint4*>(tile + (j * kTileRows + r) * 16) = chunk;
+    if constexpr (HB == 1)
+      *reinterpret_cast<uint32_t*>(tile + 8192 + (j * kTileRows + r) * 4) = plane[0];
+    else
+      *reinterpret_cast<uint2*>(tile + 8192 + (j * kTileRows + r) * 8) = make_uint2(plane[0], plane[1]);
+  }
+  *reinterpret_cast<uint4*>(tile + kS + r * 16) = make_uint4(sword[0], sword[1], sword[2], sword[3]);
+  *reinterpret_cast<uint2*>(tile + kZ + r * 8) = make_uint2(zword[0], zword[1]);
+  if (flags != 0 && status != nullptr) atomicOr(status, flags);
+}
+
+hipError_t launch_quantize_intn_g32(const void* w, int64_t n, int64_t k, int bits, void* packed,
+                                    uint32_t* status, hipStream_t stream) {
+  const int64_t tiles = ((n + kTileRows - 1) / kTileRows) * (k / kTileK);
+  const dim3 grid((unsigned)((tiles + 3) / 4)), block(256);
+  if (bits == 5)
+    hipLaunchKernelGGL(quantize_intn_g32_kernel<1>, grid, block, 0, stream, static_cast<const uint16_t*>(w),
+                       n, k, static_cast<uint8_t*>(packed), tiles, status);
+  else if (bits == 6)
+    hipLaunchKernelGGL(quantize_intn_g32_kernel<2>, grid, block, 0, stream, static_cast<const uint16_t*>(w),
+                       n, k, static_cast<uint8_t*>(packed), tiles, status);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

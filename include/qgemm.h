@@ -92,7 +92,8 @@ enum qg_status {
     QG_E_BUFFER = -6,      /* packed_bytes or ws_bytes too small */
     QG_E_ALIGN = -7,       /* a data pointer is not 16-byte aligned */
     QG_E_DTYPE = -8,       /* y_dtype is not QG_BF16 / QG_F32 */
-    QG_E_HIP = -9          /* a HIP launch failed */
+    QG_E_HIP = -9,         /* a HIP launch failed */
+    QG_E_BITS = -10        /* a code width other than 5 or 6 (INT5 / INT6 entry points) */
 };
 
 /* status_dev flag bits */
@@ -202,6 +203,42 @@ int32_t quantize_int4_g32_dq(const void *w_bf16, int64_t n, int64_t k, void *pac
 int32_t qgemm_w4a16_dq(const void *x_bf16, int64_t m, int64_t k, const void *packed,
                        int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
                        int32_t split_k, void *ws, int64_t ws_bytes, void *stream);
+
+/* ---- INT5 / INT6 group-32 (the pages' INT5/INT6 quantized-GEMM family) ---
+ * Executorch pull request #23737 lists INT5 and INT6 layers next to INT4
+ * (INT6: 4096x5376, 5376x21504, 6656x19968, 1024x6656); the quantizer
+ * recipe is [P1] `_packed_with_dense` with 2^bits - 1 steps:
+ *   s  = the smallest positive fp16 with L*s >= r, L = 31 (INT5) or 63 (INT6)
+ *   zp = clamp(rint(-lo / s), 0, L);  q = clamp(rint(v / s) + zp, 0, L)
+ * (lo, hi, r as in quantize_int4_g32).  Packed layout: tiles of 64 rows x
+ * 256 k, row-block major, 8192 + 2048*hb + 1536 bytes (hb = bits - 4; 11776
+ * for INT5, 13824 for INT6):
+ *   [0, 8192)             the low 4 bits of every code, exactly as version 1
+ *   [8192, +2048 hb)      high-bit planes: the (4 hb)-byte chunk of (group j,
+ *                         row r) at 8192 + (j*64 + r)*4*hb.  For code dword d
+ *                         and pair p (k = 8d+2p even, 8d+2p+1 odd) INT5 keeps
+ *                         the even k's bit at 4d + p and the odd k's at
+ *                         16 + 4d + p of the LE chunk; INT6 keeps in LE dword
+ *                         d/2 the even k's bits b = 0, 1 at 8(d%2) + 2p + b,
+ *                         the odd k's 16 higher
+ *   [.., +1024)           fp16 scales: row r's 8 at +16r, group j at +2j
+ *   [.., +512)            zero points, one byte each: row r at +8r, group j at +j
+ * Rows n >= N of the last row block are zero. */
+int64_t qg_intn_packed_bytes(int64_t n, int64_t k, int32_t bits);
+
+/* bf16 [n, k] -> the INT5 / INT6 packed weight above.  Arguments, status
+ * flags (per group, as quantize_int4_g32, with L*65504 for the overflow) and
+ * errors as quantize_int4_g32, plus QG_E_BITS. */
+int32_t quantize_intn_g32(const void *w_bf16, int64_t n, int64_t k, int32_t bits, void *packed,
+                          int64_t packed_bytes, uint32_t *status_dev, void *stream);
+
+/* y[1, n] = x . dequant(W)^T for an INT5 / INT6 packed weight (M = 1 in this
+ * version: QG_E_M_RANGE above), dequantized in registers, fp32 accumulation.
+ * Arguments, workspace (qg_workspace_bytes) and errors as qgemm_w4a16, with
+ * packed_bytes checked against qg_intn_packed_bytes, plus QG_E_BITS. */
+int32_t qgemm_wn_a16(const void *x_bf16, int64_t m, int64_t k, int32_t bits, const void *packed,
+                     int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype, int32_t split_k,
+                     void *ws, int64_t ws_bytes, void *stream);
 
 /* ---- qgemm_w8a16 ---------------------------------------------------------
  * [P3] `WeightOnlyInt8Linear.forward`: y[m, n] = (sum_k x[m,k] * W[n,k]) *

@@ -20,6 +20,7 @@ HEADER = os.path.join(ROOT, "include", "qgemm.h")
 LIB = os.path.join(ROOT, "gemm_decode_qgemm_amd", "libqgemm.so")
 
 OK, E_NULL, E_SHAPE, E_K, E_M, E_SPLIT, E_BUF, E_ALIGN, E_DTYPE, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+E_BITS = -10
 A = 0x10000          # a fake, 16-byte aligned "device" address (never dereferenced)
 U = 0x10008          # 8-byte aligned only
 
@@ -35,6 +36,9 @@ def lib():
         "qg_default_split_k": (I32, [I64, I64, I64]),
         "qg_workspace_bytes": (I64, [I64, I64, I64, I32]),
         "qg_int4_dq_packed_bytes": (I64, [I64, I64]),
+        "qg_intn_packed_bytes": (I64, [I64, I64, I32]),
+        "quantize_intn_g32": (I32, [P, I64, I64, I32, P, I64, P, P]),
+        "qgemm_wn_a16": (I32, [P, I64, I64, I32, P, I64, I64, P, I32, I32, P, I64, P]),
         "quantize_int4_g32": (I32, [P, I64, I64, P, I64, P, P]),
         "quantize_int4_g32_dq": (I32, [P, I64, I64, P, I64, P, P]),
         "qgemm_w4a16_dq": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
@@ -64,7 +68,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in (OK, E_NULL, E_SHAPE, E_K, E_M, E_SPLIT, E_BUF, E_ALIGN, E_DTYPE, E_HIP):
+    for code in (OK, E_NULL, E_SHAPE, E_K, E_M, E_SPLIT, E_BUF, E_ALIGN, E_DTYPE, E_HIP, E_BITS):
         s = lib.qg_status_string(code).decode()
         assert s and s != "unknown qgemm status"
     assert "multiple of 256" in lib.qg_status_string(E_K).decode()
@@ -82,6 +86,11 @@ def test_packed_bytes_formula(lib):
     assert lib.qg_int4_dq_packed_bytes(257, 512) == 5 * (128 + 2 * 8960)
     assert lib.qg_int4_dq_packed_bytes(64, 300) == E_K
     assert lib.qg_int4_dq_packed_bytes(64, 0) == E_SHAPE
+    # INT5 / INT6: tiles of 8192 + 2048 * (bits - 4) + 1536 bytes
+    assert lib.qg_intn_packed_bytes(6656, 19968, 6) == 104 * 78 * 13824
+    assert lib.qg_intn_packed_bytes(257, 512, 5) == 5 * 2 * 11776
+    assert lib.qg_intn_packed_bytes(64, 256, 4) == E_BITS
+    assert lib.qg_intn_packed_bytes(64, 300, 6) == E_K
 
 
 def test_split_rule_one_k_tile_per_split(lib):
@@ -187,6 +196,25 @@ def test_qgemm_w8a16_validates_before_launching(lib, args, expect):
 ])
 def test_quantize_int4_validates_before_launching(lib, args, expect):
     assert lib.quantize_int4_g32(*args) == expect
+
+
+def test_intn_entry_points_validate_before_launching(lib):
+    q = lib.quantize_intn_g32
+    assert q(None, 64, 256, 6, A, 1 << 20, None, None) == E_NULL
+    assert q(A, 64, 256, 7, A, 1 << 20, None, None) == E_BITS
+    assert q(A, 64, 300, 6, A, 1 << 20, None, None) == E_K
+    assert q(A, 64, 256, 6, A, 13823, None, None) == E_BUF
+    assert q(A, 64, 256, 5, A, 11776, U + 2, None) == E_ALIGN
+    g = lib.qgemm_wn_a16
+    assert g(None, 1, 256, 6, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_NULL
+    assert g(A, 1, 256, 4, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_BITS
+    assert g(A, 2, 256, 6, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
+    assert g(A, 1, 288, 6, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_K
+    assert g(A, 1, 256, 6, A, 1 << 20, 64, A, 2, 0, None, 0, None) == E_DTYPE
+    assert g(A, 1, 768, 6, A, 1 << 20, 64, A, 0, 4, A, 1 << 20, None) == E_SPLIT
+    assert g(A, 1, 256, 5, A, 11775, 64, A, 0, 0, None, 0, None) == E_BUF
+    assert g(A, 1, 4096, 6, A, 1 << 20, 64, A, 0, 4, None, 0, None) == E_NULL   # workspace missing
+    assert g(U, 1, 256, 6, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_ALIGN
 
 
 def test_quantize_int4_dq_validates_before_launching(lib):
