@@ -334,55 +334,13 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv32_kernel(
 }
 
 // ---- INT5 / INT6 (the pages' INT5/INT6 family), M = 1 ----------------------
-// Tiles of 64 rows x 256 k: the low 4 bits of every code exactly as the INT4
-// layout, then HB = bits - 4 high-bit planes (a (4 HB)-byte chunk per group
-// and row at 8192 + (j*64 + r)*4*HB), fp16 scales (row r at +16r) and one
-// zero-point byte per group (row r at +8r).  The plane's bit order puts a
-// pair's high bits where (dword >> 4i) & 0x000F000F puts its low bits, four
-// places lower: INT5: (plane >> (4d + i)) & 0x00010001; INT6: (plane dword
-// d/2 >> (8(d%2) + 2i)) & 0x00030003.  Codes up to 63 keep 128 + q exact in
-// bf16, so the arithmetic is the INT4 GEMV's.
+// Layout and pair extraction: WnLayout (w4_common.h).  The low nibbles go
+// through nibble_pair_bf16 as for INT4, the high bits are ORed in four places
+// up; the arithmetic is then the INT4 GEMV's (128 + q stays exact for q <= 63).
 template <int HB>
-struct WnRegs {
-  u32x4_t c[2];        // low-nibble chunks of groups 2lg, 2lg + 1
-  uint32_t hp[2][HB];  // their high planes
-  uint32_t sc;         // two fp16 scales
-  uint32_t zb;         // two zero-point bytes
-};
-
-template <int HB>
-__device__ __forceinline__ int wn_tile_bytes() { return 8192 + 2048 * HB + 1536; }
-
-template <int HB>
-__device__ __forceinline__ void load_wn_half(WnRegs<HB>& r, const uint8_t* tile, int half, int lg, int row) {
-  constexpr int kS = 8192 + 2048 * HB, kZ = kS + 1024;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int g = 4 * half + 2 * lg + j;
-    r.c[j] = load_stream<true>(reinterpret_cast<const u32x4_t*>(tile + (g * kTileRows + row) * 16));
-    if constexpr (HB == 1) {
-      r.hp[j][0] = load_stream<true>(reinterpret_cast<const uint32_t*>(tile + 8192 + (g * kTileRows + row) * 4));
-    } else {
-      const u32x2_t h = load_stream<true>(reinterpret_cast<const u32x2_t*>(tile + 8192 + (g * kTileRows + row) * 8));
-      r.hp[j][0] = h.x;
-      r.hp[j][1] = h.y;
-    }
-  }
-  // temporal: the other half tile's metadata shares these lines
-  r.sc = load_stream<false>(reinterpret_cast<const uint32_t*>(tile + kS + row * 16 + 8 * half + 4 * lg));
-  r.zb = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + kZ + row * 8 + 4 * half + 2 * lg));
-}
-
-template <int HB>
-__device__ __forceinline__ uint32_t wide_pair(uint32_t lo_dword, const uint32_t (&hp)[HB], int d, int i,
-                                              uint32_t mask_s, uint32_t magic_v) {
-  const uint32_t lo = nibble_pair_bf16(lo_dword, i, mask_s, magic_v);   // (128 + low) pair
-  uint32_t hi;
-  if constexpr (HB == 1)
-    hi = (hp[0] >> (4 * d + i)) & 0x00010001u;
-  else
-    hi = (hp[d >> 1] >> (8 * (d & 1) + 2 * i)) & 0x00030003u;
-  return lo | (hi << 4);
+__device__ __forceinline__ uint32_t wide_pair(const WnRegs<HB>& r, int jj, int d, int i, uint32_t mask_s,
+                                              uint32_t magic_v) {
+  return nibble_pair_bf16(r.c[jj][d], i, mask_s, magic_v) | (WnLayout<HB>::high(r, jj, d, i) << 4);
 }
 
 template <int HB, int WAVES>
@@ -399,8 +357,8 @@ __global__ __launch_bounds__(WAVES * 64) void wn_a16_gemv32_kernel(
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
-  const int tb = wn_tile_bytes<HB>();
-  const uint8_t* tiles = packed + (size_t)rb * kt_count * tb;
+  using L = WnLayout<HB>;
+  const uint8_t* tiles = packed + (size_t)rb * kt_count * L::kTile;
   const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
   const uint32_t mask_s = __builtin_amdgcn_readfirstlane(0x000F000Fu);
   uint32_t magic_v = 0x43004300u;
@@ -411,7 +369,7 @@ __global__ __launch_bounds__(WAVES * 64) void wn_a16_gemv32_kernel(
   float acc = 0.0f;
   for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {
     WnRegs<HB> r;
-    load_wn_half<HB>(r, tiles + (size_t)(hs >> 1) * tb, hs & 1, lg, row);
+    L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
     const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(x32 + (size_t)hs * 64 + 32 * lg + 2 * li);
     float p = dot2_bf16(xv.x, ones_v, 0.0f);
     p = dot2_bf16(xv.y, ones_v, p);
@@ -425,13 +383,11 @@ __global__ __launch_bounds__(WAVES * 64) void wn_a16_gemv32_kernel(
     const float s1 = fp16_to_f32(r.sc >> 16);
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
-      const u32x4_t cv = r.c[jj];
-      const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
       uint32_t pr[16];
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[4 * d + i] = wide_pair<HB>(cw[d], r.hp[jj], d, i, mask_s, magic_v);
+        for (int i = 0; i < 4; ++i) pr[4 * d + i] = wide_pair<HB>(r, jj, d, i, mask_s, magic_v);
       const float xg = jj == 0 ? dpp_mov<0x150>(xq) : dpp_mov<0x158>(xq);
       float d0 = -(jj == 0 ? zb0 : zb1) * xg, d1 = 0.0f;
       if (jj == 0)

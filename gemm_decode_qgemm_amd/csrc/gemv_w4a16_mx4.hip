@@ -61,7 +61,7 @@ constexpr int kMx4PairBytes = 144;
 
 // 8 waves per SIMD (two 16-wave workgroups per CU) keep enough weight loads
 // in flight; the kernel fits the 64 VGPRs that allows without spilling.
-template <int M, int WAVES, bool DQ = false>
+template <int M, int WAVES, class L>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8))) void w4a16_gemv_mx4_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -77,7 +77,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8)))
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
-  using L = W4Layout<DQ>;
   float step;
   const uint8_t* tiles = L::tiles(packed, rb, kt_count, row, step);
   // Staging: lane l < 16 M copies k = 8 (l % 16) .. + 8 of x row l / 16.
@@ -98,7 +97,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8)))
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 
   for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {   // tile hs/2, half hs%2
-    Half32Regs r;
+    typename L::Regs r;
     L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
     u32x4_t xv = {0u, 0u, 0u, 0u};
     if (stager) xv = *reinterpret_cast<const u32x4_t*>(xsrc + (size_t)hs * 128);
@@ -131,22 +130,20 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8)))
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         xa[q] = *reinterpret_cast<const u32x4_t*>(slot + srd + 64 * jj + 16 * q);
-      const u32x4_t cv = r.c[jj];
-      const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
       f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
       // k-step t covers k = 4t..4t+3 of the group: code dword t/2, pairs
       // 2(t%2) and 2(t%2)+1; x dwords 2t, 2t+1.
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const u32x2_t b = {code_pair(cw[t >> 1], 2 * (t & 1), mask_s, magic_v),
-                           code_pair(cw[t >> 1], 2 * (t & 1) + 1, mask_s, magic_v)};
+        const u32x2_t b = {L::pair(r, jj, t >> 1, 2 * (t & 1), mask_s, magic_v),
+                           L::pair(r, jj, t >> 1, 2 * (t & 1) + 1, mask_s, magic_v)};
         const u32x4_t xq = xa[t >> 1];
         const u32x2_t a = (t & 1) ? u32x2_t{xq.z, xq.w} : u32x2_t{xq.x, xq.y};
         d = mfma_4x4x4(a, b, d);
       }
       const float s = L::scale(r.sc, jj, step);
       const f32x4_t xg = *reinterpret_cast<const f32x4_t*>(&xsum[wave][2 * lg + jj][0]);
-      const float zb = (float)(((r.zb >> (4 * jj)) & 15u) | 0x80u);   // 128 + zp
+      const float zb = (float)(L::zero(r, jj) | 0x80u);   // 128 + zp (zp <= 63)
 #pragma unroll
       for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(s, __builtin_fmaf(-zb, xg[m], d[m]), acc[m]);
     }
@@ -176,11 +173,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8)))
   }
 }
 
-template <int M, int WAVES, bool DQ>
+template <int M, int WAVES, class L>
 static hipError_t launch_mx4_t(const void* x, const void* packed, int n, int k, void* y, int y_f32,
                                float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_gemv_mx4_kernel<M, WAVES, DQ>), dim3(2 * rbs, split), dim3(WAVES * 64), 0,
+  hipLaunchKernelGGL((w4a16_gemv_mx4_kernel<M, WAVES, L>), dim3(2 * rbs, split), dim3(WAVES * 64), 0,
                      stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
                      n, k, y, y_f32, partial, split);
   return hipGetLastError();
@@ -190,7 +187,7 @@ hipError_t launch_w4a16_gemv_mx4(int m, const void* x, const void* packed, int n
                                  int y_f32, float* partial, int split, int waves,
                                  hipStream_t stream) {
 #define QG_MX4_CASE(MM, WW) \
-  if (m == MM && waves == WW) return launch_mx4_t<MM, WW, false>(x, packed, n, k, y, y_f32, partial, split, stream);
+  if (m == MM && waves == WW) return launch_mx4_t<MM, WW, W4Layout<false>>(x, packed, n, k, y, y_f32, partial, split, stream);
 #define QG_MX4_M(MM) QG_MX4_CASE(MM, 16)
   QG_MX4_M(2) QG_MX4_M(3) QG_MX4_M(4)
 #undef QG_MX4_M
@@ -202,11 +199,30 @@ hipError_t launch_w4a16_gemv_mx4(int m, const void* x, const void* packed, int n
 hipError_t launch_w4a16_gemv_mx4_dq(int m, const void* x, const void* packed, int n, int k, void* y,
                                     int y_f32, float* partial, int split, hipStream_t stream) {
   switch (m) {
-    case 2: return launch_mx4_t<2, 16, true>(x, packed, n, k, y, y_f32, partial, split, stream);
-    case 3: return launch_mx4_t<3, 16, true>(x, packed, n, k, y, y_f32, partial, split, stream);
-    case 4: return launch_mx4_t<4, 16, true>(x, packed, n, k, y, y_f32, partial, split, stream);
+    case 2: return launch_mx4_t<2, 16, W4Layout<true>>(x, packed, n, k, y, y_f32, partial, split, stream);
+    case 3: return launch_mx4_t<3, 16, W4Layout<true>>(x, packed, n, k, y, y_f32, partial, split, stream);
+    case 4: return launch_mx4_t<4, 16, W4Layout<true>>(x, packed, n, k, y, y_f32, partial, split, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// M = 2..4 on the INT5 / INT6 layout.
+template <int HB>
+static hipError_t launch_mx4_wn(int m, const void* x, const void* packed, int n, int k, void* y, int y_f32,
+                                float* partial, int split, hipStream_t stream) {
+  switch (m) {
+    case 2: return launch_mx4_t<2, 16, WnLayout<HB>>(x, packed, n, k, y, y_f32, partial, split, stream);
+    case 3: return launch_mx4_t<3, 16, WnLayout<HB>>(x, packed, n, k, y, y_f32, partial, split, stream);
+    case 4: return launch_mx4_t<4, 16, WnLayout<HB>>(x, packed, n, k, y, y_f32, partial, split, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_wn_a16_gemv_mx4(int bits, int m, const void* x, const void* packed, int n, int k, void* y,
+                                  int y_f32, float* partial, int split, hipStream_t stream) {
+  if (bits == 5) return launch_mx4_wn<1>(m, x, packed, n, k, y, y_f32, partial, split, stream);
+  if (bits == 6) return launch_mx4_wn<2>(m, x, packed, n, k, y, y_f32, partial, split, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace qg

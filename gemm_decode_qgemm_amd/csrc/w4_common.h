@@ -61,8 +61,12 @@ __device__ __forceinline__ void load_half32(Half32Regs& r, const uint8_t* tile, 
 template <bool DQ>
 struct W4Layout;
 
+// Also used by the matrix-instruction GEMV: `pair` gives the bf16 pair
+// (128 + q(8d+2e), 128 + q(8d+2e+1)) of group jj in plain C (it may feed a
+// matrix-instruction operand), `zero` the group's zero point.
 template <>
 struct W4Layout<false> {
+  using Regs = Half32Regs;
   static constexpr int kTile = kTileBytes;
   __device__ static const uint8_t* tiles(const uint8_t* packed, int rb, int kt_count, int, float& step) {
     step = 1.0f;
@@ -75,10 +79,15 @@ struct W4Layout<false> {
   __device__ static float scale(uint32_t sc, int jj, float) {
     return fp16_to_f32((sc >> (16 * jj)) & 0xffffu);
   }
+  __device__ static uint32_t pair(const Regs& r, int jj, int d, int e, uint32_t mask_s, uint32_t magic_v) {
+    return ((r.c[jj][d] >> (4 * e)) & mask_s) | magic_v;
+  }
+  __device__ static uint32_t zero(const Regs& r, int jj) { return (r.zb >> (4 * jj)) & 15u; }
 };
 
 template <>
 struct W4Layout<true> {
+  using Regs = Half32Regs;
   static constexpr int kTile = kDqTileBytes;
   __device__ static const uint8_t* tiles(const uint8_t* packed, int rb, int kt_count, int row, float& step) {
     const uint8_t* block = packed + (size_t)rb * (kDqHeadBytes + (size_t)kt_count * kDqTileBytes);
@@ -97,6 +106,67 @@ struct W4Layout<true> {
   __device__ static float scale(uint32_t sc, int jj, float step) {
     return (float)((sc >> (8 * jj)) & 0xffu) * step;
   }
+  __device__ static uint32_t pair(const Regs& r, int jj, int d, int e, uint32_t mask_s, uint32_t magic_v) {
+    return ((r.c[jj][d] >> (4 * e)) & mask_s) | magic_v;
+  }
+  __device__ static uint32_t zero(const Regs& r, int jj) { return (r.zb >> (4 * jj)) & 15u; }
+};
+
+// INT5 / INT6 (HB = bits - 4 high-bit planes).  Tiles of 64 rows x 256 k:
+// the low 4 bits of every code exactly as version 1, then the planes (a
+// (4 HB)-byte chunk per group and row at 8192 + (j*64 + r)*4*HB), fp16
+// scales (row r at +16r) and one zero-point byte per group (row r at +8r).
+// The plane's bit order puts a pair's high bits where (dword >> 4e) &
+// 0x000F000F puts its low bits, four places lower: INT5: (plane >> (4d + e))
+// & 0x00010001; INT6: (plane dword d/2 >> (8(d%2) + 2e)) & 0x00030003.
+// Codes up to 63 keep 128 + q exact in bf16.
+template <int HB>
+struct WnRegs {
+  u32x4_t c[2];        // low-nibble chunks of groups 2lg, 2lg + 1
+  uint32_t hp[2][HB];  // their high planes
+  uint32_t sc;         // two fp16 scales
+  uint32_t zb;         // two zero-point bytes
+};
+
+template <int HB>
+struct WnLayout {
+  using Regs = WnRegs<HB>;
+  static constexpr int kTile = 8192 + 2048 * HB + 1536;
+  static constexpr int kS = 8192 + 2048 * HB, kZ = kS + 1024;
+  __device__ static const uint8_t* tiles(const uint8_t* packed, int rb, int kt_count, int, float& step) {
+    step = 1.0f;
+    return packed + (size_t)rb * kt_count * kTile;
+  }
+  __device__ static void load(Regs& r, const uint8_t* tile, int half, int lg, int row) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int g = 4 * half + 2 * lg + j;
+      r.c[j] = load_stream<true>(reinterpret_cast<const u32x4_t*>(tile + (g * kTileRows + row) * 16));
+      if constexpr (HB == 1) {
+        r.hp[j][0] = load_stream<true>(reinterpret_cast<const uint32_t*>(tile + 8192 + (g * kTileRows + row) * 4));
+      } else {
+        const u32x2_t h = load_stream<true>(reinterpret_cast<const u32x2_t*>(tile + 8192 + (g * kTileRows + row) * 8));
+        r.hp[j][0] = h.x;
+        r.hp[j][1] = h.y;
+      }
+    }
+    // temporal, as in load_half32: the other half tile's metadata shares these lines
+    r.sc = load_stream<false>(reinterpret_cast<const uint32_t*>(tile + kS + row * 16 + 8 * half + 4 * lg));
+    r.zb = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + kZ + row * 8 + 4 * half + 2 * lg));
+  }
+  __device__ static float scale(uint32_t sc, int jj, float) {
+    return fp16_to_f32((sc >> (16 * jj)) & 0xffffu);
+  }
+  __device__ static uint32_t high(const Regs& r, int jj, int d, int e) {
+    if constexpr (HB == 1)
+      return (r.hp[jj][0] >> (4 * d + e)) & 0x00010001u;
+    else
+      return (r.hp[jj][d >> 1] >> (8 * (d & 1) + 2 * e)) & 0x00030003u;
+  }
+  __device__ static uint32_t pair(const Regs& r, int jj, int d, int e, uint32_t mask_s, uint32_t magic_v) {
+    return ((r.c[jj][d] >> (4 * e)) & mask_s) | magic_v | (high(r, jj, d, e) << 4);
+  }
+  __device__ static uint32_t zero(const Regs& r, int jj) { return (r.zb >> (8 * jj)) & 0xffu; }
 };
 
 // Split-K partition of `tiles` 256-k units into `split` contiguous ranges;

@@ -1,7 +1,7 @@
 """GPU parity of the INT5 / INT6 group-32 path (the INT5/INT6 family of
 executorch pull request #23737, quantized with the INT4 recipe of
 test_int4_quantized_gemm.py `_packed_with_dense` at 2^bits - 1 steps): the
-quantizer bit for bit and the M = 1 GEMV within tolerance, against the CPU
+quantizer bit for bit and the M = 1..4 GEMVs within tolerance, against the CPU
 oracle, through the C ABI.  Layer shapes: the INT6 ones the pull request lists
 (4096x5376, 5376x21504, 6656x19968, 1024x6656); INT5 runs two INT4/INT6 shapes
 (the pull request names the count of INT5 layers, not their shapes).
@@ -109,50 +109,54 @@ def test_quantize_intn_adversarial_groups(dev, bits):
 
 @pytest.mark.parametrize("bits", [5, 6])
 @pytest.mark.parametrize("n,k", [(768, 256), (257, 512), (1536, 512), (512, 8192)])
-def test_wn_a16_small_shapes(dev, bits, n, k):
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_wn_a16_small_shapes(dev, bits, n, k, m):
     w, codes, scales, zeros = _weight(n, k, bits, n + k + bits)
     packed = qg.quantize_intn_g32(w.to(dev), bits)
-    x = si.activation(1, k, 500 + n + bits)
+    x = si.activation(m, k, 500 + n + bits + m)
     ref = _ref(x, codes, scales, zeros)
     for dt in (torch.float32, torch.bfloat16):
         y = qg.qgemm_wn_a16(x.to(dev), packed, n, bits, out_dtype=dt)
-        assert y.shape == (1, n) and y.dtype == dt
-        assert_w16(y, ref, f"INT{bits} {n}x{k} {dt}")
+        assert y.shape == (m, n) and y.dtype == dt
+        assert_w16(y, ref, f"INT{bits} {n}x{k} M={m} {dt}")
 
 
 @pytest.mark.parametrize("bits,n,k", LAYERS)
 def test_wn_a16_layers(dev, bits, n, k):
-    print(f"qgemm_wn_a16 INT{bits} {n}x{k}", flush=True)
     w, codes, scales, zeros = _weight(n, k, bits, n ^ k)
     packed = qg.quantize_intn_g32(w.to(dev), bits)
-    x = si.activation(1, k, 900 + bits)
-    ref = _ref(x, codes, scales, zeros)
-    for dt in (torch.float32, torch.bfloat16):
-        assert_w16(qg.qgemm_wn_a16(x.to(dev), packed, n, bits, out_dtype=dt), ref, f"INT{bits} {n}x{k} {dt}")
+    for m in si.DECODE_M:
+        print(f"qgemm_wn_a16 INT{bits} {n}x{k} M={m}", flush=True)
+        x = si.activation(m, k, 900 + bits + m)
+        ref = _ref(x, codes, scales, zeros)
+        for dt in (torch.float32, torch.bfloat16):
+            assert_w16(qg.qgemm_wn_a16(x.to(dev), packed, n, bits, out_dtype=dt), ref,
+                       f"INT{bits} {n}x{k} M={m} {dt}")
 
 
 @pytest.mark.parametrize("bits", [5, 6])
-def test_wn_a16_every_split_uneven(dev, bits):
+@pytest.mark.parametrize("m", [1, 4])
+def test_wn_a16_every_split_uneven(dev, bits, m):
     n, k = 257, 6656
     w, codes, scales, zeros = _weight(n, k, bits, 77)
     packed = qg.quantize_intn_g32(w.to(dev), bits)
-    x = si.activation(1, k, 33)
+    x = si.activation(m, k, 33 + m)
     ref = _ref(x, codes, scales, zeros)
     for split in si.SPLITS:
         y = qg.qgemm_wn_a16(x.to(dev), packed, n, bits, split_k=split, out_dtype=torch.float32)
-        assert_w16(y, ref, f"INT{bits} split={split}")
+        assert_w16(y, ref, f"INT{bits} M={m} split={split}")
 
 
 def test_wn_a16_graph_replay_bit_identical(dev):
     n, k = 6656, 19968
     w, *_ = _weight(n, k, 6, n ^ k)
     packed = qg.quantize_intn_g32(w.to(dev), 6)
-    x = si.activation(1, k, 5).to(dev)
-    for split in (1, 4):
+    for m, split in ((1, 1), (1, 4), (4, 1)):
+        x = si.activation(m, k, 5 + m).to(dev)
         eager = qg.qgemm_wn_a16(x, packed, n, 6, split_k=split)
         assert torch.equal(eager, qg.qgemm_wn_a16(x, packed, n, 6, split_k=split))
         out = torch.empty_like(eager)
-        ws = torch.empty(max(qg.workspace_bytes(1, n, k, split), 1), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(qg.workspace_bytes(m, n, k, split), 1), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -162,7 +166,7 @@ def test_wn_a16_graph_replay_bit_identical(dev):
             torch.cuda.synchronize()
             g.replay()
             torch.cuda.synchronize()
-            assert torch.equal(out, eager), f"replay differs (split={split})"
+            assert torch.equal(out, eager), f"replay differs (m={m}, split={split})"
             _ = qg.qgemm_wn_a16(x, packed, n, 6, split_k=1)
 
 
@@ -173,5 +177,5 @@ def test_wn_a16_rejects_bad_width_and_m(dev):
         qg.qgemm_wn_a16(si.activation(1, 768, 1).to(dev), packed, 256, 7)
     assert e.value.status == -10
     with pytest.raises(qg.QGemmError) as e:
-        qg.qgemm_wn_a16(si.activation(2, 768, 1).to(dev), packed, 256, 6)
+        qg.qgemm_wn_a16(si.activation(5, 768, 1).to(dev), packed, 256, 6)
     assert e.value.status == -4
