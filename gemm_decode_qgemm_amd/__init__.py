@@ -2,7 +2,7 @@
 
 y = x . dequant(W)^T (. per-row scale) for INT4 group-32 asymmetric weights
 (W4A16, W4A8; fp16 group scales, or uint8 scale codes with a per-row
-fp16 step as the pages store them), INT5 / INT6 group-32 weights (M = 1..4) and INT8 per-channel weights (W8A16), M = 1..64 activation rows.
+fp16 step as the pages store them), INT5 / INT6 group-32 weights and INT8 per-channel weights (W8A16), M = 1..64 activation rows.
 The computation runs in the HIP library libqgemm.so (C ABI: include/qgemm.h);
 this package only binds it.
 """

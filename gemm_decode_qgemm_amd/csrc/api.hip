@@ -28,6 +28,8 @@ hipError_t launch_wn_a16_gemv32(int bits, const void* x, const void* packed, int
                                 int y_f32, float* partial, int split, hipStream_t stream);
 hipError_t launch_wn_a16_gemv_mx4(int bits, int m, const void* x, const void* packed, int n, int k, void* y,
                                   int y_f32, float* partial, int split, hipStream_t stream);
+hipError_t launch_wn_a16_mfma(int bits, int m, const void* x, const void* packed, int n, int k, void* y,
+                              int y_f32, float* partial, int split, hipStream_t stream);
 hipError_t launch_quantize_int8_rowwise(const void* w, int64_t n, int64_t k, int8_t* q,
                                         void* scales, uint32_t* status, hipStream_t stream);
 hipError_t launch_w4a16_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
@@ -315,7 +317,6 @@ int32_t qgemm_wn_a16(const void* x_bf16, int64_t m, int64_t k, int32_t bits, con
   if (st != QG_OK) return st;
   if (bits != 5 && bits != 6) return QG_E_BITS;
   if (y_dtype != QG_BF16 && y_dtype != QG_F32) return QG_E_DTYPE;
-  if (m > 4) return QG_E_M_RANGE;
   int32_t split;
   st = resolve_split(m, n, k, split_k, &split);
   if (st != QG_OK) return st;
@@ -326,8 +327,12 @@ int32_t qgemm_wn_a16(const void* x_bf16, int64_t m, int64_t k, int32_t bits, con
     return QG_E_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
-  // M = 1: the v_dot2c GEMV; M = 2..4: the 4x4x4 matrix-instruction GEMV (as for INT4)
-  if (m >= 2)
+  // as for INT4: M = 1 the v_dot2c GEMV, M = 2..4 the 4x4x4 matrix-instruction
+  // GEMV, M = 5..64 the matrix-core kernels
+  if (m > 4)
+    st = hip_status(qg::launch_wn_a16_mfma(bits, (int)m, x_bf16, packed, (int)n, (int)k, y,
+                                           y_dtype == QG_F32, partial, split, s));
+  else if (m >= 2)
     st = hip_status(qg::launch_wn_a16_gemv_mx4(bits, (int)m, x_bf16, packed, (int)n, (int)k, y,
                                                y_dtype == QG_F32, partial, split, s));
   else

@@ -66,13 +66,49 @@ __device__ __forceinline__ uint32_t nibble_pair_mfma(uint32_t w, int e, uint32_t
   return ((w >> (4 * e)) & mask_s) | magic_v;
 }
 
+// Tile geometry of the packed weight: HB = 0 is the INT4 layout (version 1);
+// HB = 1, 2 the INT5 / INT6 layout (low nibbles as INT4, then HB high-bit
+// planes, fp16 scales, one zero-point byte per group; see WnLayout).
+template <int HB>
+struct MfmaTile {
+  static constexpr int kBytes = HB == 0 ? kTileBytes : WnLayout<HB>::kTile;
+  static constexpr int kScale = HB == 0 ? kScaleOff : WnLayout<HB>::kS;
+  static constexpr int kZero = HB == 0 ? kZeroOff : WnLayout<HB>::kZ;
+};
+
+// The high-bit plane of a (group a, row) chunk as the four registers whose
+// transpose (transpose_rows4) leaves in lane (i, a) register j the plane dword
+// holding the high bits of code dword a of group j: INT5 has one plane dword
+// for all four code dwords, INT6 one per pair of them (dword a/2).
+template <int HB>
+__device__ __forceinline__ u32x4_t plane_for_transpose(const u32x2_t& p) {
+  if constexpr (HB == 1)
+    return u32x4_t{p.x, p.x, p.x, p.x};
+  else
+    return u32x4_t{p.x, p.x, p.y, p.y};
+}
+
+// bf16 pair (128 + q) of nibble pair e of code dword `dw` (this lane's code
+// dword a of a group), with the high bits from that group's plane dword `pw`
+// (plain C, as nibble_pair_mfma).
+template <int HB>
+__device__ __forceinline__ uint32_t wide_pair_mfma(uint32_t dw, uint32_t pw, int a, int e, uint32_t mask_s,
+                                                   uint32_t magic_v) {
+  const uint32_t lo = nibble_pair_mfma(dw, e, mask_s, magic_v);
+  if constexpr (HB == 0) return lo;
+  const uint32_t hi = HB == 1 ? (pw >> (4 * a + e)) & 0x00010001u
+                              : (pw >> (8 * (a & 1) + 2 * e)) & 0x00030003u;
+  return lo | (hi << 4);
+}
+
 constexpr int kNT = 4;   // n-tiles of 16 rows per wave: a whole 64-row block
 
-template <int MT>
+template <int MT, int HB>
 struct MfmaUnit {
   u32x4_t w[kNT];      // code chunks (group a, row 16t + i), transposed after the load
+  u32x2_t hp[HB > 0 ? kNT : 1];   // their high-bit planes (INT5 / INT6)
   u32x2_t scl;         // fp16 scales of row `lane` (the half tile's 4 groups)
-  uint32_t zwl;        // zero points of row `lane` (16 bits)
+  uint32_t zwl;        // zero points of row `lane` (16 bits of nibbles; INT5/6: 4 bytes)
   u32x4_t xa[MT][4];   // A operands: x[16 mt + i][32 g + 8 a .. + 8] per group g
 };
 
@@ -80,7 +116,7 @@ struct MfmaUnit {
 // PIPE: software pipeline over two register sets (PFX: the next unit's
 // activations too), or load-wait-compute per unit with the other resident
 // waves covering the latency.
-template <int MT, int KW, int MG, bool PIPE, bool PFX>
+template <int MT, int KW, int MG, bool PIPE, bool PFX, int HB = 0>
 __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -94,7 +130,8 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
-  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
+  using T = MfmaTile<HB>;
+  const uint8_t* tiles = packed + (size_t)rb * kt_count * T::kBytes;
   const uint32_t mask_s = __builtin_amdgcn_readfirstlane(0x000F000Fu);
   uint32_t magic_v = 0x43004300u;
   asm volatile("" : "+v"(magic_v));     // an empty asm: keeps the constant in a VGPR
@@ -106,20 +143,30 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
   // zero points: lane l loads those of row l only (one 8-byte and one 2-byte
   // load per half tile; per n-tile loads with 4 lanes per row cost a quarter
   // of the kernel's time); compute() hands row 16t + i to lane (i, a).
-  auto load_w = [&](MfmaUnit<MT>& u, int hs) {
-    const uint8_t* tile = tiles + (size_t)(hs >> 1) * kTileBytes;
+  auto load_w = [&](MfmaUnit<MT, HB>& u, int hs) {
+    const uint8_t* tile = tiles + (size_t)(hs >> 1) * T::kBytes;
     const int half = hs & 1;
 #pragma unroll
-    for (int t = 0; t < kNT; ++t)
+    for (int t = 0; t < kNT; ++t) {
       u.w[t] = load_stream<true>(
           reinterpret_cast<const u32x4_t*>(tile + ((4 * half + a) * kTileRows + 16 * t + i) * 16));
-    u.scl = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + kScaleOff + lane * 16 + 8 * half));
-    u.zwl = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + kZeroOff + lane * 4 + 2 * half));
+      if constexpr (HB == 1)
+        u.hp[t].x = load_stream<true>(
+            reinterpret_cast<const uint32_t*>(tile + 8192 + ((4 * half + a) * kTileRows + 16 * t + i) * 4));
+      if constexpr (HB == 2)
+        u.hp[t] = load_stream<true>(
+            reinterpret_cast<const u32x2_t*>(tile + 8192 + ((4 * half + a) * kTileRows + 16 * t + i) * 8));
+    }
+    u.scl = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + T::kScale + lane * 16 + 8 * half));
+    if constexpr (HB == 0)
+      u.zwl = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + T::kZero + lane * 4 + 2 * half));
+    else
+      u.zwl = load_stream<false>(reinterpret_cast<const uint32_t*>(tile + T::kZero + lane * 8 + 4 * half));
   };
   // Rows of x at or past m read row m - 1 instead (a valid address, no
   // branch and no select): output row r of an MFMA depends on row r of its A
   // operand only, and those rows are never stored.
-  auto load_x = [&](MfmaUnit<MT>& u, int hs) {
+  auto load_x = [&](MfmaUnit<MT, HB>& u, int hs) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int row = min(16 * (mg * MT + mt) + i, m - 1);
@@ -135,9 +182,17 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](MfmaUnit<MT>& u) {
+  auto compute = [&](MfmaUnit<MT, HB>& u) {
 #pragma unroll
     for (int t = 0; t < kNT; ++t) transpose_rows4(u.w[t]);
+    u32x4_t hr[kNT];
+    if constexpr (HB > 0) {
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) {
+        hr[t] = plane_for_transpose<HB>(u.hp[t]);
+        transpose_rows4(hr[t]);
+      }
+    }
     // Row 16t + i's metadata to lane (i, a): the same transpose applied to
     // four copies of a register leaves row t of it, in register t, in every
     // 16-lane row.
@@ -156,13 +211,15 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
 #pragma unroll
       for (int t = 0; t < kNT; ++t) {
         const uint32_t dw = u.w[t][g];
+        const uint32_t pw = HB > 0 ? hr[t][g] : 0u;
         uint32_t bp[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bp[e] = nibble_pair_mfma(dw, e, mask_s, magic_v);
+        for (int e = 0; e < 4; ++e) bp[e] = wide_pair_mfma<HB>(dw, pw, a, e, mask_s, magic_v);
         const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, u32x4_t{bp[0], bp[1], bp[2], bp[3]});
         const uint32_t sw = g < 2 ? s0[t] : s1[t];
         const float s = fp16_to_f32((sw >> (16 * (g & 1))) & 0xffffu);
-        const float zb = (float)(((zz[t] >> (4 * g)) & 15u) | 0x80u);   // 128 + zp
+        const uint32_t zp = HB == 0 ? (zz[t] >> (4 * g)) & 15u : (zz[t] >> (8 * g)) & 0xffu;
+        const float zb = (float)(zp | 0x80u);   // 128 + zp (zp <= 63)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -185,13 +242,13 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
   int hs = 2 * t0 + kw;
   if constexpr (!PIPE) {
     for (; hs < h_end; hs += KW) {
-      MfmaUnit<MT> u;
+      MfmaUnit<MT, HB> u;
       load_w(u, hs);
       load_x(u, hs);
       compute(u);
     }
   } else if (hs < h_end) {
-    MfmaUnit<MT> ua, ub;
+    MfmaUnit<MT, HB> ua, ub;
     load_w(ua, hs);
     load_x(ua, hs);
     while (true) {
@@ -261,13 +318,15 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
 // (i, a) = (lane % 16, lane / 16) -- row 16 mt + i, piece 4 g + a -- hits 8
 // distinct bank quads in any 8 consecutive lanes; the swizzle is applied on
 // the global side of the copy, whose LDS side is 64 consecutive pieces.
+template <int HB>
 struct Mfma2W {
   u32x4_t c0, c1;   // code chunks of groups a and 4 + a, row 16t + i
+  u32x2_t h0, h1;   // their high-bit planes (INT5 / INT6)
   u32x4_t sc;       // the row's 8 fp16 scales
-  uint32_t zw;      // the row's 8 zero points
+  u32x2_t zw;       // the row's 8 zero points (nibbles in .x; INT5/6: 8 bytes)
 };
 
-template <int MT, int MG>
+template <int MT, int MG, int HB = 0>
 __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -283,7 +342,8 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
-  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
+  using T = MfmaTile<HB>;
+  const uint8_t* tiles = packed + (size_t)rb * kt_count * T::kBytes;
   const uint32_t mask_s = __builtin_amdgcn_readfirstlane(0x000F000Fu);
   uint32_t magic_v = 0x43004300u;
   asm volatile("" : "+v"(magic_v));
@@ -302,12 +362,25 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
                                        16, 0, 0);
     }
   };
-  auto load_w = [&](Mfma2W& w, int kt) {
-    const uint8_t* tile = tiles + (size_t)kt * kTileBytes;
+  auto load_w = [&](Mfma2W<HB>& w, int kt) {
+    const uint8_t* tile = tiles + (size_t)kt * T::kBytes;
     w.c0 = load_stream<true>(reinterpret_cast<const u32x4_t*>(tile + (a * kTileRows + 16 * t + i) * 16));
     w.c1 = load_stream<true>(reinterpret_cast<const u32x4_t*>(tile + ((4 + a) * kTileRows + 16 * t + i) * 16));
-    w.sc = load_stream<false>(reinterpret_cast<const u32x4_t*>(tile + kScaleOff + (16 * t + i) * 16));
-    w.zw = load_stream<false>(reinterpret_cast<const uint32_t*>(tile + kZeroOff + (16 * t + i) * 4));
+    if constexpr (HB == 1) {
+      w.h0.x = load_stream<true>(reinterpret_cast<const uint32_t*>(tile + 8192 + (a * kTileRows + 16 * t + i) * 4));
+      w.h1.x = load_stream<true>(
+          reinterpret_cast<const uint32_t*>(tile + 8192 + ((4 + a) * kTileRows + 16 * t + i) * 4));
+    }
+    if constexpr (HB == 2) {
+      w.h0 = load_stream<true>(reinterpret_cast<const u32x2_t*>(tile + 8192 + (a * kTileRows + 16 * t + i) * 8));
+      w.h1 = load_stream<true>(
+          reinterpret_cast<const u32x2_t*>(tile + 8192 + ((4 + a) * kTileRows + 16 * t + i) * 8));
+    }
+    w.sc = load_stream<false>(reinterpret_cast<const u32x4_t*>(tile + T::kScale + (16 * t + i) * 16));
+    if constexpr (HB == 0)
+      w.zw.x = load_stream<false>(reinterpret_cast<const uint32_t*>(tile + T::kZero + (16 * t + i) * 4));
+    else
+      w.zw = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + T::kZero + (16 * t + i) * 8));
   };
   // Every wave's copies into LDS must have landed before the barrier that
   // hands the buffer to the other waves.
@@ -323,20 +396,29 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
   // Per group: 2 MT products (all code products first, then all zero-point
   // products, so dependent pairs are MT instructions apart), and the previous
   // group's scale FMAs while these are in flight.
-  auto compute = [&](Mfma2W& w, int buf) {
+  auto compute = [&](Mfma2W<HB>& w, int buf) {
     transpose_rows4(w.c0);
     transpose_rows4(w.c1);
+    u32x4_t hr0{}, hr1{};
+    if constexpr (HB > 0) {
+      hr0 = plane_for_transpose<HB>(w.h0);
+      hr1 = plane_for_transpose<HB>(w.h1);
+      transpose_rows4(hr0);
+      transpose_rows4(hr1);
+    }
     const uint8_t* xb = xs[buf];
     f32x4_t dp[MT];
     float sp = 0.0f;
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const uint32_t dw = g < 4 ? w.c0[g] : w.c1[g - 4];
+      const uint32_t pw = HB > 0 ? (g < 4 ? hr0[g] : hr1[g - 4]) : 0u;
       uint32_t bp[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bp[e] = nibble_pair_mfma(dw, e, mask_s, magic_v);
+      for (int e = 0; e < 4; ++e) bp[e] = wide_pair_mfma<HB>(dw, pw, a, e, mask_s, magic_v);
       const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, u32x4_t{bp[0], bp[1], bp[2], bp[3]});
-      const uint32_t z = (w.zw >> (4 * g)) & 15u;
+      const uint32_t z = HB == 0 ? (w.zw.x >> (4 * g)) & 15u
+                                 : ((g < 4 ? w.zw.x : w.zw.y) >> (8 * (g & 3))) & 0xffu;
       const uint32_t zn = (z | (z << 16)) | 0xC300C300u;     // bf16 pair -(128 + zp)
       const bf16x8_t bz = __builtin_bit_cast(bf16x8_t, u32x4_t{zn, zn, zn, zn});
       const float s = fp16_to_f32((w.sc[g >> 1] >> (16 * (g & 1))) & 0xffffu);
@@ -379,12 +461,12 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
   };
 
   if (t0 < t1) {
-    Mfma2W cur;
+    Mfma2W<HB> cur;
     stage(t0, 0);
     load_w(cur, t0);
     sync();
     for (int kt = t0; kt < t1; ++kt) {
-      Mfma2W nxt = cur;
+      Mfma2W<HB> nxt = cur;
       const bool more = kt + 1 < t1;            // uniform
       if (more) {
         stage(kt + 1, (kt + 1 - t0) & 1);
@@ -416,21 +498,21 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
   }
 }
 
-template <int MT, int MG = 1>
+template <int MT, int MG = 1, int HB = 0>
 static hipError_t launch_mfma2_t(const void* x, int m, const void* packed, int n, int k, void* y,
                                  int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_mfma2_kernel<MT, MG>), dim3(rbs, split), dim3(256 * MG), 0, stream,
+  hipLaunchKernelGGL((w4a16_mfma2_kernel<MT, MG, HB>), dim3(rbs, split), dim3(256 * MG), 0, stream,
                      static_cast<const uint16_t*>(x), m, static_cast<const uint8_t*>(packed), n, k,
                      y, y_f32, partial, split);
   return hipGetLastError();
 }
 
-template <int MT, int KW, int MG, bool PIPE, bool PFX>
+template <int MT, int KW, int MG, bool PIPE, bool PFX, int HB = 0>
 static hipError_t launch_mfma_t(const void* x, int m, const void* packed, int n, int k, void* y,
                                 int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_mfma_kernel<MT, KW, MG, PIPE, PFX>), dim3(rbs, split),
+  hipLaunchKernelGGL((w4a16_mfma_kernel<MT, KW, MG, PIPE, PFX, HB>), dim3(rbs, split),
                      dim3(KW * MG * 64), 0, stream, static_cast<const uint16_t*>(x), m,
                      static_cast<const uint8_t*>(packed), n, k, y, y_f32, partial, split);
   return hipGetLastError();
@@ -470,6 +552,31 @@ hipError_t launch_w4a16_mfma(int m, const void* x, const void* packed, int n, in
   }
   QG_MF(1, QG_MFMA_KW1, 1, QG_MFMA_PIPE1 != 0, true);
 #undef QG_MF
+}
+
+// INT5 / INT6 on the same two forms and the same bucket choice as INT4.
+template <int HB>
+static hipError_t launch_wn_mfma_t(int m, const void* x, const void* packed, int n, int k, void* y,
+                                   int y_f32, float* partial, int split, hipStream_t stream) {
+  if (mfma_lds_form(m)) {
+    switch ((m + 15) / 16) {
+      case 2: return launch_mfma2_t<2, 1, HB>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+      case 3:
+        if (n >= 32768 && k >= 6144) return launch_mfma2_t<3, 1, HB>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+        return launch_mfma2_t<1, 3, HB>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+      case 4: return launch_mfma2_t<2, 2, HB>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return launch_mfma_t<1, QG_MFMA_KW1, 1, QG_MFMA_PIPE1 != 0, true, HB>(x, m, packed, n, k, y, y_f32, partial,
+                                                                      split, stream);
+}
+
+hipError_t launch_wn_a16_mfma(int bits, int m, const void* x, const void* packed, int n, int k, void* y,
+                              int y_f32, float* partial, int split, hipStream_t stream) {
+  if (bits == 5) return launch_wn_mfma_t<1>(m, x, packed, n, k, y, y_f32, partial, split, stream);
+  if (bits == 6) return launch_wn_mfma_t<2>(m, x, packed, n, k, y, y_f32, partial, split, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace qg

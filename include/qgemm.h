@@ -232,8 +232,9 @@ int64_t qg_intn_packed_bytes(int64_t n, int64_t k, int32_t bits);
 int32_t quantize_intn_g32(const void *w_bf16, int64_t n, int64_t k, int32_t bits, void *packed,
                           int64_t packed_bytes, uint32_t *status_dev, void *stream);
 
-/* y[m, n] = x . dequant(W)^T for an INT5 / INT6 packed weight, 1 <= m <= 4
- * (QG_E_M_RANGE above), dequantized in registers, fp32 accumulation.
+/* y[m, n] = x . dequant(W)^T for an INT5 / INT6 packed weight, 1 <= m <= 64
+ * (the INT4 kernels' buckets: M <= 4 GEMVs, 5..64 the matrix cores),
+ * dequantized in registers, fp32 accumulation.
  * Arguments, workspace (qg_workspace_bytes) and errors as qgemm_w4a16, with
  * packed_bytes checked against qg_intn_packed_bytes, plus QG_E_BITS. */
 int32_t qgemm_wn_a16(const void *x_bf16, int64_t m, int64_t k, int32_t bits, const void *packed,

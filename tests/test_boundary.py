@@ -208,7 +208,7 @@ def test_intn_entry_points_validate_before_launching(lib):
     g = lib.qgemm_wn_a16
     assert g(None, 1, 256, 6, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_NULL
     assert g(A, 1, 256, 4, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_BITS
-    assert g(A, 5, 256, 6, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
+    assert g(A, 65, 256, 6, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
     assert g(A, 1, 288, 6, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_K
     assert g(A, 1, 256, 6, A, 1 << 20, 64, A, 2, 0, None, 0, None) == E_DTYPE
     assert g(A, 1, 768, 6, A, 1 << 20, 64, A, 0, 4, A, 1 << 20, None) == E_SPLIT

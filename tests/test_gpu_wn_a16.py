@@ -1,7 +1,8 @@
 """GPU parity of the INT5 / INT6 group-32 path (the INT5/INT6 family of
 executorch pull request #23737, quantized with the INT4 recipe of
 test_int4_quantized_gemm.py `_packed_with_dense` at 2^bits - 1 steps): the
-quantizer bit for bit and the M = 1..4 GEMVs within tolerance, against the CPU
+quantizer bit for bit and the GEMVs (M = 1..4) and matrix-core kernels
+(M = 5..64, the pull request's buckets 16 and 64 among them) within tolerance, against the CPU
 oracle, through the C ABI.  Layer shapes: the INT6 ones the pull request lists
 (4096x5376, 5376x21504, 6656x19968, 1024x6656); INT5 runs two INT4/INT6 shapes
 (the pull request names the count of INT5 layers, not their shapes).
@@ -147,11 +148,49 @@ def test_wn_a16_every_split_uneven(dev, bits, m):
         assert_w16(y, ref, f"INT{bits} M={m} split={split}")
 
 
+@pytest.mark.parametrize("bits", [5, 6])
+@pytest.mark.parametrize("m", [5, 8, 16, 17, 32, 33, 48, 64])
+def test_wn_a16_matrix_core_runtime_m_and_tails(dev, bits, m):
+    """Rows padded to 16 and masked; N = 257 leaves a one-row tail block."""
+    for n, k in ((257, 768), (768, 512)):
+        w, codes, scales, zeros = _weight(n, k, bits, n + k + bits)
+        packed = qg.quantize_intn_g32(w.to(dev), bits)
+        x = si.activation(m, k, 700 + m + bits)
+        ref = _ref(x, codes, scales, zeros)
+        for dt in (torch.float32, torch.bfloat16):
+            assert_w16(qg.qgemm_wn_a16(x.to(dev), packed, n, bits, out_dtype=dt), ref,
+                       f"INT{bits} {n}x{k} M={m} {dt}")
+
+
+@pytest.mark.parametrize("n,k", INT6_SHAPES)
+@pytest.mark.parametrize("m", [16, 64])
+def test_wn_a16_int6_layers_large_buckets(dev, n, k, m):
+    print(f"qgemm_wn_a16 INT6 {n}x{k} M={m}", flush=True)
+    w, codes, scales, zeros = _weight(n, k, 6, n ^ k)
+    packed = qg.quantize_intn_g32(w.to(dev), 6)
+    x = si.activation(m, k, 1200 + m)
+    ref = _ref(x, codes, scales, zeros)
+    assert_w16(qg.qgemm_wn_a16(x.to(dev), packed, n, 6, out_dtype=torch.float32), ref, f"INT6 {n}x{k} M={m}")
+
+
+@pytest.mark.parametrize("bits", [5, 6])
+@pytest.mark.parametrize("m", [16, 64])
+def test_wn_a16_matrix_core_every_split(dev, bits, m):
+    n, k = 320, 6656
+    w, codes, scales, zeros = _weight(n, k, bits, 91)
+    packed = qg.quantize_intn_g32(w.to(dev), bits)
+    x = si.activation(m, k, 61 + m)
+    ref = _ref(x, codes, scales, zeros)
+    for split in si.SPLITS:
+        y = qg.qgemm_wn_a16(x.to(dev), packed, n, bits, split_k=split, out_dtype=torch.float32)
+        assert_w16(y, ref, f"INT{bits} M={m} split={split}")
+
+
 def test_wn_a16_graph_replay_bit_identical(dev):
     n, k = 6656, 19968
     w, *_ = _weight(n, k, 6, n ^ k)
     packed = qg.quantize_intn_g32(w.to(dev), 6)
-    for m, split in ((1, 1), (1, 4), (4, 1)):
+    for m, split in ((1, 1), (1, 4), (4, 1), (16, 2), (64, 4)):
         x = si.activation(m, k, 5 + m).to(dev)
         eager = qg.qgemm_wn_a16(x, packed, n, 6, split_k=split)
         assert torch.equal(eager, qg.qgemm_wn_a16(x, packed, n, 6, split_k=split))
@@ -177,5 +216,5 @@ def test_wn_a16_rejects_bad_width_and_m(dev):
         qg.qgemm_wn_a16(si.activation(1, 768, 1).to(dev), packed, 256, 7)
     assert e.value.status == -10
     with pytest.raises(qg.QGemmError) as e:
-        qg.qgemm_wn_a16(si.activation(5, 768, 1).to(dev), packed, 256, 6)
+        qg.qgemm_wn_a16(si.activation(65, 768, 1).to(dev), packed, 256, 6)
     assert e.value.status == -4
