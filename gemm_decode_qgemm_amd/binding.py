@@ -221,7 +221,7 @@ def qgemm_w4a16(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_k: int =
 def qgemm_w4a16_dq(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_k: int = 0,
                    out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
                    workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """y[m, n] = x . dequant(W)^T for a packed INT4 g32 weight with scale codes (m <= 4)."""
+    """y[m, n] = x . dequant(W)^T for a packed INT4 g32 weight with scale codes (m <= 64)."""
     _dev(x, "x", torch.bfloat16, 2)
     m, k = x.shape
     y, yd = _out(m, n, out_dtype, x.device, out)

@@ -30,6 +30,8 @@ hipError_t launch_wn_a16_gemv_mx4(int bits, int m, const void* x, const void* pa
                                   int y_f32, float* partial, int split, hipStream_t stream);
 hipError_t launch_wn_a16_mfma(int bits, int m, const void* x, const void* packed, int n, int k, void* y,
                               int y_f32, float* partial, int split, hipStream_t stream);
+hipError_t launch_w4a16_mfma_dq(int m, const void* x, const void* packed, int n, int k, void* y, int y_f32,
+                                float* partial, int split, hipStream_t stream);
 hipError_t launch_quantize_int8_rowwise(const void* w, int64_t n, int64_t k, int8_t* q,
                                         void* scales, uint32_t* status, hipStream_t stream);
 hipError_t launch_w4a16_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
@@ -286,7 +288,6 @@ int32_t qgemm_w4a16_dq(const void* x_bf16, int64_t m, int64_t k, const void* pac
   int32_t st = check_mnk(m, n, k);
   if (st != QG_OK) return st;
   if (y_dtype != QG_BF16 && y_dtype != QG_F32) return QG_E_DTYPE;
-  if (m > 4) return QG_E_M_RANGE;
   int32_t split;
   st = resolve_split(m, n, k, split_k, &split);
   if (st != QG_OK) return st;
@@ -297,9 +298,12 @@ int32_t qgemm_w4a16_dq(const void* x_bf16, int64_t m, int64_t k, const void* pac
     return QG_E_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
-  // the 32-row GEMVs of qgemm_w4a16 (M = 1: v_dot2c, M = 2..4: the 4x4x4
-  // matrix instruction) reading the scale-code layout
-  if (m >= 2)
+  // the kernels of qgemm_w4a16 reading the scale-code layout: M = 1 the
+  // v_dot2c GEMV, M = 2..4 the 4x4x4 matrix instruction, M = 5..64 the matrix cores
+  if (m > 4)
+    st = hip_status(qg::launch_w4a16_mfma_dq((int)m, x_bf16, packed, (int)n, (int)k, y, y_dtype == QG_F32,
+                                             partial, split, s));
+  else if (m >= 2)
     st = hip_status(qg::launch_w4a16_gemv_mx4_dq((int)m, x_bf16, packed, (int)n, (int)k, y,
                                                  y_dtype == QG_F32, partial, split, s));
   else

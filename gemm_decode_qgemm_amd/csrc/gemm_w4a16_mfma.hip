@@ -69,11 +69,18 @@ __device__ __forceinline__ uint32_t nibble_pair_mfma(uint32_t w, int e, uint32_t
 // Tile geometry of the packed weight: HB = 0 is the INT4 layout (version 1);
 // HB = 1, 2 the INT5 / INT6 layout (low nibbles as INT4, then HB high-bit
 // planes, fp16 scales, one zero-point byte per group; see WnLayout).
-template <int HB>
+// DQ: the INT4 layout with scale codes (version 2): a 128-byte head of row
+// steps per 64-row block, tiles of 8960 bytes, a group's scale = its uint8
+// code times its row's step.
+template <int HB, bool DQ = false>
 struct MfmaTile {
-  static constexpr int kBytes = HB == 0 ? kTileBytes : WnLayout<HB>::kTile;
-  static constexpr int kScale = HB == 0 ? kScaleOff : WnLayout<HB>::kS;
-  static constexpr int kZero = HB == 0 ? kZeroOff : WnLayout<HB>::kZ;
+  static constexpr int kBytes = DQ ? kDqTileBytes : (HB == 0 ? kTileBytes : WnLayout<HB>::kTile);
+  static constexpr int kScale = DQ ? kDqScodeOff : (HB == 0 ? kScaleOff : WnLayout<HB>::kS);
+  static constexpr int kZero = DQ ? kDqZeroOff : (HB == 0 ? kZeroOff : WnLayout<HB>::kZ);
+  static constexpr int kHead = DQ ? kDqHeadBytes : 0;
+  __device__ static const uint8_t* block(const uint8_t* packed, int rb, int kt_count) {
+    return packed + (size_t)rb * (kHead + (size_t)kt_count * kBytes);
+  }
 };
 
 // The high-bit plane of a (group a, row) chunk as the four registers whose
@@ -116,7 +123,7 @@ struct MfmaUnit {
 // PIPE: software pipeline over two register sets (PFX: the next unit's
 // activations too), or load-wait-compute per unit with the other resident
 // waves covering the latency.
-template <int MT, int KW, int MG, bool PIPE, bool PFX, int HB = 0>
+template <int MT, int KW, int MG, bool PIPE, bool PFX, int HB = 0, bool DQ = false>
 __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -130,8 +137,14 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
-  using T = MfmaTile<HB>;
-  const uint8_t* tiles = packed + (size_t)rb * kt_count * T::kBytes;
+  using T = MfmaTile<HB, DQ>;
+  const uint8_t* blk = T::block(packed, rb, kt_count);
+  const uint8_t* tiles = blk + T::kHead;
+  // scale codes: the steps of rows 16t + i, the rows this lane's scales belong to
+  float stp[kNT];
+#pragma unroll
+  for (int t = 0; t < kNT; ++t)
+    stp[t] = DQ ? fp16_to_f32(*reinterpret_cast<const uint16_t*>(blk + 2 * (16 * t + i))) : 1.0f;
   const uint32_t mask_s = __builtin_amdgcn_readfirstlane(0x000F000Fu);
   uint32_t magic_v = 0x43004300u;
   asm volatile("" : "+v"(magic_v));     // an empty asm: keeps the constant in a VGPR
@@ -157,7 +170,10 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
         u.hp[t] = load_stream<true>(
             reinterpret_cast<const u32x2_t*>(tile + 8192 + ((4 * half + a) * kTileRows + 16 * t + i) * 8));
     }
-    u.scl = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + T::kScale + lane * 16 + 8 * half));
+    if constexpr (DQ)
+      u.scl = u32x2_t{load_stream<false>(reinterpret_cast<const uint32_t*>(tile + T::kScale + lane * 8 + 4 * half)), 0u};
+    else
+      u.scl = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + T::kScale + lane * 16 + 8 * half));
     if constexpr (HB == 0)
       u.zwl = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + T::kZero + lane * 4 + 2 * half));
     else
@@ -217,7 +233,8 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
         for (int e = 0; e < 4; ++e) bp[e] = wide_pair_mfma<HB>(dw, pw, a, e, mask_s, magic_v);
         const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, u32x4_t{bp[0], bp[1], bp[2], bp[3]});
         const uint32_t sw = g < 2 ? s0[t] : s1[t];
-        const float s = fp16_to_f32((sw >> (16 * (g & 1))) & 0xffffu);
+        const float s = DQ ? (float)((s0[t] >> (8 * g)) & 0xffu) * stp[t]
+                           : fp16_to_f32((sw >> (16 * (g & 1))) & 0xffffu);
         const uint32_t zp = HB == 0 ? (zz[t] >> (4 * g)) & 15u : (zz[t] >> (8 * g)) & 0xffu;
         const float zb = (float)(zp | 0x80u);   // 128 + zp (zp <= 63)
 #pragma unroll
@@ -326,7 +343,7 @@ struct Mfma2W {
   u32x2_t zw;       // the row's 8 zero points (nibbles in .x; INT5/6: 8 bytes)
 };
 
-template <int MT, int MG, int HB = 0>
+template <int MT, int MG, int HB = 0, bool DQ = false>
 __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -342,8 +359,11 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
-  using T = MfmaTile<HB>;
-  const uint8_t* tiles = packed + (size_t)rb * kt_count * T::kBytes;
+  using T = MfmaTile<HB, DQ>;
+  const uint8_t* blk = T::block(packed, rb, kt_count);
+  const uint8_t* tiles = blk + T::kHead;
+  // scale codes: the step of this lane's row 16t + i
+  const float stp = DQ ? fp16_to_f32(*reinterpret_cast<const uint16_t*>(blk + 2 * (16 * t + i))) : 1.0f;
   const uint32_t mask_s = __builtin_amdgcn_readfirstlane(0x000F000Fu);
   uint32_t magic_v = 0x43004300u;
   asm volatile("" : "+v"(magic_v));
@@ -376,7 +396,12 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
       w.h1 = load_stream<true>(
           reinterpret_cast<const u32x2_t*>(tile + 8192 + ((4 + a) * kTileRows + 16 * t + i) * 8));
     }
-    w.sc = load_stream<false>(reinterpret_cast<const u32x4_t*>(tile + T::kScale + (16 * t + i) * 16));
+    if constexpr (DQ) {
+      const u32x2_t c8 = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + T::kScale + (16 * t + i) * 8));
+      w.sc = u32x4_t{c8.x, c8.y, 0u, 0u};
+    } else {
+      w.sc = load_stream<false>(reinterpret_cast<const u32x4_t*>(tile + T::kScale + (16 * t + i) * 16));
+    }
     if constexpr (HB == 0)
       w.zw.x = load_stream<false>(reinterpret_cast<const uint32_t*>(tile + T::kZero + (16 * t + i) * 4));
     else
@@ -421,7 +446,8 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
                                  : ((g < 4 ? w.zw.x : w.zw.y) >> (8 * (g & 3))) & 0xffu;
       const uint32_t zn = (z | (z << 16)) | 0xC300C300u;     // bf16 pair -(128 + zp)
       const bf16x8_t bz = __builtin_bit_cast(bf16x8_t, u32x4_t{zn, zn, zn, zn});
-      const float s = fp16_to_f32((w.sc[g >> 1] >> (16 * (g & 1))) & 0xffffu);
+      const float s = DQ ? (float)((w.sc[g >> 2] >> (8 * (g & 3))) & 0xffu) * stp
+                         : fp16_to_f32((w.sc[g >> 1] >> (16 * (g & 1))) & 0xffffu);
       bf16x8_t av[MT];
       f32x4_t d[MT];
 #pragma unroll
@@ -498,21 +524,21 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
   }
 }
 
-template <int MT, int MG = 1, int HB = 0>
+template <int MT, int MG = 1, int HB = 0, bool DQ = false>
 static hipError_t launch_mfma2_t(const void* x, int m, const void* packed, int n, int k, void* y,
                                  int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_mfma2_kernel<MT, MG, HB>), dim3(rbs, split), dim3(256 * MG), 0, stream,
+  hipLaunchKernelGGL((w4a16_mfma2_kernel<MT, MG, HB, DQ>), dim3(rbs, split), dim3(256 * MG), 0, stream,
                      static_cast<const uint16_t*>(x), m, static_cast<const uint8_t*>(packed), n, k,
                      y, y_f32, partial, split);
   return hipGetLastError();
 }
 
-template <int MT, int KW, int MG, bool PIPE, bool PFX, int HB = 0>
+template <int MT, int KW, int MG, bool PIPE, bool PFX, int HB = 0, bool DQ = false>
 static hipError_t launch_mfma_t(const void* x, int m, const void* packed, int n, int k, void* y,
                                 int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_mfma_kernel<MT, KW, MG, PIPE, PFX, HB>), dim3(rbs, split),
+  hipLaunchKernelGGL((w4a16_mfma_kernel<MT, KW, MG, PIPE, PFX, HB, DQ>), dim3(rbs, split),
                      dim3(KW * MG * 64), 0, stream, static_cast<const uint16_t*>(x), m,
                      static_cast<const uint8_t*>(packed), n, k, y, y_f32, partial, split);
   return hipGetLastError();
@@ -554,21 +580,22 @@ hipError_t launch_w4a16_mfma(int m, const void* x, const void* packed, int n, in
 #undef QG_MF
 }
 
-// INT5 / INT6 on the same two forms and the same bucket choice as INT4.
-template <int HB>
+// INT5 / INT6 and the scale-code INT4 layout on the same two forms and the
+// same bucket choice as INT4.
+template <int HB, bool DQ = false>
 static hipError_t launch_wn_mfma_t(int m, const void* x, const void* packed, int n, int k, void* y,
                                    int y_f32, float* partial, int split, hipStream_t stream) {
   if (mfma_lds_form(m)) {
     switch ((m + 15) / 16) {
-      case 2: return launch_mfma2_t<2, 1, HB>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+      case 2: return launch_mfma2_t<2, 1, HB, DQ>(x, m, packed, n, k, y, y_f32, partial, split, stream);
       case 3:
-        if (n >= 32768 && k >= 6144) return launch_mfma2_t<3, 1, HB>(x, m, packed, n, k, y, y_f32, partial, split, stream);
-        return launch_mfma2_t<1, 3, HB>(x, m, packed, n, k, y, y_f32, partial, split, stream);
-      case 4: return launch_mfma2_t<2, 2, HB>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+        if (n >= 32768 && k >= 6144) return launch_mfma2_t<3, 1, HB, DQ>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+        return launch_mfma2_t<1, 3, HB, DQ>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+      case 4: return launch_mfma2_t<2, 2, HB, DQ>(x, m, packed, n, k, y, y_f32, partial, split, stream);
       default: return hipErrorInvalidValue;
     }
   }
-  return launch_mfma_t<1, QG_MFMA_KW1, 1, QG_MFMA_PIPE1 != 0, true, HB>(x, m, packed, n, k, y, y_f32, partial,
+  return launch_mfma_t<1, QG_MFMA_KW1, 1, QG_MFMA_PIPE1 != 0, true, HB, DQ>(x, m, packed, n, k, y, y_f32, partial,
                                                                       split, stream);
 }
 
@@ -577,6 +604,11 @@ hipError_t launch_wn_a16_mfma(int bits, int m, const void* x, const void* packed
   if (bits == 5) return launch_wn_mfma_t<1>(m, x, packed, n, k, y, y_f32, partial, split, stream);
   if (bits == 6) return launch_wn_mfma_t<2>(m, x, packed, n, k, y, y_f32, partial, split, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_w4a16_mfma_dq(int m, const void* x, const void* packed, int n, int k, void* y, int y_f32,
+                                float* partial, int split, hipStream_t stream) {
+  return launch_wn_mfma_t<0, true>(m, x, packed, n, k, y, y_f32, partial, split, stream);
 }
 
 }  // namespace qg

@@ -197,9 +197,10 @@ int32_t quantize_int4_g32_dq(const void *w_bf16, int64_t n, int64_t k, void *pac
 /* ---- qgemm_w4a16_dq ------------------------------------------------------
  * qgemm_w4a16 on a version 2 (scale-code) weight:
  *   y[m, n] = sum_g c[n,g] * step[n] * sum_{k in g} x[m,k] * (q[n,k] - zp[n,g]),
- * dequantized in registers, fp32 accumulation.  Arguments, workspace
+ * dequantized in registers, fp32 accumulation, on the same kernels and
+ * buckets as qgemm_w4a16 (1 <= m <= 64).  Arguments, workspace
  * (qg_workspace_bytes) and errors as qgemm_w4a16, with packed_bytes checked
- * against qg_int4_dq_packed_bytes and 1 <= m <= 4 (QG_E_M_RANGE above). */
+ * against qg_int4_dq_packed_bytes. */
 int32_t qgemm_w4a16_dq(const void *x_bf16, int64_t m, int64_t k, const void *packed,
                        int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
                        int32_t split_k, void *ws, int64_t ws_bytes, void *stream);

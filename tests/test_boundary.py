@@ -164,7 +164,7 @@ def test_qgemm_w4a16_and_w4a8_validate_before_launching(lib, args, expect):
 def test_w4a8_m_range(lib):
     assert lib.qgemm_w4a8(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
     assert lib.qgemm_w4a8_g32(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
-    assert lib.qgemm_w4a16_dq(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
+    assert lib.qgemm_w4a16_dq(A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
     # 9088 bytes hold a 64 x 256 scale-code weight, 9087 do not
     assert lib.qgemm_w4a16_dq(A, 1, 256, A, 9087, 64, A, 0, 0, None, 0, None) == E_BUF
 

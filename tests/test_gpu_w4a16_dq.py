@@ -1,7 +1,7 @@
 """GPU parity of the scale-code form of the INT4 g32 weight (uint8 scale code
 times a per-row fp16 step, the stored form of executorch
 test_int4_quantized_gemm.py `_packed_with_dense`): the quantizer bit for bit,
-the W4A16 GEMV (M = 1..4) within tolerance, against the CPU oracle, through
+the W4A16 kernels (M = 1..64) within tolerance, against the CPU oracle, through
 the C ABI.  Shapes, buckets, the N = 257 tail and every split follow the same
 page as the fp16-scale tests.
 """
@@ -184,9 +184,34 @@ def test_w4a16_dq_repeat_and_graph_replay_are_bit_identical(dev):
                 _ = qg.qgemm_w4a16_dq(x, packed, n, split_k=1)
 
 
-def test_w4a16_dq_rejects_m_above_4(dev):
+def test_w4a16_dq_rejects_m_above_64(dev):
     w, *_ = _weight(256, 768, 3)
     packed = qg.quantize_int4_g32_dq(w.to(dev))
     with pytest.raises(qg.QGemmError) as e:
-        qg.qgemm_w4a16_dq(si.activation(5, 768, 1).to(dev), packed, 256)
+        qg.qgemm_w4a16_dq(si.activation(65, 768, 1).to(dev), packed, 256)
     assert e.value.status == -4
+
+
+@pytest.mark.parametrize("m", [5, 8, 16, 17, 32, 33, 48, 64])
+def test_w4a16_dq_matrix_core_runtime_m_and_tails(dev, m):
+    """The matrix-core kernels on the scale-code layout; N = 257 leaves a one-row tail block."""
+    for n, k in ((257, 768), (768, 512)):
+        w, codes, scode, sstep, zeros = _weight(n, k, n + k)
+        packed = qg.quantize_int4_g32_dq(w.to(dev))
+        x = si.activation(m, k, 800 + m)
+        ref = _ref(x, codes, scode, sstep, zeros)
+        for dt in (torch.float32, torch.bfloat16):
+            assert_w16(qg.qgemm_w4a16_dq(x.to(dev), packed, n, out_dtype=dt), ref, f"{n}x{k} M={m} {dt}")
+
+
+@pytest.mark.parametrize("n,k", [(39936, 6656), (6656, 19968), (8448, 6656)])
+@pytest.mark.parametrize("m", [16, 64])
+def test_w4a16_dq_large_buckets(dev, n, k, m):
+    print(f"qgemm_w4a16_dq {n}x{k} M={m}", flush=True)
+    w, codes, scode, sstep, zeros = _weight(n, k, si.model_weight_seed(n, k))
+    packed = qg.quantize_int4_g32_dq(w.to(dev))
+    x = si.activation(m, k, 1300 + m)
+    ref = _ref(x, codes, scode, sstep, zeros)
+    for split in (0, 2):
+        y = qg.qgemm_w4a16_dq(x.to(dev), packed, n, split_k=split, out_dtype=torch.float32)
+        assert_w16(y, ref, f"{n}x{k} M={m} split={split}")
