@@ -27,7 +27,8 @@ Other layers of the same path use the same protocol: --op w4a16 with
 weight, M <= 4, bytes = its packed size), --op wn_a16 --bits 5|6 (INT5 / INT6,
 M = 1, bytes = the packed size), --op w4a8 / w4a8_g32 (M <= 4) and
 --op w8a16 (int8 per-channel, bytes = N*K + 2*N); --n/--k pick the shape.  The
-offline weight quantizers run the same way: --op quantize_int4 (bytes = the
+offline weight quantizers run the same way: --op quantize_int4 / quantize_int4_dq /
+quantize_intn --bits 5|6 (bytes = the
 bf16 weight read + the packed weight written) and --op quantize_int8 (bf16
 read + int8 codes and bf16 scales written), the bf16 inputs and the outputs
 both rotating over >= 1 GiB; their CPU leg runs the oracle quantizer and
@@ -86,7 +87,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=1000,
                    help="untimed calls first; the clocks take a few hundred calls to ramp up from idle")
     p.add_argument("--op", choices=("w4a16", "w4a16_dq", "wn_a16", "w4a8", "w4a8_g32", "w8a16",
-                                    "quantize_int4", "quantize_int8"),
+                                    "quantize_int4", "quantize_int4_dq", "quantize_intn", "quantize_int8"),
                    default="w4a16")
     p.add_argument("--bits", type=int, default=6, help="code width of --op wn_a16 (5 or 6)")
     p.add_argument("--n", type=int, default=39936)
@@ -318,9 +319,18 @@ def bench_quantizer(args, torch, qg, si, dev):
     import numpy as np
 
     n, k = args.n, args.k
-    int4 = args.op == "quantize_int4"
+    op = args.op
+    int4 = op != "quantize_int8"                  # every packed INT4/5/6 layout
     w_cpu = si.int4_weight(n, k, n ^ k)           # a bf16 weight of the layers' distribution
-    out_bytes = qg.int4_packed_bytes(n, k) if int4 else n * k + 2 * n
+    if op == "quantize_int4":
+        out_bytes, quant = qg.int4_packed_bytes(n, k), qg.quantize_int4_g32
+    elif op == "quantize_int4_dq":
+        out_bytes, quant = qg.int4_dq_packed_bytes(n, k), qg.quantize_int4_g32_dq
+    elif op == "quantize_intn":
+        out_bytes = qg.intn_packed_bytes(n, k, args.bits)
+        quant = lambda w, out: qg.quantize_intn_g32(w, args.bits, out=out)
+    else:
+        out_bytes = n * k + 2 * n
     bytes_eff = 2 * n * k + out_bytes
     copies = max(2, math.ceil((1 << 30) / bytes_eff))
     w0 = w_cpu.to(dev)
@@ -329,7 +339,7 @@ def bench_quantizer(args, torch, qg, si, dev):
         outs = [torch.empty(out_bytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
 
         def call(i):
-            qg.quantize_int4_g32(ws[i % copies], out=outs[i % copies])
+            quant(ws[i % copies], out=outs[i % copies])
     else:
         outs = [(torch.empty((n, k), dtype=torch.int8, device=dev), torch.empty(n, dtype=torch.bfloat16, device=dev))
                 for _ in range(copies)]
@@ -339,7 +349,8 @@ def bench_quantizer(args, torch, qg, si, dev):
     torch.cuda.synchronize()
     us_call, per_replay, chunk, full, rest, wall = graph_time(torch, call, args.steps, args.warmup)
     gbs = bytes_eff / (us_call * 1e-6) / 1e9
-    name = "INT4-g32 quantize + pack" if int4 else "INT8 row-wise quantize"
+    name = {"quantize_int4": "INT4-g32 quantize + pack", "quantize_int4_dq": "INT4-g32 quantize + pack with scale codes",
+            "quantize_intn": f"INT{args.bits}-g32 quantize + pack", "quantize_int8": "INT8 row-wise quantize"}[op]
     out = {
         "metric": f"µs/call and streamed GB/s (% HBM peak) for the {name} of a bf16 weight",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -364,9 +375,15 @@ def bench_quantizer(args, torch, qg, si, dev):
         t_start = time.perf_counter()
         while True:
             t0 = time.perf_counter()
-            if int4:
+            if op == "quantize_int4":
                 c, s, z, _ = oracle.quantize_int4_g32(bits)
                 ref = oracle.pack_int4(c, s, z)
+            elif op == "quantize_int4_dq":
+                c, sc, st, z, _ = oracle.quantize_int4_g32_dq(bits)
+                ref = oracle.pack_int4_dq(c, sc, st, z)
+            elif op == "quantize_intn":
+                c, s, z, _ = oracle.quantize_intn_g32(bits, args.bits)
+                ref = oracle.pack_intn(c, s, z, args.bits)
             else:
                 ref = oracle.quantize_int8_rowwise(bits)
             times.append(time.perf_counter() - t0)
