@@ -66,6 +66,8 @@ def _load():
         "orc_intn_packed_bytes": (I64, [I64, I64, I]),
         "orc_pack_intn": (None, [P, P, P, I64, I64, I, P]),
         "orc_unpack_intn": (None, [P, I64, I64, I, P, P, P]),
+        "orc_qgemm_w4a8_dq": (None, [P, I64, I64, P, P, P, P, I64, P, I]),
+        "orc_qgemm_w4a8_g32_dq": (None, [P, I64, I64, P, P, P, P, I64, P, I]),
         "orc_hardware_threads": (I, []),
     }
     for name, (res, args) in sig.items():
@@ -344,3 +346,26 @@ def qgemm_w4a8(x_bits, codes, scales, zeros, threads: int = 1) -> np.ndarray:
     y = np.empty((m, n), np.float64)
     _load().orc_qgemm_w4a8(_ptr(x), m, k, _ptr(codes), _ptr(scales), _ptr(zeros), n, _ptr(y), threads)
     return y
+
+
+def _w4a8_dq(fn, x_bits, codes, scode, sstep, zeros, threads):
+    x = _u16(x_bits)
+    m, k = x.shape
+    n = codes.shape[0]
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scode = np.ascontiguousarray(scode, np.uint8)
+    sstep = _u16(sstep)
+    zeros = np.ascontiguousarray(zeros, np.uint8)
+    y = np.empty((m, n), np.float64)
+    fn(_ptr(x), m, k, _ptr(codes), _ptr(scode), _ptr(sstep), _ptr(zeros), n, _ptr(y), threads)
+    return y
+
+
+def qgemm_w4a8_dq(x_bits, codes, scode, sstep, zeros, threads: int = 1) -> np.ndarray:
+    """W4A8 (per-row int8 activations) on the scale-code weight."""
+    return _w4a8_dq(_load().orc_qgemm_w4a8_dq, x_bits, codes, scode, sstep, zeros, threads)
+
+
+def qgemm_w4a8_g32_dq(x_bits, codes, scode, sstep, zeros, threads: int = 1) -> np.ndarray:
+    """W4A8 (int8 activations, one scale per group of 32) on the scale-code weight."""
+    return _w4a8_dq(_load().orc_qgemm_w4a8_g32_dq, x_bits, codes, scode, sstep, zeros, threads)

@@ -141,6 +141,16 @@ void orc_qgemm_w4a16_dq(const uint16_t *x, int64_t m, int64_t k, const uint8_t *
                         const uint8_t *scode, const uint16_t *sstep, const uint8_t *zeros,
                         int64_t n, double *y, int threads);
 
+/* ---- W4A8 on the scale-code form: the activation quantizers above, a
+ * group's scale c * step:  per row y = sx[m] * sum_g c*step * I,
+ * per group of 32 y = sum_g sx[m,g] * c*step * I. ---- */
+void orc_qgemm_w4a8_dq(const uint16_t *x, int64_t m, int64_t k, const uint8_t *codes,
+                       const uint8_t *scode, const uint16_t *sstep, const uint8_t *zeros,
+                       int64_t n, double *y, int threads);
+void orc_qgemm_w4a8_g32_dq(const uint16_t *x, int64_t m, int64_t k, const uint8_t *codes,
+                           const uint8_t *scode, const uint16_t *sstep, const uint8_t *zeros,
+                           int64_t n, double *y, int threads);
+
 /* ---- INT5 / INT6 group-32 (the pages' INT5/INT6 quantized-GEMM family) ----
  * The INT4 reading with L = 2^bits - 1 steps: s = smallest positive fp16
  * with L*s >= r (1.0 for r == 0; 65504 and flag 2 above L*65504),

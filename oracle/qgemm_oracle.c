@@ -774,3 +774,70 @@ void orc_unpack_intn(const uint8_t *packed, int64_t n, int64_t k, int bits,
         }
     }
 }
+
+/* W4A8 on the scale-code form: the activations quantized exactly as in
+ * orc_qgemm_w4a8 / orc_qgemm_w4a8_g32, a group's scale c * step.
+ *   per row:      y[m,n] = sx[m] * sum_g (c[n,g] * step[n]) * I[m,n,g]
+ *   per group 32: y[m,n] = sum_g sx[m,g] * (c[n,g] * step[n]) * I[m,n,g]
+ * with I the exact integer group dot; c * step is exact in binary64, the
+ * products and the sum over g are binary64. */
+struct w4a8dq_ctx {
+    const int8_t *xq; const float *sx; int64_t m, k;
+    const uint8_t *codes, *scode; const uint16_t *sstep; const uint8_t *zeros;
+    int64_t n; double *y; int per_group;
+};
+
+static void w4a8_dq_rows(void *p, int64_t b, int64_t e) {
+    struct w4a8dq_ctx *c = (struct w4a8dq_ctx *)p;
+    int64_t groups = c->k / 32;
+    for (int64_t row = b; row < e; row++) {
+        double step = orc_fp16_to_double(c->sstep[row]);
+        for (int64_t mi = 0; mi < c->m; mi++) {
+            double acc = 0.0;
+            for (int64_t g = 0; g < groups; g++) {
+                int64_t isum = 0;
+                int zg = c->zeros[row * groups + g];
+                for (int64_t i = 0; i < 32; i++) {
+                    int64_t kk = g * 32 + i;
+                    isum += (int64_t)c->xq[mi * c->k + kk] *
+                            (int64_t)(c->codes[row * c->k + kk] - zg);
+                }
+                double s = (double)c->scode[row * groups + g] * step;
+                if (c->per_group)
+                    acc += (double)c->sx[mi * groups + g] * s * (double)isum;
+                else
+                    acc += s * (double)isum;
+            }
+            c->y[mi * c->n + row] = c->per_group ? acc : (double)c->sx[mi] * acc;
+        }
+    }
+}
+
+static void w4a8_dq_common(const uint16_t *x, int64_t m, int64_t k, const uint8_t *codes,
+                           const uint8_t *scode, const uint16_t *sstep, const uint8_t *zeros,
+                           int64_t n, double *y, int threads, int per_group) {
+    int64_t groups = k / 32;
+    int8_t *xq = (int8_t *)malloc((size_t)(m * k));
+    float *sx = (float *)malloc((size_t)(m * (per_group ? groups : 1)) * sizeof(float));
+    if (!xq || !sx) { free(xq); free(sx); abort(); }
+    if (per_group)
+        orc_actquant_int8_g32(x, m, k, xq, sx);
+    else
+        orc_actquant_int8(x, m, k, xq, sx);
+    struct w4a8dq_ctx c = {xq, sx, m, k, codes, scode, sstep, zeros, n, y, per_group};
+    parallel_rows(w4a8_dq_rows, &c, n, threads);
+    free(xq);
+    free(sx);
+}
+
+void orc_qgemm_w4a8_dq(const uint16_t *x, int64_t m, int64_t k, const uint8_t *codes,
+                       const uint8_t *scode, const uint16_t *sstep, const uint8_t *zeros,
+                       int64_t n, double *y, int threads) {
+    w4a8_dq_common(x, m, k, codes, scode, sstep, zeros, n, y, threads, 0);
+}
+
+void orc_qgemm_w4a8_g32_dq(const uint16_t *x, int64_t m, int64_t k, const uint8_t *codes,
+                           const uint8_t *scode, const uint16_t *sstep, const uint8_t *zeros,
+                           int64_t n, double *y, int threads) {
+    w4a8_dq_common(x, m, k, codes, scode, sstep, zeros, n, y, threads, 1);
+}

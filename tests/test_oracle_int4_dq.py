@@ -182,3 +182,43 @@ def test_gemm_rational_brute_force():
             exact = sum(bf16_value(int(x[i, kk])) * (int(codes[r, kk]) - int(zeros[r, kk // 32]))
                         * int(scode[r, kk // 32]) * fp16_value(int(sstep[r])) for kk in range(k))
             assert abs(Fraction(y[i, r]) - exact) <= abs(exact) * Fraction(1, 2 ** 45) + Fraction(1, 2 ** 80)
+
+
+@pytest.mark.parametrize("per_group", [False, True])
+def test_w4a8_equals_fp16_scale_form_when_scales_are_fp16(per_group):
+    """Power-of-two codes make c*step an fp16 value: the scale-code W4A8 must
+    then equal the (separately pinned) fp16-scale W4A8 bit for bit."""
+    rng = np.random.default_rng(21)
+    n, k, m = 24, 512, 3
+    codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    scode = (1 << rng.integers(0, 8, (n, k // 32))).astype(np.uint8)
+    sstep = rng.integers(0x1000, 0x4000, n).astype(np.uint16)
+    zeros = rng.integers(0, 16, (n, k // 32)).astype(np.uint8)
+    s64 = scode.astype(np.float64) * sstep.view(np.float16).astype(np.float64)[:, None]
+    scales = s64.astype(np.float16)
+    assert (scales.astype(np.float64) == s64).all()
+    x = bf16_bits(torch.randn(m, k, generator=torch.Generator().manual_seed(6)).to(torch.bfloat16))
+    if per_group:
+        a = oracle.qgemm_w4a8_g32_dq(x, codes, scode, sstep, zeros)
+        b = oracle.qgemm_w4a8_g32(x, codes, scales.view(np.uint16), zeros)
+    else:
+        a = oracle.qgemm_w4a8_dq(x, codes, scode, sstep, zeros)
+        b = oracle.qgemm_w4a8(x, codes, scales.view(np.uint16), zeros)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_w4a8_on_int8_grid_equals_w4a16():
+    """Activations already on the int8 grid with absmax 127 quantize to
+    themselves with sx = 1: W4A8 then equals W4A16 on the same weight."""
+    rng = np.random.default_rng(22)
+    n, k, m = 16, 256, 2
+    codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    scode = rng.integers(1, 256, (n, k // 32)).astype(np.uint8)
+    sstep = rng.integers(0x0400, 0x3000, n).astype(np.uint16)
+    zeros = rng.integers(0, 16, (n, k // 32)).astype(np.uint8)
+    xi = rng.integers(-127, 128, (m, k)).astype(np.float32)
+    xi[:, 0] = 127.0
+    x = (xi.view(np.uint32) >> 16).astype(np.uint16)
+    a16 = oracle.qgemm_w4a16_dq(x, codes, scode, sstep, zeros)
+    a8 = oracle.qgemm_w4a8_dq(x, codes, scode, sstep, zeros)
+    np.testing.assert_allclose(a8, a16, rtol=1e-12, atol=1e-12)

@@ -64,6 +64,10 @@ MUTANTS = [
      "tile[z_off + r * 8 + (j ^ 1)] = zeros[row * groups + g];"),
     ("intn_scales_at_the_v1_offset", "int64_t hi_off = 8192, s_off = 8192 + 2048 * hb, z_off = s_off + 1024;",
      "int64_t hi_off = 8192, s_off = 8192 + 1024 * hb, z_off = s_off + 1024;"),
+    ("dq_w4a8_row_scale_dropped", "c->y[mi * c->n + row] = c->per_group ? acc : (double)c->sx[mi] * acc;",
+     "c->y[mi * c->n + row] = acc;"),
+    ("dq_w4a8_scale_code_of_group_0", "double s = (double)c->scode[row * groups + g] * step;",
+     "double s = (double)c->scode[row * groups] * step;"),
     ("dq_gemm_step_of_row_0", "double step = orc_fp16_to_double(c->sstep[row]);",
      "double step = orc_fp16_to_double(c->sstep[0]);"),
 ]
