@@ -24,7 +24,8 @@ result against it.
 
 Other layers of the same path use the same protocol: --op w4a16 with
 --m 2..64 (M > 4 runs the matrix-core kernel), --op w4a16_dq (the scale-code
-weight, M <= 4, bytes = its packed size), --op wn_a16 --bits 5|6 (INT5 / INT6,
+weight, bytes = its packed size; --op w4a8_dq / w4a8_g32_dq the W4A8 forms on it),
+--op wn_a16 --bits 5|6 (INT5 / INT6,
 M = 1, bytes = the packed size), --op w4a8 / w4a8_g32 (M <= 4) and
 --op w8a16 (int8 per-channel, bytes = N*K + 2*N); --n/--k pick the shape.  The
 offline weight quantizers run the same way: --op quantize_int4 / quantize_int4_dq /
@@ -86,7 +87,7 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=1000,
                    help="untimed calls first; the clocks take a few hundred calls to ramp up from idle")
-    p.add_argument("--op", choices=("w4a16", "w4a16_dq", "wn_a16", "w4a8", "w4a8_g32", "w8a16",
+    p.add_argument("--op", choices=("w4a16", "w4a16_dq", "wn_a16", "w4a8", "w4a8_g32", "w4a8_dq", "w4a8_g32_dq", "w8a16",
                                     "quantize_int4", "quantize_int4_dq", "quantize_intn", "quantize_int8"),
                    default="w4a16")
     p.add_argument("--bits", type=int, default=6, help="code width of --op wn_a16 (5 or 6)")
@@ -125,7 +126,7 @@ def main() -> int:
         return bench_quantizer(args, torch, qg, si, dev)
     if op == "w8a16":
         bytes_eff = n * k + 2 * n
-    elif op == "w4a16_dq":
+    elif op in ("w4a16_dq", "w4a8_dq", "w4a8_g32_dq"):
         bytes_eff = qg.int4_dq_packed_bytes(n, k)
     elif op == "wn_a16":
         bytes_eff = qg.intn_packed_bytes(n, k, args.bits)
@@ -152,7 +153,7 @@ def main() -> int:
         else:
             w_cpu, x_cpu = si.int4_weight(n, k, n ^ k), si.activation(m, k, 9100 + m)
         split = args.split or qg.default_split_k(m, n, k)
-        if op == "w4a16_dq":
+        if op in ("w4a16_dq", "w4a8_dq", "w4a8_g32_dq"):
             packed0 = qg.quantize_int4_g32_dq(w_cpu.to(dev))
         elif op == "wn_a16":
             packed0 = qg.quantize_intn_g32(w_cpu.to(dev), args.bits)
@@ -162,7 +163,7 @@ def main() -> int:
         x = x_cpu.to(dev)
         ws = torch.empty(max(qg.workspace_bytes(m, n, k, split), 1), dtype=torch.uint8, device=dev)
         fn = {"w4a16": qg.qgemm_w4a16, "w4a16_dq": qg.qgemm_w4a16_dq, "w4a8": qg.qgemm_w4a8,
-              "w4a8_g32": qg.qgemm_w4a8_g32,
+              "w4a8_g32": qg.qgemm_w4a8_g32, "w4a8_dq": qg.qgemm_w4a8_dq, "w4a8_g32_dq": qg.qgemm_w4a8_g32_dq,
               "wn_a16": lambda *a, **kw: qg.qgemm_wn_a16(*a[:3], args.bits, **kw)}[op]
 
         def call(i):
@@ -217,6 +218,8 @@ def main() -> int:
              "w4a16_dq": "W4A16 INT4-g32 asymmetric, uint8 scale codes x per-row fp16 step",
              "wn_a16": f"W{args.bits}A16 INT{args.bits}-g32 asymmetric",
              "w4a8": "W4A8 INT4-g32 x per-row int8",
+             "w4a8_dq": "W4A8 INT4-g32 (scale codes) x per-row int8",
+             "w4a8_g32_dq": "W4A8 INT4-g32 (scale codes) x per-group-32 int8",
              "w4a8_g32": "W4A8 INT4-g32 x per-group-32 int8", "w8a16": "W8A16 INT8 per-channel"}[op]
     out = {
         "metric": METRIC if headline else
@@ -444,11 +447,13 @@ def cpu_baseline(args, oracle_inputs, y_gpu, bytes_eff):
 
         def run():
             return oracle.qgemm_w4a16(xb, codes, scales, zeros, threads=threads)
-    elif args.op == "w4a16_dq":
+    elif args.op in ("w4a16_dq", "w4a8_dq", "w4a8_g32_dq"):
         codes, scode, sstep, zeros, _ = oracle.quantize_int4_g32_dq(si.bf16_bits(w_cpu))
+        dq_fn = {"w4a16_dq": oracle.qgemm_w4a16_dq, "w4a8_dq": oracle.qgemm_w4a8_dq,
+                 "w4a8_g32_dq": oracle.qgemm_w4a8_g32_dq}[args.op]
 
         def run():
-            return oracle.qgemm_w4a16_dq(xb, codes, scode, sstep, zeros, threads=threads)
+            return dq_fn(xb, codes, scode, sstep, zeros, threads=threads)
     else:
         codes, scales, zeros, _ = oracle.quantize_int4_g32(si.bf16_bits(w_cpu))
         fn = {"w4a16": oracle.qgemm_w4a16, "w4a8": oracle.qgemm_w4a8,

@@ -17,7 +17,9 @@ from .binding import (  # noqa: F401
     int4_packed_bytes,
     intn_packed_bytes,
     qgemm_w4a8,
+    qgemm_w4a8_dq,
     qgemm_w4a8_g32,
+    qgemm_w4a8_g32_dq,
     qgemm_w4a16,
     qgemm_w4a16_dq,
     qgemm_w8a16,

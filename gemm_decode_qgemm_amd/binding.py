@@ -55,6 +55,8 @@ def _load() -> ctypes.CDLL:
         "qgemm_w8a16": (I32, [P, I64, I64, P, P, I64, P, I32, P]),
         "qgemm_w4a8": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "qgemm_w4a8_g32": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
+        "qgemm_w4a8_dq": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
+        "qgemm_w4a8_g32_dq": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -290,3 +292,29 @@ def qgemm_w4a8_g32(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_k: in
                             yd, split_k, _ptr(ws), ws_bytes, _stream(x.device))
     _check(st, "qgemm_w4a8_g32")
     return y
+
+
+def _w4a8_call(fn, name, x, packed, n, split_k, out_dtype, out, workspace):
+    _dev(x, "x", torch.bfloat16, 2)
+    m, k = x.shape
+    y, yd = _out(m, n, out_dtype, x.device, out)
+    ws, ws_bytes = _workspace(m, n, k, split_k, x.device, workspace)
+    st = fn(x.data_ptr(), m, k, packed.data_ptr(), packed.numel(), n, y.data_ptr(), yd, split_k, _ptr(ws),
+            ws_bytes, _stream(x.device))
+    _check(st, name)
+    return y
+
+
+def qgemm_w4a8_dq(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_k: int = 0,
+                  out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """qgemm_w4a8 (per-row int8 activations) on a scale-code packed weight (m <= 4)."""
+    return _w4a8_call(lib.qgemm_w4a8_dq, "qgemm_w4a8_dq", x, packed, n, split_k, out_dtype, out, workspace)
+
+
+def qgemm_w4a8_g32_dq(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_k: int = 0,
+                      out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """qgemm_w4a8_g32 (one activation scale per group of 32) on a scale-code packed weight (m <= 4)."""
+    return _w4a8_call(lib.qgemm_w4a8_g32_dq, "qgemm_w4a8_g32_dq", x, packed, n, split_k, out_dtype, out,
+                      workspace)

@@ -32,6 +32,8 @@ hipError_t launch_wn_a16_mfma(int bits, int m, const void* x, const void* packed
                               int y_f32, float* partial, int split, hipStream_t stream);
 hipError_t launch_w4a16_mfma_dq(int m, const void* x, const void* packed, int n, int k, void* y, int y_f32,
                                 float* partial, int split, hipStream_t stream);
+hipError_t launch_w4a8_dq(int m, bool group_scales, const void* x, const void* packed, int n, int k,
+                          void* y, int y_f32, float* partial, int split, hipStream_t stream);
 hipError_t launch_quantize_int8_rowwise(const void* w, int64_t n, int64_t k, int8_t* q,
                                         void* scales, uint32_t* status, hipStream_t stream);
 hipError_t launch_w4a16_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
@@ -362,7 +364,7 @@ int32_t qgemm_w8a16(const void* x_bf16, int64_t m, int64_t k, const int8_t* w,
 
 static int32_t w4a8_common(const void* x_bf16, int64_t m, int64_t k, const void* packed,
                            int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype, int32_t split_k,
-                           void* ws, int64_t ws_bytes, void* stream, bool group_scales) {
+                           void* ws, int64_t ws_bytes, void* stream, bool group_scales, bool dq = false) {
   if (!x_bf16 || !packed || !y) return QG_E_NULL;
   int32_t st = check_mnk(m, n, k);
   if (st != QG_OK) return st;
@@ -371,14 +373,18 @@ static int32_t w4a8_common(const void* x_bf16, int64_t m, int64_t k, const void*
   int32_t split;
   st = resolve_split(m, n, k, split_k, &split);
   if (st != QG_OK) return st;
-  if (packed_bytes < qg_int4_packed_bytes(n, k)) return QG_E_BUFFER;
+  if (packed_bytes < (dq ? qg_int4_dq_packed_bytes(n, k) : qg_int4_packed_bytes(n, k))) return QG_E_BUFFER;
   const int64_t need_ws = split > 1 ? (int64_t)split * m * n * 4 : 0;
   if (need_ws > 0 && (!ws || ws_bytes < need_ws)) return ws ? QG_E_BUFFER : QG_E_NULL;
   if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || (ws && !aligned16(ws)))
     return QG_E_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
-  if (m > 1) {
+  if (dq) {
+    // the scale-code layout: the 32-row kernels of the branches below
+    st = hip_status(qg::launch_w4a8_dq((int)m, group_scales, x_bf16, packed, (int)n, (int)k, y,
+                                       y_dtype == QG_F32, partial, split, s));
+  } else if (m > 1) {
     // M = 2..4: group dots on the 4x4x4 int8 matrix instruction
     st = hip_status(qg::launch_w4a8_gemv_mx4((int)m, group_scales, x_bf16, packed, (int)n, (int)k,
                                              y, y_dtype == QG_F32, partial, split, s));
@@ -407,6 +413,20 @@ int32_t qgemm_w4a8_g32(const void* x_bf16, int64_t m, int64_t k, const void* pac
                        void* ws, int64_t ws_bytes, void* stream) {
   return w4a8_common(x_bf16, m, k, packed, packed_bytes, n, y, y_dtype, split_k, ws, ws_bytes,
                      stream, true);
+}
+
+int32_t qgemm_w4a8_dq(const void* x_bf16, int64_t m, int64_t k, const void* packed,
+                      int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype, int32_t split_k,
+                      void* ws, int64_t ws_bytes, void* stream) {
+  return w4a8_common(x_bf16, m, k, packed, packed_bytes, n, y, y_dtype, split_k, ws, ws_bytes,
+                     stream, false, true);
+}
+
+int32_t qgemm_w4a8_g32_dq(const void* x_bf16, int64_t m, int64_t k, const void* packed,
+                          int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype, int32_t split_k,
+                          void* ws, int64_t ws_bytes, void* stream) {
+  return w4a8_common(x_bf16, m, k, packed, packed_bytes, n, y, y_dtype, split_k, ws, ws_bytes,
+                     stream, true, true);
 }
 
 }  // extern "C"

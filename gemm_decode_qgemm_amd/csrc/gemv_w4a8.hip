@@ -212,7 +212,7 @@ __global__ __launch_bounds__(WAVES * 64) void w4a8_gemv_kernel(
 template <int M, int JJ>
 __device__ __forceinline__ void do_group_a8_32(float (&acc)[M], const Half32Regs& cur,
                                                const uint32_t (&xlo)[M], const uint32_t (&xhi)[M],
-                                               const int (&sxq)[M], uint32_t nib_s) {
+                                               const int (&sxq)[M], uint32_t nib_s, float s) {
   const u32x4_t cv = cur.c[JJ];
   const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
   uint32_t lo[4], hi[4];
@@ -221,7 +221,6 @@ __device__ __forceinline__ void do_group_a8_32(float (&acc)[M], const Half32Regs
     lo[d] = cw[d] & nib_s;
     hi[d] = (cw[d] >> 4) & nib_s;
   }
-  const float s = fp16_to_f32(JJ == 0 ? (cur.sc & 0xffffu) : (cur.sc >> 16));
   const int zp = (int)((cur.zb >> (4 * JJ)) & 15u);
 #pragma unroll
   for (int m = 0; m < M; ++m) {
@@ -233,7 +232,7 @@ __device__ __forceinline__ void do_group_a8_32(float (&acc)[M], const Half32Regs
   }
 }
 
-template <int M, int WAVES>
+template <int M, int WAVES, bool DQ = false>
 __global__ __launch_bounds__(WAVES * 64) void w4a8_gemv32_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -248,7 +247,9 @@ __global__ __launch_bounds__(WAVES * 64) void w4a8_gemv32_kernel(
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
-  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
+  using L = W4Layout<DQ>;
+  float step;
+  const uint8_t* tiles = L::tiles(packed, rb, kt_count, row, step);
 
   // Per-row absmax of x over the whole K (every split needs the same scale).
 #pragma unroll
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(WAVES * 64) void w4a8_gemv32_kernel(
 
   for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {
     Half32Regs r;
-    load_half32<true>(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lg, row);
+    L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
     uint32_t xlo[M], xhi[M];
     int sxq[M];
 #pragma unroll
@@ -303,8 +304,8 @@ __global__ __launch_bounds__(WAVES * 64) void w4a8_gemv32_kernel(
       p += dpp_i<0x4E>(p);
       sxq[m] = p;
     }
-    do_group_a8_32<M, 0>(acc, r, xlo, xhi, sxq, nib_s);
-    do_group_a8_32<M, 1>(acc, r, xlo, xhi, sxq, nib_s);
+    do_group_a8_32<M, 0>(acc, r, xlo, xhi, sxq, nib_s, L::scale(r.sc, 0, step));
+    do_group_a8_32<M, 1>(acc, r, xlo, xhi, sxq, nib_s, L::scale(r.sc, 1, step));
   }
 
   // Sum over waves and over the two lane halves (same row), in a fixed order.
@@ -354,7 +355,7 @@ __device__ __forceinline__ float dpp_fa(float v) {
                                                                CTRL, 0xf, 0xf, true));
 }
 
-template <int M>
+template <int M, bool DQ = false>
 __global__ __launch_bounds__(1024) void w4a8_gemv_lds_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -372,7 +373,9 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_lds_kernel(
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
-  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
+  using L = W4Layout<DQ>;
+  float step;
+  const uint8_t* tiles = L::tiles(packed, rb, kt_count, row, step);
 
   const uint32_t nib_s = __builtin_amdgcn_readfirstlane(0x0F0F0F0Fu);
   uint32_t ones_v = 0x01010101u;
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_lds_kernel(
     const int nh = min(kA8Chunk, h1 - cb);       // half tiles in this chunk
     const int hs = cb + wave;                     // this wave's half tile
     Half32Regs r;
-    if (wave < nh) load_half32<true>(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lg, row);
+    if (wave < nh) L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
 
     // ---- quantize the chunk: thread -> (m, segment); a chunk's segment count
     // is a multiple of 16, so lane quads are whole for the DPP max.
@@ -439,7 +442,7 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_lds_kernel(
           lo[d] = cw[d] & nib_s;
           hi[d] = (cw[d] >> 4) & nib_s;
         }
-        const float s = fp16_to_f32(jj == 0 ? (r.sc & 0xffffu) : (r.sc >> 16));
+        const float s = L::scale(r.sc, jj, step);
         const int zp = (int)((r.zb >> (4 * jj)) & 15u);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
@@ -513,7 +516,7 @@ __device__ __forceinline__ float absmax8(const u32x4_t& v, float a) {
   return a;
 }
 
-template <int M, bool GS>
+template <int M, bool GS, bool DQ = false>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void w4a8_gemv_mx4_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -533,7 +536,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
-  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
+  using L = W4Layout<DQ>;
+  float step;
+  const uint8_t* tiles = L::tiles(packed, rb, kt_count, row, step);
   // Quantizing lanes: l < 16 M takes k = 8 (l % 16) .. + 8 of x row l / 16.
   const bool qlane = lane < 16 * M;
   const int qm = qlane ? lane >> 4 : 0, qs = lane & 15;
@@ -560,7 +565,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
     // with the x loads): a wave without a half tile loads the range's last
     // one, which another wave reads as well (an L2 hit), and discards it.
     const int hf = hs < h_end ? hs : h_end - 1;
-    load_half32<true>(r, tiles + (size_t)(hf >> 1) * kTileBytes, hf & 1, lg, row);
+    L::load(r, tiles + (size_t)(hf >> 1) * L::kTile, hf & 1, lg, row);
     float am[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) am[m] = absmax8(v0[m], 0.0f);
@@ -592,7 +597,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
       sx_row[m] = a / 127.0f;
     }
   } else {
-    if (hs < h_end) load_half32<true>(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lg, row);
+    if (hs < h_end) L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
   }
 
   const uint32_t nib_s = __builtin_amdgcn_readfirstlane(0x0F0F0F0Fu);
@@ -604,7 +609,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 
   for (bool first = true; hs < h_end; hs += WAVES, first = false) {   // tile hs/2, half hs%2
-    if (!first) load_half32<true>(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lg, row);
+    if (!first) L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
     u32x4_t v = {0u, 0u, 0u, 0u};
     if (qlane) v = *reinterpret_cast<const u32x4_t*>(xsrc + (size_t)hs * 128);
     // ---- quantize this lane's segment; the quad holds one group of 32.
@@ -660,7 +665,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
         d = mfma_i8_4x4x4(xa[2 * dd + 1], (cw[dd] >> 4) & nib_s, d);
       }
       const i32x4_t sg = *reinterpret_cast<const i32x4_t*>(&gsum_s[wave][g][0]);
-      const float s = fp16_to_f32(jj == 0 ? (r.sc & 0xffffu) : (r.sc >> 16));
+      const float s = L::scale(r.sc, jj, step);
       const int zp = (int)((r.zb >> (4 * jj)) & 15u);
       f32x4_t sxg = {0.0f, 0.0f, 0.0f, 0.0f};
       if constexpr (GS) sxg = *reinterpret_cast<const f32x4_t*>(&gsx_s[wave][g][0]);
@@ -697,11 +702,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
   }
 }
 
-template <int M, bool GS>
+template <int M, bool GS, bool DQ = false>
 static hipError_t launch_w4a8_mx4_t(const void* x, const void* packed, int n, int k, void* y,
                                     int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a8_gemv_mx4_kernel<M, GS>), dim3(2 * rbs, split), dim3(1024), 0, stream,
+  hipLaunchKernelGGL((w4a8_gemv_mx4_kernel<M, GS, DQ>), dim3(2 * rbs, split), dim3(1024), 0, stream,
                      static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed), n, k,
                      y, y_f32, partial, split);
   return hipGetLastError();
@@ -719,11 +724,11 @@ hipError_t launch_w4a8_gemv_mx4(int m, bool group_scales, const void* x, const v
   return hipErrorInvalidValue;
 }
 
-template <int M>
+template <int M, bool DQ = false>
 static hipError_t launch_w4a8_lds_t(const void* x, const void* packed, int n, int k, void* y,
                                     int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a8_gemv_lds_kernel<M>), dim3(2 * rbs, split), dim3(1024), 0, stream,
+  hipLaunchKernelGGL((w4a8_gemv_lds_kernel<M, DQ>), dim3(2 * rbs, split), dim3(1024), 0, stream,
                      static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed), n, k,
                      y, y_f32, partial, split);
   return hipGetLastError();
@@ -738,11 +743,11 @@ hipError_t launch_w4a8_gemv_lds(int m, bool group_scales, const void* x, const v
   return hipErrorInvalidValue;
 }
 
-template <int M, int WAVES>
+template <int M, int WAVES, bool DQ = false>
 static hipError_t launch_w4a8_32_t(const void* x, const void* packed, int n, int k, void* y,
                                    int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a8_gemv32_kernel<M, WAVES>), dim3(2 * rbs, split), dim3(WAVES * 64), 0,
+  hipLaunchKernelGGL((w4a8_gemv32_kernel<M, WAVES, DQ>), dim3(2 * rbs, split), dim3(WAVES * 64), 0,
                      stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
                      n, k, y, y_f32, partial, split);
   return hipGetLastError();
@@ -770,6 +775,23 @@ hipError_t launch_w4a8_gemv(int m, const void* x, const void* packed, int n, int
   QG_A8_M(1)
 #undef QG_A8_M
 #undef QG_A8_CASE
+  return hipErrorInvalidValue;
+}
+
+// The scale-code layout (version 2): the 32-row kernels above reading it
+// through W4Layout<true>; M = 1 per row on w4a8_gemv32_kernel, M = 1 per
+// group on w4a8_gemv_lds_kernel, M = 2..4 on w4a8_gemv_mx4_kernel.
+hipError_t launch_w4a8_dq(int m, bool group_scales, const void* x, const void* packed, int n, int k,
+                          void* y, int y_f32, float* partial, int split, hipStream_t stream) {
+  if (m == 1)
+    return group_scales ? launch_w4a8_lds_t<1, true>(x, packed, n, k, y, y_f32, partial, split, stream)
+                        : launch_w4a8_32_t<1, 16, true>(x, packed, n, k, y, y_f32, partial, split, stream);
+#define QG_A8D(MM)                                                                                       \
+  if (m == MM)                                                                                           \
+    return group_scales ? launch_w4a8_mx4_t<MM, true, true>(x, packed, n, k, y, y_f32, partial, split, stream) \
+                        : launch_w4a8_mx4_t<MM, false, true>(x, packed, n, k, y, y_f32, partial, split, stream);
+  QG_A8D(2) QG_A8D(3) QG_A8D(4)
+#undef QG_A8D
   return hipErrorInvalidValue;
 }
 

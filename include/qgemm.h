@@ -282,6 +282,20 @@ int32_t qgemm_w4a8_g32(const void *x_bf16, int64_t m, int64_t k, const void *pac
                        int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
                        int32_t split_k, void *ws, int64_t ws_bytes, void *stream);
 
+/* ---- qgemm_w4a8_dq / qgemm_w4a8_g32_dq -----------------------------------
+ * qgemm_w4a8 and qgemm_w4a8_g32 on a version 2 (scale-code) weight: the
+ * same activation quantization, a group's weight scale c[n,g] * step[n]:
+ *   per row:      y = sx[m] * sum_g c*step * sum_{k in g} xq (q - zp)
+ *   per group 32: y = sum_g sx[m,g] * c*step * sum_{k in g} xq (q - zp).
+ * Arguments, workspace and errors as qgemm_w4a8 (1 <= m <= 4), with
+ * packed_bytes checked against qg_int4_dq_packed_bytes. */
+int32_t qgemm_w4a8_dq(const void *x_bf16, int64_t m, int64_t k, const void *packed,
+                      int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
+                      int32_t split_k, void *ws, int64_t ws_bytes, void *stream);
+int32_t qgemm_w4a8_g32_dq(const void *x_bf16, int64_t m, int64_t k, const void *packed,
+                          int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
+                          int32_t split_k, void *ws, int64_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,6 +47,8 @@ def lib():
         "qgemm_w8a16": (I32, [P, I64, I64, P, P, I64, P, I32, P]),
         "qgemm_w4a8": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "qgemm_w4a8_g32": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
+        "qgemm_w4a8_dq": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
+        "qgemm_w4a8_g32_dq": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(l, name)
@@ -159,12 +161,17 @@ def test_qgemm_w4a16_and_w4a8_validate_before_launching(lib, args, expect):
     # W4A8 (both activation granularities) shares the rules
     assert lib.qgemm_w4a8(*args) == expect
     assert lib.qgemm_w4a8_g32(*args) == expect
+    assert lib.qgemm_w4a8_dq(*args) == expect
+    assert lib.qgemm_w4a8_g32_dq(*args) == expect
 
 
 def test_w4a8_m_range(lib):
     assert lib.qgemm_w4a8(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
     assert lib.qgemm_w4a8_g32(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
     assert lib.qgemm_w4a16_dq(A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
+    assert lib.qgemm_w4a8_dq(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
+    assert lib.qgemm_w4a8_g32_dq(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
+    assert lib.qgemm_w4a8_dq(A, 1, 256, A, 9087, 64, A, 0, 0, None, 0, None) == E_BUF
     # 9088 bytes hold a 64 x 256 scale-code weight, 9087 do not
     assert lib.qgemm_w4a16_dq(A, 1, 256, A, 9087, 64, A, 0, 0, None, 0, None) == E_BUF
 

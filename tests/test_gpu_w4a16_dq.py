@@ -16,7 +16,7 @@ import torch
 import oracle
 import synthetic_inputs as si
 from golden_io import read_cases
-from tolerance import assert_w16
+from tolerance import assert_w16, assert_w4a8_class
 
 pytestmark = pytest.mark.gpu
 
@@ -215,3 +215,53 @@ def test_w4a16_dq_large_buckets(dev, n, k, m):
     for split in (0, 2):
         y = qg.qgemm_w4a16_dq(x.to(dev), packed, n, split_k=split, out_dtype=torch.float32)
         assert_w16(y, ref, f"{n}x{k} M={m} split={split}")
+
+
+# ------------------------------------------------------------------ W4A8 on scale codes
+
+@pytest.mark.parametrize("per_group", [False, True])
+@pytest.mark.parametrize("n,k", [(768, 256), (257, 512), (1536, 512)])
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_w4a8_dq_small_shapes(dev, per_group, n, k, m):
+    w, codes, scode, sstep, zeros = _weight(n, k, n + k)
+    packed = qg.quantize_int4_g32_dq(w.to(dev))
+    x = si.activation(m, k, 1400 + n + m)
+    xb = si.bf16_bits(x)
+    fn, ref_fn = ((qg.qgemm_w4a8_g32_dq, oracle.qgemm_w4a8_g32_dq) if per_group
+                  else (qg.qgemm_w4a8_dq, oracle.qgemm_w4a8_dq))
+    ref = ref_fn(xb, codes, scode, sstep, zeros)
+    for dt in (torch.float32, torch.bfloat16):
+        assert_w16(fn(x.to(dev), packed, n, out_dtype=dt), ref, f"{n}x{k} M={m} group={per_group} {dt}")
+
+
+@pytest.mark.parametrize("n,k", [(8448, 6656), (6656, 19968)])
+def test_w4a8_dq_config_shapes(dev, n, k):
+    """The W4A8 layer shapes and buckets 1..4: parity with the W4A8 oracle and
+    the pages' precision class against the W4A16 oracle."""
+    w, codes, scode, sstep, zeros = _weight(n, k, si.model_weight_seed(n, k))
+    packed = qg.quantize_int4_g32_dq(w.to(dev))
+    i = si.model_shape_index(n, k)
+    for m in si.DECODE_M:
+        print(f"qgemm_w4a8_dq {n}x{k} M={m}", flush=True)
+        x = si.activation(m, k, si.model_activation_seed(i, m))
+        xb = si.bf16_bits(x)
+        ref16 = _ref(x, codes, scode, sstep, zeros)
+        for fn, ref_fn in ((qg.qgemm_w4a8_dq, oracle.qgemm_w4a8_dq), (qg.qgemm_w4a8_g32_dq, oracle.qgemm_w4a8_g32_dq)):
+            y = fn(x.to(dev), packed, n, out_dtype=torch.float32)
+            assert_w16(y, ref_fn(xb, codes, scode, sstep, zeros, threads=oracle.hardware_threads()),
+                       f"{fn.__name__} {n}x{k} M={m}")
+            assert_w4a8_class(y, ref16, f"{fn.__name__} vs W4A16 {n}x{k} M={m}")
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_w4a8_dq_every_split(dev, m):
+    n, k = 257, 6656
+    w, codes, scode, sstep, zeros = _weight(n, k, 31)
+    packed = qg.quantize_int4_g32_dq(w.to(dev))
+    x = si.activation(m, k, 90 + m)
+    xb = si.bf16_bits(x)
+    for fn, ref_fn in ((qg.qgemm_w4a8_dq, oracle.qgemm_w4a8_dq), (qg.qgemm_w4a8_g32_dq, oracle.qgemm_w4a8_g32_dq)):
+        ref = ref_fn(xb, codes, scode, sstep, zeros)
+        for split in si.SPLITS:
+            y = fn(x.to(dev), packed, n, split_k=split, out_dtype=torch.float32)
+            assert_w16(y, ref, f"{fn.__name__} M={m} split={split}")
