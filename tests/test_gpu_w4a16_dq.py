@@ -265,3 +265,27 @@ def test_w4a8_dq_every_split(dev, m):
         for split in si.SPLITS:
             y = fn(x.to(dev), packed, n, split_k=split, out_dtype=torch.float32)
             assert_w16(y, ref, f"{fn.__name__} M={m} split={split}")
+
+
+def test_w4a8_dq_graph_replay_bit_identical(dev):
+    n, k = 6656, 19968
+    w, *_ = _weight(n, k, si.model_weight_seed(n, k))
+    packed = qg.quantize_int4_g32_dq(w.to(dev))
+    for fn in (qg.qgemm_w4a8_dq, qg.qgemm_w4a8_g32_dq):
+        for m, split in ((1, 1), (4, 1), (2, 4)):
+            x = si.activation(m, k, 120 + m).to(dev)
+            eager = fn(x, packed, n, split_k=split)
+            assert torch.equal(eager, fn(x, packed, n, split_k=split))
+            out = torch.empty_like(eager)
+            ws = torch.empty(max(qg.workspace_bytes(m, n, k, split), 1), dtype=torch.uint8, device=dev)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn(x, packed, n, split_k=split, out=out, workspace=ws)
+            for _ in range(3):
+                out.zero_()
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                assert torch.equal(out, eager), f"{fn.__name__} replay differs (m={m}, split={split})"
+                _ = fn(x, packed, n, split_k=1)
