@@ -42,6 +42,7 @@ def _load() -> ctypes.CDLL:
         "qg_status_string": (ctypes.c_char_p, [I32]),
         "qg_int4_packed_bytes": (I64, [I64, I64]),
         "qg_default_split_k": (I32, [I64, I64, I64]),
+        "qg_default_split_k_intn": (I32, [I64, I64, I64]),
         "qg_workspace_bytes": (I64, [I64, I64, I64, I32]),
         "qg_int4_dq_packed_bytes": (I64, [I64, I64]),
         "qg_intn_packed_bytes": (I64, [I64, I64, I32]),
@@ -114,8 +115,12 @@ def intn_packed_bytes(n: int, k: int, bits: int) -> int:
     return v
 
 
-def default_split_k(m: int, n: int, k: int) -> int:
-    v = int(lib.qg_default_split_k(m, n, k))
+def default_split_k(m: int, n: int, k: int, bits: int = 4) -> int:
+    """The library's split for split_k = 0: INT4 layouts (bits = 4), or INT5 / INT6."""
+    if bits == 4:
+        v = int(lib.qg_default_split_k(m, n, k))
+    else:
+        v = int(lib.qg_default_split_k_intn(m, n, k))
     _check(min(v, 0), "qg_default_split_k")
     return v
 

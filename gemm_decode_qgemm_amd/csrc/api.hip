@@ -130,9 +130,27 @@ GemvShape gemv_shape(int64_t m, int64_t n, int32_t split) {
   return {32, 16};
 }
 
-int32_t resolve_split(int64_t m, int64_t n, int64_t k, int32_t split_k, int32_t* out) {
+// INT5 / INT6 on the matrix cores (M > 4) carry more work per weight than
+// INT4, and more splits pay (measured on the INT6 layers of the 30B export,
+// buckets 16 and 64: 5376 x 21504 best at 8, 4096 x 5376 and 6656 x 19968 at
+// 4, 1024 x 6656 at 8): the smallest split with 64-row blocks x split >= 400,
+// at most 8, and one step back when that leaves under 4 tiles of 256 k per
+// workgroup while the grid still has a workgroup per CU.  M <= 4 keeps the
+// INT4 rule (5376 x 21504 M = 1: 21.3 us at 1 against 19.9 at 4).
+int32_t default_split_intn(int64_t m, int64_t n, int64_t k) {
+  if (m <= 4) return default_split(m, n, k);
+  const int64_t kt = k / QG_TILE_K;
+  const int64_t rbs = (n + QG_TILE_ROWS - 1) / QG_TILE_ROWS;
+  int32_t s = 1;
+  while (s < 8 && 2 * s <= kt && rbs * s < 400) s *= 2;
+  if (s > 1 && kt < 4 * s && rbs * (s / 2) >= kCUs) s /= 2;
+  return s;
+}
+
+int32_t resolve_split(int64_t m, int64_t n, int64_t k, int32_t split_k, int32_t* out,
+                      bool intn = false) {
   if (split_k == 0) {
-    *out = default_split(m, n, k);
+    *out = intn ? default_split_intn(m, n, k) : default_split(m, n, k);
     return QG_OK;
   }
   if (split_k != 1 && split_k != 2 && split_k != 4 && split_k != 8) return QG_E_SPLIT;
@@ -195,7 +213,15 @@ int64_t qg_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k) {
   int32_t split;
   st = resolve_split(m, n, k, split_k, &split);
   if (st != QG_OK) return st;
+  // split_k = 0: enough for the default of every entry point
+  if (split_k == 0) split = split > default_split_intn(m, n, k) ? split : default_split_intn(m, n, k);
   return split > 1 ? (int64_t)split * m * n * 4 : 0;
+}
+
+int32_t qg_default_split_k_intn(int64_t m, int64_t n, int64_t k) {
+  int32_t st = check_mnk(m, n, k);
+  if (st != QG_OK) return st;
+  return default_split_intn(m, n, k);
 }
 
 int32_t quantize_int4_g32(const void* w_bf16, int64_t n, int64_t k, void* packed,
@@ -324,7 +350,7 @@ int32_t qgemm_wn_a16(const void* x_bf16, int64_t m, int64_t k, int32_t bits, con
   if (bits != 5 && bits != 6) return QG_E_BITS;
   if (y_dtype != QG_BF16 && y_dtype != QG_F32) return QG_E_DTYPE;
   int32_t split;
-  st = resolve_split(m, n, k, split_k, &split);
+  st = resolve_split(m, n, k, split_k, &split, true);
   if (st != QG_OK) return st;
   if (packed_bytes < qg_intn_packed_bytes(n, k, bits)) return QG_E_BUFFER;
   const int64_t need_ws = split > 1 ? (int64_t)split * m * n * 4 : 0;

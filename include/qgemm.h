@@ -113,9 +113,18 @@ int64_t qg_int4_packed_bytes(int64_t n, int64_t k);
  * (a static table keyed by the shape), or a negative qg_status. */
 int32_t qg_default_split_k(int64_t m, int64_t n, int64_t k);
 
-/* Workspace bytes a qgemm_w4a16 / qgemm_w4a8 call needs for (m, n, k,
- * split_k): split * m * n * 4 (fp32 partial sums) when the resolved split is
- * above 1, else 0.  Negative qg_status on bad arguments. */
+/* The split-K factor qgemm_wn_a16 (INT5 / INT6) uses for split_k = 0: the
+ * table above for m <= 4; for m > 4 the smallest split with
+ * ceil(n/64) * split >= 400 (at most 8, at most k/256), one step smaller when
+ * that leaves under 4 tiles of 256 k per split while ceil(n/64) * split/2
+ * still reaches 256.  Negative qg_status on bad arguments. */
+int32_t qg_default_split_k_intn(int64_t m, int64_t n, int64_t k);
+
+/* Workspace bytes a qgemm call needs for (m, n, k, split_k): split * m * n * 4
+ * (fp32 partial sums) when the split is above 1, else 0.  For split_k = 0
+ * the larger of the two defaults (qg_default_split_k, qg_default_split_k_intn)
+ * is assumed, so one workspace serves every entry point's default.  Negative
+ * qg_status on bad arguments. */
 int64_t qg_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k);
 
 /* ---- quantize_int4_g32 ---------------------------------------------------

@@ -34,6 +34,7 @@ def lib():
         "qg_status_string": (ctypes.c_char_p, [I32]),
         "qg_int4_packed_bytes": (I64, [I64, I64]),
         "qg_default_split_k": (I32, [I64, I64, I64]),
+        "qg_default_split_k_intn": (I32, [I64, I64, I64]),
         "qg_workspace_bytes": (I64, [I64, I64, I64, I32]),
         "qg_int4_dq_packed_bytes": (I64, [I64, I64]),
         "qg_intn_packed_bytes": (I64, [I64, I64, I32]),
@@ -135,6 +136,17 @@ def test_default_split_table(lib):
     assert lib.qg_default_split_k(48, 6656, 4096) == 4
     assert lib.qg_default_split_k(17, 5376, 4096) == 4
     assert lib.qg_default_split_k(65, 256, 256) == E_M
+    # INT5 / INT6, M > 4: ceil(N/64) * split >= 400, one step back under 4 tiles per split
+    # while a workgroup per CU remains (measured on the INT6 layers)
+    for m in (16, 64):
+        assert lib.qg_default_split_k_intn(m, 5376, 21504) == 8
+        assert lib.qg_default_split_k_intn(m, 6656, 19968) == 4
+        assert lib.qg_default_split_k_intn(m, 4096, 5376) == 4
+        assert lib.qg_default_split_k_intn(m, 1024, 6656) == 8
+    assert lib.qg_default_split_k_intn(1, 5376, 21504) == lib.qg_default_split_k(1, 5376, 21504) == 1
+    assert lib.qg_default_split_k_intn(64, 256, 512) == 2                  # capped by K / 256
+    # one workspace serves both defaults
+    assert lib.qg_workspace_bytes(64, 5376, 21504, 0) == 8 * 64 * 5376 * 4
 
 
 @pytest.mark.parametrize("args,expect", [

@@ -56,11 +56,11 @@ def _graph_us(fn, calls: int = 200, replays: int = 7) -> float:
     return statistics.median(times)
 
 
-def _regrets(shapes, buckets, seed_of):
+def _regrets(shapes, buckets, seed_of, quant=qg.quantize_int4_g32, gemm=qg.qgemm_w4a16, bits=4):
     dev = torch.device("cuda:0")
     rows = []
     for n, k in shapes:
-        p0 = qg.quantize_int4_g32(si.int4_weight(n, k, seed_of(n, k)).to(dev))
+        p0 = quant(si.int4_weight(n, k, seed_of(n, k)).to(dev))
         copies = max(2, math.ceil((1 << 30) / p0.numel()))
         packs = [p0] + [p0.clone() for _ in range(copies - 1)]
         for m in buckets:
@@ -70,8 +70,8 @@ def _regrets(shapes, buckets, seed_of):
             for split in [s for s in si.SPLITS if s <= k // 256]:
                 ws = torch.empty(max(qg.workspace_bytes(m, n, k, split), 1), dtype=torch.uint8, device=dev)
                 times[split] = _graph_us(
-                    lambda i: qg.qgemm_w4a16(x, packs[i % copies], n, split_k=split, out=y, workspace=ws))
-            pick = qg.default_split_k(m, n, k)
+                    lambda i: gemm(x, packs[i % copies], n, split_k=split, out=y, workspace=ws))
+            pick = qg.default_split_k(m, n, k, bits)
             best = min(times, key=times.get)
             rows.append(dict(n=n, k=k, m=m, pick=pick, best=best, times=times,
                              regret=times[pick] / times[best]))
@@ -104,5 +104,17 @@ def test_default_split_regret_on_the_layer_shapes():
 
 def test_default_split_regret_matrix_core_buckets():
     rows = _regrets(((39936, 6656), (8448, 6656), (6656, 19968)), (16, 32, 48, 64), lambda n, k: n ^ k)
+    worst = max(rows, key=lambda r: r["regret"])
+    assert worst["regret"] <= MAX_REGRET, worst
+
+
+# The INT6 layers of the same pull request, tuned there at buckets 1, 4, 16 and 64.
+INT6_SHAPES = ((4096, 5376), (5376, 21504), (6656, 19968), (1024, 6656))
+
+
+def test_default_split_regret_int6_layers():
+    rows = _regrets(INT6_SHAPES, (1, 4, 16, 64), lambda n, k: n ^ k,
+                    quant=lambda w: qg.quantize_intn_g32(w, 6),
+                    gemm=lambda x, p, n, **kw: qg.qgemm_wn_a16(x, p, n, 6, **kw), bits=6)
     worst = max(rows, key=lambda r: r["regret"])
     assert worst["regret"] <= MAX_REGRET, worst
