@@ -382,15 +382,19 @@ void orc_qgemm_w8a16(const uint16_t *x, int64_t m, int64_t k, const int8_t *w,
 /* ------------------------------------------------------------------ */
 /* Symmetric absmax int8 quantization of one span of activations:
  * a = max |x|; a == 0 gives xq = 0, sx = 0; otherwise inv = 127/a and
- * sx = a/127 (binary32 divisions), xq = clamp(rint(x * inv), -127, 127). */
+ * sx = a/127 (binary32 divisions), xq = clamp(rint(x * inv), -127, 127).
+ * A span holding a NaN or an infinity has no finite scale: it gets sx = NaN
+ * and codes 0, so every output it contributes to is NaN. */
 static void quant_span(const uint16_t *xr, int64_t len, int8_t *xq, float *sx) {
     float a = 0.0f;
+    int finite = 1;
     for (int64_t i = 0; i < len; i++) {
         float v = fabsf(bf16_to_float(xr[i]));
-        if (v > a) a = v;
+        if (!isfinite(v)) finite = 0;
+        else if (v > a) a = v;
     }
-    if (a == 0.0f) {
-        *sx = 0.0f;
+    if (!finite || a == 0.0f) {
+        *sx = finite ? 0.0f : NAN;
         for (int64_t i = 0; i < len; i++) xq[i] = 0;
         return;
     }

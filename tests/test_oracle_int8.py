@@ -177,3 +177,33 @@ def test_w4a8_zero_row_gives_zero():
     x[1] = bf16_bits(activation(1, 256, 2))[0]
     y = oracle.qgemm_w4a8(x, codes, scales, zeros)
     assert (y[0] == 0).all() and (y[1] != 0).any()
+
+
+# Reading: a span of activations holding a NaN or an infinity has no finite
+# absmax scale; it gets sx = NaN and codes 0, and every output it reaches is NaN.
+NON_FINITE = {"nan": 0x7FC0, "+inf": 0x7F80, "-inf": 0xFF80}
+
+
+@pytest.mark.parametrize("kind", sorted(NON_FINITE))
+def test_actquant_non_finite_row(kind):
+    x = bf16_bits(activation(3, 512, seed=21))
+    clean_q, clean_s = oracle.actquant_int8(x)
+    x[1, 300] = NON_FINITE[kind]
+    xq, sx = oracle.actquant_int8(x)
+    assert np.isnan(sx[1]) and (xq[1] == 0).all()
+    # the other rows are quantized as if the bad row were absent
+    for r in (0, 2):
+        assert sx[r] == clean_s[r] and (xq[r] == clean_q[r]).all()
+
+
+@pytest.mark.parametrize("kind", sorted(NON_FINITE))
+def test_w4a8_non_finite_activation_reaches_every_output_of_its_row(kind):
+    m, n, k = 3, 70, 512
+    codes, scales, zeros, _ = oracle.quantize_int4_g32(bf16_bits(int4_weight(n, k, 8)))
+    x = bf16_bits(activation(m, k, 9))
+    clean = oracle.qgemm_w4a8(x, codes, scales, zeros)
+    x[2, 0] = NON_FINITE[kind]
+    y = oracle.qgemm_w4a8(x, codes, scales, zeros)
+    assert np.isnan(y[2]).all()
+    np.testing.assert_array_equal(y[:2], clean[:2])
+    assert np.isfinite(y[:2]).all()

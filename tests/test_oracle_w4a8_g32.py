@@ -173,3 +173,26 @@ def test_precision_class_against_dense_small_shapes(n, k):
             if outl and precision_class_failures(oracle.qgemm_w4a8(xb, codes, scales, zeros), a16, ref_dense):
                 row_failed = True
     assert row_failed, "per-row activation scales unexpectedly pass the outlier case here"
+
+
+@pytest.mark.parametrize("bits", [0x7FC0, 0x7F80, 0xFF80], ids=["nan", "+inf", "-inf"])
+def test_non_finite_activation_poisons_its_group_and_row_only(bits):
+    """A NaN or infinite activation leaves its group of 32 without a finite
+    scale (sx = NaN, codes 0); that group reaches every output of the row,
+    which become NaN, and no other group or row changes."""
+    m, n, k = 2, 40, 512
+    codes, scales, zeros, _ = oracle.quantize_int4_g32(si.bf16_bits(si.int4_weight(n, k, 3)))
+    x = si.bf16_bits(si.activation(m, k, 4))
+    clean_q, clean_s = oracle.actquant_int8_g32(x)
+    clean_y = oracle.qgemm_w4a8_g32(x, codes, scales, zeros)
+    x[0, 5 * 32 + 17] = bits
+    xq, sx = oracle.actquant_int8_g32(x)
+    assert np.isnan(sx[0, 5]) and (xq[0, 160:192] == 0).all()
+    keep = np.ones(sx.shape, bool)
+    keep[0, 5] = False
+    np.testing.assert_array_equal(sx[keep], clean_s[keep])
+    np.testing.assert_array_equal(np.delete(xq[0], np.s_[160:192]), np.delete(clean_q[0], np.s_[160:192]))
+    np.testing.assert_array_equal(xq[1], clean_q[1])
+    y = oracle.qgemm_w4a8_g32(x, codes, scales, zeros)
+    assert np.isnan(y[0]).all()
+    np.testing.assert_array_equal(y[1], clean_y[1])
