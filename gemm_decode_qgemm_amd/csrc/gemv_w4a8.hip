@@ -6,7 +6,8 @@
 // held to the W4A16 reference's precision class.  Each row of x is quantized
 // inside the call, per row and symmetric:
 //   a = max|x[m,:]|, inv = 127/a, sx = a/127 (binary32 divisions),
-//   xq = clamp(rint(x * inv), -127, 127) (one binary32 multiply), a == 0 -> 0;
+//   xq = clamp(rint(x * inv), -127, 127) (one binary32 multiply), a == 0 -> 0,
+//   and a row holding a NaN or an infinity gets sx = NaN (no finite scale);
 // then y[m,n] = sx[m] * sum_g s[n,g] * I[m,n,g] with the exact integer group
 // dot I = sum_{k in g} xq[m,k] * (q[n,k] - zp[n,g]).
 //
@@ -61,6 +62,19 @@ __device__ __forceinline__ void group_dot4(int& i0, int& i1, uint32_t xlo, uint3
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
   return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, true);
+}
+
+// The absmax keeps a NaN: nmax is the IEEE 754-2019 maximum (one
+// v_maximum3_f32 on gfx950), which returns NaN when either input is NaN,
+// where fmaxf would return the other input.  An infinity survives any max.
+__device__ __forceinline__ float nmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// A span whose absmax is not finite (it holds a NaN or an infinity) has no
+// finite scale: its absmax becomes NaN, which gives inv = 0 through
+// a > 0 ? 127 / a : 0 and sx = a / 127 = NaN, so every output the span
+// reaches is NaN.
+__device__ __forceinline__ float finite_or_nan(float a) {
+  return a < __builtin_inff() ? a : __builtin_nanf("");
 }
 
 // Quantize 8 bf16 (one 16-byte load) to int8 with the row's inverse scale,
@@ -133,12 +147,12 @@ __global__ __launch_bounds__(WAVES * 64) void w4a8_gemv_kernel(
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        a = fmaxf(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
-        a = fmaxf(a, fabsf(bf16_to_f32(w[j] >> 16)));
+        a = nmax(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
+        a = nmax(a, fabsf(bf16_to_f32(w[j] >> 16)));
       }
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    for (int off = 32; off > 0; off >>= 1) a = nmax(a, __shfl_xor(a, off, 64));
     if (lane == 0) amax_w[wave][m] = a;
   }
   __syncthreads();
@@ -146,7 +160,8 @@ __global__ __launch_bounds__(WAVES * 64) void w4a8_gemv_kernel(
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     float a = amax_w[0][m];
-    for (int ww = 1; ww < WAVES; ++ww) a = fmaxf(a, amax_w[ww][m]);
+    for (int ww = 1; ww < WAVES; ++ww) a = nmax(a, amax_w[ww][m]);
+    a = finite_or_nan(a);
     inv[m] = a > 0.0f ? 127.0f / a : 0.0f;
     sx[m] = a / 127.0f;
   }
@@ -261,12 +276,12 @@ __global__ __launch_bounds__(WAVES * 64) void w4a8_gemv32_kernel(
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        a = fmaxf(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
-        a = fmaxf(a, fabsf(bf16_to_f32(w[j] >> 16)));
+        a = nmax(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
+        a = nmax(a, fabsf(bf16_to_f32(w[j] >> 16)));
       }
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    for (int off = 32; off > 0; off >>= 1) a = nmax(a, __shfl_xor(a, off, 64));
     if (lane == 0) amax_w[wave][m] = a;
   }
   __syncthreads();
@@ -274,7 +289,8 @@ __global__ __launch_bounds__(WAVES * 64) void w4a8_gemv32_kernel(
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     float a = amax_w[0][m];
-    for (int ww = 1; ww < WAVES; ++ww) a = fmaxf(a, amax_w[ww][m]);
+    for (int ww = 1; ww < WAVES; ++ww) a = nmax(a, amax_w[ww][m]);
+    a = finite_or_nan(a);
     inv[m] = a > 0.0f ? 127.0f / a : 0.0f;
     sx[m] = a / 127.0f;
   }
@@ -402,11 +418,11 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_lds_kernel(
         float a = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          a = fmaxf(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
-          a = fmaxf(a, fabsf(bf16_to_f32(w[j] >> 16)));
+          a = nmax(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
+          a = nmax(a, fabsf(bf16_to_f32(w[j] >> 16)));
         }
-        a = fmaxf(a, dpp_fa<0xB1>(a));          // the lane quad holds one group of 32
-        a = fmaxf(a, dpp_fa<0x4E>(a));
+        a = nmax(a, dpp_fa<0xB1>(a));          // the lane quad holds one group of 32
+        a = finite_or_nan(nmax(a, dpp_fa<0x4E>(a)));
         const float inv = a > 0.0f ? 127.0f / a : 0.0f;
         const float sxv = a / 127.0f;
         uint32_t lo, hi;
@@ -505,13 +521,13 @@ __device__ __forceinline__ i32x4_t mfma_i8_4x4x4(uint32_t a, uint32_t b, i32x4_t
 // bytes, distinct 16-byte positions modulo 128 and 256 bytes (disjoint banks).
 constexpr int kA8XRowBytes = 144;
 
-// max(a, |x|) over the 8 bf16 of a 16-byte load.
+// max(a, |x|) over the 8 bf16 of a 16-byte load, keeping a NaN.
 __device__ __forceinline__ float absmax8(const u32x4_t& v, float a) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    a = fmaxf(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
-    a = fmaxf(a, fabsf(bf16_to_f32(w[j] >> 16)));
+    a = nmax(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
+    a = nmax(a, fabsf(bf16_to_f32(w[j] >> 16)));
   }
   return a;
 }
@@ -577,14 +593,14 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
     for (int m = 0; m < M; ++m) {
       // wave max: the 16-lane rows by DPP, then the four row maxima
       float a = am[m];
-      a = fmaxf(a, dpp_fa<0xB1>(a));    // quad_perm [1,0,3,2]
-      a = fmaxf(a, dpp_fa<0x4E>(a));    // quad_perm [2,3,0,1]
-      a = fmaxf(a, dpp_fa<0x124>(a));   // row_ror:4
-      a = fmaxf(a, dpp_fa<0x128>(a));   // row_ror:8
+      a = nmax(a, dpp_fa<0xB1>(a));    // quad_perm [1,0,3,2]
+      a = nmax(a, dpp_fa<0x4E>(a));    // quad_perm [2,3,0,1]
+      a = nmax(a, dpp_fa<0x124>(a));   // row_ror:4
+      a = nmax(a, dpp_fa<0x128>(a));   // row_ror:8
       const int ai = __float_as_int(a);
-      a = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(ai, 0)),
+      a = nmax(nmax(__int_as_float(__builtin_amdgcn_readlane(ai, 0)),
                       __int_as_float(__builtin_amdgcn_readlane(ai, 16))),
-                fmaxf(__int_as_float(__builtin_amdgcn_readlane(ai, 32)),
+                nmax(__int_as_float(__builtin_amdgcn_readlane(ai, 32)),
                       __int_as_float(__builtin_amdgcn_readlane(ai, 48))));
       if (lane == 0) amax_w[wave][m] = a;
     }
@@ -592,7 +608,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       float a = amax_w[0][m];
-      for (int ww = 1; ww < WAVES; ++ww) a = fmaxf(a, amax_w[ww][m]);
+      for (int ww = 1; ww < WAVES; ++ww) a = nmax(a, amax_w[ww][m]);
+      a = finite_or_nan(a);
       if (m == qm) inv_q = a > 0.0f ? 127.0f / a : 0.0f;
       sx_row[m] = a / 127.0f;
     }
@@ -619,11 +636,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
       float a = 0.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        a = fmaxf(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
-        a = fmaxf(a, fabsf(bf16_to_f32(w[j] >> 16)));
+        a = nmax(a, fabsf(bf16_to_f32(w[j] & 0xffffu)));
+        a = nmax(a, fabsf(bf16_to_f32(w[j] >> 16)));
       }
-      a = fmaxf(a, dpp_fa<0xB1>(a));
-      a = fmaxf(a, dpp_fa<0x4E>(a));
+      a = nmax(a, dpp_fa<0xB1>(a));
+      a = finite_or_nan(nmax(a, dpp_fa<0x4E>(a)));
       inv = a > 0.0f ? 127.0f / a : 0.0f;
       sxv = a / 127.0f;
     }
