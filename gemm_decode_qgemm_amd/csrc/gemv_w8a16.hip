@@ -66,17 +66,45 @@ __global__ __launch_bounds__(kW8MaxWaves * 64) void w8a16_gemv_kernel(
   const int row0 = blockIdx.x * kW8Rows;
   const int nch = (k + 1023) >> 10;
 
+  bool valid[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    const int ch = wave * CPW + c;
+    valid[c] = ch < nch && ch * 1024 + lane * 16 < k;
+  }
+
+  // Weight loads of RB rows.  Rows past n load nothing and use w = 0 (byte
+  // 0x80 after the xor below); their sums are never stored.
+  constexpr int RB = QG_W8_RB;
+  u32x4_t wv[RB][CPW];
+  auto load_rows = [&](int r0) {
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const int row = row0 + r0 + rr;
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        wv[rr][c] = u32x4_t{0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
+        if (valid[c] && row < n)
+          wv[rr][c] = load_stream<true>(reinterpret_cast<const u32x4_t*>(
+              w + (size_t)row * k + (size_t)(wave * CPW + c) * 1024 + lane * 16));
+      }
+    }
+  };
+  // At M = 1 the first rows' weight loads go out before the x loads, so the
+  // wait for x overlaps their HBM latency instead of preceding it (8192 x 8192:
+  // 12.47 us against 12.78).  With more activation rows the weights held
+  // across the x loads and their sums cost registers, and time (M = 4:
+  // 18.6 us against 17.3), so there x comes first.
+  if constexpr (M == 1) load_rows(0);
+
   // x of this lane's chunks as bf16 pairs, and 128 * (their sum).
   uint32_t xr[M][CPW][8];
-  bool valid[CPW];
   float bias[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) bias[m] = 0.0f;
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
-    const int ch = wave * CPW + c;
-    const int kb = ch * 1024 + lane * 16;        // first k of this lane in the chunk
-    valid[c] = ch < nch && kb < k;
+    const int kb = (wave * CPW + c) * 1024 + lane * 16;   // first k of this lane in the chunk
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       u32x4_t a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
@@ -97,22 +125,8 @@ __global__ __launch_bounds__(kW8MaxWaves * 64) void w8a16_gemv_kernel(
   for (int m = 0; m < M; ++m) bias[m] *= 128.0f;
 
   const uint32_t sel_hi = __builtin_amdgcn_readfirstlane(0x07060302u);  // upper halves of (S1, S0)
-  constexpr int RB = QG_W8_RB;
   for (int r0 = 0; r0 < kW8Rows; r0 += RB) {
-    // Rows past n load nothing and use w = 0 (byte 0x80 after the xor below);
-    // their sums are never stored.
-    u32x4_t wv[RB][CPW];
-#pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-      const int row = row0 + r0 + rr;
-#pragma unroll
-      for (int c = 0; c < CPW; ++c) {
-        wv[rr][c] = u32x4_t{0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
-        if (valid[c] && row < n)
-          wv[rr][c] = load_stream<true>(reinterpret_cast<const u32x4_t*>(
-              w + (size_t)row * k + (size_t)(wave * CPW + c) * 1024 + lane * 16));
-      }
-    }
+    if (M > 1 || r0 > 0) load_rows(r0);
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
       float acc[M];
