@@ -13,7 +13,8 @@
 //    8 whole 128-byte lines of one row); wave w of a workgroup owns CPW
 //    consecutive chunks, so a workgroup of W waves covers all of K;
 //  * each lane keeps the 16 x values of its chunks in VGPRs as bf16 pairs and
-//    reuses them for every row of the workgroup's 8-row block;
+//    reuses them for every row of the workgroup's block of rows (4 at M = 1,
+//    8 otherwise);
 //  * a weight dword (4 int8) is XORed with 0x80808080, so each byte is w+128
 //    in 1..255, v_cvt_f32_ubyte0..3 turn the bytes into exact floats, and
 //    v_perm_b32 packs the upper halves of two of them into an exact bf16 pair
@@ -28,16 +29,14 @@
 
 namespace qg {
 
-// Rows per workgroup and rows whose loads are in flight together, measured on
-// MI355X (M = 1): 8192 x 8192 12.7 us with (8, 4) against 15.3 us with
-// (16, 1); 39936 x 6656 6.56 TB/s.
-#ifndef QG_W8_ROWS
-#define QG_W8_ROWS 8
-#endif
-#ifndef QG_W8_RB
-#define QG_W8_RB 4
-#endif
-constexpr int kW8Rows = QG_W8_ROWS;
+// Rows per workgroup and rows whose loads are in flight together (RB),
+// measured on MI355X at 8192 x 8192: M = 1 12.2 us with (4, 4), 12.45 with
+// (8, 4), 12.4 with (8, 2) or (16, 4), 13.4 with (16, 8), 15.3 with (16, 1);
+// M = 4 17.3 us with (8, 4), 17.1-17.6 with (16, 4), 20.0 with (4, 4).  At
+// 39936 x 6656 (M = 1) (4, 4) and (8, 4) both stream 6.6 TB/s.
+template <int M>
+constexpr int kW8Rows = M == 1 ? 4 : 8;
+constexpr int kW8RB = 4;
 constexpr int kW8MaxWaves = 16;
 
 template <int CTRL>
@@ -59,11 +58,12 @@ template <int M, int CPW>
 __global__ __launch_bounds__(kW8MaxWaves * 64) void w8a16_gemv_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ w,
     const uint16_t* __restrict__ scale, int n, int k, void* __restrict__ y, int y_f32) {
-  __shared__ float red[kW8MaxWaves][kW8Rows][4 * M];
+  constexpr int ROWS = kW8Rows<M>;
+  __shared__ float red[kW8MaxWaves][ROWS][4 * M];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id_uniform();
   const int nwaves = blockDim.x >> 6;
-  const int row0 = blockIdx.x * kW8Rows;
+  const int row0 = blockIdx.x * ROWS;
   const int nch = (k + 1023) >> 10;
 
   bool valid[CPW];
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kW8MaxWaves * 64) void w8a16_gemv_kernel(
 
   // Weight loads of RB rows.  Rows past n load nothing and use w = 0 (byte
   // 0x80 after the xor below); their sums are never stored.
-  constexpr int RB = QG_W8_RB;
+  constexpr int RB = kW8RB;
   u32x4_t wv[RB][CPW];
   auto load_rows = [&](int r0) {
 #pragma unroll
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kW8MaxWaves * 64) void w8a16_gemv_kernel(
   for (int m = 0; m < M; ++m) bias[m] *= 128.0f;
 
   const uint32_t sel_hi = __builtin_amdgcn_readfirstlane(0x07060302u);  // upper halves of (S1, S0)
-  for (int r0 = 0; r0 < kW8Rows; r0 += RB) {
+  for (int r0 = 0; r0 < ROWS; r0 += RB) {
     if (M > 1 || r0 > 0) load_rows(r0);
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kW8MaxWaves * 64) void w8a16_gemv_kernel(
   __syncthreads();
   // One thread per (row, m): waves in order, then the 4 DPP rows in order.
   const int t = threadIdx.x;
-  if (t < kW8Rows * M) {
+  if (t < ROWS * M) {
     const int r = t / M, m = t % M;
     const int row = row0 + r;
     if (row < n) {
@@ -190,7 +190,7 @@ static hipError_t launch_w8_t(const void* x, const int8_t* w, const void* scale,
                               void* y, int y_f32, hipStream_t stream) {
   const int nch = (k + 1023) / 1024;
   const int waves = (nch + CPW - 1) / CPW;
-  hipLaunchKernelGGL((w8a16_gemv_kernel<M, CPW>), dim3((n + kW8Rows - 1) / kW8Rows),
+  hipLaunchKernelGGL((w8a16_gemv_kernel<M, CPW>), dim3((n + kW8Rows<M> - 1) / kW8Rows<M>),
                      dim3(waves * 64), 0, stream, static_cast<const uint16_t*>(x), w,
                      static_cast<const uint16_t*>(scale), n, k, y, y_f32);
   return hipGetLastError();
