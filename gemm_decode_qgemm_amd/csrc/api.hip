@@ -213,9 +213,17 @@ int64_t qg_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k) {
   int32_t split;
   st = resolve_split(m, n, k, split_k, &split);
   if (st != QG_OK) return st;
-  // split_k = 0: enough for the default of every entry point
-  if (split_k == 0) split = split > default_split_intn(m, n, k) ? split : default_split_intn(m, n, k);
-  return split > 1 ? (int64_t)split * m * n * 4 : 0;
+  if (split_k != 0) return split > 1 ? (int64_t)split * m * n * 4 : 0;
+  // split_k = 0: enough for the default of every entry point, W4A8 at M > 4
+  // included (slices of 4 rows, each with the default split of 4 rows)
+  int64_t units = split > 1 ? (int64_t)split * m : 0;
+  const int32_t si = default_split_intn(m, n, k);
+  if (si > 1 && (int64_t)si * m > units) units = (int64_t)si * m;
+  if (m > 4) {
+    const int32_t s4 = default_split(4, n, k);
+    if (s4 > 1 && (int64_t)s4 * 4 > units) units = (int64_t)s4 * 4;
+  }
+  return units * n * 4;
 }
 
 int32_t qg_default_split_k_intn(int64_t m, int64_t n, int64_t k) {
@@ -388,24 +396,11 @@ int32_t qgemm_w8a16(const void* x_bf16, int64_t m, int64_t k, const int8_t* w,
                                           y_dtype == QG_F32, static_cast<hipStream_t>(stream)));
 }
 
-static int32_t w4a8_common(const void* x_bf16, int64_t m, int64_t k, const void* packed,
-                           int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype, int32_t split_k,
-                           void* ws, int64_t ws_bytes, void* stream, bool group_scales, bool dq = false) {
-  if (!x_bf16 || !packed || !y) return QG_E_NULL;
-  int32_t st = check_mnk(m, n, k);
-  if (st != QG_OK) return st;
-  if (y_dtype != QG_BF16 && y_dtype != QG_F32) return QG_E_DTYPE;
-  if (m > 4) return QG_E_M_RANGE;
-  int32_t split;
-  st = resolve_split(m, n, k, split_k, &split);
-  if (st != QG_OK) return st;
-  if (packed_bytes < (dq ? qg_int4_dq_packed_bytes(n, k) : qg_int4_packed_bytes(n, k))) return QG_E_BUFFER;
-  const int64_t need_ws = split > 1 ? (int64_t)split * m * n * 4 : 0;
-  if (need_ws > 0 && (!ws || ws_bytes < need_ws)) return ws ? QG_E_BUFFER : QG_E_NULL;
-  if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || (ws && !aligned16(ws)))
-    return QG_E_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
+// One launch sequence of the M <= 4 W4A8 kernels (plus the split-K pass).
+static int32_t w4a8_rows(const void* x_bf16, int64_t m, int64_t k, const void* packed, int64_t n,
+                         void* y, int32_t y_dtype, int32_t split, float* partial, hipStream_t s,
+                         bool group_scales, bool dq) {
+  int32_t st;
   if (dq) {
     // the scale-code layout: the 32-row kernels of the branches below
     st = hip_status(qg::launch_w4a8_dq((int)m, group_scales, x_bf16, packed, (int)n, (int)k, y,
@@ -425,6 +420,40 @@ static int32_t w4a8_common(const void* x_bf16, int64_t m, int64_t k, const void*
   }
   if (st != QG_OK || split == 1) return st;
   return hip_status(qg::launch_splitk_reduce(partial, split, m * n, y, y_dtype == QG_F32, s));
+}
+
+static int32_t w4a8_common(const void* x_bf16, int64_t m, int64_t k, const void* packed,
+                           int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype, int32_t split_k,
+                           void* ws, int64_t ws_bytes, void* stream, bool group_scales, bool dq = false) {
+  if (!x_bf16 || !packed || !y) return QG_E_NULL;
+  int32_t st = check_mnk(m, n, k);
+  if (st != QG_OK) return st;
+  if (y_dtype != QG_BF16 && y_dtype != QG_F32) return QG_E_DTYPE;
+  // M = 5..64 runs as consecutive slices of at most 4 activation rows (below).
+  const int64_t rows = m < 4 ? m : 4;
+  int32_t split;
+  st = resolve_split(rows, n, k, split_k, &split);
+  if (st != QG_OK) return st;
+  if (packed_bytes < (dq ? qg_int4_dq_packed_bytes(n, k) : qg_int4_packed_bytes(n, k))) return QG_E_BUFFER;
+  const int64_t need_ws = split > 1 ? (int64_t)split * rows * n * 4 : 0;
+  if (need_ws > 0 && (!ws || ws_bytes < need_ws)) return ws ? QG_E_BUFFER : QG_E_NULL;
+  if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || (ws && !aligned16(ws)))
+    return QG_E_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
+  // Each slice streams the whole weight again; the slices run in stream order,
+  // so they share the split-K workspace.  A slice of x starts 4 k elements
+  // further (16-byte aligned, k being a multiple of 256); y is stored element
+  // by element, so its slices need no more than the element's alignment.
+  const int64_t y_elem = y_dtype == QG_F32 ? 4 : 2;
+  for (int64_t r0 = 0; r0 < m; r0 += 4) {
+    const int64_t mc = m - r0 < 4 ? m - r0 : 4;
+    st = w4a8_rows(static_cast<const uint16_t*>(x_bf16) + r0 * k, mc, k, packed, n,
+                   static_cast<char*>(y) + r0 * n * y_elem, y_dtype, split, partial, s,
+                   group_scales, dq);
+    if (st != QG_OK) return st;
+  }
+  return QG_OK;
 }
 
 int32_t qgemm_w4a8(const void* x_bf16, int64_t m, int64_t k, const void* packed,

@@ -122,9 +122,10 @@ int32_t qg_default_split_k_intn(int64_t m, int64_t n, int64_t k);
 
 /* Workspace bytes a qgemm call needs for (m, n, k, split_k): split * m * n * 4
  * (fp32 partial sums) when the split is above 1, else 0.  For split_k = 0
- * the larger of the two defaults (qg_default_split_k, qg_default_split_k_intn)
- * is assumed, so one workspace serves every entry point's default.  Negative
- * qg_status on bad arguments. */
+ * the largest need of the defaults is assumed (qg_default_split_k and
+ * qg_default_split_k_intn at m rows, and for m > 4 also qg_default_split_k
+ * at 4 rows, the W4A8 entry points' slices), so one workspace serves every
+ * entry point's default.  Negative qg_status on bad arguments. */
 int64_t qg_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k);
 
 /* ---- quantize_int4_g32 ---------------------------------------------------
@@ -271,7 +272,10 @@ int32_t qgemm_w8a16(const void *x_bf16, int64_t m, int64_t k, const int8_t *w,
  * xq = clamp(rint(x * inv), -127, 127) in binary32; a == 0 gives a zero row),
  * then  y[m,n] = sx[m] * sum_g s[n,g] * sum_{k in g} xq[m,k] * (q[n,k] - zp[n,g])
  * with exact integer group dots.  Arguments and errors as qgemm_w4a16
- * (1 <= m <= 4 in this version: QG_E_M_RANGE above).  The per-row scale is
+ * (1 <= m <= 64).  M = 5..64 runs as consecutive slices of at most 4 rows
+ * on the M <= 4 kernels, each slice streaming the weight again (ceil(m/4)
+ * times the bytes of one call; split_k and the workspace apply per slice,
+ * slices run in stream order).  The per-row scale is
  * the pages' precision class on gaussian activations; rows with a few large
  * outlier channels lose precision (qgemm_w4a8_g32 below keeps it). */
 int32_t qgemm_w4a8(const void *x_bf16, int64_t m, int64_t k, const void *packed,
@@ -296,7 +300,7 @@ int32_t qgemm_w4a8_g32(const void *x_bf16, int64_t m, int64_t k, const void *pac
  * same activation quantization, a group's weight scale c[n,g] * step[n]:
  *   per row:      y = sx[m] * sum_g c*step * sum_{k in g} xq (q - zp)
  *   per group 32: y = sum_g sx[m,g] * c*step * sum_{k in g} xq (q - zp).
- * Arguments, workspace and errors as qgemm_w4a8 (1 <= m <= 4), with
+ * Arguments, workspace and errors as qgemm_w4a8 (1 <= m <= 64), with
  * packed_bytes checked against qg_int4_dq_packed_bytes. */
 int32_t qgemm_w4a8_dq(const void *x_bf16, int64_t m, int64_t k, const void *packed,
                       int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,

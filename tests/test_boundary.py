@@ -178,11 +178,12 @@ def test_qgemm_w4a16_and_w4a8_validate_before_launching(lib, args, expect):
 
 
 def test_w4a8_m_range(lib):
-    assert lib.qgemm_w4a8(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
-    assert lib.qgemm_w4a8_g32(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
+    # W4A8 takes every bucket up to 64 rows (M > 4 as slices of 4 rows)
+    assert lib.qgemm_w4a8(A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
+    assert lib.qgemm_w4a8_g32(A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
     assert lib.qgemm_w4a16_dq(A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
-    assert lib.qgemm_w4a8_dq(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
-    assert lib.qgemm_w4a8_g32_dq(A, 5, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
+    assert lib.qgemm_w4a8_dq(A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
+    assert lib.qgemm_w4a8_g32_dq(A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
     assert lib.qgemm_w4a8_dq(A, 1, 256, A, 9087, 64, A, 0, 0, None, 0, None) == E_BUF
     # 9088 bytes hold a 64 x 256 scale-code weight, 9087 do not
     assert lib.qgemm_w4a16_dq(A, 1, 256, A, 9087, 64, A, 0, 0, None, 0, None) == E_BUF
@@ -269,3 +270,16 @@ def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError, match="missing"):
         spec.loader.exec_module(mod)
+
+
+@pytest.mark.parametrize("m", [5, 8, 16, 33, 64])
+@pytest.mark.parametrize("n,k", [(8448, 6656), (6656, 19968), (6656, 4096), (256, 6656), (768, 256)])
+def test_default_workspace_covers_w4a8_row_slices(lib, m, n, k):
+    """W4A8 at M > 4 runs slices of 4 rows with the 4-row default split; the
+    default workspace must hold that slice's partial sums too."""
+    ws = lib.qg_workspace_bytes(m, n, k, 0)
+    s4 = lib.qg_default_split_k(4, n, k)
+    assert ws >= (s4 * 4 * n * 4 if s4 > 1 else 0)
+    for split in (1, 2, 4, 8):
+        if split <= k // 256:
+            assert lib.qg_workspace_bytes(m, n, k, split) >= (split * 4 * n * 4 if split > 1 else 0)

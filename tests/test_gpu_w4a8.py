@@ -169,11 +169,11 @@ def test_w4a8_outlier_precision_class(dev):
     assert_w4a8_class(qg.qgemm_w4a8(x.to(dev), packed, n, out_dtype=torch.float32), r16, "outliers")
 
 
-def test_w4a8_rejects_m_above_4(dev):
+def test_w4a8_rejects_m_above_64(dev):
     w, *_ = _weight(256, 256, 1)
     packed = qg.quantize_int4_g32(w.to(dev))
     with pytest.raises(qg.QGemmError) as e:
-        qg.qgemm_w4a8(si.activation(5, 256, 1).to(dev), packed, 256)
+        qg.qgemm_w4a8(si.activation(65, 256, 1).to(dev), packed, 256)
     assert e.value.status == -4
 
 

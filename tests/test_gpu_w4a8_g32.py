@@ -166,9 +166,9 @@ def test_g32_logits_top1_and_cosine(dev):
                 assert a8[r].argmax() == a16[r].argmax(), (m, r, gap16)
 
 
-def test_g32_rejects_m_above_4(dev):
+def test_g32_rejects_m_above_64(dev):
     w, *_ = _layer(256, 256, 1)
     packed = qg.quantize_int4_g32(w.to(dev))
     with pytest.raises(qg.QGemmError) as e:
-        qg.qgemm_w4a8_g32(si.activation(5, 256, 1).to(dev), packed, 256)
+        qg.qgemm_w4a8_g32(si.activation(65, 256, 1).to(dev), packed, 256)
     assert e.value.status == -4
