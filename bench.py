@@ -26,7 +26,8 @@ Other layers of the same path use the same protocol: --op w4a16 with
 --m 2..64 (M > 4 runs the matrix-core kernel), --op w4a16_dq (the scale-code
 weight, bytes = its packed size; --op w4a8_dq / w4a8_g32_dq the W4A8 forms on it),
 --op wn_a16 --bits 5|6 (INT5 / INT6,
-M = 1, bytes = the packed size), --op w4a8 / w4a8_g32 (M <= 64; M > 4 runs as
+M = 1, bytes = the packed size), --op w4a8 / w4a8_g32 (M <= 64; at M > 4 per-row
+scales run the matrix-core kernel on the quantized rows, per-group scales run
 slices of 4 rows that each stream the weight, and bytes still count it once) and
 --op w8a16 (int8 per-channel, bytes = N*K + 2*N); --n/--k pick the shape.  The
 offline weight quantizers run the same way: --op quantize_int4 / quantize_int4_dq /
@@ -153,8 +154,9 @@ def main() -> int:
             w_cpu, x_cpu = si.decode_inputs(n, k, m)
         else:
             w_cpu, x_cpu = si.int4_weight(n, k, n ^ k), si.activation(m, k, 9100 + m)
-        # W4A8 runs M > 4 as slices of 4 rows, each with the 4-row default split
-        split_rows = min(m, 4) if op.startswith("w4a8") else m
+        # W4A8 with per-group scales runs M > 4 as slices of 4 rows, each with the
+        # 4-row default split (per-row scales there use the matrix-core default)
+        split_rows = min(m, 4) if op in ("w4a8_g32", "w4a8_g32_dq") else m
         split = args.split or qg.default_split_k(split_rows, n, k, args.bits if op == "wn_a16" else 4)
         if op in ("w4a16_dq", "w4a8_dq", "w4a8_g32_dq"):
             packed0 = qg.quantize_int4_g32_dq(w_cpu.to(dev))

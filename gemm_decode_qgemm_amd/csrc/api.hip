@@ -32,6 +32,10 @@ hipError_t launch_wn_a16_mfma(int bits, int m, const void* x, const void* packed
                               int y_f32, float* partial, int split, hipStream_t stream);
 hipError_t launch_w4a16_mfma_dq(int m, const void* x, const void* packed, int n, int k, void* y, int y_f32,
                                 float* partial, int split, hipStream_t stream);
+hipError_t launch_w4a8_actquant_bf16(int m, const void* x, int k, void* xq, float* sx,
+                                     hipStream_t stream);
+hipError_t launch_w4a8_rowscale_reduce(const float* partial, int split, int m, int n, const float* sx,
+                                       void* y, int y_f32, hipStream_t stream);
 hipError_t launch_w4a8_dq(int m, bool group_scales, const void* x, const void* packed, int n, int k,
                           void* y, int y_f32, float* partial, int split, hipStream_t stream);
 hipError_t launch_quantize_int8_rowwise(const void* w, int64_t n, int64_t k, int8_t* q,
@@ -159,6 +163,12 @@ int32_t resolve_split(int64_t m, int64_t n, int64_t k, int32_t split_k, int32_t*
   return QG_OK;
 }
 
+// Workspace of W4A8 with per-row scales at m > 4: xq as bf16 [m, k], sx
+// fp32 [m] (256 bytes), then the fp32 partial sums [split, m, n], split >= 1.
+int64_t w4a8_mfma_ws(int64_t m, int64_t n, int64_t k, int32_t split) {
+  return m * k * 2 + 256 + (int64_t)split * m * n * 4;
+}
+
 }  // namespace
 
 extern "C" {
@@ -213,7 +223,12 @@ int64_t qg_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k) {
   int32_t split;
   st = resolve_split(m, n, k, split_k, &split);
   if (st != QG_OK) return st;
-  if (split_k != 0) return split > 1 ? (int64_t)split * m * n * 4 : 0;
+  if (split_k != 0) {
+    const int64_t bytes = split > 1 ? (int64_t)split * m * n * 4 : 0;
+    if (m <= 4) return bytes;
+    const int64_t w8 = w4a8_mfma_ws(m, n, k, split);   // W4A8, per-row scales, m > 4
+    return w8 > bytes ? w8 : bytes;
+  }
   // split_k = 0: enough for the default of every entry point, W4A8 at M > 4
   // included (slices of 4 rows, each with the default split of 4 rows)
   int64_t units = split > 1 ? (int64_t)split * m : 0;
@@ -223,7 +238,11 @@ int64_t qg_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k) {
     const int32_t s4 = default_split(4, n, k);
     if (s4 > 1 && (int64_t)s4 * 4 > units) units = (int64_t)s4 * 4;
   }
-  return units * n * 4;
+  const int64_t bytes = units * n * 4;
+  if (m <= 4) return bytes;
+  // W4A8 with per-row scales at m > 4 (quantized x, sx, partials at its split)
+  const int64_t w8 = w4a8_mfma_ws(m, n, k, split);
+  return w8 > bytes ? w8 : bytes;
 }
 
 int32_t qg_default_split_k_intn(int64_t m, int64_t n, int64_t k) {
@@ -429,7 +448,32 @@ static int32_t w4a8_common(const void* x_bf16, int64_t m, int64_t k, const void*
   int32_t st = check_mnk(m, n, k);
   if (st != QG_OK) return st;
   if (y_dtype != QG_BF16 && y_dtype != QG_F32) return QG_E_DTYPE;
-  // M = 5..64 runs as consecutive slices of at most 4 activation rows (below).
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m > 4 && !group_scales) {
+    // Per-row scales at 5..64 rows: x quantized once into the workspace (xq
+    // exact in bf16), the bf16 matrix-core kernel on xq, then sx per row
+    // after the split-K sum.
+    int32_t split;
+    st = resolve_split(m, n, k, split_k, &split);
+    if (st != QG_OK) return st;
+    if (packed_bytes < (dq ? qg_int4_dq_packed_bytes(n, k) : qg_int4_packed_bytes(n, k))) return QG_E_BUFFER;
+    if (!ws || ws_bytes < w4a8_mfma_ws(m, n, k, split)) return ws ? QG_E_BUFFER : QG_E_NULL;
+    if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || !aligned16(ws)) return QG_E_ALIGN;
+    char* w = static_cast<char*>(ws);
+    float* sx = reinterpret_cast<float*>(w + m * k * 2);
+    float* partial = reinterpret_cast<float*>(w + m * k * 2 + 256);
+    st = hip_status(qg::launch_w4a8_actquant_bf16((int)m, x_bf16, (int)k, w, sx, s));
+    if (st != QG_OK) return st;
+    st = hip_status(dq ? qg::launch_w4a16_mfma_dq((int)m, w, packed, (int)n, (int)k, y, y_dtype == QG_F32,
+                                                  partial, split, s)
+                       : qg::launch_w4a16_mfma((int)m, w, packed, (int)n, (int)k, y, y_dtype == QG_F32,
+                                               partial, split, s));
+    if (st != QG_OK) return st;
+    return hip_status(qg::launch_w4a8_rowscale_reduce(partial, split, (int)m, (int)n, sx, y,
+                                                      y_dtype == QG_F32, s));
+  }
+  // Otherwise M = 5..64 runs as consecutive slices of at most 4 activation
+  // rows (below).
   const int64_t rows = m < 4 ? m : 4;
   int32_t split;
   st = resolve_split(rows, n, k, split_k, &split);
@@ -439,7 +483,6 @@ static int32_t w4a8_common(const void* x_bf16, int64_t m, int64_t k, const void*
   if (need_ws > 0 && (!ws || ws_bytes < need_ws)) return ws ? QG_E_BUFFER : QG_E_NULL;
   if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || (ws && !aligned16(ws)))
     return QG_E_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
   // Each slice streams the whole weight again; the slices run in stream order,
   // so they share the split-K workspace.  A slice of x starts 4 k elements

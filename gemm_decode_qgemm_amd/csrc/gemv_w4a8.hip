@@ -812,4 +812,84 @@ hipError_t launch_w4a8_dq(int m, bool group_scales, const void* x, const void* p
   return hipErrorInvalidValue;
 }
 
+
+// ---------------------------------------------------------------------------
+// Per-row scales at 5..64 rows, on the bf16 matrix-core kernels.  xq is an
+// integer in [-127, 127], exact in bf16, so the matrix-core kernel run on xq
+// forms the same exact integer group dots (each product exact, a group's sum
+// below 2^24) and scales them by s as the int8 kernels do; sx is applied
+// after the split-K sum.
+//
+// Pass 1: one workgroup per row.  a = max|x| (the NaN-keeping max), inv and
+// sx as in the fused kernels, xq = clamp(rint(x * inv), -127, 127) in
+// binary32, stored as bf16 (the upper half of the binary32 value, exact for
+// these integers).
+__global__ __launch_bounds__(256) void w4a8_actquant_bf16_kernel(const uint16_t* __restrict__ x,
+                                                                  int k, uint16_t* __restrict__ xq,
+                                                                  float* __restrict__ sx) {
+  __shared__ float wmax[4];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)row * k);
+  const int k8 = k >> 3;
+  float a = 0.0f;
+  for (int i = tid; i < k8; i += 256) a = absmax8(xr[i], a);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) a = nmax(a, __shfl_xor(a, off, 64));
+  if ((tid & 63) == 0) wmax[tid >> 6] = a;
+  __syncthreads();
+  a = finite_or_nan(nmax(nmax(wmax[0], wmax[1]), nmax(wmax[2], wmax[3])));
+  const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+  if (tid == 0) sx[row] = a / 127.0f;
+  u32x4_t* out = reinterpret_cast<u32x4_t*>(xq + (size_t)row * k);
+  for (int i = tid; i < k8; i += 256) {
+    const u32x4_t v = xr[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t h[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float f = bf16_to_f32(e ? (w[j] >> 16) : (w[j] & 0xffffu));
+        const float t = __builtin_amdgcn_fmed3f(rintf(f * inv), -127.0f, 127.0f);
+        h[e] = __float_as_uint(t) >> 16;
+      }
+      o[j] = h[0] | (h[1] << 16);
+    }
+    out[i] = u32x4_t{o[0], o[1], o[2], o[3]};
+  }
+}
+
+// Pass 3: y[r, c] = sx[r] * sum over s (ascending) of partial[s, r, c].
+__global__ __launch_bounds__(256) void w4a8_rowscale_reduce_kernel(const float* __restrict__ partial,
+                                                                    int split, int n, int64_t mn,
+                                                                    const float* __restrict__ sx,
+                                                                    void* __restrict__ y, int y_f32) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= mn) return;
+  float v = partial[i];
+  for (int s = 1; s < split; ++s) v += partial[(int64_t)s * mn + i];
+  v *= sx[i / n];
+  if (y_f32)
+    static_cast<float*>(y)[i] = v;
+  else
+    static_cast<uint16_t*>(y)[i] = (uint16_t)f32_to_bf16_rne(v);
+}
+
+hipError_t launch_w4a8_actquant_bf16(int m, const void* x, int k, void* xq, float* sx,
+                                     hipStream_t stream) {
+  hipLaunchKernelGGL(w4a8_actquant_bf16_kernel, dim3(m), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(x), k, static_cast<uint16_t*>(xq), sx);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a8_rowscale_reduce(const float* partial, int split, int m, int n, const float* sx,
+                                       void* y, int y_f32, hipStream_t stream) {
+  const int64_t mn = (int64_t)m * n;
+  hipLaunchKernelGGL(w4a8_rowscale_reduce_kernel, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0,
+                     stream, partial, split, n, mn, sx, y, y_f32);
+  return hipGetLastError();
+}
+
 }  // namespace qg

@@ -124,8 +124,11 @@ int32_t qg_default_split_k_intn(int64_t m, int64_t n, int64_t k);
  * (fp32 partial sums) when the split is above 1, else 0.  For split_k = 0
  * the largest need of the defaults is assumed (qg_default_split_k and
  * qg_default_split_k_intn at m rows, and for m > 4 also qg_default_split_k
- * at 4 rows, the W4A8 entry points' slices), so one workspace serves every
- * entry point's default.  Negative qg_status on bad arguments. */
+ * at 4 rows, the per-group W4A8 slices), so one workspace serves every
+ * entry point's default.  For m > 4 it also holds what qgemm_w4a8 and
+ * qgemm_w4a8_dq need there: m * k * 2 bytes of quantized activations, 256
+ * bytes of row scales and split * m * n * 4 bytes of partial sums (at split 1
+ * too).  Negative qg_status on bad arguments. */
 int64_t qg_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k);
 
 /* ---- quantize_int4_g32 ---------------------------------------------------
@@ -272,10 +275,11 @@ int32_t qgemm_w8a16(const void *x_bf16, int64_t m, int64_t k, const int8_t *w,
  * xq = clamp(rint(x * inv), -127, 127) in binary32; a == 0 gives a zero row),
  * then  y[m,n] = sx[m] * sum_g s[n,g] * sum_{k in g} xq[m,k] * (q[n,k] - zp[n,g])
  * with exact integer group dots.  Arguments and errors as qgemm_w4a16
- * (1 <= m <= 64).  M = 5..64 runs as consecutive slices of at most 4 rows
- * on the M <= 4 kernels, each slice streaming the weight again (ceil(m/4)
- * times the bytes of one call; split_k and the workspace apply per slice,
- * slices run in stream order).  The per-row scale is
+ * (1 <= m <= 64).  For m > 4 the call quantizes x once into the workspace
+ * (xq held exactly as bf16 integers), runs the bf16 matrix-core kernel of
+ * qgemm_w4a16 on it (exact products, the same integer group dots), and
+ * applies sx after the split-K sum; the workspace is required there at any
+ * split (qg_workspace_bytes).  The per-row scale is
  * the pages' precision class on gaussian activations; rows with a few large
  * outlier channels lose precision (qgemm_w4a8_g32 below keeps it). */
 int32_t qgemm_w4a8(const void *x_bf16, int64_t m, int64_t k, const void *packed,
@@ -290,7 +294,11 @@ int32_t qgemm_w4a8(const void *x_bf16, int64_t m, int64_t k, const void *packed,
  *   a = max |x[m, 32g .. 32g+31]|, inv = 127/a, sx[m,g] = a/127 (binary32),
  *   xq = clamp(rint(x * inv), -127, 127); a == 0 gives a zero group;
  *   y[m,n] = sum_g sx[m,g] * s[n,g] * sum_{k in g} xq[m,k] * (q[n,k] - zp[n,g]).
- * Arguments, buffers, workspace and errors exactly as qgemm_w4a8. */
+ * Arguments, buffers, workspace and errors as qgemm_w4a8, except that
+ * m = 5..64 runs as consecutive slices of at most 4 rows on the m <= 4
+ * kernels, each slice streaming the weight again (ceil(m/4) times the bytes
+ * of one call; split_k applies per slice, slices run in stream order and
+ * share the workspace). */
 int32_t qgemm_w4a8_g32(const void *x_bf16, int64_t m, int64_t k, const void *packed,
                        int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
                        int32_t split_k, void *ws, int64_t ws_bytes, void *stream);
@@ -300,7 +308,8 @@ int32_t qgemm_w4a8_g32(const void *x_bf16, int64_t m, int64_t k, const void *pac
  * same activation quantization, a group's weight scale c[n,g] * step[n]:
  *   per row:      y = sx[m] * sum_g c*step * sum_{k in g} xq (q - zp)
  *   per group 32: y = sum_g sx[m,g] * c*step * sum_{k in g} xq (q - zp).
- * Arguments, workspace and errors as qgemm_w4a8 (1 <= m <= 64), with
+ * Arguments, workspace and errors as qgemm_w4a8 and qgemm_w4a8_g32
+ * (1 <= m <= 64, the same two forms above 4 rows), with
  * packed_bytes checked against qg_int4_dq_packed_bytes. */
 int32_t qgemm_w4a8_dq(const void *x_bf16, int64_t m, int64_t k, const void *packed,
                       int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,

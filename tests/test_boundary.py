@@ -280,6 +280,9 @@ def test_default_workspace_covers_w4a8_row_slices(lib, m, n, k):
     ws = lib.qg_workspace_bytes(m, n, k, 0)
     s4 = lib.qg_default_split_k(4, n, k)
     assert ws >= (s4 * 4 * n * 4 if s4 > 1 else 0)
+    # per-row scales: quantized x (bf16), 256 bytes of row scales, partials
+    assert ws >= m * k * 2 + 256 + lib.qg_default_split_k(m, n, k) * m * n * 4
     for split in (1, 2, 4, 8):
         if split <= k // 256:
             assert lib.qg_workspace_bytes(m, n, k, split) >= (split * 4 * n * 4 if split > 1 else 0)
+            assert lib.qg_workspace_bytes(m, n, k, split) >= m * k * 2 + 256 + split * m * n * 4

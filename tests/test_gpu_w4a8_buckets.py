@@ -1,14 +1,15 @@
 """GPU parity: W4A8 at every decode bucket above 4 rows.
 
 The pages' buckets run to 64 rows (executorch test_int4_quantized_gemm.py,
-SUPPORTED_BUCKETS); the W4A8 entry points take M = 5..64 as consecutive
-slices of at most 4 activation rows on the M <= 4 kernels.  Checked on every
-W4A8 entry point and both packed layouts against the matching W4A8 oracle,
-with the W4A16 bounds: ragged M (5, 33), whole slices (8, 16, 64), ragged N,
-one and two splits and the default, both output dtypes; the pages' W4A8
-layer shapes at M = 16 and 64 with the precision class against the W4A16
-oracle (per-row scales on gaussian activations, as for M <= 4); bit-equal
-graph replay.
+SUPPORTED_BUCKETS).  At M = 5..64 the W4A8 entry points quantize x once and
+run the bf16 matrix-core kernel on the exact int8 values (per-row scales), or
+run consecutive slices of at most 4 rows on the M <= 4 kernels (per-group
+scales).  Checked on every W4A8 entry point and both packed layouts against
+the matching W4A8 oracle with the W4A16 bounds: ragged M (5, 33), whole
+slices (8, 16, 64), ragged N, one and two splits and the default, both output
+dtypes, every split on the per-row path; the pages' W4A8 layer shapes at
+M = 16 and 64 with the precision class against the W4A16 oracle (gaussian
+activations); slices bit-equal to separate calls; bit-equal graph replay.
 """
 from __future__ import annotations
 
@@ -94,13 +95,16 @@ def test_buckets_16_and_64_layer_shapes(dev, entry, n, k):
 
 
 def test_slices_equal_separate_calls(dev):
-    """Each 4-row slice of an M = 13 call is bit-identical to a call on those
-    rows alone (same kernels, same split)."""
+    """Per-group scales at M > 4 run as 4-row slices: each slice of an M = 13
+    call is bit-identical to a call on those rows alone (same kernels, same
+    split)."""
     n, k = 1000, 2048
     w, _ = _weight(n, k, 17, False)
     packed = _packed(w, False, dev)
     x = si.activation(13, k, 18).to(dev)
-    for fn in (qg.qgemm_w4a8, qg.qgemm_w4a8_g32):
+    for fn in (qg.qgemm_w4a8_g32, qg.qgemm_w4a8_g32_dq):
+        if fn is qg.qgemm_w4a8_g32_dq:
+            packed = _packed(w, True, dev)
         for split in (1, 2):
             y = fn(x, packed, n, split_k=split, out_dtype=torch.float32)
             for r0 in range(0, 13, 4):
@@ -128,3 +132,20 @@ def test_graph_replay_bit_identical_m16(dev):
                 g.replay()
                 torch.cuda.synchronize()
                 assert torch.equal(out, eager), (fn.__name__, split)
+
+
+def test_per_row_m_above_4_uses_every_split(dev):
+    """The per-row path at M > 4 (quantized rows, matrix-core kernel, row
+    scale after the split sum) at every legal split."""
+    n, k = 520, 2048
+    for dq in (False, True):
+        w, parts = _weight(n, k, 21, dq)
+        packed = _packed(w, dq, dev)
+        fn, ref_fn = (qg.qgemm_w4a8_dq, oracle.qgemm_w4a8_dq) if dq else (qg.qgemm_w4a8, oracle.qgemm_w4a8)
+        for m in (5, 24):
+            x = si.activation(m, k, 40 + m)
+            ref = ref_fn(si.bf16_bits(x), *parts)
+            for split in si.SPLITS:
+                label = f"{fn.__name__} M={m} split={split}"
+                print(label, flush=True)
+                assert_w16(fn(x.to(dev), packed, n, split_k=split, out_dtype=torch.float32), ref, label)

@@ -5,7 +5,7 @@ what int8 activation quantization does with a NaN or an infinity.  The
 reading taken: a span (a row for per-row scales, a group of 32 for per-group
 scales) holding one has no finite absmax scale, so every output of that
 activation row is NaN; the other rows do not change.  Checked on every W4A8
-entry point, both packed layouts, buckets 1..4, both workgroup shapes
+entry point, both packed layouts, buckets 1..4 and 8, both workgroup shapes
 (N = 8200 with an 8-row tail, N = 768) and one and two splits: the bad row is
 NaN on the GPU and in the oracle, the clean rows are bit-identical to a call
 without the bad value and within the W4A16 bounds of the oracle.
@@ -61,7 +61,7 @@ def test_non_finite_activation_gives_a_nan_row(dev, entry, n, kind):
     dq, fn, ref_fn = ENTRIES[entry]
     w, parts = _weight(n, dq)
     packed = (qg.quantize_int4_g32_dq if dq else qg.quantize_int4_g32)(w.to(dev))
-    for m in (1, 2, 3, 4):
+    for m in (1, 2, 3, 4, 8):
         bad = m // 2
         x = si.activation(m, K, 700 + m)
         xbad = x.clone()
