@@ -184,6 +184,13 @@ def test_w4a8_m_range(lib):
     assert lib.qgemm_w4a16_dq(A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
     assert lib.qgemm_w4a8_dq(A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
     assert lib.qgemm_w4a8_g32_dq(A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
+    # per-row scales above 4 rows need the workspace at any split (quantized x,
+    # row scales, partials): refused before any launch when it is missing or short
+    need = lib.qg_workspace_bytes(5, 64, 256, 1)
+    assert need == 5 * 256 * 2 + 256 + 5 * 64 * 4
+    for f in (lib.qgemm_w4a8, lib.qgemm_w4a8_dq):
+        assert f(A, 5, 256, A, 1 << 20, 64, A, 0, 1, None, 0, None) == E_NULL
+        assert f(A, 5, 256, A, 1 << 20, 64, A, 0, 1, A, need - 1, None) == E_BUF
     assert lib.qgemm_w4a8_dq(A, 1, 256, A, 9087, 64, A, 0, 0, None, 0, None) == E_BUF
     # 9088 bytes hold a 64 x 256 scale-code weight, 9087 do not
     assert lib.qgemm_w4a16_dq(A, 1, 256, A, 9087, 64, A, 0, 0, None, 0, None) == E_BUF
