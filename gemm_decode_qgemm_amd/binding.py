@@ -313,13 +313,13 @@ def _w4a8_call(fn, name, x, packed, n, split_k, out_dtype, out, workspace):
 def qgemm_w4a8_dq(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_k: int = 0,
                   out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """qgemm_w4a8 (per-row int8 activations) on a scale-code packed weight (m <= 4)."""
+    """qgemm_w4a8 (per-row int8 activations) on a scale-code packed weight (m <= 64)."""
     return _w4a8_call(lib.qgemm_w4a8_dq, "qgemm_w4a8_dq", x, packed, n, split_k, out_dtype, out, workspace)
 
 
 def qgemm_w4a8_g32_dq(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_k: int = 0,
                       out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
                       workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """qgemm_w4a8_g32 (one activation scale per group of 32) on a scale-code packed weight (m <= 4)."""
+    """qgemm_w4a8_g32 (one activation scale per group of 32) on a scale-code packed weight (m <= 64)."""
     return _w4a8_call(lib.qgemm_w4a8_g32_dq, "qgemm_w4a8_g32_dq", x, packed, n, split_k, out_dtype, out,
                       workspace)
