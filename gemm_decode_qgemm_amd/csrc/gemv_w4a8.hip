@@ -820,15 +820,16 @@ hipError_t launch_w4a8_dq(int m, bool group_scales, const void* x, const void* p
 // below 2^24) and scales them by s as the int8 kernels do; sx is applied
 // after the split-K sum.
 //
-// Pass 1: one workgroup per row.  a = max|x| (the NaN-keeping max), inv and
-// sx as in the fused kernels, xq = clamp(rint(x * inv), -127, 127) in
-// binary32, stored as bf16 (the upper half of the binary32 value, exact for
-// these integers).
+// Pass 1: a workgroup per (row, chunk of 2048 k).  Each workgroup takes the
+// row's a = max|x| (the NaN-keeping max) from a full read of the row (an L2
+// hit after the first), inv and sx as in the fused kernels, and writes
+// xq = clamp(rint(x * inv), -127, 127) of its chunk as bf16 (the upper half
+// of the binary32 value, exact for these integers); chunk 0 writes sx.
 __global__ __launch_bounds__(256) void w4a8_actquant_bf16_kernel(const uint16_t* __restrict__ x,
                                                                   int k, uint16_t* __restrict__ xq,
                                                                   float* __restrict__ sx) {
   __shared__ float wmax[4];
-  const int row = blockIdx.x;
+  const int row = blockIdx.y;
   const int tid = threadIdx.x;
   const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)row * k);
   const int k8 = k >> 3;
@@ -840,37 +841,39 @@ __global__ __launch_bounds__(256) void w4a8_actquant_bf16_kernel(const uint16_t*
   __syncthreads();
   a = finite_or_nan(nmax(nmax(wmax[0], wmax[1]), nmax(wmax[2], wmax[3])));
   const float inv = a > 0.0f ? 127.0f / a : 0.0f;
-  if (tid == 0) sx[row] = a / 127.0f;
-  u32x4_t* out = reinterpret_cast<u32x4_t*>(xq + (size_t)row * k);
-  for (int i = tid; i < k8; i += 256) {
-    const u32x4_t v = xr[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
+  if (blockIdx.x == 0 && tid == 0) sx[row] = a / 127.0f;
+  const int i = blockIdx.x * 256 + tid;
+  if (i >= k8) return;
+  const u32x4_t v = xr[i];
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t h[2];
+  for (int j = 0; j < 4; ++j) {
+    uint32_t h[2];
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float f = bf16_to_f32(e ? (w[j] >> 16) : (w[j] & 0xffffu));
-        const float t = __builtin_amdgcn_fmed3f(rintf(f * inv), -127.0f, 127.0f);
-        h[e] = __float_as_uint(t) >> 16;
-      }
-      o[j] = h[0] | (h[1] << 16);
+    for (int e = 0; e < 2; ++e) {
+      const float f = bf16_to_f32(e ? (w[j] >> 16) : (w[j] & 0xffffu));
+      const float t = __builtin_amdgcn_fmed3f(rintf(f * inv), -127.0f, 127.0f);
+      h[e] = __float_as_uint(t) >> 16;
     }
-    out[i] = u32x4_t{o[0], o[1], o[2], o[3]};
+    o[j] = h[0] | (h[1] << 16);
   }
+  reinterpret_cast<u32x4_t*>(xq + (size_t)row * k)[i] = u32x4_t{o[0], o[1], o[2], o[3]};
 }
 
-// Pass 3: y[r, c] = sx[r] * sum over s (ascending) of partial[s, r, c].
+// Pass 3: y[r, c] = sx[r] * sum over s (ascending) of partial[s, r, c]; a
+// workgroup per (256 columns, row).
 __global__ __launch_bounds__(256) void w4a8_rowscale_reduce_kernel(const float* __restrict__ partial,
                                                                     int split, int n, int64_t mn,
                                                                     const float* __restrict__ sx,
                                                                     void* __restrict__ y, int y_f32) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= mn) return;
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  if (col >= n) return;
+  const int row = blockIdx.y;
+  const int64_t i = (int64_t)row * n + col;
   float v = partial[i];
   for (int s = 1; s < split; ++s) v += partial[(int64_t)s * mn + i];
-  v *= sx[i / n];
+  v *= sx[row];
   if (y_f32)
     static_cast<float*>(y)[i] = v;
   else
@@ -879,16 +882,16 @@ __global__ __launch_bounds__(256) void w4a8_rowscale_reduce_kernel(const float* 
 
 hipError_t launch_w4a8_actquant_bf16(int m, const void* x, int k, void* xq, float* sx,
                                      hipStream_t stream) {
-  hipLaunchKernelGGL(w4a8_actquant_bf16_kernel, dim3(m), dim3(256), 0, stream,
+  const int chunks = ((k >> 3) + 255) / 256;
+  hipLaunchKernelGGL(w4a8_actquant_bf16_kernel, dim3(chunks, m), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(x), k, static_cast<uint16_t*>(xq), sx);
   return hipGetLastError();
 }
 
 hipError_t launch_w4a8_rowscale_reduce(const float* partial, int split, int m, int n, const float* sx,
                                        void* y, int y_f32, hipStream_t stream) {
-  const int64_t mn = (int64_t)m * n;
-  hipLaunchKernelGGL(w4a8_rowscale_reduce_kernel, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0,
-                     stream, partial, split, n, mn, sx, y, y_f32);
+  hipLaunchKernelGGL(w4a8_rowscale_reduce_kernel, dim3((n + 255) / 256, m), dim3(256), 0, stream,
+                     partial, split, n, (int64_t)m * n, sx, y, y_f32);
   return hipGetLastError();
 }
 
