@@ -31,7 +31,8 @@ hipError_t launch_wn_a16_gemv_mx4(int bits, int m, const void* x, const void* pa
 hipError_t launch_wn_a16_mfma(int bits, int m, const void* x, const void* packed, int n, int k, void* y,
                               int y_f32, float* partial, int split, hipStream_t stream);
 hipError_t launch_w4a16_mfma_dq(int m, const void* x, const void* packed, int n, int k, void* y, int y_f32,
-                                float* partial, int split, hipStream_t stream);
+                                float* partial, int split, hipStream_t stream,
+                                const float* row_scale = nullptr);
 hipError_t launch_w4a8_actquant_bf16(int m, const void* x, int k, void* xq, float* sx,
                                      hipStream_t stream);
 hipError_t launch_w4a8_rowscale_reduce(const float* partial, int split, int m, int n, const float* sx,
@@ -51,7 +52,8 @@ hipError_t launch_splitk_reduce(const float* partial, int split, int64_t mn, voi
                                 hipStream_t stream);
 int w8a16_chunks_per_wave(int k);
 hipError_t launch_w4a16_mfma(int m, const void* x, const void* packed, int n, int k, void* y,
-                             int y_f32, float* partial, int split, hipStream_t stream);
+                             int y_f32, float* partial, int split, hipStream_t stream,
+                             const float* row_scale = nullptr);
 hipError_t launch_w4a8_gemv(int m, const void* x, const void* packed, int n, int k, void* y,
                             int y_f32, float* partial, int split, int rows, int waves,
                             hipStream_t stream);
@@ -464,6 +466,13 @@ static int32_t w4a8_common(const void* x_bf16, int64_t m, int64_t k, const void*
     float* partial = reinterpret_cast<float*>(w + m * k * 2 + 256);
     st = hip_status(qg::launch_w4a8_actquant_bf16((int)m, x_bf16, (int)k, w, sx, s));
     if (st != QG_OK) return st;
+    if (split == 1) {
+      // one split: the matrix-core kernel applies sx in its own store
+      return hip_status(dq ? qg::launch_w4a16_mfma_dq((int)m, w, packed, (int)n, (int)k, y, y_dtype == QG_F32,
+                                                      nullptr, 1, s, sx)
+                           : qg::launch_w4a16_mfma((int)m, w, packed, (int)n, (int)k, y, y_dtype == QG_F32,
+                                                   nullptr, 1, s, sx));
+    }
     st = hip_status(dq ? qg::launch_w4a16_mfma_dq((int)m, w, packed, (int)n, (int)k, y, y_dtype == QG_F32,
                                                   partial, split, s)
                        : qg::launch_w4a16_mfma((int)m, w, packed, (int)n, (int)k, y, y_dtype == QG_F32,

@@ -123,10 +123,11 @@ struct MfmaUnit {
 // PIPE: software pipeline over two register sets (PFX: the next unit's
 // activations too), or load-wait-compute per unit with the other resident
 // waves covering the latency.
-template <int MT, int KW, int MG, bool PIPE, bool PFX, int HB = 0, bool DQ = false>
+template <int MT, int KW, int MG, bool PIPE, bool PFX, int HB = 0, bool DQ = false, bool RS = false>
 __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ packed, int n, int k,
-    void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
+    void* __restrict__ y, int y_f32, float* __restrict__ partial, int split,
+    const float* __restrict__ row_scale) {
   constexpr int WAVES = KW * MG;
   __shared__ f32x4_t red[WAVES][kNT][64];
   const int lane = threadIdx.x & 63;
@@ -304,12 +305,16 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
         for (int e = 0; e < 4; ++e) {
           const int row = 16 * (g * MT + mt) + 4 * (l >> 4) + e;
           if (row < m) {
-            if (partial != nullptr)
+            if (partial != nullptr) {
               partial[((size_t)blockIdx.y * m + row) * n + col] = v[e];
-            else if (y_f32)
-              static_cast<float*>(y)[(size_t)row * n + col] = v[e];
-            else
-              static_cast<uint16_t*>(y)[(size_t)row * n + col] = (uint16_t)f32_to_bf16_rne(v[e]);
+            } else {
+              float o = v[e];
+              if constexpr (RS) o *= row_scale[row];
+              if (y_f32)
+                static_cast<float*>(y)[(size_t)row * n + col] = o;
+              else
+                static_cast<uint16_t*>(y)[(size_t)row * n + col] = (uint16_t)f32_to_bf16_rne(o);
+            }
           }
         }
       }
@@ -343,10 +348,11 @@ struct Mfma2W {
   u32x2_t zw;       // the row's 8 zero points (nibbles in .x; INT5/6: 8 bytes)
 };
 
-template <int MT, int MG, int HB = 0, bool DQ = false>
+template <int MT, int MG, int HB = 0, bool DQ = false, bool RS = false>
 __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ packed, int n, int k,
-    void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
+    void* __restrict__ y, int y_f32, float* __restrict__ partial, int split,
+    const float* __restrict__ row_scale) {
   constexpr int MR = 16 * MT * MG;                 // staged x rows
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][MR * 512];
   const int tid = threadIdx.x;
@@ -513,34 +519,40 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * (mg * MT + mt) + 4 * a + e;
         if (row < m) {
-          if (partial != nullptr)
+          if (partial != nullptr) {
             partial[((size_t)blockIdx.y * m + row) * n + col] = acc[mt][e];
-          else if (y_f32)
-            static_cast<float*>(y)[(size_t)row * n + col] = acc[mt][e];
-          else
-            static_cast<uint16_t*>(y)[(size_t)row * n + col] = (uint16_t)f32_to_bf16_rne(acc[mt][e]);
+          } else {
+            float o = acc[mt][e];
+            if constexpr (RS) o *= row_scale[row];
+            if (y_f32)
+              static_cast<float*>(y)[(size_t)row * n + col] = o;
+            else
+              static_cast<uint16_t*>(y)[(size_t)row * n + col] = (uint16_t)f32_to_bf16_rne(o);
+          }
         }
       }
   }
 }
 
-template <int MT, int MG = 1, int HB = 0, bool DQ = false>
+template <int MT, int MG = 1, int HB = 0, bool DQ = false, bool RS = false>
 static hipError_t launch_mfma2_t(const void* x, int m, const void* packed, int n, int k, void* y,
-                                 int y_f32, float* partial, int split, hipStream_t stream) {
+                                 int y_f32, float* partial, int split, hipStream_t stream,
+                                 const float* row_scale = nullptr) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_mfma2_kernel<MT, MG, HB, DQ>), dim3(rbs, split), dim3(256 * MG), 0, stream,
+  hipLaunchKernelGGL((w4a16_mfma2_kernel<MT, MG, HB, DQ, RS>), dim3(rbs, split), dim3(256 * MG), 0, stream,
                      static_cast<const uint16_t*>(x), m, static_cast<const uint8_t*>(packed), n, k,
-                     y, y_f32, partial, split);
+                     y, y_f32, partial, split, row_scale);
   return hipGetLastError();
 }
 
-template <int MT, int KW, int MG, bool PIPE, bool PFX, int HB = 0, bool DQ = false>
+template <int MT, int KW, int MG, bool PIPE, bool PFX, int HB = 0, bool DQ = false, bool RS = false>
 static hipError_t launch_mfma_t(const void* x, int m, const void* packed, int n, int k, void* y,
-                                int y_f32, float* partial, int split, hipStream_t stream) {
+                                int y_f32, float* partial, int split, hipStream_t stream,
+                                const float* row_scale = nullptr) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_mfma_kernel<MT, KW, MG, PIPE, PFX, HB, DQ>), dim3(rbs, split),
+  hipLaunchKernelGGL((w4a16_mfma_kernel<MT, KW, MG, PIPE, PFX, HB, DQ, RS>), dim3(rbs, split),
                      dim3(KW * MG * 64), 0, stream, static_cast<const uint16_t*>(x), m,
-                     static_cast<const uint8_t*>(packed), n, k, y, y_f32, partial, split);
+                     static_cast<const uint8_t*>(packed), n, k, y, y_f32, partial, split, row_scale);
   return hipGetLastError();
 }
 
@@ -557,10 +569,12 @@ static hipError_t launch_mfma_t(const void* x, int m, const void* packed, int n,
 // or wave groups along M ran 32..64 rows before the LDS-staged form, which
 // is faster there (39936 x 6656: 32 rows 57.4 us against 52.7, 64 rows 115.5
 // against 91.9).
-hipError_t launch_w4a16_mfma(int m, const void* x, const void* packed, int n, int k, void* y,
-                             int y_f32, float* partial, int split, hipStream_t stream) {
+template <bool RS>
+static hipError_t launch_w4a16_mfma_rs(int m, const void* x, const void* packed, int n, int k, void* y,
+                                      int y_f32, float* partial, int split, hipStream_t stream,
+                                      const float* row_scale) {
 #define QG_MF(MT, KW, MG, PIPE, PFX) \
-  return launch_mfma_t<MT, KW, MG, PIPE, PFX>(x, m, packed, n, k, y, y_f32, partial, split, stream)
+  return launch_mfma_t<MT, KW, MG, PIPE, PFX, 0, false, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale)
   if (mfma_lds_form(m)) {
     // (m-tiles per wave, waves per n-tile): 64 rows as 2 x 2 (94 VGPRs, 4 waves
     // per SIMD) beat 4 x 1 (150 VGPRs, 2 per SIMD) everywhere measured
@@ -568,11 +582,12 @@ hipError_t launch_w4a16_mfma(int m, const void* x, const void* packed, int n, in
     // 48 rows as 1 x 3, except on the largest layers, where 3 x 1 wins
     // (39936 x 6656: 83.3 us against 94.6; 8448 x 6656: 36.4 against 31.8).
     switch ((m + 15) / 16) {
-      case 2: return launch_mfma2_t<2, 1>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+      case 2: return launch_mfma2_t<2, 1, 0, false, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
       case 3:
-        if (n >= 32768 && k >= 6144) return launch_mfma2_t<3, 1>(x, m, packed, n, k, y, y_f32, partial, split, stream);
-        return launch_mfma2_t<1, 3>(x, m, packed, n, k, y, y_f32, partial, split, stream);
-      case 4: return launch_mfma2_t<2, 2>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+        if (n >= 32768 && k >= 6144)
+          return launch_mfma2_t<3, 1, 0, false, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
+        return launch_mfma2_t<1, 3, 0, false, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
+      case 4: return launch_mfma2_t<2, 2, 0, false, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
       default: return hipErrorInvalidValue;
     }
   }
@@ -580,23 +595,35 @@ hipError_t launch_w4a16_mfma(int m, const void* x, const void* packed, int n, in
 #undef QG_MF
 }
 
+// row_scale (optional, [m] fp32): each row's result times its scale before
+// the store; only where the kernel writes y itself (no partial sums).
+hipError_t launch_w4a16_mfma(int m, const void* x, const void* packed, int n, int k, void* y,
+                             int y_f32, float* partial, int split, hipStream_t stream,
+                             const float* row_scale) {
+  if (row_scale != nullptr && partial == nullptr)
+    return launch_w4a16_mfma_rs<true>(m, x, packed, n, k, y, y_f32, partial, split, stream, row_scale);
+  return launch_w4a16_mfma_rs<false>(m, x, packed, n, k, y, y_f32, partial, split, stream, nullptr);
+}
+
 // INT5 / INT6 and the scale-code INT4 layout on the same two forms and the
 // same bucket choice as INT4.
-template <int HB, bool DQ = false>
+template <int HB, bool DQ = false, bool RS = false>
 static hipError_t launch_wn_mfma_t(int m, const void* x, const void* packed, int n, int k, void* y,
-                                   int y_f32, float* partial, int split, hipStream_t stream) {
+                                   int y_f32, float* partial, int split, hipStream_t stream,
+                                   const float* row_scale = nullptr) {
   if (mfma_lds_form(m)) {
     switch ((m + 15) / 16) {
-      case 2: return launch_mfma2_t<2, 1, HB, DQ>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+      case 2: return launch_mfma2_t<2, 1, HB, DQ, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
       case 3:
-        if (n >= 32768 && k >= 6144) return launch_mfma2_t<3, 1, HB, DQ>(x, m, packed, n, k, y, y_f32, partial, split, stream);
-        return launch_mfma2_t<1, 3, HB, DQ>(x, m, packed, n, k, y, y_f32, partial, split, stream);
-      case 4: return launch_mfma2_t<2, 2, HB, DQ>(x, m, packed, n, k, y, y_f32, partial, split, stream);
+        if (n >= 32768 && k >= 6144)
+          return launch_mfma2_t<3, 1, HB, DQ, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
+        return launch_mfma2_t<1, 3, HB, DQ, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
+      case 4: return launch_mfma2_t<2, 2, HB, DQ, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
       default: return hipErrorInvalidValue;
     }
   }
-  return launch_mfma_t<1, QG_MFMA_KW1, 1, QG_MFMA_PIPE1 != 0, true, HB, DQ>(x, m, packed, n, k, y, y_f32, partial,
-                                                                      split, stream);
+  return launch_mfma_t<1, QG_MFMA_KW1, 1, QG_MFMA_PIPE1 != 0, true, HB, DQ, RS>(x, m, packed, n, k, y, y_f32, partial,
+                                                                      split, stream, row_scale);
 }
 
 hipError_t launch_wn_a16_mfma(int bits, int m, const void* x, const void* packed, int n, int k, void* y,
@@ -607,7 +634,9 @@ hipError_t launch_wn_a16_mfma(int bits, int m, const void* x, const void* packed
 }
 
 hipError_t launch_w4a16_mfma_dq(int m, const void* x, const void* packed, int n, int k, void* y, int y_f32,
-                                float* partial, int split, hipStream_t stream) {
+                                float* partial, int split, hipStream_t stream, const float* row_scale) {
+  if (row_scale != nullptr && partial == nullptr)
+    return launch_wn_mfma_t<0, true, true>(m, x, packed, n, k, y, y_f32, partial, split, stream, row_scale);
   return launch_wn_mfma_t<0, true>(m, x, packed, n, k, y, y_f32, partial, split, stream);
 }
 
