@@ -56,14 +56,19 @@ def _compile(src: str, extra: list[str], objdir: str) -> str:
 
 
 def build(out: str = LIB, extra: list[str] | None = None, objdir: str = OBJDIR,
-          verbose: bool = False) -> str:
-    """Compile all sources (always; no staleness check) and link `out`."""
+          verbose: bool = False, link: list[str] | None = None) -> str:
+    """Compile all sources (always; no staleness check) and link `out`.
+
+    `extra` is added to every compile line; `link`, if given, replaces the
+    default link driver (hipcc) with that command prefix (the objects, -shared
+    and -o are appended)."""
     extra = list(extra or [])
     os.makedirs(objdir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra, objdir), SOURCES))
     tmp = out + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    head = list(link) if link else [HIPCC, "--offload-arch=gfx950"]
+    cmd = [*head, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -384,7 +384,10 @@ void orc_qgemm_w8a16(const uint16_t *x, int64_t m, int64_t k, const int8_t *w,
  * a = max |x|; a == 0 gives xq = 0, sx = 0; otherwise inv = 127/a and
  * sx = a/127 (binary32 divisions), xq = clamp(rint(x * inv), -127, 127).
  * A span holding a NaN or an infinity has no finite scale: it gets sx = NaN
- * and codes 0, so every output it contributes to is NaN. */
+ * and codes 0, so every output it contributes to is NaN.
+ * A span so small that 127/a overflows binary32 (a <= 127 * 2^-128, the
+ * largest such bf16 value; every |x| in it is below 3.8e-37) has no finite
+ * inverse scale either; it is read as a zero span: sx = 0 and codes 0. */
 static void quant_span(const uint16_t *xr, int64_t len, int8_t *xq, float *sx) {
     float a = 0.0f;
     int finite = 1;
@@ -399,6 +402,11 @@ static void quant_span(const uint16_t *xr, int64_t len, int8_t *xq, float *sx) {
         return;
     }
     float inv = 127.0f / a;
+    if (isinf(inv)) {
+        *sx = 0.0f;
+        for (int64_t i = 0; i < len; i++) xq[i] = 0;
+        return;
+    }
     *sx = a / 127.0f;
     for (int64_t i = 0; i < len; i++) {
         float t = rintf(bf16_to_float(xr[i]) * inv);

@@ -18,6 +18,11 @@ def _bf16_exact_bits(v: float) -> int:
     return u >> 16
 
 
+def _number(tok: str) -> float:
+    """A decimal, or a C99 hexadecimal float such as 0x1p-121 or -0xffp-130."""
+    return float.fromhex(tok) if "0x" in tok.lower() else float(tok)
+
+
 def read_cases(name: str, width: int = 32):
     """Parse a fixture: list of dicts with 'name', 'bits' (uint16[width]) and fields."""
     cases = []
@@ -37,9 +42,9 @@ def read_cases(name: str, width: int = 32):
                 fill = 0.0
                 for tok in rest.split():
                     if tok.startswith("rest="):
-                        fill = float(tok[5:])
+                        fill = _number(tok[5:])
                     else:
-                        vals.append(float(tok))
+                        vals.append(_number(tok))
                 vals += [fill] * (width - len(vals))
                 assert len(vals) == width, (cur, len(vals))
                 cur["values"] = vals

@@ -17,7 +17,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qgemm.h")
-LIB = os.path.join(ROOT, "gemm_decode_qgemm_amd", "libqgemm.so")
+LIB = os.environ.get("QGEMM_LIB") or os.path.join(ROOT, "gemm_decode_qgemm_amd", "libqgemm.so")
 
 OK, E_NULL, E_SHAPE, E_K, E_M, E_SPLIT, E_BUF, E_ALIGN, E_DTYPE, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 E_BITS = -10

@@ -179,6 +179,34 @@ def test_w4a8_zero_row_gives_zero():
     assert (y[0] == 0).all() and (y[1] != 0).any()
 
 
+def test_w4a8_span_with_an_overflowing_inverse_scale_is_a_zero_span():
+    """Reading for a span whose 127/a overflows binary32 (hand-worked cases A5
+    and A7): no finite inverse scale, read as a zero span.  Its row's outputs
+    are exactly 0 while a row just above the threshold (case A6) is not; the
+    other rows are untouched."""
+    cases = {c["name"]: c for c in read_cases("actquant_rows.txt")}
+    codes, scales, zeros, _ = oracle.quantize_int4_g32(bf16_bits(int4_weight(16, 256, 3)))
+    x = bf16_bits(activation(4, 256, seed=8))
+    clean = oracle.qgemm_w4a8(x, codes, scales, zeros)
+    x[1] = 0
+    x[1, 64:96] = cases["A5"]["bits"]
+    x[1, 160:192] = cases["A7"]["bits"]
+    x[2] = 0
+    x[2, 32:64] = cases["A6"]["bits"]
+    y = oracle.qgemm_w4a8(x, codes, scales, zeros)
+    assert (y[1] == 0).all()
+    assert (y[2] != 0).any() and np.isfinite(y[2]).all()
+    np.testing.assert_array_equal(y[[0, 3]], clean[[0, 3]])
+    # per group of 32: the flushed groups contribute nothing, the rest of the
+    # row is as if those groups were zero
+    xg = bf16_bits(activation(2, 256, seed=9))
+    xg[0, 64:96] = cases["A5"]["bits"]
+    xz = xg.copy()
+    xz[0, 64:96] = 0
+    np.testing.assert_array_equal(oracle.qgemm_w4a8_g32(xg, codes, scales, zeros),
+                                  oracle.qgemm_w4a8_g32(xz, codes, scales, zeros))
+
+
 # Reading: a span of activations holding a NaN or an infinity has no finite
 # absmax scale; it gets sx = NaN and codes 0, and every output it reaches is NaN.
 NON_FINITE = {"nan": 0x7FC0, "+inf": 0x7F80, "-inf": 0xFF80}

@@ -38,6 +38,7 @@ MUTANTS = [
     ("int8_scale_one_ulp_big", "smallest_bf16_covering(amax, 127.0)", "(smallest_bf16_covering(amax, 127.0) + 1)"),
     ("actquant_128_levels", "float inv = 127.0f / a;", "float inv = 128.0f / a;"),
     ("actquant_non_finite_ignored", "if (!isfinite(v)) finite = 0;", "if (0) finite = 0;"),
+    ("actquant_tiny_span_kept", "if (isinf(inv)) {", "if (0) {"),
     ("w4a8_zero_point_dropped", "(int64_t)(c->codes[row * c->k + kk] - z)", "(int64_t)(c->codes[row * c->k + kk])"),
     ("w4a8_act_scale_dropped", "c->y[mi * c->n + row] = (double)c->sx[mi] * acc;", "c->y[mi * c->n + row] = acc;"),
     ("g32_first_group_scale_for_all", "(double)c->sx[mi * groups + g] *", "(double)c->sx[mi * groups] *"),

@@ -34,7 +34,7 @@ def _f32(v):
     return Fraction(float(np.float32(v)))
 
 
-@pytest.mark.parametrize("order", [(0, 1, 2), (2, 0, 1), (1, 2, 0, 0)])
+@pytest.mark.parametrize("order", [(0, 1, 2), (2, 0, 1), (1, 2, 0, 0), (3, 4, 5, 6), (4, 0, 6, 3, 5, 1)])
 def test_groups_quantize_like_the_hand_worked_rows(order):
     bits = np.concatenate([CASES[i]["bits"] for i in order]).reshape(1, -1)
     xq, sx = oracle.actquant_int8_g32(bits)
