@@ -7,7 +7,8 @@
 // inside the call, per row and symmetric:
 //   a = max|x[m,:]|, inv = 127/a, sx = a/127 (binary32 divisions),
 //   xq = clamp(rint(x * inv), -127, 127) (one binary32 multiply), a == 0 -> 0,
-//   and a row holding a NaN or an infinity gets sx = NaN (no finite scale);
+//   a row holding a NaN or an infinity gets sx = NaN (no finite scale), and a
+//   row so small that 127/a overflows binary32 is a zero row (sx = 0, xq = 0);
 // then y[m,n] = sx[m] * sum_g s[n,g] * I[m,n,g] with the exact integer group
 // dot I = sum_{k in g} xq[m,k] * (q[n,k] - zp[n,g]).
 //
@@ -75,6 +76,21 @@ __device__ __forceinline__ float nmax(float a, float b) { return __builtin_eleme
 // reaches is NaN.
 __device__ __forceinline__ float finite_or_nan(float a) {
   return a < __builtin_inff() ? a : __builtin_nanf("");
+}
+
+// The span's scales from its absmax a (>= 0, or NaN as above): inv = 127 / a
+// and sx = a / 127, both correctly rounded binary32 divisions.  Where 127 / a
+// is not a finite binary32 number there is no inverse scale and inv = 0, so
+// every code is 0: for a == 0 and for a span so small that the quotient
+// overflows (a <= 127 * 2^-128), sx = 0 as well (a zero span, outputs 0); for
+// a NaN absmax sx stays NaN.
+__device__ __forceinline__ void span_scale(float a, float& inv, float& sx) {
+  inv = 127.0f / a;
+  sx = a / 127.0f;
+  if (!(inv <= __FLT_MAX__)) {
+    inv = 0.0f;
+    if (a == a) sx = 0.0f;
+  }
 }
 
 // Quantize 8 bf16 (one 16-byte load) to int8 with the row's inverse scale,
@@ -161,9 +177,7 @@ __global__ __launch_bounds__(WAVES * 64) void w4a8_gemv_kernel(
   for (int m = 0; m < M; ++m) {
     float a = amax_w[0][m];
     for (int ww = 1; ww < WAVES; ++ww) a = nmax(a, amax_w[ww][m]);
-    a = finite_or_nan(a);
-    inv[m] = a > 0.0f ? 127.0f / a : 0.0f;
-    sx[m] = a / 127.0f;
+    span_scale(finite_or_nan(a), inv[m], sx[m]);
   }
 
   const uint32_t nib_s = __builtin_amdgcn_readfirstlane(0x0F0F0F0Fu);
@@ -290,9 +304,7 @@ __global__ __launch_bounds__(WAVES * 64) void w4a8_gemv32_kernel(
   for (int m = 0; m < M; ++m) {
     float a = amax_w[0][m];
     for (int ww = 1; ww < WAVES; ++ww) a = nmax(a, amax_w[ww][m]);
-    a = finite_or_nan(a);
-    inv[m] = a > 0.0f ? 127.0f / a : 0.0f;
-    sx[m] = a / 127.0f;
+    span_scale(finite_or_nan(a), inv[m], sx[m]);
   }
 
   const uint32_t nib_s = __builtin_amdgcn_readfirstlane(0x0F0F0F0Fu);
@@ -422,9 +434,8 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_lds_kernel(
           a = nmax(a, fabsf(bf16_to_f32(w[j] >> 16)));
         }
         a = nmax(a, dpp_fa<0xB1>(a));          // the lane quad holds one group of 32
-        a = finite_or_nan(nmax(a, dpp_fa<0x4E>(a)));
-        const float inv = a > 0.0f ? 127.0f / a : 0.0f;
-        const float sxv = a / 127.0f;
+        float inv, sxv;
+        span_scale(finite_or_nan(nmax(a, dpp_fa<0x4E>(a))), inv, sxv);
         uint32_t lo, hi;
         quant8(v, inv, lo, hi);
         xq_s[buf][m][sg] = u32x2_t{lo, hi};
@@ -609,9 +620,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
     for (int m = 0; m < M; ++m) {
       float a = amax_w[0][m];
       for (int ww = 1; ww < WAVES; ++ww) a = nmax(a, amax_w[ww][m]);
-      a = finite_or_nan(a);
-      if (m == qm) inv_q = a > 0.0f ? 127.0f / a : 0.0f;
-      sx_row[m] = a / 127.0f;
+      float inv_m;
+      span_scale(finite_or_nan(a), inv_m, sx_row[m]);
+      if (m == qm) inv_q = inv_m;
     }
   } else {
     if (hs < h_end) L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
@@ -640,9 +651,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
         a = nmax(a, fabsf(bf16_to_f32(w[j] >> 16)));
       }
       a = nmax(a, dpp_fa<0xB1>(a));
-      a = finite_or_nan(nmax(a, dpp_fa<0x4E>(a)));
-      inv = a > 0.0f ? 127.0f / a : 0.0f;
-      sxv = a / 127.0f;
+      span_scale(finite_or_nan(nmax(a, dpp_fa<0x4E>(a))), inv, sxv);
     }
     uint32_t lo, hi;
     quant8(v, inv, lo, hi);
@@ -839,9 +848,9 @@ __global__ __launch_bounds__(256) void w4a8_actquant_bf16_kernel(const uint16_t*
   for (int off = 32; off > 0; off >>= 1) a = nmax(a, __shfl_xor(a, off, 64));
   if ((tid & 63) == 0) wmax[tid >> 6] = a;
   __syncthreads();
-  a = finite_or_nan(nmax(nmax(wmax[0], wmax[1]), nmax(wmax[2], wmax[3])));
-  const float inv = a > 0.0f ? 127.0f / a : 0.0f;
-  if (blockIdx.x == 0 && tid == 0) sx[row] = a / 127.0f;
+  float inv, sxv;
+  span_scale(finite_or_nan(nmax(nmax(wmax[0], wmax[1]), nmax(wmax[2], wmax[3]))), inv, sxv);
+  if (blockIdx.x == 0 && tid == 0) sx[row] = sxv;
   const int i = blockIdx.x * 256 + tid;
   if (i >= k8) return;
   const u32x4_t v = xr[i];
