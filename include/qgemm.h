@@ -272,7 +272,9 @@ int32_t qgemm_w8a16(const void *x_bf16, int64_t m, int64_t k, const int8_t *w,
  * [P1] `Int4QuantizedGemmPrecisionTest`: the decode kernels run the packed
  * INT4 weight against int8 activations.  Each row of x is quantized inside
  * the call (per-row symmetric absmax: a = max|x|, inv = 127/a, sx = a/127,
- * xq = clamp(rint(x * inv), -127, 127) in binary32; a == 0 gives a zero row),
+ * xq = clamp(rint(x * inv), -127, 127) in binary32; a == 0, and a row so
+ * small that 127/a overflows binary32 (a <= 127 * 2^-128), give a zero row;
+ * a row holding a NaN or an infinity gives a NaN row),
  * then  y[m,n] = sx[m] * sum_g s[n,g] * sum_{k in g} xq[m,k] * (q[n,k] - zp[n,g])
  * with exact integer group dots.  Arguments and errors as qgemm_w4a16
  * (1 <= m <= 64).  For m > 4 the call quantizes x once into the workspace
@@ -292,7 +294,8 @@ int32_t qgemm_w4a8(const void *x_bf16, int64_t m, int64_t k, const void *packed,
  * activation scale per group of 32 consecutive k of a row, so an outlier
  * only coarsens its own group.  Per row m and group g:
  *   a = max |x[m, 32g .. 32g+31]|, inv = 127/a, sx[m,g] = a/127 (binary32),
- *   xq = clamp(rint(x * inv), -127, 127); a == 0 gives a zero group;
+ *   xq = clamp(rint(x * inv), -127, 127); a == 0 or 127/a overflowing gives a
+ *   zero group, a NaN or an infinity in the group a NaN row;
  *   y[m,n] = sum_g sx[m,g] * s[n,g] * sum_{k in g} xq[m,k] * (q[n,k] - zp[n,g]).
  * Arguments, buffers, workspace and errors as qgemm_w4a8, except that
  * m = 5..64 runs as consecutive slices of at most 4 rows on the m <= 4
