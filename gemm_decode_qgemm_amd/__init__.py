@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     FLAG_OVERFLOW,
     QG_BF16,
     QG_F32,
+    SCRATCH_BYTES,
     QGemmError,
     default_split_k,
     int4_dq_packed_bytes,
@@ -22,6 +23,7 @@ from .binding import (  # noqa: F401
     qgemm_w4a8_g32_dq,
     qgemm_w4a16,
     qgemm_w4a16_dq,
+    qgemm_w4a16_noalloc,
     qgemm_w8a16,
     qgemm_wn_a16,
     quantize_int4_g32,

@@ -21,6 +21,7 @@ TILE_K = 256
 TILE_BYTES = 9472
 GROUP = 32
 MAX_M = 64
+SCRATCH_BYTES = 16 * 1024 * 1024      # QG_SCRATCH_BYTES of include/qgemm.h
 FLAG_NONFINITE = 1
 FLAG_OVERFLOW = 2
 
@@ -53,6 +54,7 @@ def _load() -> ctypes.CDLL:
         "qgemm_w4a16_dq": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "quantize_int8_rowwise": (I32, [P, I64, I64, P, P, P, P]),
         "qgemm_w4a16": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
+        "qgemm_w4a16_noalloc": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P]),
         "qgemm_w8a16": (I32, [P, I64, I64, P, P, I64, P, I32, P]),
         "qgemm_w4a8": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "qgemm_w4a8_g32": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
@@ -222,6 +224,22 @@ def qgemm_w4a16(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_k: int =
     st = lib.qgemm_w4a16(x.data_ptr(), m, k, packed.data_ptr(), packed.numel(), n, y.data_ptr(),
                          yd, split_k, _ptr(ws), ws_bytes, _stream(x.device))
     _check(st, "qgemm_w4a16")
+    return y
+
+
+def qgemm_w4a16_noalloc(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_k: int = 0,
+                        out_dtype: torch.dtype = torch.bfloat16,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """qgemm_w4a16 with the split-K partial sums in the library's static device
+    scratch (no workspace; the C call allocates nothing).  Pass `out` to keep
+    the wrapper from allocating the output.  Calls that overlap on one device
+    share the scratch and must not run concurrently."""
+    _dev(x, "x", torch.bfloat16, 2)
+    m, k = x.shape
+    y, yd = _out(m, n, out_dtype, x.device, out)
+    st = lib.qgemm_w4a16_noalloc(x.data_ptr(), m, k, packed.data_ptr(), packed.numel(), n, y.data_ptr(),
+                                 yd, split_k, _stream(x.device))
+    _check(st, "qgemm_w4a16_noalloc")
     return y
 
 

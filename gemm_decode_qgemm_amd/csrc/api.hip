@@ -10,6 +10,9 @@
 // never synchronizes.
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "qg_common.h"
 #include "qgemm.h"
 
@@ -188,6 +191,9 @@ const char* qg_status_string(int32_t s) {
     case QG_E_DTYPE: return "y_dtype must be QG_BF16 or QG_F32";
     case QG_E_HIP: return "a HIP launch failed";
     case QG_E_BITS: return "bits must be 5 or 6";
+    case QG_E_SCRATCH:
+      return "the split needs more partial-sum space than the library's static scratch holds "
+             "(split * m * n * 4 > QG_SCRATCH_BYTES); pass a smaller split_k or use qgemm_w4a16";
     default: return "unknown qgemm status";
   }
 }
@@ -299,23 +305,31 @@ int32_t quantize_int8_rowwise(const void* w_bf16, int64_t n, int64_t k, int8_t* 
                                                      static_cast<hipStream_t>(stream)));
 }
 
-int32_t qgemm_w4a16(const void* x_bf16, int64_t m, int64_t k, const void* packed,
-                    int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype, int32_t split_k,
-                    void* ws, int64_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of qgemm_w4a16 that do not involve the workspace; sets the split.
+int32_t w4a16_check(const void* x_bf16, int64_t m, int64_t k, const void* packed,
+                    int64_t packed_bytes, int64_t n, const void* y, int32_t y_dtype,
+                    int32_t split_k, int32_t* split) {
   if (!x_bf16 || !packed || !y) return QG_E_NULL;
   int32_t st = check_mnk(m, n, k);
   if (st != QG_OK) return st;
   if (y_dtype != QG_BF16 && y_dtype != QG_F32) return QG_E_DTYPE;
-  int32_t split;
-  st = resolve_split(m, n, k, split_k, &split);
+  st = resolve_split(m, n, k, split_k, split);
   if (st != QG_OK) return st;
   if (packed_bytes < qg_int4_packed_bytes(n, k)) return QG_E_BUFFER;
-  const int64_t need_ws = split > 1 ? (int64_t)split * m * n * 4 : 0;
-  if (need_ws > 0 && (!ws || ws_bytes < need_ws)) return ws ? QG_E_BUFFER : QG_E_NULL;
-  if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || (ws && !aligned16(ws)))
-    return QG_E_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
+  if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y)) return QG_E_ALIGN;
+  return QG_OK;
+}
+
+// The launches of qgemm_w4a16 once every argument is checked; `partial` holds
+// split * m * n fp32 partial sums when split > 1 (every element the reduce
+// pass reads is written by the first pass of the same call).
+int32_t w4a16_launch(const void* x_bf16, int64_t m, int64_t k, const void* packed, int64_t n,
+                     void* y, int32_t y_dtype, int32_t split, float* partial, hipStream_t s) {
+  int32_t st;
   if (m > 4) {
     // 5..64 rows: matrix-core kernel (rows padded to 16 and masked).
     st = hip_status(qg::launch_w4a16_mfma((int)m, x_bf16, packed, (int)n, (int)k, y,
@@ -336,6 +350,79 @@ int32_t qgemm_w4a16(const void* x_bf16, int64_t m, int64_t k, const void* packed
   }
   if (st != QG_OK || split == 1) return st;
   return hip_status(qg::launch_splitk_reduce(partial, split, m * n, y, y_dtype == QG_F32, s));
+}
+
+// The library's own device scratch for qgemm_w4a16_noalloc: one array per
+// device (each GPU the library runs on holds its copy until the process
+// ends).  Host code never uses the name `scratch` as an address (on the host
+// it is a stand-in, not device memory): the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and is
+// kept in scratch_addr.
+static __device__ __align__(256) unsigned char scratch[QG_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+std::mutex scratch_mutex;
+
+// Device address of the scratch array on the device `stream` belongs to (the
+// current device for the default stream).
+int32_t scratch_on(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (stream ? hipStreamGetDevice(stream, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+    return QG_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return QG_E_HIP;
+  void* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (p) {
+    *out = p;
+    return QG_OK;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  p = scratch_addr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return QG_E_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return QG_E_HIP;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return QG_E_HIP;
+    if (e != hipSuccess || !p) return QG_E_HIP;
+    scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t qgemm_w4a16(const void* x_bf16, int64_t m, int64_t k, const void* packed,
+                    int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype, int32_t split_k,
+                    void* ws, int64_t ws_bytes, void* stream) {
+  int32_t split;
+  int32_t st = w4a16_check(x_bf16, m, k, packed, packed_bytes, n, y, y_dtype, split_k, &split);
+  if (st != QG_OK) return st;
+  const int64_t need_ws = split > 1 ? (int64_t)split * m * n * 4 : 0;
+  if (need_ws > 0 && (!ws || ws_bytes < need_ws)) return ws ? QG_E_BUFFER : QG_E_NULL;
+  if (ws && !aligned16(ws)) return QG_E_ALIGN;
+  return w4a16_launch(x_bf16, m, k, packed, n, y, y_dtype, split,
+                      split > 1 ? static_cast<float*>(ws) : nullptr, static_cast<hipStream_t>(stream));
+}
+
+int32_t qgemm_w4a16_noalloc(const void* x_bf16, int64_t m, int64_t k, const void* packed,
+                            int64_t packed_bytes, int64_t n, void* y, int32_t y_dtype,
+                            int32_t split_k, void* stream) {
+  int32_t split;
+  int32_t st = w4a16_check(x_bf16, m, k, packed, packed_bytes, n, y, y_dtype, split_k, &split);
+  if (st != QG_OK) return st;
+  const int64_t need = split > 1 ? (int64_t)split * m * n * 4 : 0;
+  if (need > QG_SCRATCH_BYTES) return QG_E_SCRATCH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* partial = nullptr;
+  if (need > 0) {
+    st = scratch_on(s, &partial);
+    if (st != QG_OK) return st;
+  }
+  return w4a16_launch(x_bf16, m, k, packed, n, y, y_dtype, split, static_cast<float*>(partial), s);
 }
 
 int32_t qgemm_w4a16_dq(const void* x_bf16, int64_t m, int64_t k, const void* packed,

@@ -23,7 +23,9 @@
  *    bf16 / fp16 values are their 16-bit IEEE patterns.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *    asynchronous on that stream; the library never allocates, never
- *    synchronizes, and keeps no mutable global state (calls are re-entrant).
+ *    synchronizes, and keeps no mutable global state (calls are re-entrant),
+ *    with one exception: qgemm_w4a16_noalloc, which uses the library's own
+ *    static device scratch (see there).
  *  - The caller owns every buffer.  Outputs must not alias inputs.
  *  - On an argument error the call returns a negative qg_status and launches
  *    nothing (the checks run on the host before any launch).  A HIP launch
@@ -93,7 +95,8 @@ enum qg_status {
     QG_E_ALIGN = -7,       /* a data pointer is not 16-byte aligned */
     QG_E_DTYPE = -8,       /* y_dtype is not QG_BF16 / QG_F32 */
     QG_E_HIP = -9,         /* a HIP launch failed */
-    QG_E_BITS = -10        /* a code width other than 5 or 6 (INT5 / INT6 entry points) */
+    QG_E_BITS = -10,       /* a code width other than 5 or 6 (INT5 / INT6 entry points) */
+    QG_E_SCRATCH = -11     /* qgemm_w4a16_noalloc: the split's partial sums exceed QG_SCRATCH_BYTES */
 };
 
 /* status_dev flag bits */
@@ -180,6 +183,28 @@ int32_t quantize_int8_rowwise(const void *w_bf16, int64_t n, int64_t k, int8_t *
 int32_t qgemm_w4a16(const void *x_bf16, int64_t m, int64_t k, const void *packed,
                     int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
                     int32_t split_k, void *ws, int64_t ws_bytes, void *stream);
+
+/* ---- qgemm_w4a16_noalloc -------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): qgemm_w4a16
+ * without a workspace argument.  The split-K partial sums (split * m * n * 4
+ * bytes when the split is above 1) go to a static device array of
+ * QG_SCRATCH_BYTES inside the library, one per device, which each device the
+ * library runs on holds until the process ends.  The call allocates nothing
+ * (no hipMalloc, no hipFree, no allocating library routine); its first call
+ * on a device looks the array's address up once (hipGetSymbolAddress).
+ * Every call on a device shares that device's array and leaves its
+ * contents behind: calls that overlap on one device (concurrent streams,
+ * threads) race and must be serialized by the caller.  Nothing in the array
+ * needs to start at zero (each call writes every partial it reads).
+ * Arguments, kernels, results (bit-identical to qgemm_w4a16 at the same
+ * split) and errors as qgemm_w4a16, plus QG_E_SCRATCH when an explicit
+ * split_k needs more than QG_SCRATCH_BYTES (nothing is launched); the
+ * default split (split_k = 0) always fits. */
+#define QG_SCRATCH_BYTES (16 * 1024 * 1024)
+int32_t qgemm_w4a16_noalloc(const void *x_bf16, int64_t m, int64_t k, const void *packed,
+                            int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
+                            int32_t split_k, void *stream);
 
 /* Bytes of the version 2 (scale-code) buffer for an N x K weight:
  * ceil(N/64) * (128 + (K/256) * 8960), or a negative qg_status as above. */

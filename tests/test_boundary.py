@@ -21,6 +21,8 @@ LIB = os.environ.get("QGEMM_LIB") or os.path.join(ROOT, "gemm_decode_qgemm_amd",
 
 OK, E_NULL, E_SHAPE, E_K, E_M, E_SPLIT, E_BUF, E_ALIGN, E_DTYPE, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 E_BITS = -10
+E_SCRATCH = -11
+SCRATCH_BYTES = 16 * 1024 * 1024
 A = 0x10000          # a fake, 16-byte aligned "device" address (never dereferenced)
 U = 0x10008          # 8-byte aligned only
 
@@ -45,6 +47,7 @@ def lib():
         "qgemm_w4a16_dq": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "quantize_int8_rowwise": (I32, [P, I64, I64, P, P, P, P]),
         "qgemm_w4a16": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
+        "qgemm_w4a16_noalloc": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P]),
         "qgemm_w8a16": (I32, [P, I64, I64, P, P, I64, P, I32, P]),
         "qgemm_w4a8": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "qgemm_w4a8_g32": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
@@ -71,7 +74,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in (OK, E_NULL, E_SHAPE, E_K, E_M, E_SPLIT, E_BUF, E_ALIGN, E_DTYPE, E_HIP, E_BITS):
+    for code in (OK, E_NULL, E_SHAPE, E_K, E_M, E_SPLIT, E_BUF, E_ALIGN, E_DTYPE, E_HIP, E_BITS, E_SCRATCH):
         s = lib.qg_status_string(code).decode()
         assert s and s != "unknown qgemm status"
     assert "multiple of 256" in lib.qg_status_string(E_K).decode()
@@ -293,3 +296,28 @@ def test_default_workspace_covers_w4a8_row_slices(lib, m, n, k):
         if split <= k // 256:
             assert lib.qg_workspace_bytes(m, n, k, split) >= (split * 4 * n * 4 if split > 1 else 0)
             assert lib.qg_workspace_bytes(m, n, k, split) >= m * k * 2 + 256 + split * m * n * 4
+
+
+def test_noalloc_checks_before_anything(lib):
+    """qgemm_w4a16_noalloc: qgemm_w4a16's argument rules, and an explicit split
+    whose partial sums exceed the static scratch is refused (QG_E_SCRATCH)
+    before any HIP call; the default split always fits the scratch."""
+    f = lib.qgemm_w4a16_noalloc
+    n, k = 39936, 6656
+    pb = lib.qg_int4_packed_bytes(n, k)
+    assert f(A, 64, k, A, pb, n, A, 0, 8, None) == E_SCRATCH          # 8 * 64 * 39936 * 4 > 16 MiB
+    assert f(A, 1, k, A, pb, n, A, 0, 3, None) == E_SPLIT
+    assert f(None, 1, k, A, pb, n, A, 0, 0, None) == E_NULL
+    assert f(A, 65, k, A, pb, n, A, 0, 0, None) == E_M
+    assert f(A, 1, 300, A, pb, n, A, 0, 0, None) == E_K
+    assert f(A, 1, k, A, pb - 1, n, A, 0, 0, None) == E_BUF
+    assert f(U, 1, k, A, pb, n, A, 0, 0, None) == E_ALIGN
+    assert f(A, 1, k, A, pb, n, A, 7, 0, None) == E_DTYPE
+    assert "QG_SCRATCH_BYTES" in lib.qg_status_string(E_SCRATCH).decode()
+    # the default split's partials always fit
+    for m in (1, 2, 4, 5, 16, 17, 33, 48, 64):
+        for n2 in (1, 63, 256, 768, 2048, 2431, 4096, 6656, 8448, 16384, 39936):
+            for k2 in (256, 2048, 6656, 19968, 131072):
+                s = lib.qg_default_split_k(m, n2, k2)
+                need = s * m * n2 * 4 if s > 1 else 0
+                assert need <= SCRATCH_BYTES, (m, n2, k2, s)
