@@ -12,7 +12,20 @@ not divide K), bracketed by device synchronizations; an event on the stream
 the kernels run on is recorded between replays, so the whole timed region and
 each replay are timed on the GPU's clock.  value = K calls / the whole timed
 region; the median, min and p90 of the per-replay time per call are reported
-beside it.
+beside it.  Before the W warm-up calls, untimed replays run for --settle-s
+seconds (0.5 by default): an idle MI355X holds its graphics clock near 160
+MHz and takes a few hundred calls to reach full speed, so a short timed
+region right after start-up would time the ramp.  The graphics and memory
+clocks, power draw and power cap (amdgpu sysfs, as amd-smi reports them),
+read during those replays and after the timed region, are recorded in the
+line.  A short spin kernel before the start event keeps the first replay's
+submission latency out of the timed region.
+
+Beside the layer, the same rotating buffers are read by a plain streaming
+kernel (qg_stream_read: 16-byte non-temporal loads, best of a few grid sizes)
+and the line reports the layer's rate as a percentage of that measured read
+ceiling (pct_of_stream_ceiling); --op stream_read --bytes N measures the
+ceiling alone.
 
 Effective weight bytes per call = N*K/2 (codes) + N*K/32 * 2.5 (fp16 scale +
 4-bit zero per group of 32), the packed buffer size.  The roofline is HBM
@@ -55,8 +68,10 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix-core peak of an MI355X
 METRIC = "µs/call and effective weight GB/s (% HBM peak) for INT4-g32 GEMV at M=1"
 COUNTERS = os.path.join(ROOT, "profiles", "w4a16_gemv_39936x6656_m1_counters.json")
+# The timed kernel's source and the host rules that pick it and its launch
+# shape (split table, workgroup shape).
 KERNEL_SOURCES = ["gemm_decode_qgemm_amd/csrc/gemv_w4a16.hip", "gemm_decode_qgemm_amd/csrc/w4_common.h",
-                  "gemm_decode_qgemm_amd/csrc/qg_common.h", "gemm_decode_qgemm_amd/csrc/api.hip"]
+                  "gemm_decode_qgemm_amd/csrc/qg_common.h", "gemm_decode_qgemm_amd/csrc/dispatch.h"]
 
 
 def kernel_source_hash() -> str:
@@ -90,7 +105,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=1000,
                    help="untimed calls first; the clocks take a few hundred calls to ramp up from idle")
     p.add_argument("--op", choices=("w4a16", "w4a16_dq", "wn_a16", "w4a8", "w4a8_g32", "w4a8_dq", "w4a8_g32_dq", "w8a16",
-                                    "quantize_int4", "quantize_int4_dq", "quantize_intn", "quantize_int8"),
+                                    "quantize_int4", "quantize_int4_dq", "quantize_intn", "quantize_int8",
+                                    "stream_read"),
                    default="w4a16")
     p.add_argument("--bits", type=int, default=6, help="code width of --op wn_a16 (5 or 6)")
     p.add_argument("--n", type=int, default=39936)
@@ -103,6 +119,12 @@ def parse():
                         "the FETCH_SIZE / WRITE_SIZE counters to bytes), then exit")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="rough budget of CPU work for the oracle sample")
+    p.add_argument("--settle-s", type=float, default=0.5,
+                   help="seconds of untimed calls before the warm-up, so the timed calls run at the "
+                        "clocks a busy GPU holds (an idle MI355X sits near 160 MHz and needs a few "
+                        "hundred calls to ramp up)")
+    p.add_argument("--bytes", type=int, default=0,
+                   help="--op stream_read: bytes per read (default: the packed 39936x6656 weight)")
     return p.parse_args()
 
 
@@ -126,6 +148,8 @@ def main() -> int:
     op = args.op
     if op.startswith("quantize"):
         return bench_quantizer(args, torch, qg, si, dev)
+    if op == "stream_read":
+        return bench_stream_read(args, torch, qg, dev)
     if op == "w8a16":
         bytes_eff = n * k + 2 * n
     elif op in ("w4a16_dq", "w4a8_dq", "w4a8_g32_dq"):
@@ -202,15 +226,21 @@ def main() -> int:
     replays = [g_chunk] * full + ([g_rest] if rest else [])
     events = [torch.cuda.Event(enable_timing=True) for _ in range(len(replays) + 1)]
     with torch.cuda.stream(stream):
+        settle = settle_clocks(torch, g_chunk, chunk, args.settle_s)
         g_warm.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        # A short spin kernel holds the stream while the host submits the
+        # start event and the graphs, so the timed region holds the K calls
+        # back to back and not the submission latency of the first replay.
+        torch.cuda._sleep(200_000)
         events[0].record(stream)
         for g, ev in zip(replays, events[1:]):
             g.replay()
             ev.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+    state_after = gpu_state()
     ms_total = events[0].elapsed_time(events[-1])
     us_call = ms_total * 1e3 / args.steps
     per_replay = sorted(events[i].elapsed_time(events[i + 1]) * 1e3 / chunk for i in range(full))
@@ -256,6 +286,9 @@ def main() -> int:
                                    "p90": round(float(np.percentile(per_replay, 90)), 3) if per_replay else None},
             "hip_runtime": torch.version.hip,
             "wall_s": round(wall, 4),
+            "clock_settle": {k2: v for k2, v in settle.items() if k2 != "state"},
+            "gpu_state": {"during_settle": settle.get("state"), "after_timing": state_after,
+                          "note": "amdgpu sysfs readings; they trail the load by a few hundred ms"},
         },
         "roofline": {
             "bound": "hbm",
@@ -266,6 +299,13 @@ def main() -> int:
             "traffic": measured_traffic(n, k, m) if headline else None,
         },
     }
+    # The measured read ceiling of the same rotating buffers (a plain 16-byte
+    # non-temporal streaming read of bytes_eff each), same clocks and protocol.
+    bufs = wqs if op == "w8a16" else packs
+    read_bytes = min(bytes_eff, bufs[0].numel() * bufs[0].element_size()) // 16 * 16
+    ceiling = stream_ceiling(torch, qg, bufs, read_bytes)
+    out["config"]["stream_ceiling"] = ceiling
+    out["pct_of_stream_ceiling"] = round(100.0 * gbs / ceiling["gbs"], 2)
     if m > 4:
         tflops = 2.0 * m * n * k / (us_call * 1e-6) / 1e12
         out["roofline"]["matrix_core"] = {"achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
@@ -278,7 +318,7 @@ def main() -> int:
     return 0
 
 
-def graph_time(torch, call, steps, warmup):
+def graph_time(torch, call, steps, warmup, settle_s=0.5):
     """The timing protocol of main(): warm-up graph, then `steps` calls in
     replays of one captured chunk, events on the capture stream.  Returns
     (us per call, per-replay us per call sorted, chunk, full, rest, wall s)."""
@@ -307,9 +347,11 @@ def graph_time(torch, call, steps, warmup):
     replays = [g_chunk] * full + ([g_rest] if rest else [])
     events = [torch.cuda.Event(enable_timing=True) for _ in range(len(replays) + 1)]
     with torch.cuda.stream(stream):
+        settle_clocks(torch, g_chunk, chunk, settle_s)
         g_warm.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        torch.cuda._sleep(200_000)
         events[0].record(stream)
         for g, ev in zip(replays, events[1:]):
             g.replay()
@@ -319,6 +361,134 @@ def graph_time(torch, call, steps, warmup):
     us_call = events[0].elapsed_time(events[-1]) * 1e3 / steps
     per_replay = sorted(events[i].elapsed_time(events[i + 1]) * 1e3 / chunk for i in range(full))
     return us_call, per_replay, chunk, full, rest, wall
+
+
+def gpu_state():
+    """Graphics and memory clock, power draw and power cap of the GPU, read
+    from the amdgpu driver's sysfs files (the source amd-smi reads; no
+    program is started from this GPU process).  The driver refreshes these
+    figures every few hundred milliseconds, so a reading trails the load by
+    about that much.  None where a file is missing."""
+    import glob
+
+    def first(pattern):
+        for f in sorted(glob.glob(pattern)):
+            try:
+                with open(f) as fh:
+                    return fh.read()
+            except OSError:
+                continue
+        return None
+
+    def current_mhz(text):
+        for line in (text or "").splitlines():
+            if line.rstrip().endswith("*"):
+                digits = "".join(ch for ch in line.split(":", 1)[-1] if ch.isdigit())
+                return int(digits) if digits else None
+        return None
+
+    def watts(text):
+        try:
+            return int(text.strip()) / 1e6
+        except (AttributeError, ValueError):
+            return None
+
+    return {"sclk_mhz": current_mhz(first("/sys/class/drm/card*/device/pp_dpm_sclk")),
+            "mclk_mhz": current_mhz(first("/sys/class/drm/card*/device/pp_dpm_mclk")),
+            "power_w": watts(first("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input")
+                             or first("/sys/class/drm/card*/device/hwmon/hwmon*/power1_average")),
+            "power_cap_w": watts(first("/sys/class/drm/card*/device/hwmon/hwmon*/power1_cap"))}
+
+
+def settle_clocks(torch, graph, calls_per_replay, seconds):
+    """Replay `graph` (untimed) for at least `seconds`, reading the GPU's
+    clocks once while it is busy.  Returns the calls run and that reading."""
+    t0 = time.perf_counter()
+    replays = 0
+    state = None
+    while time.perf_counter() - t0 < seconds or replays == 0:
+        for _ in range(8):
+            graph.replay()
+        replays += 8
+        if state is None and time.perf_counter() - t0 >= 0.8 * seconds:
+            state = gpu_state()            # read while the replays just queued run
+        torch.cuda.synchronize()
+    return {"calls": replays * calls_per_replay, "s": round(time.perf_counter() - t0, 3),
+            "state": state}
+
+
+STREAM_BLOCKS = (512, 1024, 2048, 4096)
+
+
+def stream_ceiling(torch, qg, bufs, nbytes, calls=400, replays=3):
+    """GB/s of qg_stream_read over the rotating buffers `bufs` (nbytes each),
+    best over a few grid sizes, each timed as `replays` replays of a
+    `calls`-call graph (clocks already up)."""
+    import numpy as np
+
+    dev = bufs[0].device
+    sink = torch.empty(max(STREAM_BLOCKS) * 4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.Stream()
+    best = None
+    for blocks in STREAM_BLOCKS:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            qg.stream_read(bufs[0], nbytes, sink, blocks)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(calls):
+                    qg.stream_read(bufs[i % len(bufs)], nbytes, sink, blocks)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
+            ev[0].record(stream)
+            for r in range(replays):
+                g.replay()
+                ev[r + 1].record(stream)
+            torch.cuda.synchronize()
+        us = float(np.median([ev[r].elapsed_time(ev[r + 1]) * 1e3 / calls for r in range(replays)]))
+        gbs = nbytes / (us * 1e-6) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": round(gbs, 2), "us_per_read": round(us, 3), "blocks": blocks, "bytes": nbytes}
+    best["kernel"] = "qg_stream_read: 256 lanes x 2 x 16-byte non-temporal loads per step, grid-strided"
+    best["timing"] = f"median of {replays} replays of a {calls}-call graph per grid size {list(STREAM_BLOCKS)}"
+    return best
+
+
+def bench_stream_read(args, torch, qg, dev):
+    """The plain streaming-read rate of `--bytes` over rotating copies
+    (>= 1 GiB): the ceiling the GEMVs' effective bandwidth is compared with."""
+    nbytes = args.bytes or qg.int4_packed_bytes(39936, 6656)
+    nbytes -= nbytes % 16
+    copies = max(2, math.ceil((1 << 30) / nbytes))
+    bufs = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev) for _ in range(copies)]
+    torch.cuda.synchronize()
+    sink = torch.empty(max(STREAM_BLOCKS) * 4, dtype=torch.int32, device=dev)
+
+    def call(i):
+        qg.stream_read(bufs[i % copies], nbytes, sink, 1024)
+
+    # bring the clocks up with untimed reads, then sweep the grid sizes
+    settle_t0 = time.perf_counter()
+    while time.perf_counter() - settle_t0 < args.settle_s:
+        for i in range(50):
+            call(i)
+        torch.cuda.synchronize()
+    best = stream_ceiling(torch, qg, bufs, nbytes, calls=max(args.steps, 2 * copies), replays=3)
+    out = {
+        "metric": f"streaming-read GB/s (% HBM peak) of {nbytes} bytes per read",
+        "value": best["gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": best["us_per_read"] / 1e3, "us_per_call": best["us_per_read"],
+        "pct_hbm_peak": round(100.0 * best["gbs"] / HBM_PEAK_GBS, 2), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": f"stream read {nbytes} B", "op": "stream_read", "bytes": nbytes,
+                   "rotating_copies": copies, **best, "gpu_state": gpu_state()},
+        "roofline": {"bound": "hbm", "achieved": best["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(best["gbs"] / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def bench_quantizer(args, torch, qg, si, dev):
@@ -355,7 +525,7 @@ def bench_quantizer(args, torch, qg, si, dev):
         def call(i):
             qg.quantize_int8_rowwise(ws[i % copies], out=outs[i % copies])
     torch.cuda.synchronize()
-    us_call, per_replay, chunk, full, rest, wall = graph_time(torch, call, args.steps, args.warmup)
+    us_call, per_replay, chunk, full, rest, wall = graph_time(torch, call, args.steps, args.warmup, args.settle_s)
     gbs = bytes_eff / (us_call * 1e-6) / 1e9
     name = {"quantize_int4": "INT4-g32 quantize + pack", "quantize_int4_dq": "INT4-g32 quantize + pack with scale codes",
             "quantize_intn": f"INT{args.bits}-g32 quantize + pack", "quantize_int8": "INT8 row-wise quantize"}[op]

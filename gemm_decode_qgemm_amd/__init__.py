@@ -31,5 +31,6 @@ from .binding import (  # noqa: F401
     quantize_int8_rowwise,
     quantize_intn_g32,
     status_string,
+    stream_read,
     workspace_bytes,
 )

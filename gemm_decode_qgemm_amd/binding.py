@@ -55,6 +55,7 @@ def _load() -> ctypes.CDLL:
         "quantize_int8_rowwise": (I32, [P, I64, I64, P, P, P, P]),
         "qgemm_w4a16": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "qgemm_w4a16_noalloc": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P]),
+        "qg_stream_read": (I32, [P, I64, P, I32, P]),
         "qgemm_w8a16": (I32, [P, I64, I64, P, P, I64, P, I32, P]),
         "qgemm_w4a8": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "qgemm_w4a8_g32": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
@@ -241,6 +242,18 @@ def qgemm_w4a16_noalloc(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_
                                  yd, split_k, _stream(x.device))
     _check(st, "qgemm_w4a16_noalloc")
     return y
+
+
+def stream_read(src: torch.Tensor, nbytes: int, sink: torch.Tensor, blocks: int = 1024) -> None:
+    """qg_stream_read: read the first `nbytes` bytes of `src` once (the plain
+    streaming-read rate the GEMVs are compared with); `sink` receives
+    blocks * 4 XOR words (int32, at least that many elements)."""
+    if not src.is_cuda or not sink.is_cuda or sink.dtype != torch.int32 or sink.numel() < 4 * blocks:
+        raise ValueError("src and sink must be device tensors, sink int32 with >= 4 * blocks elements")
+    if nbytes > src.numel() * src.element_size():
+        raise ValueError("nbytes exceeds src")
+    _check(lib.qg_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), blocks, _stream(src.device)),
+           "qg_stream_read")
 
 
 def qgemm_w4a16_dq(x: torch.Tensor, packed: torch.Tensor, n: int, *, split_k: int = 0,

@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libqgemm.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["api.hip", "quantize.hip", "gemv_w4a16.hip", "gemv_w8a16.hip", "gemv_w4a8.hip",
-           "gemm_w4a16_mfma.hip", "gemv_w4a16_mx4.hip"]
+           "gemm_w4a16_mfma.hip", "gemv_w4a16_mx4.hip", "stream_read.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

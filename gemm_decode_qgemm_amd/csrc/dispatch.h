@@ -1,0 +1,89 @@
+// dispatch.h -- host-side dispatch rules of the C ABI (include/qgemm.h):
+// the split-K table for split_k = 0 and the GEMV workgroup shape, measured
+// on MI355X.  Internal header, included by api.hip only.
+#pragma once
+
+#include <stdint.h>
+
+#include "qgemm.h"
+#include "qg_common.h"
+
+namespace qg {
+
+constexpr int64_t kCUs = 256;   // compute units of an MI355X
+
+// Split-K default, measured on MI355X at the decode layer shapes.
+//  * M <= 4 (GEMV, 32-row workgroups): one split whenever the grid has at
+//    least half a workgroup per CU (N >= 4096): a second split costs a second
+//    launch and the partials' traffic, which the extra parallelism does not
+//    repay at these shapes (6656 x 4096: 5.1 us at 1 against 7.1 at 2 for
+//    M = 1, 5.4 against 7.4 for M = 4; 8448 x 6656, M = 4: 10.7 against
+//    11.1); below that, the smallest split giving a workgroup per CU, at
+//    most 4 (2048 x 8192, M = 4: 6.7 us at 4 against 7.4 at 1; 256 x 6656:
+//    5.3 us at 4, 5.9 at 8).
+//  * M > 4 (matrix-core kernels): the smallest split with 64-row blocks x
+//    split >= 120 for the register form, at most 8 (6656 x 19968, M = 16:
+//    24.7 us at 2 against 40.3 at 1; 8448 x 6656: 15.7 us at 1 against 17.7
+//    at 2), >= 300 for the LDS-staged form (17..64 rows), whose workgroups
+//    hold more LDS and need more of them in flight (8448 x 6656, M = 32: 19.6
+//    us at 4 against 26.5 at 1; M = 64: 32.4 at 4 against 37.6 at 1).
+// Both are capped by K / 256 (one tile per split).
+inline int32_t default_split(int64_t m, int64_t n, int64_t k) {
+  const int64_t kt = k / QG_TILE_K;
+  int32_t s = 1;
+  if (m <= 4) {
+    const int64_t n32 = (n + 31) / 32;
+    if (n32 >= kCUs / 2) return 1;
+    while (s < 4 && 2 * s <= kt && n32 * s < kCUs) s *= 2;
+    return s;
+  }
+  const int64_t rbs = (n + QG_TILE_ROWS - 1) / QG_TILE_ROWS;
+  const int64_t want = qg::mfma_lds_form(m) ? 300 : 120;
+  while (s < 8 && 2 * s <= kt && rbs * s < want) s *= 2;
+  return s;
+}
+
+// Workgroup shape of the M <= 4 INT4 GEMVs: 32 rows and 16 waves, except
+// where the 32-row grid spills a few workgroups into a second round over the
+// CUs while the 64-row grid fits in one (N = 8448: 264 against 132
+// workgroups; 9.1 us against 10.2 at M = 1), for M = 1 and one split (at
+// M = 2 the matrix-instruction GEMV on 32 rows is as fast: 10.7 us).
+struct GemvShape {
+  int rows, waves;
+};
+inline GemvShape gemv_shape(int64_t m, int64_t n, int32_t split) {
+  const int64_t n32 = (n + 31) / 32, n64 = (n + 63) / 64;
+  if (m == 1 && split == 1 && n32 > kCUs && n64 <= kCUs) return {64, 16};
+  return {32, 16};
+}
+
+// INT5 / INT6 on the matrix cores (M > 4) carry more work per weight than
+// INT4, and more splits pay (measured on the INT6 layers of the 30B export,
+// buckets 16 and 64: 5376 x 21504 best at 8, 4096 x 5376 and 6656 x 19968 at
+// 4, 1024 x 6656 at 8): the smallest split with 64-row blocks x split >= 400,
+// at most 8, and one step back when that leaves under 4 tiles of 256 k per
+// workgroup while the grid still has a workgroup per CU.  M <= 4 keeps the
+// INT4 rule (5376 x 21504 M = 1: 21.3 us at 1 against 19.9 at 4).
+inline int32_t default_split_intn(int64_t m, int64_t n, int64_t k) {
+  if (m <= 4) return default_split(m, n, k);
+  const int64_t kt = k / QG_TILE_K;
+  const int64_t rbs = (n + QG_TILE_ROWS - 1) / QG_TILE_ROWS;
+  int32_t s = 1;
+  while (s < 8 && 2 * s <= kt && rbs * s < 400) s *= 2;
+  if (s > 1 && kt < 4 * s && rbs * (s / 2) >= kCUs) s /= 2;
+  return s;
+}
+
+inline int32_t resolve_split(int64_t m, int64_t n, int64_t k, int32_t split_k, int32_t* out,
+                      bool intn = false) {
+  if (split_k == 0) {
+    *out = intn ? default_split_intn(m, n, k) : default_split(m, n, k);
+    return QG_OK;
+  }
+  if (split_k != 1 && split_k != 2 && split_k != 4 && split_k != 8) return QG_E_SPLIT;
+  if (split_k > k / QG_TILE_K) return QG_E_SPLIT;
+  *out = split_k;
+  return QG_OK;
+}
+
+}  // namespace qg

@@ -346,6 +346,16 @@ int32_t qgemm_w4a8_g32_dq(const void *x_bf16, int64_t m, int64_t k, const void *
                           int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
                           int32_t split_k, void *ws, int64_t ws_bytes, void *stream);
 
+/* ---- qg_stream_read (measurement helper, not part of the layer) ---------
+ * Reads `bytes` bytes of device memory at `src` once, with one 16-byte
+ * non-temporal load per lane per step over `blocks` workgroups of 256 lanes
+ * (2 x 16 bytes per lane per step, grid-strided), and writes one XOR word per
+ * wave to `sink` (blocks * 4 uint32).  The plain streaming-read rate of a
+ * buffer, against which the GEMVs' effective bandwidth is compared.
+ * bytes: a multiple of 16; src 16-byte aligned; 1 <= blocks <= 65536.
+ * Errors: QG_E_NULL, QG_E_SHAPE, QG_E_ALIGN, QG_E_HIP. */
+int32_t qg_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t blocks, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

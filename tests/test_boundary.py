@@ -48,6 +48,7 @@ def lib():
         "quantize_int8_rowwise": (I32, [P, I64, I64, P, P, P, P]),
         "qgemm_w4a16": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "qgemm_w4a16_noalloc": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P]),
+        "qg_stream_read": (I32, [P, I64, P, I32, P]),
         "qgemm_w8a16": (I32, [P, I64, I64, P, P, I64, P, I32, P]),
         "qgemm_w4a8": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
         "qgemm_w4a8_g32": (I32, [P, I64, I64, P, I64, I64, P, I32, I32, P, I64, P]),
