@@ -39,9 +39,9 @@ Other layers of the same path use the same protocol: --op w4a16 with
 --m 2..64 (M > 4 runs the matrix-core kernel), --op w4a16_dq (the scale-code
 weight, bytes = its packed size; --op w4a8_dq / w4a8_g32_dq the W4A8 forms on it),
 --op wn_a16 --bits 5|6 (INT5 / INT6,
-M = 1, bytes = the packed size), --op w4a8 / w4a8_g32 (M <= 64; at M > 4 per-row
-scales run the matrix-core kernel on the quantized rows, per-group scales run
-slices of 4 rows that each stream the weight, and bytes still count it once) and
+M = 1, bytes = the packed size), --op w4a8 / w4a8_g32 (M <= 64; at M > 4 the
+activations are quantized once into the workspace and the matrix-core kernel
+runs on the int8 codes, one weight pass) and
 --op w8a16 (int8 per-channel, bytes = N*K + 2*N); --n/--k pick the shape.  The
 offline weight quantizers run the same way: --op quantize_int4 / quantize_int4_dq /
 quantize_intn --bits 5|6 (bytes = the
@@ -178,10 +178,7 @@ def main() -> int:
             w_cpu, x_cpu = si.decode_inputs(n, k, m)
         else:
             w_cpu, x_cpu = si.int4_weight(n, k, n ^ k), si.activation(m, k, 9100 + m)
-        # W4A8 with per-group scales runs M > 4 as slices of 4 rows, each with the
-        # 4-row default split (per-row scales there use the matrix-core default)
-        split_rows = min(m, 4) if op in ("w4a8_g32", "w4a8_g32_dq") else m
-        split = args.split or qg.default_split_k(split_rows, n, k, args.bits if op == "wn_a16" else 4)
+        split = args.split or qg.default_split_k(m, n, k, args.bits if op == "wn_a16" else 4)
         if op in ("w4a16_dq", "w4a8_dq", "w4a8_g32_dq"):
             packed0 = qg.quantize_int4_g32_dq(w_cpu.to(dev))
         elif op == "wn_a16":

@@ -37,6 +37,10 @@ hipError_t launch_wn_a16_mfma(int bits, int m, const void* x, const void* packed
 hipError_t launch_w4a16_mfma_dq(int m, const void* x, const void* packed, int n, int k, void* y, int y_f32,
                                 float* partial, int split, hipStream_t stream,
                                 const float* row_scale = nullptr);
+hipError_t launch_w4a8_actquant_g32_bf16(int m, const void* x, int k, void* xq, float* sxg,
+                                         hipStream_t stream);
+hipError_t launch_w4a8g_mfma(bool dq, int m, const void* xq, const float* act_scale, const void* packed, int n,
+                             int k, void* y, int y_f32, float* partial, int split, hipStream_t stream);
 hipError_t launch_w4a8_actquant_bf16(int m, const void* x, int k, void* xq, float* sx,
                                      hipStream_t stream);
 hipError_t launch_w4a8_rowscale_reduce(const float* partial, int split, int m, int n, const float* sx,
@@ -101,10 +105,12 @@ int32_t check_mnk(int64_t m, int64_t n, int64_t k) {
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? QG_OK : QG_E_HIP; }
 
-// Workspace of W4A8 with per-row scales at m > 4: xq as bf16 [m, k], sx
-// fp32 [m] (256 bytes), then the fp32 partial sums [split, m, n], split >= 1.
+// Workspace of W4A8 at m > 4: xq as bf16 [m, k]; then the activation
+// scales: per row, fp32 [m] (256 bytes), per group of 32, fp32 [k/32][64]
+// (8 k bytes); then the fp32 partial sums [split, m, n], split >= 1.
+int64_t w4a8_scales_bytes(int64_t k) { return k * 8 > 256 ? k * 8 : 256; }
 int64_t w4a8_mfma_ws(int64_t m, int64_t n, int64_t k, int32_t split) {
-  return m * k * 2 + 256 + (int64_t)split * m * n * 4;
+  return m * k * 2 + w4a8_scales_bytes(k) + (int64_t)split * m * n * 4;
 }
 
 }  // namespace
@@ -167,21 +173,16 @@ int64_t qg_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k) {
   if (split_k != 0) {
     const int64_t bytes = split > 1 ? (int64_t)split * m * n * 4 : 0;
     if (m <= 4) return bytes;
-    const int64_t w8 = w4a8_mfma_ws(m, n, k, split);   // W4A8, per-row scales, m > 4
+    const int64_t w8 = w4a8_mfma_ws(m, n, k, split);   // W4A8 at m > 4
     return w8 > bytes ? w8 : bytes;
   }
   // split_k = 0: enough for the default of every entry point, W4A8 at M > 4
-  // included (slices of 4 rows, each with the default split of 4 rows)
+  // included (quantized x, its scales and the partials at that default)
   int64_t units = split > 1 ? (int64_t)split * m : 0;
   const int32_t si = default_split_intn(m, n, k);
   if (si > 1 && (int64_t)si * m > units) units = (int64_t)si * m;
-  if (m > 4) {
-    const int32_t s4 = default_split(4, n, k);
-    if (s4 > 1 && (int64_t)s4 * 4 > units) units = (int64_t)s4 * 4;
-  }
   const int64_t bytes = units * n * 4;
   if (m <= 4) return bytes;
-  // W4A8 with per-row scales at m > 4 (quantized x, sx, partials at its split)
   const int64_t w8 = w4a8_mfma_ws(m, n, k, split);
   return w8 > bytes ? w8 : bytes;
 }
@@ -483,7 +484,7 @@ static int32_t w4a8_common(const void* x_bf16, int64_t m, int64_t k, const void*
     if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || !aligned16(ws)) return QG_E_ALIGN;
     char* w = static_cast<char*>(ws);
     float* sx = reinterpret_cast<float*>(w + m * k * 2);
-    float* partial = reinterpret_cast<float*>(w + m * k * 2 + 256);
+    float* partial = reinterpret_cast<float*>(w + m * k * 2 + w4a8_scales_bytes(k));
     st = hip_status(qg::launch_w4a8_actquant_bf16((int)m, x_bf16, (int)k, w, sx, s));
     if (st != QG_OK) return st;
     if (split == 1) {
@@ -501,9 +502,27 @@ static int32_t w4a8_common(const void* x_bf16, int64_t m, int64_t k, const void*
     return hip_status(qg::launch_w4a8_rowscale_reduce(partial, split, (int)m, (int)n, sx, y,
                                                       y_dtype == QG_F32, s));
   }
-  // Otherwise M = 5..64 runs as consecutive slices of at most 4 activation
-  // rows (below).
-  const int64_t rows = m < 4 ? m : 4;
+  if (m > 4) {
+    // One scale per group of 32 at 5..64 rows: x quantized once into the
+    // workspace (xq exact in bf16, sx group-major), then the matrix-core
+    // kernel scales each group's integer dot by s * sx, one weight pass.
+    int32_t split;
+    st = resolve_split(m, n, k, split_k, &split);
+    if (st != QG_OK) return st;
+    if (packed_bytes < (dq ? qg_int4_dq_packed_bytes(n, k) : qg_int4_packed_bytes(n, k))) return QG_E_BUFFER;
+    if (!ws || ws_bytes < w4a8_mfma_ws(m, n, k, split)) return ws ? QG_E_BUFFER : QG_E_NULL;
+    if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || !aligned16(ws)) return QG_E_ALIGN;
+    char* w = static_cast<char*>(ws);
+    float* sxg = reinterpret_cast<float*>(w + m * k * 2);
+    float* partial = split > 1 ? reinterpret_cast<float*>(w + m * k * 2 + w4a8_scales_bytes(k)) : nullptr;
+    st = hip_status(qg::launch_w4a8_actquant_g32_bf16((int)m, x_bf16, (int)k, w, sxg, s));
+    if (st != QG_OK) return st;
+    st = hip_status(qg::launch_w4a8g_mfma(dq, (int)m, w, sxg, packed, (int)n, (int)k, y, y_dtype == QG_F32,
+                                          partial, split, s));
+    if (st != QG_OK || split == 1) return st;
+    return hip_status(qg::launch_splitk_reduce(partial, split, m * n, y, y_dtype == QG_F32, s));
+  }
+  const int64_t rows = m;
   int32_t split;
   st = resolve_split(rows, n, k, split_k, &split);
   if (st != QG_OK) return st;
@@ -513,19 +532,7 @@ static int32_t w4a8_common(const void* x_bf16, int64_t m, int64_t k, const void*
   if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y) || (ws && !aligned16(ws)))
     return QG_E_ALIGN;
   float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
-  // Each slice streams the whole weight again; the slices run in stream order,
-  // so they share the split-K workspace.  A slice of x starts 4 k elements
-  // further (16-byte aligned, k being a multiple of 256); y is stored element
-  // by element, so its slices need no more than the element's alignment.
-  const int64_t y_elem = y_dtype == QG_F32 ? 4 : 2;
-  for (int64_t r0 = 0; r0 < m; r0 += 4) {
-    const int64_t mc = m - r0 < 4 ? m - r0 : 4;
-    st = w4a8_rows(static_cast<const uint16_t*>(x_bf16) + r0 * k, mc, k, packed, n,
-                   static_cast<char*>(y) + r0 * n * y_elem, y_dtype, split, partial, s,
-                   group_scales, dq);
-    if (st != QG_OK) return st;
-  }
-  return QG_OK;
+  return w4a8_rows(x_bf16, m, k, packed, n, y, y_dtype, split, partial, s, group_scales, dq);
 }
 
 int32_t qgemm_w4a8(const void* x_bf16, int64_t m, int64_t k, const void* packed,

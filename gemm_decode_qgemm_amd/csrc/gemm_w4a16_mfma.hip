@@ -110,24 +110,30 @@ __device__ __forceinline__ uint32_t wide_pair_mfma(uint32_t dw, uint32_t pw, int
 
 constexpr int kNT = 4;   // n-tiles of 16 rows per wave: a whole 64-row block
 
-template <int MT, int HB>
+template <int MT, int HB, bool AS = false>
 struct MfmaUnit {
   u32x4_t w[kNT];      // code chunks (group a, row 16t + i), transposed after the load
   u32x2_t hp[HB > 0 ? kNT : 1];   // their high-bit planes (INT5 / INT6)
   u32x2_t scl;         // fp16 scales of row `lane` (the half tile's 4 groups)
   uint32_t zwl;        // zero points of row `lane` (16 bits of nibbles; INT5/6: 4 bytes)
   u32x4_t xa[MT][4];   // A operands: x[16 mt + i][32 g + 8 a .. + 8] per group g
+  f32x4_t sxa[AS ? MT : 1][AS ? 4 : 1];   // activation scales of rows 16 mt + 4a + e, per group g
 };
 
 // A wave owns one 64-row block (the 4 n-tiles) for a range of half tiles.
 // PIPE: software pipeline over two register sets (PFX: the next unit's
 // activations too), or load-wait-compute per unit with the other resident
 // waves covering the latency.
-template <int MT, int KW, int MG, bool PIPE, bool PFX, int HB = 0, bool DQ = false, bool RS = false>
+// AS (W4A8 with one activation scale per group of 32): x holds the int8 codes
+// xq (exact bf16 integers), act_scale their scales group-major, sx of row r
+// and group g at act_scale[64 g + r]; each group's integer dot is multiplied
+// by s[n,g] * sx[m,g] before it is added.
+template <int MT, int KW, int MG, bool PIPE, bool PFX, int HB = 0, bool DQ = false, bool RS = false,
+          bool AS = false>
 __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split,
-    const float* __restrict__ row_scale) {
+    const float* __restrict__ row_scale, const float* __restrict__ act_scale) {
   constexpr int WAVES = KW * MG;
   __shared__ f32x4_t red[WAVES][kNT][64];
   const int lane = threadIdx.x & 63;
@@ -157,7 +163,7 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
   // zero points: lane l loads those of row l only (one 8-byte and one 2-byte
   // load per half tile; per n-tile loads with 4 lanes per row cost a quarter
   // of the kernel's time); compute() hands row 16t + i to lane (i, a).
-  auto load_w = [&](MfmaUnit<MT, HB>& u, int hs) {
+  auto load_w = [&](MfmaUnit<MT, HB, AS>& u, int hs) {
     const uint8_t* tile = tiles + (size_t)(hs >> 1) * T::kBytes;
     const int half = hs & 1;
 #pragma unroll
@@ -183,13 +189,21 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
   // Rows of x at or past m read row m - 1 instead (a valid address, no
   // branch and no select): output row r of an MFMA depends on row r of its A
   // operand only, and those rows are never stored.
-  auto load_x = [&](MfmaUnit<MT, HB>& u, int hs) {
+  auto load_x = [&](MfmaUnit<MT, HB, AS>& u, int hs) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int row = min(16 * (mg * MT + mt) + i, m - 1);
       const uint16_t* xr = x + (size_t)row * k + (size_t)hs * 128 + 8 * a;
 #pragma unroll
       for (int g = 0; g < 4; ++g) u.xa[mt][g] = *reinterpret_cast<const u32x4_t*>(xr + 32 * g);
+      if constexpr (AS) {
+        // rows 16 mt + 4a .. + 3 of groups 4 hs .. 4 hs + 3 (rows past m are
+        // read but never stored)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          u.sxa[mt][g] = *reinterpret_cast<const f32x4_t*>(act_scale + (size_t)(4 * hs + g) * 64 +
+                                                           16 * (mg * MT + mt) + 4 * a);
+      }
     }
   };
 
@@ -199,7 +213,7 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](MfmaUnit<MT, HB>& u) {
+  auto compute = [&](MfmaUnit<MT, HB, AS>& u) {
 #pragma unroll
     for (int t = 0; t < kNT; ++t) transpose_rows4(u.w[t]);
     u32x4_t hr[kNT];
@@ -243,8 +257,10 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
           const f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8_t, u.xa[mt][g]), bv, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[t][mt][e] = __builtin_fmaf(s, __builtin_fmaf(-zb, xg[mt][e], p[e]), acc[t][mt][e]);
+          for (int e = 0; e < 4; ++e) {
+            const float se = AS ? s * u.sxa[mt][g][e] : s;
+            acc[t][mt][e] = __builtin_fmaf(se, __builtin_fmaf(-zb, xg[mt][e], p[e]), acc[t][mt][e]);
+          }
         }
       }
       // keep each group's MFMA results from being hoisted into the next group
@@ -260,13 +276,13 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
   int hs = 2 * t0 + kw;
   if constexpr (!PIPE) {
     for (; hs < h_end; hs += KW) {
-      MfmaUnit<MT, HB> u;
+      MfmaUnit<MT, HB, AS> u;
       load_w(u, hs);
       load_x(u, hs);
       compute(u);
     }
   } else if (hs < h_end) {
-    MfmaUnit<MT, HB> ua, ub;
+    MfmaUnit<MT, HB, AS> ua, ub;
     load_w(ua, hs);
     load_x(ua, hs);
     while (true) {
@@ -348,13 +364,16 @@ struct Mfma2W {
   u32x2_t zw;       // the row's 8 zero points (nibbles in .x; INT5/6: 8 bytes)
 };
 
-template <int MT, int MG, int HB = 0, bool DQ = false, bool RS = false>
+// AS: as for the register form; the tile's 8 groups x 64 rows of activation
+// scales are copied into LDS with its activations.
+template <int MT, int MG, int HB = 0, bool DQ = false, bool RS = false, bool AS = false>
 __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split,
-    const float* __restrict__ row_scale) {
+    const float* __restrict__ row_scale, const float* __restrict__ act_scale) {
   constexpr int MR = 16 * MT * MG;                 // staged x rows
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][MR * 512];
+  __shared__ __attribute__((aligned(16))) float sxs[AS ? 2 : 1][AS ? 8 * 64 : 4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int i = lane & 15, a = lane >> 4;
@@ -386,6 +405,13 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
       __builtin_amdgcn_global_load_lds(x + (size_t)src * k + (size_t)kt * 256 + 8 * c,
                                        (__attribute__((address_space(3))) void*)(xs[buf] + 1024 * u),
                                        16, 0, 0);
+    }
+    if constexpr (AS) {
+      // groups 8 kt .. 8 kt + 7, 64 rows each: 2 KB, contiguous in act_scale
+      if (wv < 2)
+        __builtin_amdgcn_global_load_lds(act_scale + (size_t)kt * 512 + 256 * wv + 4 * lane,
+                                         (__attribute__((address_space(3))) void*)(&sxs[buf][256 * wv]),
+                                         16, 0, 0);
     }
   };
   auto load_w = [&](Mfma2W<HB>& w, int kt) {
@@ -440,6 +466,7 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
     const uint8_t* xb = xs[buf];
     f32x4_t dp[MT];
     float sp = 0.0f;
+    f32x4_t sxp[AS ? MT : 1];     // the previous group's activation scales
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const uint32_t dw = g < 4 ? w.c0[g] : w.c1[g - 4];
@@ -471,7 +498,7 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            acc[mt][e] = __builtin_fmaf(sp, dp[mt][e], acc[mt][e]);
+            acc[mt][e] = __builtin_fmaf(AS ? sp * sxp[mt][e] : sp, dp[mt][e], acc[mt][e]);
             // pin the update here: left alone, the compiler sinks every
             // group's FMAs past the tile's barrier and keeps all 8 groups'
             // products live
@@ -481,13 +508,18 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) dp[mt] = d[mt];
       sp = s;
+      if constexpr (AS) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          sxp[mt] = *reinterpret_cast<const f32x4_t*>(&sxs[buf][64 * g + 16 * (mg * MT + mt) + 4 * a]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[mt][e] = __builtin_fmaf(sp, dp[mt][e], acc[mt][e]);
+        acc[mt][e] = __builtin_fmaf(AS ? sp * sxp[mt][e] : sp, dp[mt][e], acc[mt][e]);
         asm volatile("" : "+v"(acc[mt][e]));
       }
   };
@@ -534,25 +566,27 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
   }
 }
 
-template <int MT, int MG = 1, int HB = 0, bool DQ = false, bool RS = false>
+template <int MT, int MG = 1, int HB = 0, bool DQ = false, bool RS = false, bool AS = false>
 static hipError_t launch_mfma2_t(const void* x, int m, const void* packed, int n, int k, void* y,
                                  int y_f32, float* partial, int split, hipStream_t stream,
-                                 const float* row_scale = nullptr) {
+                                 const float* row_scale = nullptr, const float* act_scale = nullptr) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_mfma2_kernel<MT, MG, HB, DQ, RS>), dim3(rbs, split), dim3(256 * MG), 0, stream,
+  hipLaunchKernelGGL((w4a16_mfma2_kernel<MT, MG, HB, DQ, RS, AS>), dim3(rbs, split), dim3(256 * MG), 0, stream,
                      static_cast<const uint16_t*>(x), m, static_cast<const uint8_t*>(packed), n, k,
-                     y, y_f32, partial, split, row_scale);
+                     y, y_f32, partial, split, row_scale, act_scale);
   return hipGetLastError();
 }
 
-template <int MT, int KW, int MG, bool PIPE, bool PFX, int HB = 0, bool DQ = false, bool RS = false>
+template <int MT, int KW, int MG, bool PIPE, bool PFX, int HB = 0, bool DQ = false, bool RS = false,
+          bool AS = false>
 static hipError_t launch_mfma_t(const void* x, int m, const void* packed, int n, int k, void* y,
                                 int y_f32, float* partial, int split, hipStream_t stream,
-                                const float* row_scale = nullptr) {
+                                const float* row_scale = nullptr, const float* act_scale = nullptr) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_mfma_kernel<MT, KW, MG, PIPE, PFX, HB, DQ, RS>), dim3(rbs, split),
+  hipLaunchKernelGGL((w4a16_mfma_kernel<MT, KW, MG, PIPE, PFX, HB, DQ, RS, AS>), dim3(rbs, split),
                      dim3(KW * MG * 64), 0, stream, static_cast<const uint16_t*>(x), m,
-                     static_cast<const uint8_t*>(packed), n, k, y, y_f32, partial, split, row_scale);
+                     static_cast<const uint8_t*>(packed), n, k, y, y_f32, partial, split, row_scale,
+                     act_scale);
   return hipGetLastError();
 }
 
@@ -607,23 +641,25 @@ hipError_t launch_w4a16_mfma(int m, const void* x, const void* packed, int n, in
 
 // INT5 / INT6 and the scale-code INT4 layout on the same two forms and the
 // same bucket choice as INT4.
-template <int HB, bool DQ = false, bool RS = false>
+template <int HB, bool DQ = false, bool RS = false, bool AS = false>
 static hipError_t launch_wn_mfma_t(int m, const void* x, const void* packed, int n, int k, void* y,
                                    int y_f32, float* partial, int split, hipStream_t stream,
-                                   const float* row_scale = nullptr) {
+                                   const float* row_scale = nullptr, const float* act_scale = nullptr) {
+#define QG_MF2(MT, MG) \
+  launch_mfma2_t<MT, MG, HB, DQ, RS, AS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale, act_scale)
   if (mfma_lds_form(m)) {
     switch ((m + 15) / 16) {
-      case 2: return launch_mfma2_t<2, 1, HB, DQ, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
+      case 2: return QG_MF2(2, 1);
       case 3:
-        if (n >= 32768 && k >= 6144)
-          return launch_mfma2_t<3, 1, HB, DQ, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
-        return launch_mfma2_t<1, 3, HB, DQ, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
-      case 4: return launch_mfma2_t<2, 2, HB, DQ, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
+        if (n >= 32768 && k >= 6144) return QG_MF2(3, 1);
+        return QG_MF2(1, 3);
+      case 4: return QG_MF2(2, 2);
       default: return hipErrorInvalidValue;
     }
   }
-  return launch_mfma_t<1, QG_MFMA_KW1, 1, QG_MFMA_PIPE1 != 0, true, HB, DQ, RS>(x, m, packed, n, k, y, y_f32, partial,
-                                                                      split, stream, row_scale);
+#undef QG_MF2
+  return launch_mfma_t<1, QG_MFMA_KW1, 1, QG_MFMA_PIPE1 != 0, true, HB, DQ, RS, AS>(
+      x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale, act_scale);
 }
 
 hipError_t launch_wn_a16_mfma(int bits, int m, const void* x, const void* packed, int n, int k, void* y,
@@ -638,6 +674,18 @@ hipError_t launch_w4a16_mfma_dq(int m, const void* x, const void* packed, int n,
   if (row_scale != nullptr && partial == nullptr)
     return launch_wn_mfma_t<0, true, true>(m, x, packed, n, k, y, y_f32, partial, split, stream, row_scale);
   return launch_wn_mfma_t<0, true>(m, x, packed, n, k, y, y_f32, partial, split, stream);
+}
+
+// W4A8 with one activation scale per group of 32, 5..64 rows: x holds the
+// int8 codes as exact bf16 integers and act_scale their scales group-major
+// (64 per group); both packed layouts, the W4A16 forms and bucket choice.
+hipError_t launch_w4a8g_mfma(bool dq, int m, const void* xq, const float* act_scale, const void* packed, int n,
+                             int k, void* y, int y_f32, float* partial, int split, hipStream_t stream) {
+  if (dq)
+    return launch_wn_mfma_t<0, true, false, true>(m, xq, packed, n, k, y, y_f32, partial, split, stream, nullptr,
+                                                  act_scale);
+  return launch_wn_mfma_t<0, false, false, true>(m, xq, packed, n, k, y, y_f32, partial, split, stream, nullptr,
+                                                 act_scale);
 }
 
 }  // namespace qg

@@ -870,6 +870,44 @@ __global__ __launch_bounds__(256) void w4a8_actquant_bf16_kernel(const uint16_t*
   reinterpret_cast<u32x4_t*>(xq + (size_t)row * k)[i] = u32x4_t{o[0], o[1], o[2], o[3]};
 }
 
+// One activation scale per group of 32 at 5..64 rows: the quantize pass of
+// the M <= 4 per-group kernels, written out once for the matrix-core kernels.
+// A workgroup takes 2048 k of one row, a thread 8 k, a lane quad one group:
+// a = max|x| over the group (the NaN-keeping max, DPP over the quad), inv and
+// sx as everywhere (span_scale), xq = clamp(rint(x * inv), -127, 127) stored
+// as exact bf16 integers in xq [m, k], and sx of row r, group g stored
+// group-major at sxg[64 g + r].
+__global__ __launch_bounds__(256) void w4a8_actquant_g32_bf16_kernel(const uint16_t* __restrict__ x, int k,
+                                                                      uint16_t* __restrict__ xq,
+                                                                      float* __restrict__ sxg) {
+  const int row = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;     // 16-byte piece of the row
+  const int k8 = k >> 3;                             // a multiple of 32: quads stay whole
+  const bool live = i < k8;
+  const u32x4_t v = live ? reinterpret_cast<const u32x4_t*>(x + (size_t)row * k)[i] : u32x4_t{0u, 0u, 0u, 0u};
+  float a = absmax8(v, 0.0f);
+  a = nmax(a, dpp_fa<0xB1>(a));
+  a = nmax(a, dpp_fa<0x4E>(a));
+  float inv, sxv;
+  span_scale(finite_or_nan(a), inv, sxv);
+  if (!live) return;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t h[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float f = bf16_to_f32(e ? (w[j] >> 16) : (w[j] & 0xffffu));
+      const float t = __builtin_amdgcn_fmed3f(rintf(f * inv), -127.0f, 127.0f);
+      h[e] = __float_as_uint(t) >> 16;
+    }
+    o[j] = h[0] | (h[1] << 16);
+  }
+  reinterpret_cast<u32x4_t*>(xq + (size_t)row * k)[i] = u32x4_t{o[0], o[1], o[2], o[3]};
+  if ((i & 3) == 0) sxg[(size_t)(i >> 2) * 64 + row] = sxv;
+}
+
 // Pass 3: y[r, c] = sx[r] * sum over s (ascending) of partial[s, r, c]; a
 // workgroup per (256 columns, row).
 __global__ __launch_bounds__(256) void w4a8_rowscale_reduce_kernel(const float* __restrict__ partial,
@@ -894,6 +932,14 @@ hipError_t launch_w4a8_actquant_bf16(int m, const void* x, int k, void* xq, floa
   const int chunks = ((k >> 3) + 255) / 256;
   hipLaunchKernelGGL(w4a8_actquant_bf16_kernel, dim3(chunks, m), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(x), k, static_cast<uint16_t*>(xq), sx);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a8_actquant_g32_bf16(int m, const void* x, int k, void* xq, float* sxg,
+                                         hipStream_t stream) {
+  const int chunks = ((k >> 3) + 255) / 256;
+  hipLaunchKernelGGL(w4a8_actquant_g32_bf16_kernel, dim3(chunks, m), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(x), k, static_cast<uint16_t*>(xq), sxg);
   return hipGetLastError();
 }
 

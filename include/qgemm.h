@@ -128,9 +128,10 @@ int32_t qg_default_split_k_intn(int64_t m, int64_t n, int64_t k);
  * the largest need of the defaults is assumed (qg_default_split_k and
  * qg_default_split_k_intn at m rows, and for m > 4 also qg_default_split_k
  * at 4 rows, the per-group W4A8 slices), so one workspace serves every
- * entry point's default.  For m > 4 it also holds what qgemm_w4a8 and
- * qgemm_w4a8_dq need there: m * k * 2 bytes of quantized activations, 256
- * bytes of row scales and split * m * n * 4 bytes of partial sums (at split 1
+ * entry point's default.  For m > 4 it also holds what the W4A8 entry
+ * points need there: m * k * 2 bytes of quantized activations, max(256,
+ * 8 * k) bytes of activation scales (per row, or per group of 32 as
+ * k/32 x 64 floats) and split * m * n * 4 bytes of partial sums (at split 1
  * too).  Negative qg_status on bad arguments. */
 int64_t qg_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k);
 
@@ -322,11 +323,12 @@ int32_t qgemm_w4a8(const void *x_bf16, int64_t m, int64_t k, const void *packed,
  *   xq = clamp(rint(x * inv), -127, 127); a == 0 or 127/a overflowing gives a
  *   zero group, a NaN or an infinity in the group a NaN row;
  *   y[m,n] = sum_g sx[m,g] * s[n,g] * sum_{k in g} xq[m,k] * (q[n,k] - zp[n,g]).
- * Arguments, buffers, workspace and errors as qgemm_w4a8, except that
- * m = 5..64 runs as consecutive slices of at most 4 rows on the m <= 4
- * kernels, each slice streaming the weight again (ceil(m/4) times the bytes
- * of one call; split_k applies per slice, slices run in stream order and
- * share the workspace). */
+ * Arguments, buffers, workspace and errors as qgemm_w4a8.  For m = 5..64 the
+ * call quantizes x once into the workspace (xq as exact bf16 integers, the
+ * group scales group-major) and runs the matrix-core kernel of qgemm_w4a16
+ * on xq, multiplying each group's exact integer dot by s[n,g] * sx[m,g]: one
+ * pass over the weight; the workspace is required there at any split
+ * (qg_workspace_bytes). */
 int32_t qgemm_w4a8_g32(const void *x_bf16, int64_t m, int64_t k, const void *packed,
                        int64_t packed_bytes, int64_t n, void *y, int32_t y_dtype,
                        int32_t split_k, void *ws, int64_t ws_bytes, void *stream);

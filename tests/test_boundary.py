@@ -182,17 +182,19 @@ def test_qgemm_w4a16_and_w4a8_validate_before_launching(lib, args, expect):
 
 
 def test_w4a8_m_range(lib):
-    # W4A8 takes every bucket up to 64 rows (M > 4 as slices of 4 rows)
+    # W4A8 takes every bucket up to 64 rows (M > 4 on the matrix cores)
     assert lib.qgemm_w4a8(A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
     assert lib.qgemm_w4a8_g32(A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
     assert lib.qgemm_w4a16_dq(A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
     assert lib.qgemm_w4a8_dq(A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
     assert lib.qgemm_w4a8_g32_dq(A, 65, 256, A, 1 << 20, 64, A, 0, 0, None, 0, None) == E_M
-    # per-row scales above 4 rows need the workspace at any split (quantized x,
-    # row scales, partials): refused before any launch when it is missing or short
+    # above 4 rows every W4A8 entry point needs the workspace at any split
+    # (quantized x, its scales -- per row 256 bytes, per group of 32 k/32 x 64
+    # floats -- and partials): refused before any launch when missing or short
     need = lib.qg_workspace_bytes(5, 64, 256, 1)
-    assert need == 5 * 256 * 2 + 256 + 5 * 64 * 4
-    for f in (lib.qgemm_w4a8, lib.qgemm_w4a8_dq):
+    assert need == 5 * 256 * 2 + max(256, 256 // 32 * 64 * 4) + 5 * 64 * 4
+    assert lib.qg_workspace_bytes(64, 64, 6656, 2) == 64 * 6656 * 2 + 6656 // 32 * 64 * 4 + 2 * 64 * 64 * 4
+    for f in (lib.qgemm_w4a8, lib.qgemm_w4a8_dq, lib.qgemm_w4a8_g32, lib.qgemm_w4a8_g32_dq):
         assert f(A, 5, 256, A, 1 << 20, 64, A, 0, 1, None, 0, None) == E_NULL
         assert f(A, 5, 256, A, 1 << 20, 64, A, 0, 1, A, need - 1, None) == E_BUF
     assert lib.qgemm_w4a8_dq(A, 1, 256, A, 9087, 64, A, 0, 0, None, 0, None) == E_BUF

@@ -1,15 +1,16 @@
 """GPU parity: W4A8 at every decode bucket above 4 rows.
 
 The pages' buckets run to 64 rows (executorch test_int4_quantized_gemm.py,
-SUPPORTED_BUCKETS).  At M = 5..64 the W4A8 entry points quantize x once and
-run the bf16 matrix-core kernel on the exact int8 values (per-row scales), or
-run consecutive slices of at most 4 rows on the M <= 4 kernels (per-group
-scales).  Checked on every W4A8 entry point and both packed layouts against
-the matching W4A8 oracle with the W4A16 bounds: ragged M (5, 33), whole
-slices (8, 16, 64), ragged N, one and two splits and the default, both output
-dtypes, every split on the per-row path; the pages' W4A8 layer shapes at
-M = 16 and 64 with the precision class against the W4A16 oracle (gaussian
-activations); slices bit-equal to separate calls; bit-equal graph replay.
+SUPPORTED_BUCKETS).  At M = 5..64 the W4A8 entry points quantize x once into
+the workspace and run the bf16 matrix-core kernel on the exact int8 values,
+one pass over the weight: per-row scales are applied after the sum over K,
+per-group scales to each group's integer dot.  Checked on every W4A8 entry
+point and both packed layouts against the matching W4A8 oracle with the
+W4A16 bounds: ragged M (5, 33), M = 8, 16, 64, ragged N, one and two splits
+and the default, both output dtypes, every split on both paths; the pages'
+W4A8 layer shapes at M = 16 and 64 with the precision class against the W4A16
+oracle (gaussian activations); rows independent of the rows padded next to
+them; bit-equal graph replay.
 """
 from __future__ import annotations
 
@@ -94,22 +95,24 @@ def test_buckets_16_and_64_layer_shapes(dev, entry, n, k):
         assert_w4a8_class(y, ref16, label + " vs W4A16 oracle")
 
 
-def test_slices_equal_separate_calls(dev):
-    """Per-group scales at M > 4 run as 4-row slices: each slice of an M = 13
-    call is bit-identical to a call on those rows alone (same kernels, same
-    split)."""
+def test_rows_are_independent_of_their_padding(dev):
+    """An M = 13 call runs the 16-row kernel with 3 padded rows: its rows are
+    bit-identical to the first 13 rows of an M = 16 call whose last 3 rows
+    hold other activations (same kernel and split), on every W4A8 entry
+    point."""
     n, k = 1000, 2048
-    w, _ = _weight(n, k, 17, False)
-    packed = _packed(w, False, dev)
-    x = si.activation(13, k, 18).to(dev)
-    for fn in (qg.qgemm_w4a8_g32, qg.qgemm_w4a8_g32_dq):
-        if fn is qg.qgemm_w4a8_g32_dq:
-            packed = _packed(w, True, dev)
-        for split in (1, 2):
-            y = fn(x, packed, n, split_k=split, out_dtype=torch.float32)
-            for r0 in range(0, 13, 4):
-                part = fn(x[r0:r0 + 4].contiguous(), packed, n, split_k=split, out_dtype=torch.float32)
-                assert torch.equal(y[r0:r0 + 4], part), (fn.__name__, split, r0)
+    x16 = si.activation(16, k, 18)
+    x16[13:] = si.activation(3, k, 19) * 40       # different scales in the extra rows
+    x13 = x16[:13].contiguous()
+    for dq in (False, True):
+        w, _ = _weight(n, k, 17, dq)
+        packed = _packed(w, dq, dev)
+        fns = (qg.qgemm_w4a8_dq, qg.qgemm_w4a8_g32_dq) if dq else (qg.qgemm_w4a8, qg.qgemm_w4a8_g32)
+        for fn in fns:
+            for split in (1, 2):
+                y13 = fn(x13.to(dev), packed, n, split_k=split, out_dtype=torch.float32)
+                y16 = fn(x16.to(dev), packed, n, split_k=split, out_dtype=torch.float32)
+                assert torch.equal(y13, y16[:13]), (fn.__name__, split)
 
 
 def test_graph_replay_bit_identical_m16(dev):
@@ -134,18 +137,22 @@ def test_graph_replay_bit_identical_m16(dev):
                 assert torch.equal(out, eager), (fn.__name__, split)
 
 
-def test_per_row_m_above_4_uses_every_split(dev):
-    """The per-row path at M > 4 (quantized rows, matrix-core kernel, row
-    scale after the split sum) at every legal split."""
+def test_m_above_4_uses_every_split(dev):
+    """Both paths at M > 4 (quantized rows on the matrix-core kernels; per-row
+    scale after the split sum, per-group scales inside it) at every legal
+    split, both forms of the kernel (5 and 16 rows: registers; 24 and 64:
+    LDS-staged)."""
     n, k = 520, 2048
     for dq in (False, True):
         w, parts = _weight(n, k, 21, dq)
         packed = _packed(w, dq, dev)
-        fn, ref_fn = (qg.qgemm_w4a8_dq, oracle.qgemm_w4a8_dq) if dq else (qg.qgemm_w4a8, oracle.qgemm_w4a8)
-        for m in (5, 24):
-            x = si.activation(m, k, 40 + m)
-            ref = ref_fn(si.bf16_bits(x), *parts)
-            for split in si.SPLITS:
-                label = f"{fn.__name__} M={m} split={split}"
-                print(label, flush=True)
-                assert_w16(fn(x.to(dev), packed, n, split_k=split, out_dtype=torch.float32), ref, label)
+        pairs = ((qg.qgemm_w4a8_dq, oracle.qgemm_w4a8_dq), (qg.qgemm_w4a8_g32_dq, oracle.qgemm_w4a8_g32_dq)) if dq \
+            else ((qg.qgemm_w4a8, oracle.qgemm_w4a8), (qg.qgemm_w4a8_g32, oracle.qgemm_w4a8_g32))
+        for fn, ref_fn in pairs:
+            for m in (5, 16, 24, 64):
+                x = si.activation(m, k, 40 + m)
+                ref = ref_fn(si.bf16_bits(x), *parts)
+                for split in si.SPLITS:
+                    label = f"{fn.__name__} M={m} split={split}"
+                    print(label, flush=True)
+                    assert_w16(fn(x.to(dev), packed, n, split_k=split, out_dtype=torch.float32), ref, label)

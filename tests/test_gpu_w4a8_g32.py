@@ -117,12 +117,12 @@ def test_g32_graph_replay_is_bit_identical(dev):
 @pytest.mark.parametrize("n,k", si.MODEL_SHAPES + si.SMALL_SHAPES)
 def test_g32_precision_class_against_dense(dev, n, k):
     """Int4QuantizedGemmPrecisionTest: Gaussian and outlier activations, W4A8
-    buckets 1 and 4, the weight's dense (unquantized) product as reference."""
+    buckets 1 to 4, the weight's dense (unquantized) product as reference."""
     shape_index = (si.MODEL_SHAPES + si.SMALL_SHAPES).index((n, k))
     w, codes, scales, zeros = _layer(n, k, 1200 + shape_index)
     packed = qg.quantize_int4_g32(w.to(dev))
     dense = oracle.bf16_to_float64(si.bf16_bits(w))
-    for m in (1, 4):
+    for m in si.DECODE_M:
         for outl in (False, True):
             x = si.activation(m, k, 9100 + shape_index * 31 + m)
             if outl:
@@ -146,7 +146,7 @@ def test_g32_logits_top1_and_cosine(dev):
     is not tiny, and equals W4A16's wherever W4A16's margin exceeds the row's
     W4A8 error."""
     n, k = 32768, 6656
-    w, codes, scales, zeros = _layer(n, k, 4242)
+    w, codes, scales, zeros = _logits_layer()
     packed = qg.quantize_int4_g32(w.to(dev))
     threads = oracle.hardware_threads()
     for m in si.DECODE_M:
@@ -164,6 +164,39 @@ def test_g32_logits_top1_and_cosine(dev):
             gap16 = np.diff(np.sort(a16[r])[-2:])[0]
             if gap16 > 2 * np.abs(a8[r] - a16[r]).max():
                 assert a8[r].argmax() == a16[r].argmax(), (m, r, gap16)
+
+
+# The oracle of this arithmetic on the same rows (32768 x 6656, seeds 4300 +
+# bucket, outlier activations): bucket 3's second row has a W4A16 top-1 /
+# top-2 gap of 0.33, the W4A8 oracle's argmax differs from W4A16's there (and
+# W4A16's differs from the dense product's), so that bucket agrees on 2 of 3
+# rows in the arithmetic itself; buckets 1, 2 and 4 agree on every row.
+_LOGITS_BUCKETS = [1, 2, pytest.param(3, marks=pytest.mark.xfail(
+    reason="the W4A8 oracle itself agrees with W4A16 on 2 of bucket 3's 3 rows (top-2 gap 0.33)",
+    strict=False)), 4]
+
+
+@pytest.mark.parametrize("m", _LOGITS_BUCKETS)
+def test_g32_logits_top1_and_cosine_literal(dev, m):
+    """Int4QuantizedGemmPrecisionTest.test_logits_top1_and_cosine as the pages
+    state it: on 32768 x 6656 with outlier activations, per bucket, the W4A8
+    logits' argmax agrees with the W4A16 logits' on at least 99 % of the rows
+    (every row, at 1..4 rows) and their cosine is at least 0.999."""
+    n, k = 32768, 6656
+    w, codes, scales, zeros = _logits_layer()
+    packed = qg.quantize_int4_g32(w.to(dev))
+    x = _outliers(si.activation(m, k, 4300 + m))
+    a16 = oracle.qgemm_w4a16(si.bf16_bits(x), codes, scales, zeros, threads=oracle.hardware_threads())
+    a8 = qg.qgemm_w4a8_g32(x.to(dev), packed, n, out_dtype=torch.float32).cpu().double().numpy()
+    cos = (a8 * a16).sum(1) / (np.linalg.norm(a8, axis=1) * np.linalg.norm(a16, axis=1))
+    assert cos.min() >= 0.999, cos
+    agree = float((a8.argmax(1) == a16.argmax(1)).mean())
+    assert agree >= 0.99, f"bucket {m}: argmax agreement {agree:.3f}"
+
+
+@functools.lru_cache(maxsize=1)
+def _logits_layer():
+    return _layer(32768, 6656, 4242)
 
 
 def test_g32_rejects_m_above_64(dev):
