@@ -12,7 +12,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libqgemm.so")
+# QGEMM_LIB names another build of the same library (for comparing builds).
+LIB_PATH = os.environ.get("QGEMM_LIB") or os.path.join(_PKG, "libqgemm.so")
 
 QG_BF16 = 0
 QG_F32 = 1

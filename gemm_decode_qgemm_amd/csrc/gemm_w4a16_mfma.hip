@@ -352,9 +352,9 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
 // into the other LDS buffer by global_load_lds_dwordx4 (no VGPRs) and its
 // codes and metadata are loaded into the other register set; one barrier per
 // tile.  LDS layout: 16-byte piece c of x row r (k = 8c .. 8c+8 of the tile)
-// sits at piece index 32 r + (c ^ (r & 7)), so the A-operand read of lanes
-// (i, a) = (lane % 16, lane / 16) -- row 16 mt + i, piece 4 g + a -- hits 8
-// distinct bank quads in any 8 consecutive lanes; the swizzle is applied on
+// sits at piece index 32 r + (c ^ (r & 15)), so the A-operand read of lanes
+// (i, a) = (lane % 16, lane / 16) -- row 16 mt + i, piece 4 g + a -- hits 16
+// distinct bank quads in any 16 consecutive lanes; the swizzle is applied on
 // the global side of the copy, whose LDS side is 64 consecutive pieces.
 template <int HB>
 struct Mfma2W {
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
 #pragma unroll
     for (int u = wv; u < MR / 2; u += 4 * MG) {
       const int r = 2 * u + (lane >> 5);
-      const int c = (lane & 31) ^ (r & 7);
+      const int c = (lane & 31) ^ (r & 15);
       const int src = r < m ? r : m - 1;
       __builtin_amdgcn_global_load_lds(x + (size_t)src * k + (size_t)kt * 256 + 8 * c,
                                        (__attribute__((address_space(3))) void*)(xs[buf] + 1024 * u),
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
       for (int mt = 0; mt < MT; ++mt) {
         const int r = 16 * (mg * MT + mt) + i;
         av[mt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
-                                                  xb + 16 * (32 * r + ((4 * g + a) ^ (r & 7)))));
+                                                  xb + 16 * (32 * r + ((4 * g + a) ^ (r & 15)))));
         d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
       }
 #pragma unroll
