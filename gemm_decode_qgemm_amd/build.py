@@ -25,7 +25,8 @@ LIB = os.path.join(PKG, "libqgemm.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["api.hip", "quantize.hip", "gemv_w4a16.hip", "gemv_w8a16.hip", "gemv_w4a8.hip",
-           "gemm_w4a16_mfma.hip", "gemv_w4a16_mx4.hip", "stream_read.hip"]
+           "gemm_w4a16_mfma.hip", "gemv_w4a16_mx4.hip", "stream_read.hip",
+           "gemm_w8a16_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -43,7 +44,8 @@ FLAGS = [
 # element before the fp32 epilogue of every group).
 SOURCE_FLAGS = {"gemm_w4a16_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                 "gemv_w4a16_mx4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-                "gemv_w4a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+                "gemv_w4a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "gemm_w8a16_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, extra: list[str], objdir: str) -> str:

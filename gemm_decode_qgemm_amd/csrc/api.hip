@@ -73,6 +73,8 @@ hipError_t launch_w4a8_gemv_mx4(int m, bool group_scales, const void* x, const v
                                 hipStream_t stream);
 hipError_t launch_w8a16_gemv(int m, const void* x, const int8_t* w, const void* scale, int n,
                              int k, void* y, int y_f32, hipStream_t stream);
+hipError_t launch_w8a16_mfma(int m, const void* x, const int8_t* w, const void* scale, int n, int k, void* y,
+                             int y_f32, hipStream_t stream);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int blocks,
                               hipStream_t stream);
 }  // namespace qg
@@ -430,12 +432,16 @@ int32_t qgemm_w8a16(const void* x_bf16, int64_t m, int64_t k, const int8_t* w,
   int32_t st = check_mnk(m, n, k);
   if (st != QG_OK) return st;
   if (y_dtype != QG_BF16 && y_dtype != QG_F32) return QG_E_DTYPE;
-  if (m > 4) return QG_E_M_RANGE;
-  if (qg::w8a16_chunks_per_wave((int)k) < 0) return QG_E_SHAPE;   // K above 65536
+  // the M <= 4 GEMV holds a lane's x in registers: K up to 65536
+  if (m <= 4 && qg::w8a16_chunks_per_wave((int)k) < 0) return QG_E_SHAPE;
   if (!aligned16(x_bf16) || !aligned16(w) || !aligned16(y) || ((uintptr_t)scale_bf16 & 1u))
     return QG_E_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m > 4)   // 5..64 rows: the matrix cores
+    return hip_status(qg::launch_w8a16_mfma((int)m, x_bf16, w, scale_bf16, (int)n, (int)k, y,
+                                            y_dtype == QG_F32, s));
   return hip_status(qg::launch_w8a16_gemv((int)m, x_bf16, w, scale_bf16, (int)n, (int)k, y,
-                                          y_dtype == QG_F32, static_cast<hipStream_t>(stream)));
+                                          y_dtype == QG_F32, s));
 }
 
 // One launch sequence of the M <= 4 W4A8 kernels (plus the split-K pass).

@@ -286,8 +286,11 @@ int32_t qgemm_wn_a16(const void *x_bf16, int64_t m, int64_t k, int32_t bits, con
  * scale[n], fp32 accumulation, the int8 -> float convert fused into the dot
  * product.  W int8 [n, k] row-major as given (no repacking, 16-byte aligned),
  * scale bf16 [n] (2-byte aligned).
- *   x_bf16 in: bf16 [m, k], 1 <= m <= 4 in this version (QG_E_M_RANGE above);
- *   k <= 65536 (QG_E_SHAPE above);  y out: [m, n] bf16 or fp32.
+ *   x_bf16 in: bf16 [m, k], 1 <= m <= 64;  y out: [m, n] bf16 or fp32.
+ * M <= 4 runs the VALU GEMV (k <= 65536, QG_E_SHAPE above); 5 <= M <= 64 the
+ * matrix cores (the [P3] question of a fused kernel above batch size 1):
+ * bf16 products of x with the exact w + 128, accumulated over all of K, then
+ * y = s * (sum - 128 * sum_k x).
  * Errors: QG_E_NULL, QG_E_SHAPE, QG_E_K_MULTIPLE, QG_E_M_RANGE, QG_E_ALIGN,
  * QG_E_DTYPE, QG_E_HIP. */
 int32_t qgemm_w8a16(const void *x_bf16, int64_t m, int64_t k, const int8_t *w,

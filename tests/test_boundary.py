@@ -207,7 +207,8 @@ def test_w4a8_m_range(lib):
     ((A, 1, 256, None, A, 64, A, 0, None), E_NULL),
     ((A, 1, 256, A, None, 64, A, 0, None), E_NULL),
     ((A, 1, 300, A, A, 64, A, 0, None), E_K),
-    ((A, 5, 256, A, A, 64, A, 0, None), E_M),
+    ((A, 65, 256, A, A, 64, A, 0, None), E_M),
+    ((A, 5, 65536 + 256, A, A, 64, A, 7, None), E_DTYPE),      # M > 4 takes any K; dtype still checked
     ((A, 1, 256, A, A, 64, A, 7, None), E_DTYPE),
     ((A, 1, 256, A, A, 0, A, 0, None), E_SHAPE),
     ((A, 1, 65536 + 256, A, A, 64, A, 0, None), E_SHAPE),       # K above the VGPR-resident limit

@@ -236,7 +236,7 @@ def test_w8a16_integer_activations_one_rounding(dev, n):
     w = torch.randint(-127, 128, (n, K), dtype=torch.int8)
     scale = torch.randn(n, dtype=torch.bfloat16)
     wd, sd = w.to(dev), scale.to(dev)
-    for m in (1, 2, 3, 4):
+    for m in BUCKETS:
         x = _int_x(m, 15, 1500 + m)     # |partial sums of x * (w + 128)| < 2^24
         ref = oracle.qgemm_w8a16(si.bf16_bits(x), w.numpy(), si.bf16_bits(scale),
                                  threads=oracle.hardware_threads())

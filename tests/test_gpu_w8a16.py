@@ -1,5 +1,6 @@
-"""GPU parity: INT8 row-wise quantizer (bit-exact) and W8A16 GEMV (tolerance)
-against the CPU oracle, through the C ABI.
+"""GPU parity: INT8 row-wise quantizer (bit-exact) and W8A16 (tolerance: the
+GEMV at 1..4 rows, the matrix cores at 5..64) against the CPU oracle, through
+the C ABI.
 
 The layer is gpt-fast issue #114's WeightOnlyInt8Linear: int8 [out, in]
 weight, one bf16 scale per output row, y = (x . W^T) * scale; its benchmark
@@ -70,7 +71,7 @@ def test_quantize_int8_hand_worked_rows(dev):
 # ------------------------------------------------------------------ W8A16 GEMV
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 16, 33, 64])
 def test_w8a16_gpt_fast_config(dev, m):
     """N = K = 8192, int8 uniform in [-127, 127], bf16 randn scales and x."""
     w, s, x = si.int8_layer(m=m)
@@ -82,7 +83,7 @@ def test_w8a16_gpt_fast_config(dev, m):
 
 @pytest.mark.parametrize("n,k", [(1, 256), (17, 768), (257, 1280), (600, 4096), (333, 6656),
                                  (64, 19968), (48, 65536)])
-@pytest.mark.parametrize("m", [1, 3, 4])
+@pytest.mark.parametrize("m", [1, 3, 4, 5, 17, 48, 64])
 def test_w8a16_shapes_and_tails(dev, n, k, m):
     w, s, x = si.int8_layer(n=n, k=k, m=m, seed=n + k + m)
     ref = _ref(x, w, s)
@@ -100,8 +101,19 @@ def test_w8a16_quantized_weight_round_trip(dev):
     assert_w16(qg.qgemm_w8a16(x.to(dev), q, s, out_dtype=torch.float32), ref, "round trip")
 
 
+def test_w8a16_every_bucket_ragged_n(dev):
+    """Every M from 1 to 64 (GEMV to 4, the matrix cores above, rows masked
+    to 16-row tiles) on N = 257 (a 1-row tail past the 32-row workgroups)."""
+    n, k = 257, 1024
+    w, s, _ = si.int8_layer(n=n, k=k, m=1, seed=5)
+    wd, sd = w.to(dev), s.to(dev)
+    for m in range(1, 65):
+        x = si.activation(m, k, 300 + m)
+        assert_w16(qg.qgemm_w8a16(x.to(dev), wd, sd, out_dtype=torch.float32), _ref(x, w, s), f"M={m}")
+
+
 def test_w8a16_argument_errors(dev):
-    w, s, x = si.int8_layer(n=64, k=512, m=5, seed=1)
+    w, s, x = si.int8_layer(n=64, k=512, m=65, seed=1)
     with pytest.raises(qg.QGemmError) as e:
         qg.qgemm_w8a16(x.to(dev), w.to(dev), s.to(dev))
     assert e.value.status == -4             # QG_E_M_RANGE
@@ -111,8 +123,9 @@ def test_w8a16_argument_errors(dev):
     assert e.value.status == -3             # QG_E_K_MULTIPLE
 
 
-def test_w8a16_repeat_and_graph_replay_are_bit_identical(dev):
-    w, s, x = si.int8_layer(n=4096, k=8192, m=1, seed=9)
+@pytest.mark.parametrize("m", [1, 16, 64])
+def test_w8a16_repeat_and_graph_replay_are_bit_identical(dev, m):
+    w, s, x = si.int8_layer(n=4096, k=8192, m=m, seed=9)
     w, s, x = w.to(dev), s.to(dev), x.to(dev)
     eager = qg.qgemm_w8a16(x, w, s)
     assert torch.equal(eager, qg.qgemm_w8a16(x, w, s))
