@@ -19,12 +19,13 @@
 // the matrix unit from the first k to the last.
 //
 // Mapping (gfx950, wave64): a workgroup owns 32 weight rows (2 n-tiles of
-// 16) and all M rows (MT m-tiles of 16); its KW waves take the 128-k blocks of
-// K round robin.  In a block, lane (i, a) = (lane % 16, lane / 16) loads 32
-// contiguous weight bytes of row 16 t + i (k = 128 b + 32 a .. + 32) and the
-// same 32 k of x row 16 mt + i; step j of 4 uses k = 128 b + 32 a + 8 j .. + 8
-// in lane group a, the same for A and B, so the 4 steps cover the block's 128 k
-// once.  The next block's weights are loaded while the current one computes.
+// 16) and all M rows (MT m-tiles of 16); its KW waves take the BK-k blocks of
+// K round robin.  In a block, lane (i, a) = (lane % 16, lane / 16) loads BK/4
+// contiguous weight bytes of row 16 t + i (k = BK b + (BK/4) a .. + BK/4) and
+// the same k of x row 16 mt + i; step j of BK/32 uses k = BK b + (BK/4) a +
+// 8 j .. + 8 in lane group a, the same for A and B, so the steps cover the
+// block's k once.  The next block's weights and activations are loaded while
+// the current one computes.
 // The KW partial sums meet in LDS and are added in wave order.
 #include "qg_common.h"
 
@@ -50,17 +51,28 @@ __device__ __forceinline__ bf16x8_t w8_operand(uint32_t d0, uint32_t d1, uint32_
   return __builtin_bit_cast(bf16x8_t, u32x4_t{b[0], b[1], b[2], b[3]});
 }
 
-template <int MT>
+// One block of BK k: a lane's weight bytes (BK / 4 contiguous k of each of
+// the 2 rows 16 t + i it owns) and activations (the same k of its MT rows).
+template <int MT, int BK, bool PX>
+struct W8Blk {
+  u32x4_t w[kW8NT][BK / 64];                     // 16 bytes = 16 k each
+  u32x4_t xa[PX ? MT : 1][PX ? BK / 32 : 1];     // 8 bf16 = 8 k each (PX: loaded ahead)
+};
+
+// PX: the activations are loaded a block ahead with the weights (registers
+// permitting); otherwise at the start of their block.
+template <int MT, int BK, bool PX>
 __global__ __launch_bounds__(kW8KW * 64) void w8a16_mfma_kernel(
     const uint16_t* __restrict__ x, int m, const int8_t* __restrict__ w,
     const uint16_t* __restrict__ scale, int n, int k, void* __restrict__ y, int y_f32) {
   constexpr int NACC = kW8NT * MT + MT;            // per wave: the products, then X
+  constexpr int KL = BK / 4;                       // k per lane group and block
   __shared__ f32x4_t red[kW8KW][NACC][64];
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, a = lane >> 4;
   const int wave = wave_id_uniform();
   const int row0 = blockIdx.x * (16 * kW8NT);
-  const int nblk = k >> 7;
+  const int nblk = k / BK;
   const uint32_t sel_hi = __builtin_amdgcn_readfirstlane(0x07060302u);   // upper halves of (S1, S0)
   uint32_t one2 = 0x3f803f80u;           // bf16 pair (1, 1), kept in a VGPR
   asm volatile("" : "+v"(one2));
@@ -70,10 +82,10 @@ __global__ __launch_bounds__(kW8KW * 64) void w8a16_mfma_kernel(
   // results are never stored.
   const int8_t* wr[kW8NT];
 #pragma unroll
-  for (int t = 0; t < kW8NT; ++t) wr[t] = w + (size_t)min(row0 + 16 * t + i, n - 1) * k + 32 * a;
+  for (int t = 0; t < kW8NT; ++t) wr[t] = w + (size_t)min(row0 + 16 * t + i, n - 1) * k + KL * a;
   const uint16_t* xr[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) xr[mt] = x + (size_t)min(16 * mt + i, m - 1) * k + 32 * a;
+  for (int mt = 0; mt < MT; ++mt) xr[mt] = x + (size_t)min(16 * mt + i, m - 1) * k + KL * a;
 
   f32x4_t acc[kW8NT][MT], xs[MT];
 #pragma unroll
@@ -83,47 +95,61 @@ __global__ __launch_bounds__(kW8KW * 64) void w8a16_mfma_kernel(
     for (int t = 0; t < kW8NT; ++t) acc[t][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  auto load_w = [&](u32x4_t (&wv)[kW8NT][2], int b) {
+  auto load = [&](W8Blk<MT, BK, PX>& u, int b) {
 #pragma unroll
-    for (int t = 0; t < kW8NT; ++t) {
-      const u32x4_t* p = reinterpret_cast<const u32x4_t*>(wr[t] + 128 * (size_t)b);
-      wv[t][0] = load_stream<true>(p);
-      wv[t][1] = load_stream<true>(p + 1);
-    }
-  };
-  auto compute = [&](const u32x4_t (&wv)[kW8NT][2], int b) {
+    for (int t = 0; t < kW8NT; ++t)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8_t av[MT];
+      for (int q = 0; q < BK / 64; ++q)
+        u.w[t][q] = load_stream<true>(reinterpret_cast<const u32x4_t*>(wr[t] + (size_t)b * BK) + q);
+    if constexpr (PX) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        av[mt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xr[mt] + 128 * (size_t)b + 8 * j));
+#pragma unroll
+        for (int j = 0; j < BK / 32; ++j)
+          u.xa[mt][j] = *reinterpret_cast<const u32x4_t*>(xr[mt] + (size_t)b * BK + 8 * j);
+    }
+  };
+  // step j: k = BK b + KL a + 8 j .. + 8 in lane group a, for A and B alike
+  auto compute = [&](const W8Blk<MT, BK, PX>& u, int b) {
+    u32x4_t xl[PX ? 1 : MT][PX ? 1 : BK / 32];
+    if constexpr (!PX) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < BK / 32; ++j)
+          xl[mt][j] = *reinterpret_cast<const u32x4_t*>(xr[mt] + (size_t)b * BK + 8 * j);
+    }
+    auto xa = [&](int mt, int j) { return __builtin_bit_cast(bf16x8_t, PX ? u.xa[mt][j] : xl[mt][j]); };
+#pragma unroll
+    for (int j = 0; j < BK / 32; ++j) {
 #pragma unroll
       for (int t = 0; t < kW8NT; ++t) {
-        const u32x4_t& q = wv[t][j >> 1];
+        const u32x4_t& q = u.w[t][j >> 1];
         const bf16x8_t bv = (j & 1) ? w8_operand(q.z, q.w, sel_hi) : w8_operand(q.x, q.y, sel_hi);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv, acc[t][mt], 0, 0, 0);
+        for (int mt = 0; mt < MT; ++mt)
+          acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa(mt, j), bv, acc[t][mt], 0, 0, 0);
       }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) xs[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], ones, xs[mt], 0, 0, 0);
+      for (int mt = 0; mt < MT; ++mt)
+        xs[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa(mt, j), ones, xs[mt], 0, 0, 0);
     }
   };
 
-  // Two register sets used in turn: the next block's weights are loaded
-  // before the current block computes (the loop conditions are uniform).
+  // Two register sets used in turn: the next block's weights and activations
+  // are loaded before the current block computes (uniform loop conditions).
   int b = wave;
   if (b < nblk) {
-    u32x4_t wa[kW8NT][2], wb[kW8NT][2];
-    load_w(wa, b);
+    W8Blk<MT, BK, PX> ua, ub;
+    load(ua, b);
     while (true) {
-      if (b + kW8KW >= nblk) { compute(wa, b); break; }
-      load_w(wb, b + kW8KW);
-      compute(wa, b);
+      if (b + kW8KW >= nblk) { compute(ua, b); break; }
+      load(ub, b + kW8KW);
+      compute(ua, b);
       b += kW8KW;
-      if (b + kW8KW >= nblk) { compute(wb, b); break; }
-      load_w(wa, b + kW8KW);
-      compute(wb, b);
+      if (b + kW8KW >= nblk) { compute(ub, b); break; }
+      load(ua, b + kW8KW);
+      compute(ub, b);
       b += kW8KW;
     }
   }
@@ -162,23 +188,27 @@ __global__ __launch_bounds__(kW8KW * 64) void w8a16_mfma_kernel(
   }
 }
 
-template <int MT>
+template <int MT, int BK, bool PX>
 static hipError_t launch_w8_mfma_t(const void* x, int m, const int8_t* w, const void* scale, int n, int k,
                                    void* y, int y_f32, hipStream_t stream) {
-  hipLaunchKernelGGL((w8a16_mfma_kernel<MT>), dim3((n + 16 * kW8NT - 1) / (16 * kW8NT)), dim3(kW8KW * 64), 0,
+  hipLaunchKernelGGL((w8a16_mfma_kernel<MT, BK, PX>), dim3((n + 16 * kW8NT - 1) / (16 * kW8NT)), dim3(kW8KW * 64), 0,
                      stream, static_cast<const uint16_t*>(x), m, w, static_cast<const uint16_t*>(scale), n, k, y,
                      y_f32);
   return hipGetLastError();
 }
 
-// 5..64 rows: MT = ceil(m / 16) m-tiles, rows past m masked.
+// 5..64 rows: MT = ceil(m / 16) m-tiles, rows past m masked; blocks of 128
+// k.  Loading the activations a block ahead pays at 17..32 rows only
+// (8192 x 8192: 28.8 us against 33.3 at 32 rows, but 30.7 against 25.0 at 16;
+// 256-k blocks at 16 rows: 30.7); above 32 rows two register sets of them
+// would spill.
 hipError_t launch_w8a16_mfma(int m, const void* x, const int8_t* w, const void* scale, int n, int k, void* y,
                              int y_f32, hipStream_t stream) {
   switch ((m + 15) / 16) {
-    case 1: return launch_w8_mfma_t<1>(x, m, w, scale, n, k, y, y_f32, stream);
-    case 2: return launch_w8_mfma_t<2>(x, m, w, scale, n, k, y, y_f32, stream);
-    case 3: return launch_w8_mfma_t<3>(x, m, w, scale, n, k, y, y_f32, stream);
-    case 4: return launch_w8_mfma_t<4>(x, m, w, scale, n, k, y, y_f32, stream);
+    case 1: return launch_w8_mfma_t<1, 128, false>(x, m, w, scale, n, k, y, y_f32, stream);
+    case 2: return launch_w8_mfma_t<2, 128, true>(x, m, w, scale, n, k, y, y_f32, stream);
+    case 3: return launch_w8_mfma_t<3, 128, false>(x, m, w, scale, n, k, y, y_f32, stream);
+    case 4: return launch_w8_mfma_t<4, 128, false>(x, m, w, scale, n, k, y, y_f32, stream);
     default: return hipErrorInvalidValue;
   }
 }
