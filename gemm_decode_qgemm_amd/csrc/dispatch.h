@@ -10,8 +10,6 @@
 
 namespace qg {
 
-constexpr int64_t kCUs = 256;   // compute units of an MI355X
-
 // Split-K default, measured on MI355X at the decode layer shapes.
 //  * M <= 4 (GEMV, 32-row workgroups): one split whenever the grid has at
 //    least half a workgroup per CU (N >= 4096): a second split costs a second

@@ -42,8 +42,10 @@ struct XHalf {
 template <int M>
 __device__ __forceinline__ void load_xhalf(XHalf<M>& xr, const uint32_t* x32, int k32, int hs, int li) {
 #pragma unroll
-  for (int m = 0; m < M; ++m)
-    xr.v[m] = *reinterpret_cast<const u32x4_t*>(x32 + (size_t)m * k32 + (size_t)hs * 64 + li * 4);
+  for (int m = 0; m < M; ++m) {
+    const BufView xb(x32 + (size_t)m * k32 + (size_t)hs * 64, 256);
+    xr.v[m] = xb.b128<false>((uint32_t)li * 16u);
+  }
 }
 
 // d0 += x . (128+q) over the even dwords and d1 over the odd dwords of one
@@ -146,7 +148,7 @@ __device__ __forceinline__ void half_compute(float (&acc)[M], const HalfRegs& cu
 // ... of its row block's split-K range: load, wait, compute (the other
 // resident waves keep the memory system busy; a register look-ahead of one or
 // two units measured no faster on MI355X).
-template <int M, int WAVES>
+template <int M, int WAVES, bool PF = false>
 __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -175,12 +177,38 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 
-  for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {   // tile hs/2, half hs%2
-    HalfRegs r;
-    XHalf<M> xr;
-    load_half<true>(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lane);
+  auto load = [&](HalfRegs& r, XHalf<M>& xr, int hs) {   // tile hs/2, half hs%2
+    load_half_buf(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lane);
     load_xhalf<M>(xr, x32, k32, hs, li);
-    half_compute<M>(acc, r, xr, mask_s, magic_v, ones_v);
+  };
+  if constexpr (!PF) {
+    for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {
+      HalfRegs r;
+      XHalf<M> xr;
+      load(r, xr, hs);
+      half_compute<M>(acc, r, xr, mask_s, magic_v, ones_v);
+    }
+  } else {
+    const int h_end = 2 * t1;
+    int hs = 2 * t0 + wave;
+    if (hs < h_end) {
+      HalfRegs ra, rb;
+      XHalf<M> xa, xb;
+      load(ra, xa, hs);
+      __builtin_amdgcn_sched_barrier(0);
+      while (true) {
+        if (hs + WAVES >= h_end) { half_compute<M>(acc, ra, xa, mask_s, magic_v, ones_v); break; }
+        load(rb, xb, hs + WAVES);
+        __builtin_amdgcn_sched_barrier(0);
+        half_compute<M>(acc, ra, xa, mask_s, magic_v, ones_v);
+        hs += WAVES;
+        if (hs + WAVES >= h_end) { half_compute<M>(acc, rb, xb, mask_s, magic_v, ones_v); break; }
+        load(ra, xa, hs + WAVES);
+        __builtin_amdgcn_sched_barrier(0);
+        half_compute<M>(acc, rb, xb, mask_s, magic_v, ones_v);
+        hs += WAVES;
+      }
+    }
   }
 
   // Cross-wave sum in wave order (fixed, so repeat calls are bit-identical).
@@ -236,7 +264,12 @@ __device__ __forceinline__ void group_dot_2r(float& d0, float& d1, const u32x2_t
   if constexpr (JJ == 1) asm(QG_DOT16_2R(8, 9, 10, 11, 12, 13, 14, 15) QG_DOT16_2R_OPERANDS);
 }
 
-template <int M, int WAVES, bool DQ = false>
+// PF: two register sets used in turn, so that a wave has the next half
+// tile's loads in flight while it computes the current one (for grids of at
+// most one workgroup per CU, where nothing else hides the load latency).  The
+// scheduling barriers keep the compiler from sinking the loads below the
+// computation they are meant to overlap.
+template <int M, int WAVES, bool DQ = false, bool PF = false>
 __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv32_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -248,11 +281,11 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv32_kernel(
   const int rb = blockIdx.x >> 1;                 // 64-row block
   const int row = 32 * (blockIdx.x & 1) + (lane & 31);   // row within the block
   const int kt_count = k >> 8;
-  int t0, t1;
-  split_range(kt_count, split, blockIdx.y, t0, t1);
   using L = W4Layout<DQ>;
   float step;
   const uint8_t* tiles = L::tiles(packed, rb, kt_count, row, step);
+  int t0, t1;
+  split_range(kt_count, split, blockIdx.y, t0, t1);
   const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
   const int k32 = k >> 1;
   const uint32_t mask_s = __builtin_amdgcn_readfirstlane(0x000F000Fu);
@@ -265,13 +298,16 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv32_kernel(
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 
-  for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {
-    Half32Regs r;
-    L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
-    u32x2_t xv[M];
+  // Buffer views per half tile: of its weight tile and of its 128 k of x.
+  auto load = [&](Half32Regs& r, u32x2_t (&xv)[M], int hs) {
+    L::load_buf(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
 #pragma unroll
-    for (int m = 0; m < M; ++m)
-      xv[m] = *reinterpret_cast<const u32x2_t*>(x32 + (size_t)m * k32 + (size_t)hs * 64 + 32 * lg + 2 * li);
+    for (int m = 0; m < M; ++m) {
+      const BufView xb(x32 + (size_t)m * k32 + (size_t)hs * 64, 256);
+      xv[m] = xb.b64((uint32_t)(32 * lg + 2 * li) * 4u);
+    }
+  };
+  auto compute = [&](const Half32Regs& r, const u32x2_t (&xv)[M]) {
     // group sums: 8 lanes per group (quad_perm [1,0,3,2], [2,3,0,1], half-row mirror)
     float xq[M];
 #pragma unroll
@@ -305,6 +341,36 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv32_kernel(
         else
           group_dot_2r<1>(d0, d1, xv[m], pr);
         acc[m] = __builtin_fmaf(jj == 0 ? s0 : s1, d0 + d1, acc[m]);
+      }
+    }
+  };
+
+  if constexpr (!PF) {
+    for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {
+      Half32Regs r;
+      u32x2_t xv[M];
+      load(r, xv, hs);
+      compute(r, xv);
+    }
+  } else {
+    const int h_end = 2 * t1;
+    int hs = 2 * t0 + wave;
+    if (hs < h_end) {                                    // uniform
+      Half32Regs ra, rb;
+      u32x2_t xa[M], xb[M];
+      load(ra, xa, hs);
+      __builtin_amdgcn_sched_barrier(0);
+      while (true) {
+        if (hs + WAVES >= h_end) { compute(ra, xa); break; }
+        load(rb, xb, hs + WAVES);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(ra, xa);
+        hs += WAVES;
+        if (hs + WAVES >= h_end) { compute(rb, xb); break; }
+        load(ra, xa, hs + WAVES);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(rb, xb);
+        hs += WAVES;
       }
     }
   }
@@ -455,23 +521,40 @@ hipError_t launch_splitk_reduce(const float* partial, int split, int64_t mn, voi
   return hipGetLastError();
 }
 
+#ifndef QG_GEMV64_PF
+#define QG_GEMV64_PF 1
+#endif
+
 template <int M, int WAVES>
 static hipError_t launch_w4a16_t(const void* x, const void* packed, int n, int k, void* y,
                                  int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_gemv_kernel<M, WAVES>), dim3(rbs, split), dim3(WAVES * 64), 0,
-                     stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
-                     n, k, y, y_f32, partial, split);
+  if (QG_GEMV64_PF && rbs * split <= kCUs)
+    hipLaunchKernelGGL((w4a16_gemv_kernel<M, WAVES, true>), dim3(rbs, split), dim3(WAVES * 64), 0,
+                       stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
+                       n, k, y, y_f32, partial, split);
+  else
+    hipLaunchKernelGGL((w4a16_gemv_kernel<M, WAVES>), dim3(rbs, split), dim3(WAVES * 64), 0,
+                       stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
+                       n, k, y, y_f32, partial, split);
   return hipGetLastError();
 }
 
-template <int M, int WAVES>
-static hipError_t launch_w4a16_32_t(const void* x, const void* packed, int n, int k, void* y,
-                                    int y_f32, float* partial, int split, hipStream_t stream) {
+// M = 1 on either layout: half a 64-row block per workgroup, with the
+// two-register-set loop when the grid has at most one workgroup per CU.
+template <bool DQ>
+static hipError_t launch_gemv32_m1(const void* x, const void* packed, int n, int k, void* y, int y_f32,
+                                   float* partial, int split, hipStream_t stream) {
+  const auto* xs = static_cast<const uint16_t*>(x);
+  const auto* ps = static_cast<const uint8_t*>(packed);
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_gemv32_kernel<M, WAVES>), dim3(2 * rbs, split), dim3(WAVES * 64),
-                     0, stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
-                     n, k, y, y_f32, partial, split);
+  const dim3 grid(2 * rbs, split), block(16 * 64);
+  if (2 * rbs * split <= kCUs)
+    hipLaunchKernelGGL((w4a16_gemv32_kernel<1, 16, DQ, true>), grid, block, 0, stream, xs, ps, n, k, y, y_f32,
+                       partial, split);
+  else
+    hipLaunchKernelGGL((w4a16_gemv32_kernel<1, 16, DQ>), grid, block, 0, stream, xs, ps, n, k, y, y_f32,
+                       partial, split);
   return hipGetLastError();
 }
 
@@ -479,23 +562,14 @@ static hipError_t launch_w4a16_32_t(const void* x, const void* packed, int n, in
 hipError_t launch_w4a16_gemv32_dq(int m, const void* x, const void* packed, int n, int k, void* y,
                                   int y_f32, float* partial, int split, hipStream_t stream) {
   if (m != 1) return hipErrorInvalidValue;
-  const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_gemv32_kernel<1, 16, true>), dim3(2 * rbs, split), dim3(16 * 64), 0, stream,
-                     static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed), n, k, y, y_f32,
-                     partial, split);
-  return hipGetLastError();
+  return launch_gemv32_m1<true>(x, packed, n, k, y, y_f32, partial, split, stream);
 }
 
+// M = 2..4 run on the matrix-instruction GEMV (gemv_w4a16_mx4.hip).
 hipError_t launch_w4a16_gemv32(int m, const void* x, const void* packed, int n, int k, void* y,
                                int y_f32, float* partial, int split, int waves, hipStream_t stream) {
-#define QG_W32_CASE(MM, WW) \
-  if (m == MM && waves == WW) return launch_w4a16_32_t<MM, WW>(x, packed, n, k, y, y_f32, partial, split, stream);
-  // M = 2..4 run on the matrix-instruction GEMV (gemv_w4a16_mx4.hip).
-#define QG_W32_M(MM) QG_W32_CASE(MM, 16)
-  QG_W32_M(1)
-#undef QG_W32_M
-#undef QG_W32_CASE
-  return hipErrorInvalidValue;
+  if (m != 1 || waves != 16) return hipErrorInvalidValue;
+  return launch_gemv32_m1<false>(x, packed, n, k, y, y_f32, partial, split, stream);
 }
 
 hipError_t launch_w4a16_gemv(int m, const void* x, const void* packed, int n, int k, void* y,

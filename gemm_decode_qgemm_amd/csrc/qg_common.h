@@ -13,6 +13,7 @@ namespace qg {
 // Packed INT4 layout, version 1 (see include/qgemm.h): tiles of 64 rows x
 // 256 k, codes | fp16 scales | 4-bit zero points, 9472 bytes.
 constexpr int kTileRows = 64;
+constexpr int64_t kCUs = 256;   // compute units of an MI355X
 constexpr int kTileK = 256;
 constexpr int kGroupsPerTile = 8;
 constexpr int kScaleOff = 8192;

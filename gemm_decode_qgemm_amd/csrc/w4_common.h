@@ -15,18 +15,65 @@ struct HalfRegs {
   uint32_t zw;
 };
 
+// A wave-uniform base plus an unsigned 32-bit per-lane byte offset: the form
+// the scalar-base + vector-offset global loads take, so that stepping through
+// tiles costs scalar adds only (a signed or 64-bit offset makes the compiler
+// build a 64-bit vector address for every load).
+template <typename T>
+__device__ __forceinline__ const T* lane_at(const uint8_t* base, uint32_t off) {
+  return reinterpret_cast<const T*>(base + off);
+}
+
+// A raw buffer over `bytes` bytes at a wave-uniform `base`: its loads take an
+// unsigned 32-bit per-lane offset and no vector address arithmetic (the
+// descriptor lives in scalar registers, built per tile from the scalar tile
+// address), and a read at or past `bytes` returns zero.  Cache policy of the
+// streaming loads: non-temporal (bit 1 of the policy operand on gfx950).
+struct BufView {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ BufView(const void* base, int bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000)) {}
+  template <bool NT>
+  __device__ __forceinline__ u32x4_t b128(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0);
+  }
+  __device__ __forceinline__ u32x2_t b64(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  }
+  __device__ __forceinline__ uint32_t b32(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  __device__ __forceinline__ uint32_t b16(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  }
+  __device__ __forceinline__ uint32_t b8(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+  }
+};
+
 template <bool NT>
 __device__ __forceinline__ void load_half(HalfRegs& r, const uint8_t* tile, int half, int lane) {
+  const uint8_t* th = tile + half * (4 * kTileRows * 16);
+  const uint32_t co = (uint32_t)lane * 16u;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    r.c[j] = load_stream<NT>(
-        reinterpret_cast<const u32x4_t*>(tile + ((4 * half + j) * kTileRows + lane) * 16));
+    r.c[j] = load_stream<NT>(lane_at<u32x4_t>(th + j * (kTileRows * 16), co));
   // Scales and zero points of the two half tiles share 128-byte lines, and
   // the other half is read by another wave of the same workgroup moments
   // later: these loads keep the default (temporal) policy so that wave hits
   // in L2 instead of fetching the line from HBM again.
-  r.sc = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + kScaleOff + lane * 16 + 8 * half));
-  r.zw = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + kZeroOff + lane * 4 + 2 * half));
+  r.sc = load_stream<false>(lane_at<u32x2_t>(tile + kScaleOff + 8 * half, (uint32_t)lane * 16u));
+  r.zw = load_stream<false>(lane_at<uint16_t>(tile + kZeroOff + 2 * half, (uint32_t)lane * 4u));
+}
+
+// load_half through a buffer view of the tile (`tile` wave-uniform).
+__device__ __forceinline__ void load_half_buf(HalfRegs& r, const uint8_t* tile, int half, int lane) {
+  const BufView v(tile, kTileBytes);
+  const uint32_t co = (uint32_t)((4 * half * kTileRows + lane) * 16);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r.c[j] = v.b128<true>(co + j * (kTileRows * 16));
+  r.sc = v.b64((uint32_t)(kScaleOff + lane * 16 + 8 * half));
+  r.zw = v.b16((uint32_t)(kZeroOff + lane * 4 + 2 * half));
 }
 
 // The 32-row mapping: a workgroup owns rows [32h, 32h + 32) of a 64-row block
@@ -44,13 +91,13 @@ struct Half32Regs {
 template <bool NT>
 __device__ __forceinline__ void load_half32(Half32Regs& r, const uint8_t* tile, int half, int lg,
                                             int row) {
+  const uint8_t* th = tile + half * (4 * kTileRows * 16);
+  const uint32_t co = (uint32_t)(2 * lg * kTileRows + row) * 16u;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    r.c[j] = load_stream<NT>(
-        reinterpret_cast<const u32x4_t*>(tile + ((4 * half + 2 * lg + j) * kTileRows + row) * 16));
+  for (int j = 0; j < 2; ++j) r.c[j] = load_stream<NT>(lane_at<u32x4_t>(th + j * (kTileRows * 16), co));
   // Temporal, as in load_half: the other half tile's metadata shares these lines.
-  r.sc = load_stream<false>(reinterpret_cast<const uint32_t*>(tile + kScaleOff + row * 16 + 8 * half + 4 * lg));
-  r.zb = load_stream<false>(tile + kZeroOff + row * 4 + 2 * half + lg);
+  r.sc = load_stream<false>(lane_at<uint32_t>(tile + kScaleOff + 8 * half, (uint32_t)(row * 16 + 4 * lg)));
+  r.zb = load_stream<false>(lane_at<uint8_t>(tile + kZeroOff + 2 * half, (uint32_t)(row * 4 + lg)));
 }
 
 // The two packed layouts seen by the 32-row kernels.  Version 1: tiles of
@@ -75,6 +122,15 @@ struct W4Layout<false> {
   __device__ static void load(Half32Regs& r, const uint8_t* tile, int half, int lg, int row) {
     load_half32<true>(r, tile, half, lg, row);
   }
+  // The same loads through a buffer view of the tile (`tile` wave-uniform).
+  __device__ static void load_buf(Half32Regs& r, const uint8_t* tile, int half, int lg, int row) {
+    const BufView v(tile, kTileBytes);
+    const uint32_t co = (uint32_t)(((4 * half + 2 * lg) * kTileRows + row) * 16);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) r.c[j] = v.b128<true>(co + j * (kTileRows * 16));
+    r.sc = v.b32((uint32_t)(kScaleOff + row * 16 + 8 * half + 4 * lg));
+    r.zb = v.b8((uint32_t)(kZeroOff + row * 4 + 2 * half + lg));
+  }
   // scale of group 2 lg + jj of the half tile
   __device__ static float scale(uint32_t sc, int jj, float) {
     return fp16_to_f32((sc >> (16 * jj)) & 0xffffu);
@@ -95,13 +151,21 @@ struct W4Layout<true> {
     return block + kDqHeadBytes;
   }
   __device__ static void load(Half32Regs& r, const uint8_t* tile, int half, int lg, int row) {
+    const uint8_t* th = tile + half * (4 * kTileRows * 16);
+    const uint32_t co = (uint32_t)(2 * lg * kTileRows + row) * 16u;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      r.c[j] = load_stream<true>(
-          reinterpret_cast<const u32x4_t*>(tile + ((4 * half + 2 * lg + j) * kTileRows + row) * 16));
+    for (int j = 0; j < 2; ++j) r.c[j] = load_stream<true>(lane_at<u32x4_t>(th + j * (kTileRows * 16), co));
     // temporal, as in load_half32: the other half tile's metadata shares these lines
-    r.sc = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + kDqScodeOff + row * 8 + 4 * half + 2 * lg));
-    r.zb = load_stream<false>(tile + kDqZeroOff + row * 4 + 2 * half + lg);
+    r.sc = load_stream<false>(lane_at<uint16_t>(tile + kDqScodeOff + 4 * half, (uint32_t)(row * 8 + 2 * lg)));
+    r.zb = load_stream<false>(lane_at<uint8_t>(tile + kDqZeroOff + 2 * half, (uint32_t)(row * 4 + lg)));
+  }
+  __device__ static void load_buf(Half32Regs& r, const uint8_t* tile, int half, int lg, int row) {
+    const BufView v(tile, kDqTileBytes);
+    const uint32_t co = (uint32_t)(((4 * half + 2 * lg) * kTileRows + row) * 16);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) r.c[j] = v.b128<true>(co + j * (kTileRows * 16));
+    r.sc = v.b16((uint32_t)(kDqScodeOff + row * 8 + 4 * half + 2 * lg));
+    r.zb = v.b8((uint32_t)(kDqZeroOff + row * 4 + 2 * half + lg));
   }
   __device__ static float scale(uint32_t sc, int jj, float step) {
     return (float)((sc >> (8 * jj)) & 0xffu) * step;
@@ -138,21 +202,22 @@ struct WnLayout {
     return packed + (size_t)rb * kt_count * kTile;
   }
   __device__ static void load(Regs& r, const uint8_t* tile, int half, int lg, int row) {
+    const int g0 = 4 * half;                        // uniform
+    const uint32_t rl = (uint32_t)(2 * lg * kTileRows + row);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int g = 4 * half + 2 * lg + j;
-      r.c[j] = load_stream<true>(reinterpret_cast<const u32x4_t*>(tile + (g * kTileRows + row) * 16));
+      r.c[j] = load_stream<true>(lane_at<u32x4_t>(tile + (g0 + j) * (kTileRows * 16), rl * 16u));
       if constexpr (HB == 1) {
-        r.hp[j][0] = load_stream<true>(reinterpret_cast<const uint32_t*>(tile + 8192 + (g * kTileRows + row) * 4));
+        r.hp[j][0] = load_stream<true>(lane_at<uint32_t>(tile + 8192 + (g0 + j) * (kTileRows * 4), rl * 4u));
       } else {
-        const u32x2_t h = load_stream<true>(reinterpret_cast<const u32x2_t*>(tile + 8192 + (g * kTileRows + row) * 8));
+        const u32x2_t h = load_stream<true>(lane_at<u32x2_t>(tile + 8192 + (g0 + j) * (kTileRows * 8), rl * 8u));
         r.hp[j][0] = h.x;
         r.hp[j][1] = h.y;
       }
     }
     // temporal, as in load_half32: the other half tile's metadata shares these lines
-    r.sc = load_stream<false>(reinterpret_cast<const uint32_t*>(tile + kS + row * 16 + 8 * half + 4 * lg));
-    r.zb = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + kZ + row * 8 + 4 * half + 2 * lg));
+    r.sc = load_stream<false>(lane_at<uint32_t>(tile + kS + 8 * half, (uint32_t)(row * 16 + 4 * lg)));
+    r.zb = load_stream<false>(lane_at<uint16_t>(tile + kZ + 4 * half, (uint32_t)(row * 8 + 2 * lg)));
   }
   __device__ static float scale(uint32_t sc, int jj, float) {
     return fp16_to_f32((sc >> (16 * jj)) & 0xffffu);

@@ -277,6 +277,8 @@ def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     """The binding raises instead of falling back to anything when the .so is missing."""
     import importlib.util
 
+    monkeypatch.delenv("QGEMM_LIB", raising=False)   # a run that points at another build
+
     src = os.path.join(ROOT, "gemm_decode_qgemm_amd", "binding.py")
     copy = tmp_path / "binding.py"
     copy.write_text(open(src).read())

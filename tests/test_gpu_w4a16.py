@@ -183,6 +183,25 @@ def test_w4a16_both_workgroup_shapes_ragged_n(dev, m):
             assert_w16(y, ref, f"N=8200 M={m} split={split} {dt}")
 
 
+@pytest.mark.parametrize("n", [4097, 5000, 6600, 8191, 8192, 8193])
+def test_w4a16_prefetch_grid(dev, n):
+    """M = 1 with at most one 32-row workgroup per CU (2 x 64-row blocks x
+    split <= 256) takes the two-register-set loop: 130 workgroups at N = 4097
+    (one live row in the last), the padded rows of a partial last block, and
+    the edge at N = 8192 (256 workgroups, prefetching) against 8193 (258, the
+    plain loop); split 0 (the default) and 1, both output types."""
+    k = 768
+    w, codes, scales, zeros = _weight(n, k, 70 + n)
+    packed = _gpu_packed(w, dev)
+    x = si.activation(1, k, 80 + n)
+    ref = _ref(x, codes, scales, zeros)
+    print(f"qgemm_w4a16 prefetch grid N={n}", flush=True)
+    for split in (0, 1):
+        for dt in (torch.float32, torch.bfloat16):
+            y = qg.qgemm_w4a16(x.to(dev), packed, n, split_k=split, out_dtype=dt)
+            assert_w16(y, ref, f"N={n} split={split} {dt}")
+
+
 def test_w4a16_uneven_split_partition(dev):
     """K = 6656 has 26 tiles: splits 4 and 8 give uneven ranges (7,7,6,6 / 4,4,3,...)."""
     n, k = 320, 6656

@@ -160,6 +160,32 @@ def test_w4a16_dq_non_finite_row_gives_nan(dev):
     assert torch.isfinite(torch.cat([y[0, :5], y[0, 6:]])).all()
 
 
+@pytest.mark.parametrize("n", [4097, 6600, 8192, 8193])
+def test_w4a16_dq_prefetch_grid(dev, n):
+    """The two-register-set loop (M = 1, at most 256 workgroups of 32 rows)
+    on the scale-code layout, on both sides of the 256-workgroup edge."""
+    k = 512
+    w, codes, scode, sstep, zeros = _weight(n, k, 90 + n)
+    packed = qg.quantize_int4_g32_dq(w.to(dev))
+    x = si.activation(1, k, 95 + n)
+    ref = _ref(x, codes, scode, sstep, zeros)
+    print(f"qgemm_w4a16_dq prefetch grid N={n}", flush=True)
+    for dt in (torch.float32, torch.bfloat16):
+        assert_w16(qg.qgemm_w4a16_dq(x.to(dev), packed, n, out_dtype=dt), ref, f"N={n} {dt}")
+
+
+def test_w4a16_dq_prefetch_grid_non_finite_row(dev):
+    """N = 6656 (208 workgroups, prefetching): a non-finite weight in row 70
+    makes that row's step NaN, and only y[70] may be NaN."""
+    n, k = 6656, 256
+    w = si.int4_weight(n, k, 4).clone()
+    w[70, 9] = float("inf")
+    packed = qg.quantize_int4_g32_dq(w.to(dev))
+    y = qg.qgemm_w4a16_dq(si.activation(1, k, 6).to(dev), packed, n, out_dtype=torch.float32).cpu()
+    assert torch.isnan(y[0, 70])
+    assert torch.isfinite(torch.cat([y[0, :70], y[0, 71:]])).all()
+
+
 def test_w4a16_dq_repeat_and_graph_replay_are_bit_identical(dev):
     n, k = 8448, 6656
     w, *_ = _weight(n, k, si.model_weight_seed(n, k))
