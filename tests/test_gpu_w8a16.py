@@ -91,6 +91,20 @@ def test_w8a16_shapes_and_tails(dev, n, k, m):
     assert_w16(y, ref, f"{n}x{k} M={m}")
 
 
+@pytest.mark.parametrize("m", [17, 24, 32, 33])
+def test_w8a16_64_row_workgroups_on_tall_layers(dev, m):
+    """From 32768 rows, 17..32 activation rows take workgroups of 64 weight
+    rows (4 n-tiles); N = 32801 leaves a 33-row tail in the last workgroup
+    (and 33 activation rows stay on 32-row workgroups)."""
+    n, k = 32801, 256
+    w, s, x = si.int8_layer(n=n, k=k, m=m, seed=700 + m)
+    ref = _ref(x, w, s)
+    print(f"qgemm_w8a16 {n}x{k} M={m}", flush=True)
+    for dt in (torch.float32, torch.bfloat16):
+        y = qg.qgemm_w8a16(x.to(dev), w.to(dev), s.to(dev), out_dtype=dt)
+        assert_w16(y, ref, f"{n}x{k} M={m} {dt}")
+
+
 def test_w8a16_quantized_weight_round_trip(dev):
     """Quantize bf16 weights on the GPU, then run the GEMV on them."""
     n, k = 512, 4096
