@@ -178,7 +178,7 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 
   auto load = [&](HalfRegs& r, XHalf<M>& xr, int hs) {   // tile hs/2, half hs%2
-    load_half_buf(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lane);
+    load_half(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lane);
     load_xhalf<M>(xr, x32, k32, hs, li);
   };
   if constexpr (!PF) {
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv32_kernel(
 
   // Buffer views per half tile: of its weight tile and of its 128 k of x.
   auto load = [&](Half32Regs& r, u32x2_t (&xv)[M], int hs) {
-    L::load_buf(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
+    L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const BufView xb(x32 + (size_t)m * k32 + (size_t)hs * 64, 256);
@@ -436,7 +436,8 @@ __global__ __launch_bounds__(WAVES * 64) void wn_a16_gemv32_kernel(
   for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {
     WnRegs<HB> r;
     L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
-    const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(x32 + (size_t)hs * 64 + 32 * lg + 2 * li);
+    const u32x2_t xv = BufView(x32 + (size_t)hs * 64, 256).b64((uint32_t)(32 * lg + 2 * li) * 4u);
+    __builtin_amdgcn_sched_barrier(0);   // every load of the step issued before the first wait
     float p = dot2_bf16(xv.x, ones_v, 0.0f);
     p = dot2_bf16(xv.y, ones_v, p);
     p += dpp_mov<0xB1>(p);

@@ -190,7 +190,7 @@ __global__ __launch_bounds__(WAVES * 64) void w4a8_gemv_kernel(
 
   for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {
     HalfRegs r;
-    load_half<true>(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lane);
+    load_half(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lane);
     uint32_t xlo[M], xhi[M];
     int sxq[M];
 #pragma unroll

@@ -15,15 +15,6 @@ struct HalfRegs {
   uint32_t zw;
 };
 
-// A wave-uniform base plus an unsigned 32-bit per-lane byte offset: the form
-// the scalar-base + vector-offset global loads take, so that stepping through
-// tiles costs scalar adds only (a signed or 64-bit offset makes the compiler
-// build a 64-bit vector address for every load).
-template <typename T>
-__device__ __forceinline__ const T* lane_at(const uint8_t* base, uint32_t off) {
-  return reinterpret_cast<const T*>(base + off);
-}
-
 // A raw buffer over `bytes` bytes at a wave-uniform `base`: its loads take an
 // unsigned 32-bit per-lane offset and no vector address arithmetic (the
 // descriptor lives in scalar registers, built per tile from the scalar tile
@@ -37,11 +28,13 @@ struct BufView {
   __device__ __forceinline__ u32x4_t b128(uint32_t off) const {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0);
   }
+  template <bool NT = false>
   __device__ __forceinline__ u32x2_t b64(uint32_t off) const {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, NT ? 2 : 0);
   }
+  template <bool NT = false>
   __device__ __forceinline__ uint32_t b32(uint32_t off) const {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, NT ? 2 : 0);
   }
   __device__ __forceinline__ uint32_t b16(uint32_t off) const {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
@@ -51,23 +44,13 @@ struct BufView {
   }
 };
 
-template <bool NT>
+// One half tile of one lane's row (64-row mapping: lane = row), through a
+// buffer view of the tile (`tile` wave-uniform).  Codes are streamed
+// non-temporally.  Scales and zero points of the two half tiles share
+// 128-byte lines, and the other half is read by another wave of the same
+// workgroup moments later: those loads keep the default (temporal) policy so
+// that wave hits in L2 instead of fetching the line from HBM again.
 __device__ __forceinline__ void load_half(HalfRegs& r, const uint8_t* tile, int half, int lane) {
-  const uint8_t* th = tile + half * (4 * kTileRows * 16);
-  const uint32_t co = (uint32_t)lane * 16u;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    r.c[j] = load_stream<NT>(lane_at<u32x4_t>(th + j * (kTileRows * 16), co));
-  // Scales and zero points of the two half tiles share 128-byte lines, and
-  // the other half is read by another wave of the same workgroup moments
-  // later: these loads keep the default (temporal) policy so that wave hits
-  // in L2 instead of fetching the line from HBM again.
-  r.sc = load_stream<false>(lane_at<u32x2_t>(tile + kScaleOff + 8 * half, (uint32_t)lane * 16u));
-  r.zw = load_stream<false>(lane_at<uint16_t>(tile + kZeroOff + 2 * half, (uint32_t)lane * 4u));
-}
-
-// load_half through a buffer view of the tile (`tile` wave-uniform).
-__device__ __forceinline__ void load_half_buf(HalfRegs& r, const uint8_t* tile, int half, int lane) {
   const BufView v(tile, kTileBytes);
   const uint32_t co = (uint32_t)((4 * half * kTileRows + lane) * 16);
 #pragma unroll
@@ -88,18 +71,6 @@ struct Half32Regs {
   uint32_t zb;
 };
 
-template <bool NT>
-__device__ __forceinline__ void load_half32(Half32Regs& r, const uint8_t* tile, int half, int lg,
-                                            int row) {
-  const uint8_t* th = tile + half * (4 * kTileRows * 16);
-  const uint32_t co = (uint32_t)(2 * lg * kTileRows + row) * 16u;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) r.c[j] = load_stream<NT>(lane_at<u32x4_t>(th + j * (kTileRows * 16), co));
-  // Temporal, as in load_half: the other half tile's metadata shares these lines.
-  r.sc = load_stream<false>(lane_at<uint32_t>(tile + kScaleOff + 8 * half, (uint32_t)(row * 16 + 4 * lg)));
-  r.zb = load_stream<false>(lane_at<uint8_t>(tile + kZeroOff + 2 * half, (uint32_t)(row * 4 + lg)));
-}
-
 // The two packed layouts seen by the 32-row kernels.  Version 1: tiles of
 // 9472 bytes with fp16 scales.  Version 2 (scale codes): each 64-row block
 // starts with a 128-byte head of fp16 row steps, its tiles are 8960 bytes,
@@ -119,11 +90,9 @@ struct W4Layout<false> {
     step = 1.0f;
     return packed + (size_t)rb * kt_count * kTileBytes;
   }
+  // One half tile of one lane's row and group pair (32-row mapping), through
+  // a buffer view of the tile (`tile` wave-uniform); policies as load_half.
   __device__ static void load(Half32Regs& r, const uint8_t* tile, int half, int lg, int row) {
-    load_half32<true>(r, tile, half, lg, row);
-  }
-  // The same loads through a buffer view of the tile (`tile` wave-uniform).
-  __device__ static void load_buf(Half32Regs& r, const uint8_t* tile, int half, int lg, int row) {
     const BufView v(tile, kTileBytes);
     const uint32_t co = (uint32_t)(((4 * half + 2 * lg) * kTileRows + row) * 16);
 #pragma unroll
@@ -151,15 +120,6 @@ struct W4Layout<true> {
     return block + kDqHeadBytes;
   }
   __device__ static void load(Half32Regs& r, const uint8_t* tile, int half, int lg, int row) {
-    const uint8_t* th = tile + half * (4 * kTileRows * 16);
-    const uint32_t co = (uint32_t)(2 * lg * kTileRows + row) * 16u;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) r.c[j] = load_stream<true>(lane_at<u32x4_t>(th + j * (kTileRows * 16), co));
-    // temporal, as in load_half32: the other half tile's metadata shares these lines
-    r.sc = load_stream<false>(lane_at<uint16_t>(tile + kDqScodeOff + 4 * half, (uint32_t)(row * 8 + 2 * lg)));
-    r.zb = load_stream<false>(lane_at<uint8_t>(tile + kDqZeroOff + 2 * half, (uint32_t)(row * 4 + lg)));
-  }
-  __device__ static void load_buf(Half32Regs& r, const uint8_t* tile, int half, int lg, int row) {
     const BufView v(tile, kDqTileBytes);
     const uint32_t co = (uint32_t)(((4 * half + 2 * lg) * kTileRows + row) * 16);
 #pragma unroll
@@ -201,23 +161,25 @@ struct WnLayout {
     step = 1.0f;
     return packed + (size_t)rb * kt_count * kTile;
   }
+  // Through a buffer view of the tile (`tile` wave-uniform); the planes are
+  // streamed like the codes, scales and zero points as in load_half.
   __device__ static void load(Regs& r, const uint8_t* tile, int half, int lg, int row) {
-    const int g0 = 4 * half;                        // uniform
+    const BufView v(tile, kTile);
+    const int g0 = 4 * half;
     const uint32_t rl = (uint32_t)(2 * lg * kTileRows + row);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      r.c[j] = load_stream<true>(lane_at<u32x4_t>(tile + (g0 + j) * (kTileRows * 16), rl * 16u));
+      r.c[j] = v.b128<true>((uint32_t)((g0 + j) * (kTileRows * 16)) + rl * 16u);
       if constexpr (HB == 1) {
-        r.hp[j][0] = load_stream<true>(lane_at<uint32_t>(tile + 8192 + (g0 + j) * (kTileRows * 4), rl * 4u));
+        r.hp[j][0] = v.b32<true>((uint32_t)(8192 + (g0 + j) * (kTileRows * 4)) + rl * 4u);
       } else {
-        const u32x2_t h = load_stream<true>(lane_at<u32x2_t>(tile + 8192 + (g0 + j) * (kTileRows * 8), rl * 8u));
+        const u32x2_t h = v.b64<true>((uint32_t)(8192 + (g0 + j) * (kTileRows * 8)) + rl * 8u);
         r.hp[j][0] = h.x;
         r.hp[j][1] = h.y;
       }
     }
-    // temporal, as in load_half32: the other half tile's metadata shares these lines
-    r.sc = load_stream<false>(lane_at<uint32_t>(tile + kS + 8 * half, (uint32_t)(row * 16 + 4 * lg)));
-    r.zb = load_stream<false>(lane_at<uint16_t>(tile + kZ + 4 * half, (uint32_t)(row * 8 + 2 * lg)));
+    r.sc = v.b32((uint32_t)(kS + row * 16 + 8 * half + 4 * lg));
+    r.zb = v.b16((uint32_t)(kZ + row * 8 + 4 * half + 2 * lg));
   }
   __device__ static float scale(uint32_t sc, int jj, float) {
     return fp16_to_f32((sc >> (16 * jj)) & 0xffffu);
