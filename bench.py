@@ -178,7 +178,8 @@ def main() -> int:
             w_cpu, x_cpu = si.decode_inputs(n, k, m)
         else:
             w_cpu, x_cpu = si.int4_weight(n, k, n ^ k), si.activation(m, k, 9100 + m)
-        split = args.split or qg.default_split_k(m, n, k, args.bits if op == "wn_a16" else 4)
+        split = args.split or qg.default_split_k(m, n, k, args.bits if op == "wn_a16" else 4,
+                                                 group_scales=op in ("w4a8_g32", "w4a8_g32_dq"))
         if op in ("w4a16_dq", "w4a8_dq", "w4a8_g32_dq"):
             packed0 = qg.quantize_int4_g32_dq(w_cpu.to(dev))
         elif op == "wn_a16":

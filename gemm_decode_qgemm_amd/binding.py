@@ -45,6 +45,7 @@ def _load() -> ctypes.CDLL:
         "qg_int4_packed_bytes": (I64, [I64, I64]),
         "qg_default_split_k": (I32, [I64, I64, I64]),
         "qg_default_split_k_intn": (I32, [I64, I64, I64]),
+        "qg_default_split_k_g32": (I32, [I64, I64, I64]),
         "qg_workspace_bytes": (I64, [I64, I64, I64, I32]),
         "qg_int4_dq_packed_bytes": (I64, [I64, I64]),
         "qg_intn_packed_bytes": (I64, [I64, I64, I32]),
@@ -119,12 +120,15 @@ def intn_packed_bytes(n: int, k: int, bits: int) -> int:
     return v
 
 
-def default_split_k(m: int, n: int, k: int, bits: int = 4) -> int:
-    """The library's split for split_k = 0: INT4 layouts (bits = 4), or INT5 / INT6."""
-    if bits == 4:
-        v = int(lib.qg_default_split_k(m, n, k))
-    else:
+def default_split_k(m: int, n: int, k: int, bits: int = 4, group_scales: bool = False) -> int:
+    """The library's split for split_k = 0: INT4 layouts (bits = 4; with
+    group_scales, W4A8 with one activation scale per group of 32), or INT5 / INT6."""
+    if bits != 4:
         v = int(lib.qg_default_split_k_intn(m, n, k))
+    elif group_scales:
+        v = int(lib.qg_default_split_k_g32(m, n, k))
+    else:
+        v = int(lib.qg_default_split_k(m, n, k))
     _check(min(v, 0), "qg_default_split_k")
     return v
 

@@ -185,8 +185,16 @@ int64_t qg_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k) {
   if (si > 1 && (int64_t)si * m > units) units = (int64_t)si * m;
   const int64_t bytes = units * n * 4;
   if (m <= 4) return bytes;
-  const int64_t w8 = w4a8_mfma_ws(m, n, k, split);
+  int64_t w8 = w4a8_mfma_ws(m, n, k, split);
+  const int64_t w8g = w4a8_mfma_ws(m, n, k, qg::default_split_g32(m, n, k));   // per group of 32
+  if (w8g > w8) w8 = w8g;
   return w8 > bytes ? w8 : bytes;
+}
+
+int32_t qg_default_split_k_g32(int64_t m, int64_t n, int64_t k) {
+  int32_t st = check_mnk(m, n, k);
+  if (st != QG_OK) return st;
+  return qg::default_split_g32(m, n, k);
 }
 
 int32_t qg_default_split_k_intn(int64_t m, int64_t n, int64_t k) {
@@ -402,7 +410,7 @@ int32_t qgemm_wn_a16(const void* x_bf16, int64_t m, int64_t k, int32_t bits, con
   if (bits != 5 && bits != 6) return QG_E_BITS;
   if (y_dtype != QG_BF16 && y_dtype != QG_F32) return QG_E_DTYPE;
   int32_t split;
-  st = resolve_split(m, n, k, split_k, &split, true);
+  st = resolve_split(m, n, k, split_k, &split, qg::SplitRule::kIntN);
   if (st != QG_OK) return st;
   if (packed_bytes < qg_intn_packed_bytes(n, k, bits)) return QG_E_BUFFER;
   const int64_t need_ws = split > 1 ? (int64_t)split * m * n * 4 : 0;
@@ -513,7 +521,7 @@ static int32_t w4a8_common(const void* x_bf16, int64_t m, int64_t k, const void*
     // workspace (xq exact in bf16, sx group-major), then the matrix-core
     // kernel scales each group's integer dot by s * sx, one weight pass.
     int32_t split;
-    st = resolve_split(m, n, k, split_k, &split);
+    st = resolve_split(m, n, k, split_k, &split, qg::SplitRule::kW4A8G32);
     if (st != QG_OK) return st;
     if (packed_bytes < (dq ? qg_int4_dq_packed_bytes(n, k) : qg_int4_packed_bytes(n, k))) return QG_E_BUFFER;
     if (!ws || ws_bytes < w4a8_mfma_ws(m, n, k, split)) return ws ? QG_E_BUFFER : QG_E_NULL;

@@ -72,10 +72,31 @@ inline int32_t default_split_intn(int64_t m, int64_t n, int64_t k) {
   return s;
 }
 
+// W4A8 with one activation scale per group of 32, M > 4: the matrix-core
+// kernels also load each group's activation scales and multiply them in, and
+// above 32 rows more splits pay than for W4A16 (measured, µs, best split
+// marked *: 39936 x 6656 M = 64: 126.5 at 1, 113.2* at 2; 8448 x 6656 M = 64:
+// 42.9 at 4, 41.0* at 8, M = 48: 40.6 / 38.7*; 6656 x 4096 M = 64: 22.8* at
+// 4, 27.8 at 8; the one loss, 6656 x 19968 M = 64: 67.8 at 4, 69.0 at 8):
+// the smallest split with 64-row blocks x split >= 1200, at most 8, with at
+// least 3 tiles of 256 k per split.  Up to 32 rows the W4A16 rule.
+inline int32_t default_split_g32(int64_t m, int64_t n, int64_t k) {
+  if (m <= 32) return default_split(m, n, k);
+  const int64_t kt = k / QG_TILE_K;
+  const int64_t rbs = (n + QG_TILE_ROWS - 1) / QG_TILE_ROWS;
+  int32_t s = 1;
+  while (s < 8 && kt >= 3 * (2 * s) && rbs * s < 1200) s *= 2;
+  return s;
+}
+
+enum class SplitRule { kW4, kIntN, kW4A8G32 };
+
 inline int32_t resolve_split(int64_t m, int64_t n, int64_t k, int32_t split_k, int32_t* out,
-                      bool intn = false) {
+                             SplitRule rule = SplitRule::kW4) {
   if (split_k == 0) {
-    *out = intn ? default_split_intn(m, n, k) : default_split(m, n, k);
+    *out = rule == SplitRule::kIntN     ? default_split_intn(m, n, k)
+           : rule == SplitRule::kW4A8G32 ? default_split_g32(m, n, k)
+                                         : default_split(m, n, k);
     return QG_OK;
   }
   if (split_k != 1 && split_k != 2 && split_k != 4 && split_k != 8) return QG_E_SPLIT;

@@ -123,12 +123,18 @@ int32_t qg_default_split_k(int64_t m, int64_t n, int64_t k);
  * still reaches 256.  Negative qg_status on bad arguments. */
 int32_t qg_default_split_k_intn(int64_t m, int64_t n, int64_t k);
 
+/* The split-K factor qgemm_w4a8_g32 and qgemm_w4a8_g32_dq use for
+ * split_k = 0: qg_default_split_k up to 32 rows; above 32 rows the smallest
+ * split with ceil(n/64) * split >= 1200, at most 8 and with at least 3 tiles
+ * of 256 k per split (these kernels also multiply in each group's activation
+ * scale, and more splits pay).  Negative qg_status on bad arguments. */
+int32_t qg_default_split_k_g32(int64_t m, int64_t n, int64_t k);
+
 /* Workspace bytes a qgemm call needs for (m, n, k, split_k): split * m * n * 4
  * (fp32 partial sums) when the split is above 1, else 0.  For split_k = 0
- * the largest need of the defaults is assumed (qg_default_split_k and
- * qg_default_split_k_intn at m rows, and for m > 4 also qg_default_split_k
- * at 4 rows, the per-group W4A8 slices), so one workspace serves every
- * entry point's default.  For m > 4 it also holds what the W4A8 entry
+ * the largest need of the defaults is assumed (qg_default_split_k,
+ * qg_default_split_k_intn and qg_default_split_k_g32 at m rows), so one
+ * workspace serves every entry point's default.  For m > 4 it also holds what the W4A8 entry
  * points need there: m * k * 2 bytes of quantized activations, max(256,
  * 8 * k) bytes of activation scales (per row, or per group of 32 as
  * k/32 x 64 floats) and split * m * n * 4 bytes of partial sums (at split 1

@@ -37,6 +37,7 @@ def lib():
         "qg_int4_packed_bytes": (I64, [I64, I64]),
         "qg_default_split_k": (I32, [I64, I64, I64]),
         "qg_default_split_k_intn": (I32, [I64, I64, I64]),
+        "qg_default_split_k_g32": (I32, [I64, I64, I64]),
         "qg_workspace_bytes": (I64, [I64, I64, I64, I32]),
         "qg_int4_dq_packed_bytes": (I64, [I64, I64]),
         "qg_intn_packed_bytes": (I64, [I64, I64, I32]),
@@ -148,9 +149,22 @@ def test_default_split_table(lib):
         assert lib.qg_default_split_k_intn(m, 4096, 5376) == 4
         assert lib.qg_default_split_k_intn(m, 1024, 6656) == 8
     assert lib.qg_default_split_k_intn(1, 5376, 21504) == lib.qg_default_split_k(1, 5376, 21504) == 1
+    # W4A8 per group of 32: the W4A16 rule up to 32 rows; above, row blocks x
+    # split >= 1200, at most 8, at least 3 tiles of 256 k per split
+    for m in (1, 4, 16, 32):
+        for n, k in ((39936, 6656), (8448, 6656), (6656, 19968), (6656, 4096)):
+            assert lib.qg_default_split_k_g32(m, n, k) == lib.qg_default_split_k(m, n, k), (m, n, k)
+    assert lib.qg_default_split_k_g32(64, 39936, 6656) == 2
+    assert lib.qg_default_split_k_g32(64, 8448, 6656) == 8
+    assert lib.qg_default_split_k_g32(48, 8448, 6656) == 8
+    assert lib.qg_default_split_k_g32(64, 6656, 19968) == 8
+    assert lib.qg_default_split_k_g32(64, 6656, 4096) == 4      # 3 tiles per split at most 8 / 2
+    assert lib.qg_default_split_k_g32(64, 256, 512) == 1        # 2 tiles: no split keeps 3
+    assert lib.qg_default_split_k_g32(65, 256, 256) == E_M
     assert lib.qg_default_split_k_intn(64, 256, 512) == 2                  # capped by K / 256
-    # one workspace serves both defaults
-    assert lib.qg_workspace_bytes(64, 5376, 21504, 0) == 8 * 64 * 5376 * 4
+    # one workspace serves every default: here per-group W4A8 at its split 8
+    # (quantized x, group scales, partials) needs the most
+    assert lib.qg_workspace_bytes(64, 5376, 21504, 0) == 64 * 21504 * 2 + 8 * 21504 + 8 * 64 * 5376 * 4
 
 
 @pytest.mark.parametrize("args,expect", [
@@ -290,18 +304,17 @@ def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
 
 @pytest.mark.parametrize("m", [5, 8, 16, 33, 64])
 @pytest.mark.parametrize("n,k", [(8448, 6656), (6656, 19968), (6656, 4096), (256, 6656), (768, 256)])
-def test_default_workspace_covers_w4a8_row_slices(lib, m, n, k):
-    """W4A8 at M > 4 runs slices of 4 rows with the 4-row default split; the
-    default workspace must hold that slice's partial sums too."""
+def test_default_workspace_covers_w4a8_above_4_rows(lib, m, n, k):
+    """At M > 4 both W4A8 forms put quantized x (bf16), the activation scales
+    (max(256, 8k) bytes) and the partial sums at their own default split in
+    the workspace; the split_k = 0 size must hold either."""
     ws = lib.qg_workspace_bytes(m, n, k, 0)
-    s4 = lib.qg_default_split_k(4, n, k)
-    assert ws >= (s4 * 4 * n * 4 if s4 > 1 else 0)
-    # per-row scales: quantized x (bf16), 256 bytes of row scales, partials
-    assert ws >= m * k * 2 + 256 + lib.qg_default_split_k(m, n, k) * m * n * 4
+    scales = max(256, 8 * k)
+    assert ws >= m * k * 2 + scales + lib.qg_default_split_k(m, n, k) * m * n * 4
+    assert ws >= m * k * 2 + scales + lib.qg_default_split_k_g32(m, n, k) * m * n * 4
     for split in (1, 2, 4, 8):
         if split <= k // 256:
-            assert lib.qg_workspace_bytes(m, n, k, split) >= (split * 4 * n * 4 if split > 1 else 0)
-            assert lib.qg_workspace_bytes(m, n, k, split) >= m * k * 2 + 256 + split * m * n * 4
+            assert lib.qg_workspace_bytes(m, n, k, split) >= m * k * 2 + scales + split * m * n * 4
 
 
 def test_noalloc_checks_before_anything(lib):
