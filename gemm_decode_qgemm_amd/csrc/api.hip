@@ -24,6 +24,8 @@ hipError_t launch_quantize_int4_g32_dq(const void* w, int64_t n, int64_t k, void
                                        uint32_t* status, hipStream_t stream);
 hipError_t launch_w4a16_gemv32_dq(int m, const void* x, const void* packed, int n, int k, void* y,
                                   int y_f32, float* partial, int split, hipStream_t stream);
+hipError_t launch_w4a16_gemv_dq(int m, const void* x, const void* packed, int n, int k, void* y,
+                                int y_f32, float* partial, int split, hipStream_t stream);
 hipError_t launch_w4a16_gemv_mx4_dq(int m, const void* x, const void* packed, int n, int k, void* y,
                                     int y_f32, float* partial, int split, hipStream_t stream);
 hipError_t launch_quantize_intn_g32(const void* w, int64_t n, int64_t k, int bits, void* packed,
@@ -387,13 +389,17 @@ int32_t qgemm_w4a16_dq(const void* x_bf16, int64_t m, int64_t k, const void* pac
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* partial = split > 1 ? static_cast<float*>(ws) : nullptr;
   // the kernels of qgemm_w4a16 reading the scale-code layout: M = 1 the
-  // v_dot2c GEMV, M = 2..4 the 4x4x4 matrix instruction, M = 5..64 the matrix cores
+  // v_dot2c GEMV (32- or 64-row workgroups by the same rule), M = 2..4 the
+  // 4x4x4 matrix instruction, M = 5..64 the matrix cores
   if (m > 4)
     st = hip_status(qg::launch_w4a16_mfma_dq((int)m, x_bf16, packed, (int)n, (int)k, y, y_dtype == QG_F32,
                                              partial, split, s));
   else if (m >= 2)
     st = hip_status(qg::launch_w4a16_gemv_mx4_dq((int)m, x_bf16, packed, (int)n, (int)k, y,
                                                  y_dtype == QG_F32, partial, split, s));
+  else if (gemv_shape(m, n, split).rows == 64)
+    st = hip_status(qg::launch_w4a16_gemv_dq((int)m, x_bf16, packed, (int)n, (int)k, y,
+                                             y_dtype == QG_F32, partial, split, s));
   else
     st = hip_status(qg::launch_w4a16_gemv32_dq((int)m, x_bf16, packed, (int)n, (int)k, y,
                                                y_dtype == QG_F32, partial, split, s));

@@ -90,10 +90,11 @@ __device__ __forceinline__ void group_dot(float& d0, float& d1, const u32x4_t& x
 }
 
 
-template <int M, int JJ>
+// DQ: the group's scale is its uint8 code times the row's step.
+template <int M, int JJ, bool DQ>
 __device__ __forceinline__ void do_group(float (&acc)[M], const HalfRegs& cur, const XHalf<M>& xc,
                                          const float (&xq)[M], const float (&zb)[4],
-                                         uint32_t mask_s, uint32_t magic_v) {
+                                         uint32_t mask_s, uint32_t magic_v, float step) {
   const u32x4_t cv = cur.c[JJ];
   const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
   uint32_t pr[16];
@@ -101,8 +102,13 @@ __device__ __forceinline__ void do_group(float (&acc)[M], const HalfRegs& cur, c
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[4 * d + i] = nibble_pair_bf16(cw[d], i, mask_s, magic_v);
-  const uint32_t sw = (JJ < 2) ? cur.sc.x : cur.sc.y;
-  const float s = fp16_to_f32((sw >> (16 * (JJ & 1))) & 0xffffu);
+  float s;
+  if constexpr (DQ) {
+    s = (float)((cur.sc.x >> (8 * JJ)) & 0xffu) * step;
+  } else {
+    const uint32_t sw = (JJ < 2) ? cur.sc.x : cur.sc.y;
+    s = fp16_to_f32((sw >> (16 * (JJ & 1))) & 0xffffu);
+  }
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     // The dot starts from -(128 + zp) * X_g, so it ends at sum x * (q - zp).
@@ -114,10 +120,10 @@ __device__ __forceinline__ void do_group(float (&acc)[M], const HalfRegs& cur, c
 }
 
 // One half tile: group sums of x, then 4 groups of dequant-dot-correct.
-template <int M>
+template <int M, bool DQ = false>
 __device__ __forceinline__ void half_compute(float (&acc)[M], const HalfRegs& cur,
                                              const XHalf<M>& xc, uint32_t mask_s,
-                                             uint32_t magic_v, uint32_t ones_v) {
+                                             uint32_t magic_v, uint32_t ones_v, float step = 1.0f) {
   // X_g: lane i of a row sums its 4 dwords (group i/4 of the half), then the
   // quad of lanes sharing a group adds up (DPP quad_perm [1,0,3,2], [2,3,0,1]).
   float xq[M];
@@ -138,17 +144,17 @@ __device__ __forceinline__ void half_compute(float (&acc)[M], const HalfRegs& cu
   const uint32_t z13 = ((cur.zw >> 4) & 0x0F0Fu) | 0x8080u;   // groups 1, 3
   const float zb[4] = {(float)(z02 & 0xffu), (float)(z13 & 0xffu), (float)(z02 >> 8),
                        (float)(z13 >> 8)};
-  do_group<M, 0>(acc, cur, xc, xq, zb, mask_s, magic_v);
-  do_group<M, 1>(acc, cur, xc, xq, zb, mask_s, magic_v);
-  do_group<M, 2>(acc, cur, xc, xq, zb, mask_s, magic_v);
-  do_group<M, 3>(acc, cur, xc, xq, zb, mask_s, magic_v);
+  do_group<M, 0, DQ>(acc, cur, xc, xq, zb, mask_s, magic_v, step);
+  do_group<M, 1, DQ>(acc, cur, xc, xq, zb, mask_s, magic_v, step);
+  do_group<M, 2, DQ>(acc, cur, xc, xq, zb, mask_s, magic_v, step);
+  do_group<M, 3, DQ>(acc, cur, xc, xq, zb, mask_s, magic_v, step);
 }
 
 // Work unit = half tile.  Wave w of a workgroup takes half tiles w, w+WAVES,
 // ... of its row block's split-K range: load, wait, compute (the other
 // resident waves keep the memory system busy; a register look-ahead of one or
 // two units measured no faster on MI355X).
-template <int M, int WAVES, bool PF = false>
+template <int M, int WAVES, bool PF = false, bool DQ = false>
 __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -160,7 +166,16 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
-  const uint8_t* tiles = packed + (size_t)rb * kt_count * kTileBytes;
+  constexpr int kTile = DQ ? kDqTileBytes : kTileBytes;
+  const uint8_t* tiles;
+  float step = 1.0f;
+  if constexpr (DQ) {   // the block's head holds each row's fp16 step
+    const uint8_t* block = packed + (size_t)rb * (kDqHeadBytes + (size_t)kt_count * kDqTileBytes);
+    step = fp16_to_f32(*reinterpret_cast<const uint16_t*>(block + 2 * lane));
+    tiles = block + kDqHeadBytes;
+  } else {
+    tiles = packed + (size_t)rb * kt_count * kTileBytes;
+  }
   const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
   const int k32 = k >> 1;
   const uint32_t mask_s = __builtin_amdgcn_readfirstlane(0x000F000Fu);
@@ -178,7 +193,7 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 
   auto load = [&](HalfRegs& r, XHalf<M>& xr, int hs) {   // tile hs/2, half hs%2
-    load_half(r, tiles + (size_t)(hs >> 1) * kTileBytes, hs & 1, lane);
+    load_half<DQ>(r, tiles + (size_t)(hs >> 1) * kTile, hs & 1, lane);
     load_xhalf<M>(xr, x32, k32, hs, li);
   };
   if constexpr (!PF) {
@@ -186,7 +201,7 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
       HalfRegs r;
       XHalf<M> xr;
       load(r, xr, hs);
-      half_compute<M>(acc, r, xr, mask_s, magic_v, ones_v);
+      half_compute<M, DQ>(acc, r, xr, mask_s, magic_v, ones_v, step);
     }
   } else {
     const int h_end = 2 * t1;
@@ -197,15 +212,15 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
       load(ra, xa, hs);
       __builtin_amdgcn_sched_barrier(0);
       while (true) {
-        if (hs + WAVES >= h_end) { half_compute<M>(acc, ra, xa, mask_s, magic_v, ones_v); break; }
+        if (hs + WAVES >= h_end) { half_compute<M, DQ>(acc, ra, xa, mask_s, magic_v, ones_v, step); break; }
         load(rb, xb, hs + WAVES);
         __builtin_amdgcn_sched_barrier(0);
-        half_compute<M>(acc, ra, xa, mask_s, magic_v, ones_v);
+        half_compute<M, DQ>(acc, ra, xa, mask_s, magic_v, ones_v, step);
         hs += WAVES;
-        if (hs + WAVES >= h_end) { half_compute<M>(acc, rb, xb, mask_s, magic_v, ones_v); break; }
+        if (hs + WAVES >= h_end) { half_compute<M, DQ>(acc, rb, xb, mask_s, magic_v, ones_v, step); break; }
         load(ra, xa, hs + WAVES);
         __builtin_amdgcn_sched_barrier(0);
-        half_compute<M>(acc, rb, xb, mask_s, magic_v, ones_v);
+        half_compute<M, DQ>(acc, rb, xb, mask_s, magic_v, ones_v, step);
         hs += WAVES;
       }
     }
@@ -526,19 +541,26 @@ hipError_t launch_splitk_reduce(const float* partial, int split, int64_t mn, voi
 #define QG_GEMV64_PF 1
 #endif
 
-template <int M, int WAVES>
+template <int M, int WAVES, bool DQ = false>
 static hipError_t launch_w4a16_t(const void* x, const void* packed, int n, int k, void* y,
                                  int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
   if (QG_GEMV64_PF && rbs * split <= kCUs)
-    hipLaunchKernelGGL((w4a16_gemv_kernel<M, WAVES, true>), dim3(rbs, split), dim3(WAVES * 64), 0,
+    hipLaunchKernelGGL((w4a16_gemv_kernel<M, WAVES, true, DQ>), dim3(rbs, split), dim3(WAVES * 64), 0,
                        stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
                        n, k, y, y_f32, partial, split);
   else
-    hipLaunchKernelGGL((w4a16_gemv_kernel<M, WAVES>), dim3(rbs, split), dim3(WAVES * 64), 0,
+    hipLaunchKernelGGL((w4a16_gemv_kernel<M, WAVES, false, DQ>), dim3(rbs, split), dim3(WAVES * 64), 0,
                        stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
                        n, k, y, y_f32, partial, split);
   return hipGetLastError();
+}
+
+// M = 1 on the scale-code layout, one 64-row block per workgroup.
+hipError_t launch_w4a16_gemv_dq(int m, const void* x, const void* packed, int n, int k, void* y,
+                                int y_f32, float* partial, int split, hipStream_t stream) {
+  if (m != 1) return hipErrorInvalidValue;
+  return launch_w4a16_t<1, 16, true>(x, packed, n, k, y, y_f32, partial, split, stream);
 }
 
 // M = 1 on either layout: half a 64-row block per workgroup, with the

@@ -50,13 +50,20 @@ struct BufView {
 // 128-byte lines, and the other half is read by another wave of the same
 // workgroup moments later: those loads keep the default (temporal) policy so
 // that wave hits in L2 instead of fetching the line from HBM again.
+// DQ (scale-code layout): sc.x holds the half's 4 uint8 scale codes instead.
+template <bool DQ = false>
 __device__ __forceinline__ void load_half(HalfRegs& r, const uint8_t* tile, int half, int lane) {
-  const BufView v(tile, kTileBytes);
+  const BufView v(tile, DQ ? kDqTileBytes : kTileBytes);
   const uint32_t co = (uint32_t)((4 * half * kTileRows + lane) * 16);
 #pragma unroll
   for (int j = 0; j < 4; ++j) r.c[j] = v.b128<true>(co + j * (kTileRows * 16));
-  r.sc = v.b64((uint32_t)(kScaleOff + lane * 16 + 8 * half));
-  r.zw = v.b16((uint32_t)(kZeroOff + lane * 4 + 2 * half));
+  if constexpr (DQ) {
+    r.sc = u32x2_t{v.b32((uint32_t)(kDqScodeOff + lane * 8 + 4 * half)), 0u};
+    r.zw = v.b16((uint32_t)(kDqZeroOff + lane * 4 + 2 * half));
+  } else {
+    r.sc = v.b64((uint32_t)(kScaleOff + lane * 16 + 8 * half));
+    r.zw = v.b16((uint32_t)(kZeroOff + lane * 4 + 2 * half));
+  }
 }
 
 // The 32-row mapping: a workgroup owns rows [32h, 32h + 32) of a 64-row block

@@ -186,6 +186,34 @@ def test_w4a16_dq_prefetch_grid_non_finite_row(dev):
     assert torch.isfinite(torch.cat([y[0, :70], y[0, 71:]])).all()
 
 
+def test_w4a16_dq_64_row_workgroups_ragged_n(dev):
+    """N = 8200 at M = 1: one split takes 64-row workgroups (129, the last with
+    8 live rows), two splits 32-row ones; both read each row's step from its
+    block's head."""
+    n, k = 8200, 512
+    w, codes, scode, sstep, zeros = _weight(n, k, 46)
+    packed = qg.quantize_int4_g32_dq(w.to(dev))
+    x = si.activation(1, k, 61)
+    ref = _ref(x, codes, scode, sstep, zeros)
+    print("qgemm_w4a16_dq 64-row workgroups N=8200", flush=True)
+    for split in (1, 2):
+        for dt in (torch.float32, torch.bfloat16):
+            y = qg.qgemm_w4a16_dq(x.to(dev), packed, n, split_k=split, out_dtype=dt)
+            assert_w16(y, ref, f"N=8200 split={split} {dt}")
+
+
+def test_w4a16_dq_64_row_workgroups_non_finite_row(dev):
+    """8448 rows (64-row workgroups at M = 1): a non-finite weight in row 8400
+    of the last block makes only y[8400] NaN."""
+    n, k = 8448, 256
+    w = si.int4_weight(n, k, 8).clone()
+    w[8400, 3] = float("-inf")
+    packed = qg.quantize_int4_g32_dq(w.to(dev))
+    y = qg.qgemm_w4a16_dq(si.activation(1, k, 9).to(dev), packed, n, out_dtype=torch.float32).cpu()
+    assert torch.isnan(y[0, 8400])
+    assert torch.isfinite(torch.cat([y[0, :8400], y[0, 8401:]])).all()
+
+
 def test_w4a16_dq_repeat_and_graph_replay_are_bit_identical(dev):
     n, k = 8448, 6656
     w, *_ = _weight(n, k, si.model_weight_seed(n, k))
