@@ -424,7 +424,9 @@ __device__ __forceinline__ uint32_t wide_pair(const WnRegs<HB>& r, int jj, int d
   return nibble_pair_bf16(r.c[jj][d], i, mask_s, magic_v) | (WnLayout<HB>::high(r, jj, d, i) << 4);
 }
 
-template <int HB, int WAVES>
+// PF: the two-register-set loop of w4a16_gemv32_kernel, for grids of at most
+// one workgroup per CU.
+template <int HB, int WAVES, bool PF = false>
 __global__ __launch_bounds__(WAVES * 64) void wn_a16_gemv32_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
@@ -448,11 +450,11 @@ __global__ __launch_bounds__(WAVES * 64) void wn_a16_gemv32_kernel(
   asm volatile("" : "+v"(ones_v));
 
   float acc = 0.0f;
-  for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {
-    WnRegs<HB> r;
+  auto load = [&](WnRegs<HB>& r, u32x2_t& xv, int hs) {
     L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
-    const u32x2_t xv = BufView(x32 + (size_t)hs * 64, 256).b64((uint32_t)(32 * lg + 2 * li) * 4u);
-    __builtin_amdgcn_sched_barrier(0);   // every load of the step issued before the first wait
+    xv = BufView(x32 + (size_t)hs * 64, 256).b64((uint32_t)(32 * lg + 2 * li) * 4u);
+  };
+  auto compute = [&](const WnRegs<HB>& r, const u32x2_t& xv) {
     float p = dot2_bf16(xv.x, ones_v, 0.0f);
     p = dot2_bf16(xv.y, ones_v, p);
     p += dpp_mov<0xB1>(p);
@@ -478,6 +480,37 @@ __global__ __launch_bounds__(WAVES * 64) void wn_a16_gemv32_kernel(
         group_dot_2r<1>(d0, d1, xv, pr);
       acc = __builtin_fmaf(jj == 0 ? s0 : s1, d0 + d1, acc);
     }
+  };
+
+  if constexpr (!PF) {
+    for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {
+      WnRegs<HB> r;
+      u32x2_t xv;
+      load(r, xv, hs);
+      __builtin_amdgcn_sched_barrier(0);   // every load of the step issued before the first wait
+      compute(r, xv);
+    }
+  } else {
+    const int h_end = 2 * t1;
+    int hs = 2 * t0 + wave;
+    if (hs < h_end) {                                    // uniform
+      WnRegs<HB> ra, rb;
+      u32x2_t xa, xb;
+      load(ra, xa, hs);
+      __builtin_amdgcn_sched_barrier(0);
+      while (true) {
+        if (hs + WAVES >= h_end) { compute(ra, xa); break; }
+        load(rb, xb, hs + WAVES);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(ra, xa);
+        hs += WAVES;
+        if (hs + WAVES >= h_end) { compute(rb, xb); break; }
+        load(ra, xa, hs + WAVES);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(rb, xb);
+        hs += WAVES;
+      }
+    }
   }
 
   red[wave * 64 + lane] = acc;
@@ -501,19 +534,27 @@ __global__ __launch_bounds__(WAVES * 64) void wn_a16_gemv32_kernel(
   }
 }
 
-hipError_t launch_wn_a16_gemv32(int bits, const void* x, const void* packed, int n, int k, void* y,
-                                int y_f32, float* partial, int split, hipStream_t stream) {
+template <int HB>
+static hipError_t launch_wn_t(const void* x, const void* packed, int n, int k, void* y, int y_f32,
+                              float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
   const dim3 grid(2 * rbs, split), block(16 * 64);
-  if (bits == 5)
-    hipLaunchKernelGGL((wn_a16_gemv32_kernel<1, 16>), grid, block, 0, stream, static_cast<const uint16_t*>(x),
-                       static_cast<const uint8_t*>(packed), n, k, y, y_f32, partial, split);
-  else if (bits == 6)
-    hipLaunchKernelGGL((wn_a16_gemv32_kernel<2, 16>), grid, block, 0, stream, static_cast<const uint16_t*>(x),
-                       static_cast<const uint8_t*>(packed), n, k, y, y_f32, partial, split);
+  const auto* xs = static_cast<const uint16_t*>(x);
+  const auto* ps = static_cast<const uint8_t*>(packed);
+  if (2 * rbs * split <= kCUs)
+    hipLaunchKernelGGL((wn_a16_gemv32_kernel<HB, 16, true>), grid, block, 0, stream, xs, ps, n, k, y, y_f32,
+                       partial, split);
   else
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((wn_a16_gemv32_kernel<HB, 16>), grid, block, 0, stream, xs, ps, n, k, y, y_f32, partial,
+                       split);
   return hipGetLastError();
+}
+
+hipError_t launch_wn_a16_gemv32(int bits, const void* x, const void* packed, int n, int k, void* y,
+                                int y_f32, float* partial, int split, hipStream_t stream) {
+  if (bits == 5) return launch_wn_t<1>(x, packed, n, k, y, y_f32, partial, split, stream);
+  if (bits == 6) return launch_wn_t<2>(x, packed, n, k, y, y_f32, partial, split, stream);
+  return hipErrorInvalidValue;
 }
 
 // Second split-K pass: y = sum over s (ascending) of partial[s], no atomics.
