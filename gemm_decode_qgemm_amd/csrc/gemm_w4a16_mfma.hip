@@ -163,28 +163,25 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
   // zero points: lane l loads those of row l only (one 8-byte and one 2-byte
   // load per half tile; per n-tile loads with 4 lanes per row cost a quarter
   // of the kernel's time); compute() hands row 16t + i to lane (i, a).
+  // Through a buffer view of the (wave-uniform) tile: 32-bit lane offsets.
   auto load_w = [&](MfmaUnit<MT, HB, AS>& u, int hs) {
-    const uint8_t* tile = tiles + (size_t)(hs >> 1) * T::kBytes;
+    const BufView v(tiles + (size_t)(hs >> 1) * T::kBytes, T::kBytes);
     const int half = hs & 1;
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-      u.w[t] = load_stream<true>(
-          reinterpret_cast<const u32x4_t*>(tile + ((4 * half + a) * kTileRows + 16 * t + i) * 16));
-      if constexpr (HB == 1)
-        u.hp[t].x = load_stream<true>(
-            reinterpret_cast<const uint32_t*>(tile + 8192 + ((4 * half + a) * kTileRows + 16 * t + i) * 4));
-      if constexpr (HB == 2)
-        u.hp[t] = load_stream<true>(
-            reinterpret_cast<const u32x2_t*>(tile + 8192 + ((4 * half + a) * kTileRows + 16 * t + i) * 8));
+      const uint32_t r = (uint32_t)((4 * half + a) * kTileRows + 16 * t + i);
+      u.w[t] = v.b128<true>(r * 16u);
+      if constexpr (HB == 1) u.hp[t].x = v.b32<true>(8192u + r * 4u);
+      if constexpr (HB == 2) u.hp[t] = v.b64<true>(8192u + r * 8u);
     }
     if constexpr (DQ)
-      u.scl = u32x2_t{load_stream<false>(reinterpret_cast<const uint32_t*>(tile + T::kScale + lane * 8 + 4 * half)), 0u};
+      u.scl = u32x2_t{v.b32((uint32_t)(T::kScale + lane * 8 + 4 * half)), 0u};
     else
-      u.scl = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + T::kScale + lane * 16 + 8 * half));
+      u.scl = v.b64((uint32_t)(T::kScale + lane * 16 + 8 * half));
     if constexpr (HB == 0)
-      u.zwl = load_stream<false>(reinterpret_cast<const uint16_t*>(tile + T::kZero + lane * 4 + 2 * half));
+      u.zwl = v.b16((uint32_t)(T::kZero + lane * 4 + 2 * half));
     else
-      u.zwl = load_stream<false>(reinterpret_cast<const uint32_t*>(tile + T::kZero + lane * 8 + 4 * half));
+      u.zwl = v.b32((uint32_t)(T::kZero + lane * 8 + 4 * half));
   };
   // Rows of x at or past m read row m - 1 instead (a valid address, no
   // branch and no select): output row r of an MFMA depends on row r of its A
@@ -414,30 +411,31 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
                                          16, 0, 0);
     }
   };
+  // Through a buffer view of the (uniform) tile: 32-bit lane offsets.
   auto load_w = [&](Mfma2W<HB>& w, int kt) {
-    const uint8_t* tile = tiles + (size_t)kt * T::kBytes;
-    w.c0 = load_stream<true>(reinterpret_cast<const u32x4_t*>(tile + (a * kTileRows + 16 * t + i) * 16));
-    w.c1 = load_stream<true>(reinterpret_cast<const u32x4_t*>(tile + ((4 + a) * kTileRows + 16 * t + i) * 16));
+    const BufView v(tiles + (size_t)kt * T::kBytes, T::kBytes);
+    const uint32_t r0 = (uint32_t)(a * kTileRows + 16 * t + i), r1 = r0 + 4 * kTileRows;
+    const uint32_t row = (uint32_t)(16 * t + i);
+    w.c0 = v.b128<true>(r0 * 16u);
+    w.c1 = v.b128<true>(r1 * 16u);
     if constexpr (HB == 1) {
-      w.h0.x = load_stream<true>(reinterpret_cast<const uint32_t*>(tile + 8192 + (a * kTileRows + 16 * t + i) * 4));
-      w.h1.x = load_stream<true>(
-          reinterpret_cast<const uint32_t*>(tile + 8192 + ((4 + a) * kTileRows + 16 * t + i) * 4));
+      w.h0.x = v.b32<true>(8192u + r0 * 4u);
+      w.h1.x = v.b32<true>(8192u + r1 * 4u);
     }
     if constexpr (HB == 2) {
-      w.h0 = load_stream<true>(reinterpret_cast<const u32x2_t*>(tile + 8192 + (a * kTileRows + 16 * t + i) * 8));
-      w.h1 = load_stream<true>(
-          reinterpret_cast<const u32x2_t*>(tile + 8192 + ((4 + a) * kTileRows + 16 * t + i) * 8));
+      w.h0 = v.b64<true>(8192u + r0 * 8u);
+      w.h1 = v.b64<true>(8192u + r1 * 8u);
     }
     if constexpr (DQ) {
-      const u32x2_t c8 = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + T::kScale + (16 * t + i) * 8));
+      const u32x2_t c8 = v.b64((uint32_t)T::kScale + row * 8u);
       w.sc = u32x4_t{c8.x, c8.y, 0u, 0u};
     } else {
-      w.sc = load_stream<false>(reinterpret_cast<const u32x4_t*>(tile + T::kScale + (16 * t + i) * 16));
+      w.sc = v.b128<false>((uint32_t)T::kScale + row * 16u);
     }
     if constexpr (HB == 0)
-      w.zw.x = load_stream<false>(reinterpret_cast<const uint32_t*>(tile + T::kZero + (16 * t + i) * 4));
+      w.zw.x = v.b32((uint32_t)T::kZero + row * 4u);
     else
-      w.zw = load_stream<false>(reinterpret_cast<const u32x2_t*>(tile + T::kZero + (16 * t + i) * 8));
+      w.zw = v.b64((uint32_t)T::kZero + row * 8u);
   };
   // Every wave's copies into LDS must have landed before the barrier that
   // hands the buffer to the other waves.
