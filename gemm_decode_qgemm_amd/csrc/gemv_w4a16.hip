@@ -9,10 +9,17 @@
 // convert costs the GEMV its bandwidth.
 //
 // Mapping (gfx950, wave64):
-//  * a workgroup owns one 64-row block and one split-K range of 256-k tiles;
-//    lane r of every wave owns row r, waves take tiles round robin, so each
-//    wave streams whole tiles: 10 loads of 16/4 B per lane, every one a run of
-//    whole 128-byte lines;
+//  * a workgroup owns one 64-row block (or, in the 32-row variant below, half
+//    of one) and one split-K range of 256-k tiles; lane r of every wave owns
+//    row r, waves take half tiles round robin: per half tile and lane 4 code
+//    chunks of 16 B, the scales and the zero nibbles, each wave-wide load a
+//    run of whole 128-byte lines, all through a buffer view of the tile (a
+//    descriptor built in scalar registers from the tile's address, 32-bit
+//    lane offsets: no vector address arithmetic);
+//  * where the grid has at most one workgroup per CU a wave keeps two register
+//    sets and loads the next half tile while it computes the current one;
+//  * both packed layouts: fp16 scales (v1) or uint8 scale codes times the
+//    row's fp16 step (v2, scale codes);
 //  * x is the same for all 64 lanes, so each lane keeps only 1/16 of a tile's
 //    x in VGPRs (two 16-byte loads per row m per tile, L2-resident) and
 //    v_dot2c_f32_bf16 takes the x pair it needs from the lane that holds it
@@ -151,9 +158,10 @@ __device__ __forceinline__ void half_compute(float (&acc)[M], const HalfRegs& cu
 }
 
 // Work unit = half tile.  Wave w of a workgroup takes half tiles w, w+WAVES,
-// ... of its row block's split-K range: load, wait, compute (the other
-// resident waves keep the memory system busy; a register look-ahead of one or
-// two units measured no faster on MI355X).
+// ... of its row block's split-K range: load, wait, compute, the other
+// resident waves keeping the memory system busy.  PF: the two-register-set
+// loop, for grids of at most one workgroup per CU (8448 x 6656: 8.77 -> 8.69
+// us; 12288 x 4096: 7.09 -> 6.92).  DQ: the scale-code layout.
 template <int M, int WAVES, bool PF = false, bool DQ = false>
 __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
@@ -254,7 +262,7 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
 // groups {0,1} of each half tile for rows 0-31, lanes 32-63 groups {2,3}; each
 // wave-wide code load is two runs of 512 contiguous bytes.  x of a half tile
 // sits 2 dwords per lane: DPP rows 0-1 hold groups {0,1}, rows 2-3 {2,3}
-// (Half32Regs / load_half32 in w4_common.h).
+// (Half32Regs / W4Layout::load in w4_common.h).
 #define QG_DOT16_2R(L0, L1, L2, L3, L4, L5, L6, L7)                                       \
   "s_nop 1\n\t"                                                                            \
   QG_DPP_DOT("%0", "%2", "%4", L0) QG_DPP_DOT("%1", "%3", "%5", L0)                        \

@@ -1,6 +1,7 @@
-// w4_common.h -- pieces shared by the kernels that read the packed INT4
-// group-32 weight (layout v1, include/qgemm.h): the per-lane half-tile load,
-// the split-K partition and a DPP move helper.  Internal header.
+// w4_common.h -- pieces shared by the kernels that read the packed weights
+// (include/qgemm.h: INT4 layout v1, scale codes v2, INT5 / INT6): the raw
+// buffer view the loads go through, the per-lane half-tile loads of each
+// layout, the split-K partition and a DPP move helper.  Internal header.
 #pragma once
 
 #include "qg_common.h"
