@@ -1,6 +1,6 @@
 // dispatch.h -- host-side dispatch rules of the C ABI (include/qgemm.h):
 // the split-K table for split_k = 0 and the GEMV workgroup shape, measured
-// on MI355X.  Internal header, included by api.hip only.
+// on MI355X.  Internal header of the host-side launch code.
 #pragma once
 
 #include <stdint.h>
@@ -41,17 +41,20 @@ inline int32_t default_split(int64_t m, int64_t n, int64_t k) {
   return s;
 }
 
-// Workgroup shape of the M <= 4 INT4 GEMVs: 32 rows and 16 waves, except
-// where the 32-row grid spills a few workgroups into a second round over the
-// CUs while the 64-row grid fits in one (N = 8448: 264 against 132
-// workgroups; 9.1 us against 10.2 at M = 1), for M = 1 and one split (at
-// M = 2 the matrix-instruction GEMV on 32 rows is as fast: 10.7 us).
+// Workgroup shape of the M <= 4 GEMVs: 32 rows and 16 waves, except with one
+// split where the 32-row grid spills a few workgroups into a second round
+// over the CUs while the 64-row grid fits in one (N = 8448: 264 against 132
+// workgroups; M = 1: 9.1 us against 10.2).  The M = 2..4 matrix-instruction
+// GEMV places two 32-row workgroups per CU, so once most CUs hold two its
+// 32-row form wins again (measured, us, 64 / 32 rows: 8448 x 6656 M = 4
+// 10.07 / 10.65, 10240 x 5120 M = 2 8.66 / 8.90, 12288 x 4096 M = 4 8.09 /
+// 7.95, 16384 x 6656 M = 4 12.33 / 11.86): there 64 rows up to 160 blocks.
 struct GemvShape {
   int rows, waves;
 };
 inline GemvShape gemv_shape(int64_t m, int64_t n, int32_t split) {
   const int64_t n32 = (n + 31) / 32, n64 = (n + 63) / 64;
-  if (m == 1 && split == 1 && n32 > kCUs && n64 <= kCUs) return {64, 16};
+  if (split == 1 && n32 > kCUs && n64 <= (m == 1 ? kCUs : kCUs * 5 / 8)) return {64, 16};
   return {32, 16};
 }
 

@@ -31,7 +31,14 @@
 //    give D[m] = sum x (128 + q); then acc[m] += s (D[m] - (128 + zp) X_g[m]).
 // A rows at or above M repeat row M - 1: their results land in result
 // registers that are never read, so no masking is needed.
+// With one split and a little over one 32-row workgroup per CU (N = 8448:
+// 264, leaving a few CUs with two and the rest with one), the kernel takes
+// whole 64-row blocks instead (132 workgroups): lane = row, each lane
+// loads both group pairs of its row and takes the half tile's 4 groups in
+// turn, and with one workgroup per CU it keeps the next half tile's loads in
+// flight in a second register set (the rule is in dispatch.h).
 #include "qg_common.h"
+#include "dispatch.h"
 #include "w4_common.h"
 
 namespace qg {
@@ -61,19 +68,22 @@ constexpr int kMx4PairBytes = 144;
 
 // 8 waves per SIMD (two 16-wave workgroups per CU) keep enough weight loads
 // in flight; the kernel fits the 64 VGPRs that allows without spilling.
-template <int M, int WAVES, class L>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8))) void w4a16_gemv_mx4_kernel(
+// R64: one 64-row block per workgroup, one workgroup per CU, so 128 VGPRs and
+// two register sets in turn (the next half tile's loads in flight while the
+// current one is computed).
+template <int M, int WAVES, class L, bool R64 = false>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(R64 ? 4 : 8))) void w4a16_gemv_mx4_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[WAVES][M * kMx4RowBytes];
   __shared__ __attribute__((aligned(16))) float xsum[WAVES][4][4];   // [group][m]
   __shared__ float red[WAVES * M * 64];
   const int lane = threadIdx.x & 63;
-  const int lg = lane >> 5;                        // group pair of this lane
+  const int lg = R64 ? 0 : lane >> 5;              // group pair of this lane (R64: both, in turn)
   const int xrow = (lane & 3) < M ? (lane & 3) : M - 1;   // A row of this lane
   const int wave = wave_id_uniform();
-  const int rb = blockIdx.x >> 1;                  // 64-row block
-  const int row = 32 * (blockIdx.x & 1) + (lane & 31);
+  const int rb = R64 ? blockIdx.x : blockIdx.x >> 1;       // 64-row block
+  const int row = R64 ? lane : 32 * (blockIdx.x & 1) + (lane & 31);
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
@@ -96,11 +106,15 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8)))
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 
-  for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {   // tile hs/2, half hs%2
-    typename L::Regs r;
-    L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
-    u32x4_t xv = {0u, 0u, 0u, 0u};
+  constexpr int NP = R64 ? 2 : 1;   // group pairs per lane
+  using Regs = typename L::Regs;
+  auto load = [&](Regs (&r)[NP], u32x4_t& xv, int hs) {   // tile hs/2, half hs%2
+#pragma unroll
+    for (int p = 0; p < NP; ++p) L::load(r[p], tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg + p, row);
+    xv = u32x4_t{0u, 0u, 0u, 0u};
     if (stager) xv = *reinterpret_cast<const u32x4_t*>(xsrc + (size_t)hs * 128);
+  };
+  auto compute = [&](const Regs (&r)[NP], const u32x4_t& xv) {
     // Group sums of x: 8 k per stager lane, then the 4 lanes of a group.
     float xp = dot2_bf16(xv.x, ones_v, 0.0f);
     xp = dot2_bf16(xv.y, ones_v, xp);
@@ -122,46 +136,84 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8)))
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // One group at a time: 8 A reads, x[xrow][32 (2 lg + jj) + 8 q .. + 8]
-    // (two k-steps each), 8 chained products, the group's epilogue.
+    // One group at a time: 8 A reads, x[xrow][32 (2 pr + jj) + 8 q .. + 8]
+    // for group pair pr = lg + p (two k-steps each), 8 chained products, the
+    // group's epilogue.
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       u32x4_t xa[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        xa[q] = *reinterpret_cast<const u32x4_t*>(slot + srd + 64 * jj + 16 * q);
+        xa[q] = *reinterpret_cast<const u32x4_t*>(slot + srd + p * kMx4PairBytes + 64 * jj + 16 * q);
       f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
       // k-step t covers k = 4t..4t+3 of the group: code dword t/2, pairs
       // 2(t%2) and 2(t%2)+1; x dwords 2t, 2t+1.
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const u32x2_t b = {L::pair(r, jj, t >> 1, 2 * (t & 1), mask_s, magic_v),
-                           L::pair(r, jj, t >> 1, 2 * (t & 1) + 1, mask_s, magic_v)};
+        const u32x2_t b = {L::pair(r[p], jj, t >> 1, 2 * (t & 1), mask_s, magic_v),
+                           L::pair(r[p], jj, t >> 1, 2 * (t & 1) + 1, mask_s, magic_v)};
         const u32x4_t xq = xa[t >> 1];
         const u32x2_t a = (t & 1) ? u32x2_t{xq.z, xq.w} : u32x2_t{xq.x, xq.y};
         d = mfma_4x4x4(a, b, d);
       }
-      const float s = L::scale(r.sc, jj, step);
-      const f32x4_t xg = *reinterpret_cast<const f32x4_t*>(&xsum[wave][2 * lg + jj][0]);
-      const float zb = (float)(L::zero(r, jj) | 0x80u);   // 128 + zp (zp <= 63)
+      const float s = L::scale(r[p].sc, jj, step);
+      const f32x4_t xg = *reinterpret_cast<const f32x4_t*>(&xsum[wave][2 * (lg + p) + jj][0]);
+      const float zb = (float)(L::zero(r[p], jj) | 0x80u);   // 128 + zp (zp <= 63)
 #pragma unroll
       for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(s, __builtin_fmaf(-zb, xg[m], d[m]), acc[m]);
     }
+  };
+
+  if constexpr (!R64) {
+    for (int hs = 2 * t0 + wave; hs < 2 * t1; hs += WAVES) {
+      Regs r[NP];
+      u32x4_t xv;
+      load(r, xv, hs);
+      compute(r, xv);
+    }
+  } else {
+    // One workgroup per CU: two register sets used in turn, the next half
+    // tile's loads in flight while the current one is computed (scheduling
+    // barriers keep the compiler from sinking the loads).
+    const int h_end = 2 * t1;
+    int hs = 2 * t0 + wave;
+    if (hs < h_end) {                                    // uniform
+      Regs ra[NP], rb_[NP];
+      u32x4_t xa, xb;
+      load(ra, xa, hs);
+      __builtin_amdgcn_sched_barrier(0);
+      while (true) {
+        if (hs + WAVES >= h_end) { compute(ra, xa); break; }
+        load(rb_, xb, hs + WAVES);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(ra, xa);
+        hs += WAVES;
+        if (hs + WAVES >= h_end) { compute(rb_, xb); break; }
+        load(ra, xa, hs + WAVES);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(rb_, xb);
+        hs += WAVES;
+      }
+    }
   }
 
-  // Sum over waves and over the two lane halves (same row), in a fixed order.
+  // Sum over waves and (32-row form) over the two lane halves of a row, in a
+  // fixed order.
 #pragma unroll
   for (int m = 0; m < M; ++m) red[(wave * M + m) * 64 + lane] = acc[m];
   __syncthreads();
   const int t = threadIdx.x;
-  if (t < 32 * M) {
-    const int m = t >> 5, l = t & 31;
+  constexpr int RW = R64 ? 64 : 32;   // output rows of the workgroup
+  if (t < RW * M) {
+    const int m = t / RW, l = t % RW;
     float v = 0.0f;
     for (int w = 0; w < WAVES; ++w) {
       v += red[(w * M + m) * 64 + l];
-      v += red[(w * M + m) * 64 + l + 32];
+      if constexpr (!R64) v += red[(w * M + m) * 64 + l + 32];
     }
-    const int col = rb * kTileRows + 32 * (blockIdx.x & 1) + l;
+    const int col = R64 ? rb * kTileRows + l : rb * kTileRows + 32 * (blockIdx.x & 1) + l;
     if (col < n) {
       if (partial != nullptr)
         partial[((size_t)blockIdx.y * M + m) * n + col] = v;
@@ -177,9 +229,14 @@ template <int M, int WAVES, class L>
 static hipError_t launch_mx4_t(const void* x, const void* packed, int n, int k, void* y, int y_f32,
                                float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a16_gemv_mx4_kernel<M, WAVES, L>), dim3(2 * rbs, split), dim3(WAVES * 64), 0,
-                     stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
-                     n, k, y, y_f32, partial, split);
+  if (gemv_shape(M, n, split).rows == 64)
+    hipLaunchKernelGGL((w4a16_gemv_mx4_kernel<M, WAVES, L, true>), dim3(rbs, split), dim3(WAVES * 64), 0,
+                       stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
+                       n, k, y, y_f32, partial, split);
+  else
+    hipLaunchKernelGGL((w4a16_gemv_mx4_kernel<M, WAVES, L>), dim3(2 * rbs, split), dim3(WAVES * 64), 0,
+                       stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
+                       n, k, y, y_f32, partial, split);
   return hipGetLastError();
 }
 

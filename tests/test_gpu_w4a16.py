@@ -170,8 +170,9 @@ def test_w4a16_every_split(dev, m):
 @pytest.mark.parametrize("m", [1, 2, 3, 4])
 def test_w4a16_both_workgroup_shapes_ragged_n(dev, m):
     """N = 8200 (8200 % 64 = 8): 257 workgroups of 32 rows or 129 of 64.  With
-    one split and M <= 2 the library takes the 64-row GEMV, otherwise the
-    32-row one; both must mask the 8-row tail and match the oracle."""
+    one split the library takes 64-row workgroups (M = 1 the v_dot2c GEMV,
+    M = 2..4 the matrix-instruction one), with two splits 32-row ones; both
+    must mask the 8-row tail and match the oracle."""
     n, k = 8200, 512
     w, codes, scales, zeros = _weight(n, k, 44)
     packed = _gpu_packed(w, dev)
@@ -181,6 +182,20 @@ def test_w4a16_both_workgroup_shapes_ragged_n(dev, m):
         for dt in (torch.float32, torch.bfloat16):
             y = qg.qgemm_w4a16(x.to(dev), packed, n, split_k=split, out_dtype=dt)
             assert_w16(y, ref, f"N=8200 M={m} split={split} {dt}")
+
+
+@pytest.mark.parametrize("m", [2, 4])
+def test_w4a16_64_row_workgroups_non_finite_row(dev, m):
+    """8448 rows at M = 2..4 and one split (64-row matrix-instruction
+    workgroups): a non-finite weight in row 8400 of the last block makes only
+    column 8400 of y NaN, in every activation row."""
+    n, k = 8448, 256
+    w = si.int4_weight(n, k, 8).clone()
+    w[8400, 3] = float("-inf")
+    packed = _gpu_packed(w, dev)
+    y = qg.qgemm_w4a16(si.activation(m, k, 9).to(dev), packed, n, split_k=1, out_dtype=torch.float32).cpu()
+    assert torch.isnan(y[:, 8400]).all()
+    assert torch.isfinite(torch.cat([y[:, :8400], y[:, 8401:]], dim=1)).all()
 
 
 @pytest.mark.parametrize("n", [4097, 5000, 6600, 8191, 8192, 8193])

@@ -186,20 +186,21 @@ def test_w4a16_dq_prefetch_grid_non_finite_row(dev):
     assert torch.isfinite(torch.cat([y[0, :70], y[0, 71:]])).all()
 
 
-def test_w4a16_dq_64_row_workgroups_ragged_n(dev):
-    """N = 8200 at M = 1: one split takes 64-row workgroups (129, the last with
-    8 live rows), two splits 32-row ones; both read each row's step from its
-    block's head."""
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_w4a16_dq_64_row_workgroups_ragged_n(dev, m):
+    """N = 8200 at M = 1..4: one split takes 64-row workgroups (129, the last
+    with 8 live rows; M >= 2 on the matrix instruction), two splits 32-row
+    ones; both read each row's step from its block's head."""
     n, k = 8200, 512
     w, codes, scode, sstep, zeros = _weight(n, k, 46)
     packed = qg.quantize_int4_g32_dq(w.to(dev))
-    x = si.activation(1, k, 61)
+    x = si.activation(m, k, 61 + m)
     ref = _ref(x, codes, scode, sstep, zeros)
-    print("qgemm_w4a16_dq 64-row workgroups N=8200", flush=True)
+    print(f"qgemm_w4a16_dq 64-row workgroups N=8200 M={m}", flush=True)
     for split in (1, 2):
         for dt in (torch.float32, torch.bfloat16):
             y = qg.qgemm_w4a16_dq(x.to(dev), packed, n, split_k=split, out_dtype=dt)
-            assert_w16(y, ref, f"N=8200 split={split} {dt}")
+            assert_w16(y, ref, f"N=8200 M={m} split={split} {dt}")
 
 
 def test_w4a16_dq_64_row_workgroups_non_finite_row(dev):

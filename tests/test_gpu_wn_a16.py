@@ -149,6 +149,24 @@ def test_wn_a16_every_split_uneven(dev, bits, m):
 
 
 @pytest.mark.parametrize("bits", [5, 6])
+@pytest.mark.parametrize("m", [2, 3, 4])
+def test_wn_a16_64_row_workgroups_ragged_n(dev, bits, m):
+    """N = 8200 (8200 % 64 = 8) at M = 2..4: one split takes 64-row
+    matrix-instruction workgroups (129, the last with 8 live rows), two
+    splits 32-row ones."""
+    n, k = 8200, 512
+    w, codes, scales, zeros = _weight(n, k, bits, 48 + bits)
+    packed = qg.quantize_intn_g32(w.to(dev), bits)
+    x = si.activation(m, k, 62 + bits + m)
+    ref = _ref(x, codes, scales, zeros)
+    print(f"qgemm_wn_a16 INT{bits} 64-row workgroups N=8200 M={m}", flush=True)
+    for split in (1, 2):
+        for dt in (torch.float32, torch.bfloat16):
+            y = qg.qgemm_wn_a16(x.to(dev), packed, n, bits, split_k=split, out_dtype=dt)
+            assert_w16(y, ref, f"INT{bits} N=8200 M={m} split={split} {dt}")
+
+
+@pytest.mark.parametrize("bits", [5, 6])
 @pytest.mark.parametrize("m", [5, 8, 16, 17, 32, 33, 48, 64])
 def test_wn_a16_matrix_core_runtime_m_and_tails(dev, bits, m):
     """Rows padded to 16 and masked; N = 257 leaves a one-row tail block."""
