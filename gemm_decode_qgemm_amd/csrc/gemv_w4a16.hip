@@ -586,15 +586,11 @@ hipError_t launch_splitk_reduce(const float* partial, int split, int64_t mn, voi
   return hipGetLastError();
 }
 
-#ifndef QG_GEMV64_PF
-#define QG_GEMV64_PF 1
-#endif
-
 template <int M, int WAVES, bool DQ = false>
 static hipError_t launch_w4a16_t(const void* x, const void* packed, int n, int k, void* y,
                                  int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  if (QG_GEMV64_PF && rbs * split <= kCUs)
+  if (rbs * split <= kCUs)
     hipLaunchKernelGGL((w4a16_gemv_kernel<M, WAVES, true, DQ>), dim3(rbs, split), dim3(WAVES * 64), 0,
                        stream, static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed),
                        n, k, y, y_f32, partial, split);

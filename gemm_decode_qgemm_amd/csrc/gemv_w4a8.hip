@@ -29,6 +29,7 @@
 //    the lane holding it (DPP row_newbcast), accumulating in int32; the zero
 //    point comes off as zp * (group sum of xq), also broadcast by DPP.
 #include "qg_common.h"
+#include "dispatch.h"
 #include "w4_common.h"
 
 namespace qg {
@@ -543,8 +544,13 @@ __device__ __forceinline__ float absmax8(const u32x4_t& v, float a) {
   return a;
 }
 
-template <int M, bool GS, bool DQ = false>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void w4a8_gemv_mx4_kernel(
+// R64: one 64-row block per workgroup (lane = row; each lane loads both group
+// pairs of its row and takes the half tile's 4 groups in turn), one workgroup
+// per CU, so 128 VGPRs and two register sets used in turn: the next half
+// tile's loads are in flight while the current one is computed (the grids it
+// is used on are in dispatch.h, gemv_shape).
+template <int M, bool GS, bool DQ = false, bool R64 = false>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(R64 ? 4 : 8))) void w4a8_gemv_mx4_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, int n, int k,
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split) {
   constexpr int WAVES = 16;
@@ -555,15 +561,16 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
   __shared__ float amax_w[WAVES][M];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int lg = lane >> 5;
+  const int lg = R64 ? 0 : lane >> 5;              // group pair (R64: both, in turn)
   const int xrow = (lane & 3) < M ? (lane & 3) : M - 1;   // A row of this lane
   const int wave = wave_id_uniform();
-  const int rb = blockIdx.x >> 1;
-  const int row = 32 * (blockIdx.x & 1) + (lane & 31);
+  const int rb = R64 ? blockIdx.x : blockIdx.x >> 1;
+  const int row = R64 ? lane : 32 * (blockIdx.x & 1) + (lane & 31);
   const int kt_count = k >> 8;
   int t0, t1;
   split_range(kt_count, split, blockIdx.y, t0, t1);
   using L = W4Layout<DQ>;
+  constexpr int NP = R64 ? 2 : 1;   // group pairs per lane
   float step;
   const uint8_t* tiles = L::tiles(packed, rb, kt_count, row, step);
   // Quantizing lanes: l < 16 M takes k = 8 (l % 16) .. + 8 of x row l / 16.
@@ -574,7 +581,16 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
 
   int hs = 2 * t0 + wave;
   const int h_end = 2 * t1;
-  Half32Regs r;
+  Half32Regs r[NP];
+  auto load_w = [&](Half32Regs (&rr)[NP], int h) {   // tile h/2, half h%2
+#pragma unroll
+    for (int p = 0; p < NP; ++p) L::load(rr[p], tiles + (size_t)(h >> 1) * L::kTile, h & 1, lg + p, row);
+  };
+  auto load_x = [&](int h) {
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (qlane) v = *reinterpret_cast<const u32x4_t*>(xsrc + (size_t)h * 128);
+    return v;
+  };
   float inv_q = 0.0f, sx_row[M];
   if constexpr (!GS) {
     // Per-row absmax over the whole row (the workgroup reads x once from L2).
@@ -591,8 +607,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
     // Unconditional (a branch here makes the compiler wait for these loads
     // with the x loads): a wave without a half tile loads the range's last
     // one, which another wave reads as well (an L2 hit), and discards it.
-    const int hf = hs < h_end ? hs : h_end - 1;
-    L::load(r, tiles + (size_t)(hf >> 1) * L::kTile, hf & 1, lg, row);
+    load_w(r, hs < h_end ? hs : h_end - 1);
     float am[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) am[m] = absmax8(v0[m], 0.0f);
@@ -625,7 +640,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
       if (m == qm) inv_q = inv_m;
     }
   } else {
-    if (hs < h_end) L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
+    if (hs < h_end) load_w(r, hs);
   }
 
   const uint32_t nib_s = __builtin_amdgcn_readfirstlane(0x0F0F0F0Fu);
@@ -636,10 +651,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 
-  for (bool first = true; hs < h_end; hs += WAVES, first = false) {   // tile hs/2, half hs%2
-    if (!first) L::load(r, tiles + (size_t)(hs >> 1) * L::kTile, hs & 1, lg, row);
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (qlane) v = *reinterpret_cast<const u32x4_t*>(xsrc + (size_t)hs * 128);
+  auto compute = [&](const Half32Regs (&rr)[NP], const u32x4_t& v) {
     // ---- quantize this lane's segment; the quad holds one group of 32.
     float inv = inv_q, sxv = 0.0f;
     if constexpr (GS) {
@@ -676,8 +688,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
 #pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
-      const int g = 2 * lg + jj;                   // group within the half tile
+      const int g = 2 * (lg + p) + jj;             // group within the half tile
+      const Half32Regs& r = rr[p];
       const uint8_t* xp = slot + xrow * kA8XRowBytes + 32 * g;
       const u32x4_t xa0 = *reinterpret_cast<const u32x4_t*>(xp);
       const u32x4_t xa1 = *reinterpret_cast<const u32x4_t*>(xp + 16);
@@ -702,20 +717,46 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
         acc[m] = __builtin_fmaf(scale, (float)ig, acc[m]);
       }
     }
+  };
+
+  if constexpr (!R64) {
+    for (bool first = true; hs < h_end; hs += WAVES, first = false) {
+      if (!first) load_w(r, hs);
+      compute(r, load_x(hs));
+    }
+  } else if (hs < h_end) {                         // uniform; r holds half tile hs
+    Half32Regs r2[NP];
+    u32x4_t va = load_x(hs), vb;
+    __builtin_amdgcn_sched_barrier(0);
+    while (true) {
+      if (hs + WAVES >= h_end) { compute(r, va); break; }
+      load_w(r2, hs + WAVES);
+      vb = load_x(hs + WAVES);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(r, va);
+      hs += WAVES;
+      if (hs + WAVES >= h_end) { compute(r2, vb); break; }
+      load_w(r, hs + WAVES);
+      va = load_x(hs + WAVES);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(r2, vb);
+      hs += WAVES;
+    }
   }
 
 #pragma unroll
   for (int m = 0; m < M; ++m) red[(wave * M + m) * 64 + lane] = acc[m];
   __syncthreads();
   const int t = threadIdx.x;
-  if (t < 32 * M) {
-    const int m = t >> 5, l = t & 31;
+  constexpr int RW = R64 ? 64 : 32;   // output rows of the workgroup
+  if (t < RW * M) {
+    const int m = t / RW, l = t % RW;
     float v = 0.0f;
     for (int w = 0; w < WAVES; ++w) {
       v += red[(w * M + m) * 64 + l];
-      v += red[(w * M + m) * 64 + l + 32];
+      if constexpr (!R64) v += red[(w * M + m) * 64 + l + 32];
     }
-    const int col = rb * kTileRows + 32 * (blockIdx.x & 1) + l;
+    const int col = R64 ? rb * kTileRows + l : rb * kTileRows + 32 * (blockIdx.x & 1) + l;
     if (col < n) {
       if constexpr (!GS) v *= sx_row[m];
       if (partial != nullptr)
@@ -732,9 +773,14 @@ template <int M, bool GS, bool DQ = false>
 static hipError_t launch_w4a8_mx4_t(const void* x, const void* packed, int n, int k, void* y,
                                     int y_f32, float* partial, int split, hipStream_t stream) {
   const int rbs = (n + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL((w4a8_gemv_mx4_kernel<M, GS, DQ>), dim3(2 * rbs, split), dim3(1024), 0, stream,
-                     static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed), n, k,
-                     y, y_f32, partial, split);
+  if (gemv_shape(M, n, split).rows == 64)
+    hipLaunchKernelGGL((w4a8_gemv_mx4_kernel<M, GS, DQ, true>), dim3(rbs, split), dim3(1024), 0, stream,
+                       static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed), n, k,
+                       y, y_f32, partial, split);
+  else
+    hipLaunchKernelGGL((w4a8_gemv_mx4_kernel<M, GS, DQ>), dim3(2 * rbs, split), dim3(1024), 0, stream,
+                       static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(packed), n, k,
+                       y, y_f32, partial, split);
   return hipGetLastError();
 }
 

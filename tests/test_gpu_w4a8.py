@@ -84,8 +84,9 @@ def test_w4a8_small_shapes(dev, n, k, m):
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4])
 def test_w4a8_both_workgroup_shapes_ragged_n(dev, m):
-    """N = 8200: the 64-row kernel (one split, M <= 2) and the 32-row kernel
-    (otherwise), each with an 8-row tail, against the W4A8 oracle."""
+    """N = 8200: 64-row workgroups with one split (M = 1 the v_dot4c GEMV,
+    M = 2..4 the matrix-instruction one) and 32-row ones with two, each with
+    an 8-row tail, against the W4A8 oracle."""
     n, k = 8200, 512
     w, codes, scales, zeros = _weight(n, k, 45)
     packed = qg.quantize_int4_g32(w.to(dev))
