@@ -98,6 +98,23 @@ def test_w4a8_both_workgroup_shapes_ragged_n(dev, m):
         assert_w4a8_class(y, r16, f"N=8200 M={m} split={split}")
 
 
+@pytest.mark.parametrize("entry", ["qgemm_w4a8", "qgemm_w4a8_g32", "qgemm_w4a8_dq", "qgemm_w4a8_g32_dq"])
+def test_w4a8_64_row_workgroups_non_finite_weight_row(dev, entry):
+    """8448 rows at M = 2 and 4 with one split (64-row matrix-instruction
+    workgroups on both layouts and scale kinds): a non-finite weight in row
+    8400 of the last block makes only column 8400 of y NaN, in every row."""
+    n, k = 8448, 256
+    w = si.int4_weight(n, k, 8).clone()
+    w[8400, 3] = float("-inf")
+    dq = entry.endswith("_dq")
+    packed = (qg.quantize_int4_g32_dq if dq else qg.quantize_int4_g32)(w.to(dev))
+    fn = getattr(qg, entry)
+    for m in (2, 4):
+        y = fn(si.activation(m, k, 9 + m).to(dev), packed, n, split_k=1, out_dtype=torch.float32).cpu()
+        assert torch.isnan(y[:, 8400]).all(), f"{entry} M={m}"
+        assert torch.isfinite(torch.cat([y[:, :8400], y[:, 8401:]], dim=1)).all(), f"{entry} M={m}"
+
+
 def test_w4a8_every_split(dev):
     n, k = 320, 6656
     w, codes, scales, zeros = _weight(n, k, 12)
