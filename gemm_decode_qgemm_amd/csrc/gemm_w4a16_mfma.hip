@@ -39,10 +39,6 @@
 namespace qg {
 
 
-#ifndef QG_MFMA_SCHED_BARRIER
-#define QG_MFMA_SCHED_BARRIER 1
-#endif
-
 // (row r, register j) -> (row j, register r) over the wave's four 16-lane rows:
 // v_permlane32_swap exchanges the upper 32 lanes of its first operand with the
 // lower 32 of its second, v_permlane16_swap the odd 16-lane rows of the first
@@ -262,7 +258,7 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
       }
       // keep each group's MFMA results from being hoisted into the next group
       // (their registers would all be live at once)
-      if constexpr (QG_MFMA_SCHED_BARRIER) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -588,13 +584,6 @@ static hipError_t launch_mfma_t(const void* x, int m, const void* packed, int n,
   return hipGetLastError();
 }
 
-#ifndef QG_MFMA_KW1
-#define QG_MFMA_KW1 4
-#endif
-#ifndef QG_MFMA_PIPE1
-#define QG_MFMA_PIPE1 1
-#endif
-
 // Register form, up to 16 rows: one m-tile per wave, 4 waves along K,
 // pipelined with activation prefetch (measured on MI355X at 39936 x 6656,
 // 8448 x 6656 and 6656 x 19968).  The same template with 2 m-tiles per wave
@@ -623,7 +612,7 @@ static hipError_t launch_w4a16_mfma_rs(int m, const void* x, const void* packed,
       default: return hipErrorInvalidValue;
     }
   }
-  QG_MF(1, QG_MFMA_KW1, 1, QG_MFMA_PIPE1 != 0, true);
+  QG_MF(1, 4, 1, true, true);
 #undef QG_MF
 }
 
@@ -656,7 +645,7 @@ static hipError_t launch_wn_mfma_t(int m, const void* x, const void* packed, int
     }
   }
 #undef QG_MF2
-  return launch_mfma_t<1, QG_MFMA_KW1, 1, QG_MFMA_PIPE1 != 0, true, HB, DQ, RS, AS>(
+  return launch_mfma_t<1, 4, 1, true, true, HB, DQ, RS, AS>(
       x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale, act_scale);
 }
 

@@ -65,11 +65,6 @@ __device__ __forceinline__ void load_xhalf(XHalf<M>& xr, const uint32_t* x32, in
 // product without it and are exact with one or more.
 #define QG_DPP_DOT(acc, xr, pr, L) \
   "v_dot2c_f32_bf16_dpp " acc ", " xr ", " pr " row_newbcast:" #L " row_mask:0xf bank_mask:0xf\n\t"
-#ifndef QG_DOT_TAIL_NOP
-#define QG_DOT_TAIL_NOP 2
-#endif
-#define QG_STR2(x) #x
-#define QG_STR(x) QG_STR2(x)
 #define QG_DOT16(L0, L1, L2, L3)                                                              \
   "s_nop 1\n\t"                                                                              \
   QG_DPP_DOT("%0", "%2", "%6", L0) QG_DPP_DOT("%1", "%3", "%7", L0)                          \
@@ -80,7 +75,7 @@ __device__ __forceinline__ void load_xhalf(XHalf<M>& xr, const uint32_t* x32, in
   QG_DPP_DOT("%0", "%4", "%16", L2) QG_DPP_DOT("%1", "%5", "%17", L2)                        \
   QG_DPP_DOT("%0", "%2", "%18", L3) QG_DPP_DOT("%1", "%3", "%19", L3)                        \
   QG_DPP_DOT("%0", "%4", "%20", L3) QG_DPP_DOT("%1", "%5", "%21", L3)                        \
-  "s_nop " QG_STR(QG_DOT_TAIL_NOP) "\n\t"
+  "s_nop 2\n\t"
 #define QG_DOT16_OPERANDS                                                                    \
   : "+v"(d0), "+v"(d1)                                                                       \
   : "v"(xv.x), "v"(xv.y), "v"(xv.z), "v"(xv.w), "v"(pr[0]), "v"(pr[1]), "v"(pr[2]),          \
@@ -273,7 +268,7 @@ __global__ __launch_bounds__(WAVES * 64) void w4a16_gemv_kernel(
   QG_DPP_DOT("%0", "%2", "%14", L5) QG_DPP_DOT("%1", "%3", "%15", L5)                      \
   QG_DPP_DOT("%0", "%2", "%16", L6) QG_DPP_DOT("%1", "%3", "%17", L6)                      \
   QG_DPP_DOT("%0", "%2", "%18", L7) QG_DPP_DOT("%1", "%3", "%19", L7)                      \
-  "s_nop " QG_STR(QG_DOT_TAIL_NOP) "\n\t"
+  "s_nop 2\n\t"
 #define QG_DOT16_2R_OPERANDS                                                               \
   : "+v"(d0), "+v"(d1)                                                                     \
   : "v"(xv.x), "v"(xv.y), "v"(pr[0]), "v"(pr[1]), "v"(pr[2]), "v"(pr[3]), "v"(pr[4]),      \
