@@ -90,12 +90,14 @@ __global__ __launch_bounds__(kW8MaxWaves * 64) void w8a16_gemv_kernel(
       }
     }
   };
-  // At M = 1 the first rows' weight loads go out before the x loads, so the
+  // At M <= 2 the first rows' weight loads go out before the x loads, so the
   // wait for x overlaps their HBM latency instead of preceding it (8192 x 8192:
-  // 12.47 us against 12.78).  With more activation rows the weights held
-  // across the x loads and their sums cost registers, and time (M = 4:
-  // 18.6 us against 17.3), so there x comes first.
-  if constexpr (M == 1) load_rows(0);
+  // M = 1 12.47 us against 12.78, M = 2 13.54 against 13.92).  With more
+  // activation rows the weights held across the x loads and their sums cost
+  // registers, and time (M = 3: 15.85 against 15.05, M = 4: 17.8 against
+  // 16.8; all 8 rows of the block in flight at once was slower still), so
+  // there x comes first.
+  if constexpr (M <= 2) load_rows(0);
 
   // x of this lane's chunks as bf16 pairs, and 128 * (their sum).
   uint32_t xr[M][CPW][8];
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(kW8MaxWaves * 64) void w8a16_gemv_kernel(
 
   const uint32_t sel_hi = __builtin_amdgcn_readfirstlane(0x07060302u);  // upper halves of (S1, S0)
   for (int r0 = 0; r0 < ROWS; r0 += RB) {
-    if (M > 1 || r0 > 0) load_rows(r0);
+    if (M > 2 || r0 > 0) load_rows(r0);
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
       float acc[M];
