@@ -184,6 +184,23 @@ def test_w4a16_both_workgroup_shapes_ragged_n(dev, m):
             assert_w16(y, ref, f"N=8200 M={m} split={split} {dt}")
 
 
+@pytest.mark.parametrize("n", [8193, 10240, 10241])
+def test_w4a16_matrix_instruction_gemv_row_form_edges(dev, n):
+    """M = 2..4, one split, at the edges of the 64-row form: N = 8193 (257
+    32-row blocks, the first N that takes 64-row workgroups, 129 of them, the
+    last with one live row), N = 10240 (160 blocks of 64, the last N that
+    does) and N = 10241 (back to 32-row workgroups)."""
+    k = 256
+    w, codes, scales, zeros = _weight(n, k, 90 + n)
+    packed = _gpu_packed(w, dev)
+    for m in (2, 3, 4):
+        x = si.activation(m, k, 95 + m)
+        ref = _ref(x, codes, scales, zeros)
+        print(f"qgemm_w4a16 row-form edge N={n} M={m}", flush=True)
+        y = qg.qgemm_w4a16(x.to(dev), packed, n, split_k=1, out_dtype=torch.float32)
+        assert_w16(y, ref, f"N={n} M={m}")
+
+
 @pytest.mark.parametrize("m", [2, 4])
 def test_w4a16_64_row_workgroups_non_finite_row(dev, m):
     """8448 rows at M = 2..4 and one split (64-row matrix-instruction

@@ -98,6 +98,24 @@ def test_w4a8_both_workgroup_shapes_ragged_n(dev, m):
         assert_w4a8_class(y, r16, f"N=8200 M={m} split={split}")
 
 
+@pytest.mark.parametrize("n", [8193, 10240, 10241])
+def test_w4a8_matrix_instruction_gemv_row_form_edges(dev, n):
+    """M = 2..4, one split, per-row and per-group scales, at the edges of the
+    64-row form (N = 8193 and 10240 take it, 10241 does not)."""
+    k = 256
+    w, codes, scales, zeros = _weight(n, k, 91 + n)
+    packed = qg.quantize_int4_g32(w.to(dev))
+    t = oracle.hardware_threads()
+    for m in (2, 3, 4):
+        x = si.activation(m, k, 97 + m)
+        xb = si.bf16_bits(x)
+        print(f"qgemm_w4a8 row-form edge N={n} M={m}", flush=True)
+        y = qg.qgemm_w4a8(x.to(dev), packed, n, split_k=1, out_dtype=torch.float32)
+        assert_w16(y, oracle.qgemm_w4a8(xb, codes, scales, zeros, threads=t), f"per row N={n} M={m}")
+        y = qg.qgemm_w4a8_g32(x.to(dev), packed, n, split_k=1, out_dtype=torch.float32)
+        assert_w16(y, oracle.qgemm_w4a8_g32(xb, codes, scales, zeros, threads=t), f"per group N={n} M={m}")
+
+
 @pytest.mark.parametrize("entry", ["qgemm_w4a8", "qgemm_w4a8_g32", "qgemm_w4a8_dq", "qgemm_w4a8_g32_dq"])
 def test_w4a8_64_row_workgroups_non_finite_weight_row(dev, entry):
     """8448 rows at M = 2 and 4 with one split (64-row matrix-instruction
