@@ -94,11 +94,11 @@ static float clampf(float v, float lo, float hi) {
 /* ------------------------------------------------------------------ */
 /* INT4 group-32 asymmetric min-max quantizer.                         */
 /* [P1] `_packed_with_dense`: QuantConfig(bits=4, group_size=32,        */
-/* symmetric=False, method="min_max").  The pages print no formula; the */
-/* reading (range widened to hold 0, 15 steps, fp16 scale rounded up so */
-/* every dequantized value is within half a step, integer zero point,   */
-/* round-half-even, round then add the zero point) is recorded in the   */
-/* design notes.                                                        */
+/* symmetric=False, method="min_max").  The pages print no formula;    */
+/* this is the plainest reading of those settings: range widened to     */
+/* hold 0, 15 steps, fp16 scale rounded up so every dequantized value   */
+/* is within half a step, integer zero point, round-half-even, round    */
+/* then add the zero point.                                             */
 /* ------------------------------------------------------------------ */
 /* One group of 32 with `levels` steps (15 for INT4, 31 for INT5, 63 for
  * INT6): the same reading with 2^bits - 1 in place of 15. */
@@ -510,9 +510,9 @@ void orc_qgemm_w4a8_g32(const uint16_t *x, int64_t m, int64_t k,
 /* `_packed_with_dense` (`scale` uint8 codes, `scale_step` fp16 per     */
 /* row; legality rules "scale codes must be uint8", "scale_step must be */
 /* float16", step shape [N, 1]).  A group's scale is code x row step.   */
-/* Reading recorded in the design notes: the row step is the smallest   */
-/* fp16 with 255 x 15 x step >= the row's largest group range, a        */
-/* group's code the smallest c in 1..255 with 15 x c x step >= its      */
+/* Where the pages are silent, the reading taken: the row step is the   */
+/* smallest fp16 with 255 x 15 x step >= the row's largest group range, */
+/* a group's code the smallest c in 1..255 with 15 x c x step >= its    */
 /* range, so every group still spans its range in 15 steps; zero points */
 /* stay integers 0..15 (zero_point_step 1); then the codes exactly as   */
 /* in orc_quantize_group32, with the scale c x step.                    */
