@@ -337,7 +337,10 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
 // waves (wave w: n-tile w % 4, m-tiles MT (w / 4) .. + MT) and streams x
 // through LDS one 256-k tile at a time, shared by all its waves; a wave keeps
 // its MT m-tiles of its n-tile in registers, so a weight operand is expanded
-// once for MT products (and by MG waves).  The zero point rides in a
+// once for MT products (and by MG waves).  The launchers take MG = 1 (all
+// m-tiles of a row block in one wave: the decode is the largest share of a
+// wave's issue time, so it is spread over as many products as possible).
+// The zero point rides in a
 // second MFMA per product whose B operand is -(128 + zp) in every slot (an
 // exact bf16), so each group ends with one FMA per output: y += s * D.
 //
@@ -414,6 +417,12 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
     const uint32_t row = (uint32_t)(16 * t + i);
     w.c0 = v.b128<true>(r0 * 16u);
     w.c1 = v.b128<true>(r1 * 16u);
+    if constexpr (HB == 0) {
+      // unused, but set: left undefined, the copies between the two register
+      // sets kept a stack slot that the compiler moved into LDS
+      w.h0 = u32x2_t{0u, 0u};
+      w.h1 = u32x2_t{0u, 0u};
+    }
     if constexpr (HB == 1) {
       w.h0.x = v.b32<true>(8192u + r0 * 4u);
       w.h1.x = v.b32<true>(8192u + r1 * 4u);
@@ -589,7 +598,7 @@ static hipError_t launch_mfma_t(const void* x, int m, const void* packed, int n,
 // 8448 x 6656 and 6656 x 19968).  The same template with 2 m-tiles per wave
 // or wave groups along M ran 32..64 rows before the LDS-staged form, which
 // is faster there (39936 x 6656: 32 rows 57.4 us against 52.7, 64 rows 115.5
-// against 91.9).
+// against 91.9 in the LDS form's 2 x 2 mapping of then, 87.5 in its 4 x 1).
 template <bool RS>
 static hipError_t launch_w4a16_mfma_rs(int m, const void* x, const void* packed, int n, int k, void* y,
                                       int y_f32, float* partial, int split, hipStream_t stream,
@@ -597,18 +606,18 @@ static hipError_t launch_w4a16_mfma_rs(int m, const void* x, const void* packed,
 #define QG_MF(MT, KW, MG, PIPE, PFX) \
   return launch_mfma_t<MT, KW, MG, PIPE, PFX, 0, false, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale)
   if (mfma_lds_form(m)) {
-    // (m-tiles per wave, waves per n-tile): 64 rows as 2 x 2 (94 VGPRs, 4 waves
-    // per SIMD) beat 4 x 1 (150 VGPRs, 2 per SIMD) everywhere measured
-    // (39936 x 6656: 91.9 us against 99.1; 8448 x 6656: 32.4 against 41.3);
-    // 48 rows as 1 x 3, except on the largest layers, where 3 x 1 wins
-    // (39936 x 6656: 83.3 us against 94.6; 8448 x 6656: 36.4 against 31.8).
+    // (m-tiles per wave, waves per n-tile): every m-tile in one wave, so that
+    // each wave's weight decode serves them all.  Measured on MI355X against
+    // the forms with wave groups along M (us; 4 x 1: 144 VGPRs, 2 waves per
+    // SIMD): 64 rows as 4 x 1 against 2 x 2 (and 1 x 4), 39936 x 6656 87.5
+    // against 95.7 (131.2), 8448 x 6656 31.4 against 32.9, 6656 x 19968 47.7
+    // against 52.2, 32768 x 8192 80.0 against 87.5; 48 rows as 3 x 1 against
+    // 1 x 3, 8448 x 6656 23.9 against 30.9, 6656 x 19968 40.2 against 52.0,
+    // 6656 x 4096 15.4 against 18.1.
     switch ((m + 15) / 16) {
       case 2: return launch_mfma2_t<2, 1, 0, false, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
-      case 3:
-        if (n >= 32768 && k >= 6144)
-          return launch_mfma2_t<3, 1, 0, false, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
-        return launch_mfma2_t<1, 3, 0, false, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
-      case 4: return launch_mfma2_t<2, 2, 0, false, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
+      case 3: return launch_mfma2_t<3, 1, 0, false, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
+      case 4: return launch_mfma2_t<4, 1, 0, false, RS>(x, m, packed, n, k, y, y_f32, partial, split, stream, row_scale);
       default: return hipErrorInvalidValue;
     }
   }
@@ -637,10 +646,8 @@ static hipError_t launch_wn_mfma_t(int m, const void* x, const void* packed, int
   if (mfma_lds_form(m)) {
     switch ((m + 15) / 16) {
       case 2: return QG_MF2(2, 1);
-      case 3:
-        if (n >= 32768 && k >= 6144) return QG_MF2(3, 1);
-        return QG_MF2(1, 3);
-      case 4: return QG_MF2(2, 2);
+      case 3: return QG_MF2(3, 1);
+      case 4: return QG_MF2(4, 1);
       default: return hipErrorInvalidValue;
     }
   }
