@@ -230,7 +230,7 @@ def test_one_hot_activations_exact(dev, entry, n):
 # ---------------------------------------------------------------- W8A16
 
 
-@pytest.mark.parametrize("n", [768, 8200])
+@pytest.mark.parametrize("n", [768, 8200, 16400])
 def test_w8a16_integer_activations_one_rounding(dev, n):
     torch.manual_seed(77 + n)
     w = torch.randint(-127, 128, (n, K), dtype=torch.int8)

@@ -93,9 +93,9 @@ def test_w8a16_shapes_and_tails(dev, n, k, m):
 
 @pytest.mark.parametrize("m", [17, 24, 32, 33])
 def test_w8a16_64_row_workgroups_on_tall_layers(dev, m):
-    """From 32768 rows, 17..32 activation rows take workgroups of 64 weight
-    rows (4 n-tiles); N = 32801 leaves a 33-row tail in the last workgroup
-    (and 33 activation rows stay on 32-row workgroups)."""
+    """From 16384 rows every M takes the LDS-staged form with workgroups of
+    64 weight rows (4 n-tiles); N = 32801 leaves a 33-row tail in the last
+    workgroup."""
     n, k = 32801, 256
     w, s, x = si.int8_layer(n=n, k=k, m=m, seed=700 + m)
     ref = _ref(x, w, s)
@@ -103,6 +103,22 @@ def test_w8a16_64_row_workgroups_on_tall_layers(dev, m):
     for dt in (torch.float32, torch.bfloat16):
         y = qg.qgemm_w8a16(x.to(dev), w.to(dev), s.to(dev), out_dtype=dt)
         assert_w16(y, ref, f"{n}x{k} M={m} {dt}")
+
+
+@pytest.mark.parametrize("n,m", [(16400, 5), (16400, 64), (4097, 40), (6000, 33), (300, 64), (4096, 49)])
+def test_w8a16_lds_form_tile_counts(dev, n, m):
+    """The LDS-staged form (4 n-tiles per workgroup from 16384 rows, 2 above
+    4096, 1 below; above 32 activation rows on smaller layers) on 1..7 tiles
+    of 256 k, so its three-way unrolled tile loop leaves at every point, with
+    ragged N (16400 = 256 * 64 + 16, 4097, 300) and ragged M."""
+    for tiles in range(1, 8):
+        k = 256 * tiles
+        w, s, x = si.int8_layer(n=n, k=k, m=m, seed=900 + n + m + tiles)
+        ref = _ref(x, w, s)
+        label = f"qgemm_w8a16 {n}x{k} M={m}"
+        print(label, flush=True)
+        y = qg.qgemm_w8a16(x.to(dev), w.to(dev), s.to(dev), out_dtype=torch.float32)
+        assert_w16(y, ref, label)
 
 
 def test_w8a16_quantized_weight_round_trip(dev):
