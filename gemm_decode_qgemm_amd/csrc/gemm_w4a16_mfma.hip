@@ -347,7 +347,8 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
 // Pipeline: while tile kt is computed, tile kt+1's activations are copied
 // into the other LDS buffer by global_load_lds_dwordx4 (no VGPRs) and its
 // codes and metadata are loaded into the other register set; one barrier per
-// tile.  LDS layout: 16-byte piece c of x row r (k = 8c .. 8c+8 of the tile)
+// tile.  From 48 rows a single x buffer (copied between two barriers) leaves
+// room for more workgroups per CU, which overlap each other's copies.  LDS layout: 16-byte piece c of x row r (k = 8c .. 8c+8 of the tile)
 // sits at piece index 32 r + (c ^ (r & 15)), so the A-operand read of lanes
 // (i, a) = (lane % 16, lane / 16) -- row 16 mt + i, piece 4 g + a -- hits 16
 // distinct bank quads in any 16 consecutive lanes; the swizzle is applied on
@@ -368,8 +369,16 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
     void* __restrict__ y, int y_f32, float* __restrict__ partial, int split,
     const float* __restrict__ row_scale, const float* __restrict__ act_scale) {
   constexpr int MR = 16 * MT * MG;                 // staged x rows
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][MR * 512];
-  __shared__ __attribute__((aligned(16))) float sxs[AS ? 2 : 1][AS ? 8 * 64 : 4];
+  // x buffers: two (the next tile copied while this one computes) up to 32
+  // rows; one from 48 rows, where a second 24-32 KB buffer would leave room
+  // for only 2 workgroups per CU while the registers allow 3-4: the other
+  // workgroups of the CU then fill each one's copy time (measured on MI355X,
+  // us, one / two buffers: 64 rows 39936 x 6656 83.1 / 90.9, 8448 x 6656
+  // 29.5 / 31.9, per-group W4A8 39936 x 6656 97.8 / 112.6; 48 rows 39936 x
+  // 6656 66.8 / 71.5).
+  constexpr int NB = MT >= 3 ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[NB][MR * 512];
+  __shared__ __attribute__((aligned(16))) float sxs[AS ? NB : 1][AS ? 8 * 64 : 4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int i = lane & 15, a = lane >> 4;
@@ -535,13 +544,26 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
     for (int kt = t0; kt < t1; ++kt) {
       Mfma2W<HB> nxt = cur;
       const bool more = kt + 1 < t1;            // uniform
-      if (more) {
-        stage(kt + 1, (kt + 1 - t0) & 1);
-        load_w(nxt, kt + 1);
+      if constexpr (NB == 2) {
+        if (more) {
+          stage(kt + 1, (kt + 1 - t0) & 1);
+          load_w(nxt, kt + 1);
+        }
+        compute(cur, (kt - t0) & 1);
+        cur = nxt;
+        if (more) sync();
+      } else {
+        // one buffer: the codes still go a tile ahead; x is copied once
+        // every wave is done with the tile before
+        if (more) load_w(nxt, kt + 1);
+        compute(cur, 0);
+        cur = nxt;
+        if (more) {
+          __syncthreads();
+          stage(kt + 1, 0);
+          sync();
+        }
       }
-      compute(cur, (kt - t0) & 1);
-      cur = nxt;
-      if (more) sync();
     }
   }
 
