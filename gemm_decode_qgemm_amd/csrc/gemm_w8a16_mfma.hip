@@ -201,6 +201,14 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
+// A barrier that leaves vector-memory loads in flight: this wave's LDS reads
+// are complete first (lgkmcnt 0; vmcnt 63 and expcnt 7 mean no wait), so no
+// other wave's copy into the buffer they read can overtake them.
+__device__ __forceinline__ void barrier_keep_loads() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // LDS-staged form: a workgroup of 4 waves owns NT n-tiles (16 NT weight rows)
 // and all M rows, and streams x through LDS one 256-k tile at a time (copied
@@ -305,11 +313,12 @@ __global__ __launch_bounds__(256) void w8a16_mfma2_kernel(
   // Weights two tiles ahead, activations one.  Loads complete in issue order,
   // so before the barrier that hands over x tile kt + 1 a wave waits until
   // only its weight loads of tile kt + 2 are outstanding.  The barrier is a
-  // bare s_barrier: a fenced one would wait for those loads too.  Three
-  // register sets take turns (the loop is unrolled three times), so no
-  // register holding a load in flight is ever copied.  A tile's loads are
-  // issued after its first k-step: the compiler's own waits at the loop
-  // head (it cannot prove the weights there have landed) then cost nothing.
+  // bare s_barrier after this wave's LDS reads: a fenced one would wait for
+  // those loads too.  Three register sets take turns (the loop is unrolled
+  // three times), so no register holding a load in flight is ever copied.
+  // A tile's loads are issued after its first k-step: the compiler's own
+  // waits at the loop head (it cannot prove the weights there have landed)
+  // then cost nothing.
   // One tile; returns whether another follows (the loop leaves exactly on
   // the path that skips the wait, so no path into the next step carries a
   // load the wait did not cover).
@@ -325,7 +334,7 @@ __global__ __launch_bounds__(256) void w8a16_mfma2_kernel(
       wait_vm<QW>();
     else
       wait_vm<0>();
-    asm volatile("s_barrier" ::: "memory");
+    barrier_keep_loads();
     return true;
   };
   {
@@ -338,7 +347,7 @@ __global__ __launch_bounds__(256) void w8a16_mfma2_kernel(
     } else {
       wait_vm<0>();
     }
-    asm volatile("s_barrier" ::: "memory");
+    barrier_keep_loads();
     for (int kt = 0;; kt += 3) {
       if (!step(kt, wa, wc)) break;
       if (!step(kt + 1, wb, wa)) break;
