@@ -347,7 +347,7 @@ __global__ __launch_bounds__(KW * MG * 64) void w4a16_mfma_kernel(
 // Pipeline: while tile kt is computed, tile kt+1's activations are copied
 // into the other LDS buffer by global_load_lds_dwordx4 (no VGPRs) and its
 // codes and metadata are loaded into the other register set; one barrier per
-// tile.  From 48 rows a single x buffer (copied between two barriers) leaves
+// tile.  From 33 rows a single x buffer (copied between two barriers) leaves
 // room for more workgroups per CU, which overlap each other's copies.  LDS layout: 16-byte piece c of x row r (k = 8c .. 8c+8 of the tile)
 // sits at piece index 32 r + (c ^ (r & 15)), so the A-operand read of lanes
 // (i, a) = (lane % 16, lane / 16) -- row 16 mt + i, piece 4 g + a -- hits 16
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
     const float* __restrict__ row_scale, const float* __restrict__ act_scale) {
   constexpr int MR = 16 * MT * MG;                 // staged x rows
   // x buffers: two (the next tile copied while this one computes) up to 32
-  // rows; one from 48 rows, where a second 24-32 KB buffer would leave room
+  // rows; one from 33 rows, where a second 24-32 KB buffer would leave room
   // for only 2 workgroups per CU while the registers allow 3-4: the other
   // workgroups of the CU then fill each one's copy time (measured on MI355X,
   // us, one / two buffers: 64 rows 39936 x 6656 83.1 / 90.9, 8448 x 6656

@@ -112,10 +112,30 @@ def test_m_above_64_is_rejected(dev):
     assert e.value.status == -4
 
 
+@pytest.mark.parametrize("m", [32, 33, 64])
+@pytest.mark.parametrize("k", [256, 512, 768])
+def test_mfma_lds_form_short_k_every_split(dev, k, m):
+    """The LDS-staged form on 1..3 tiles of 256 k at every legal split, so a
+    workgroup's range can be a single tile: the two-buffer pipeline (32 rows)
+    and the one-buffer one (33 and 64 rows) at their first and last tile,
+    with N = 200 (an 8-row tail past the 64-row blocks)."""
+    n = 200
+    w, codes, scales, zeros = _weight(n, k, 31 * k + m)
+    packed = qg.quantize_int4_g32(w.to(dev))
+    x = si.activation(m, k, 1300 + m + k)
+    ref = _ref(x, codes, scales, zeros)
+    xd = x.to(dev)
+    for split in [s for s in si.SPLITS if s <= k // 256]:
+        label = f"qgemm_w4a16 {n}x{k} M={m} split={split}"
+        print(label, flush=True)
+        y = qg.qgemm_w4a16(xd, packed, n, split_k=split, out_dtype=torch.float32)
+        assert_w16(y, ref, label)
+
+
 @pytest.mark.parametrize("m", [17, 24, 32, 33, 47, 48])
 @pytest.mark.parametrize("n,k", [(320, 6656), (257, 6144), (1100, 6400)])
 def test_mfma_lds_form_ragged(dev, n, k, m):
-    """The LDS-staged form (17..32 rows, and 33..48 rows with K >= 6144): runtime
+    """The LDS-staged form (17..64 rows; here 17..48, one x buffer from 33): runtime
     M inside a bucket, N tails (257, 1100), an odd tile count (K = 6400: 25
     tiles, uneven split ranges) and every legal split."""
     w, codes, scales, zeros = _weight(n, k, 7 * n + k)

@@ -153,9 +153,13 @@ def test_w8a16_argument_errors(dev):
     assert e.value.status == -3             # QG_E_K_MULTIPLE
 
 
+@pytest.mark.parametrize("n,k", [(4096, 8192), (6000, 4096), (16400, 2048)])
 @pytest.mark.parametrize("m", [1, 16, 64])
-def test_w8a16_repeat_and_graph_replay_are_bit_identical(dev, m):
-    w, s, x = si.int8_layer(n=4096, k=8192, m=m, seed=9)
+def test_w8a16_repeat_and_graph_replay_are_bit_identical(dev, n, k, m):
+    """Every form (GEMV, register form, LDS-staged form with 1, 2 and 4
+    n-tiles per workgroup): repeated calls and graph replays give the same
+    bits."""
+    w, s, x = si.int8_layer(n=n, k=k, m=m, seed=9)
     w, s, x = w.to(dev), s.to(dev), x.to(dev)
     eager = qg.qgemm_w8a16(x, w, s)
     assert torch.equal(eager, qg.qgemm_w8a16(x, w, s))
