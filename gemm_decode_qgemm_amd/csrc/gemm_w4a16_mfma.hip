@@ -401,9 +401,14 @@ __global__ __launch_bounds__(256 * MG) void w4a16_mfma2_kernel(
   // Copy x[:, 256 kt .. +256] into xs[buf]: wave t issues pieces 64u .. 64u+63
   // for u = t, t + 4, ...; rows at or past m repeat row m - 1 (their outputs
   // are never stored).
+  // (a fixed count per wave: with the bound on wv unknown to the compiler,
+  // a loop to MR / 2 kept a branch per copy and 14 more VGPRs at 64 rows)
+  constexpr int NJ = MR / 2 / (4 * MG);           // copies per wave and tile
+  static_assert(NJ * 4 * MG * 2 == MR, "every wave issues the same number of copies");
   auto stage = [&](int kt, int buf) {
 #pragma unroll
-    for (int u = wv; u < MR / 2; u += 4 * MG) {
+    for (int j = 0; j < NJ; ++j) {
+      const int u = wv + 4 * MG * j;
       const int r = 2 * u + (lane >> 5);
       const int c = (lane & 31) ^ (r & 15);
       const int src = r < m ? r : m - 1;
